@@ -1,0 +1,383 @@
+"""Oracle model: GPT-2 forward and hand-written backward in plain NumPy.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Readings of the pages adopted here (each is listed with its justification in
+the design notes of the repository):
+  * pre-LN residual block, x + attn(ln_1(x)) then x + mlp(ln_2(x)): the
+    printed Block.forward in [train-124M] §2.11 overwrites the residual; §2.13
+    says the residual connections are the ``+=`` additions, §7 counts two
+    residual additions per layer, and [repro-124M] calls the model Pre-Norm.
+  * c_proj is applied after the heads are concatenated ([train-124M] §2.4
+    lists c_attn and c_proj inside attn; the §2.12 listing omits it).
+  * causal mask: key s is visible to query t iff s <= t ([train-124M] §5,
+    ``is_causal=True``).
+  * lm_head has no bias and shares its weight with wte ([train-124M] §4).
+  * the softmax of the loss runs over every padded vocabulary column
+    ([train-124M] §8.3 pads 50257 -> 50304; the logits are (B, T, vocab_size)).
+  * GELU is the tanh approximation ([train-124M] §2.13); LayerNorm uses
+    eps = 1e-5 with the biased variance (nn.LayerNorm defaults, §2.3).
+  * targets equal to -1 are ignored and the mean divides by the number of
+    valid targets ([grad-accum] "Cross-entropy averages within one micro-batch"
+    divides by the targets of the call; the ignore index is the isolated
+    lm_head workload's convention).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+LN_EPS = 1e-5
+GELU_C = 0.044715
+
+
+@dataclass(frozen=True)
+class Config:
+    """Model hyper-parameters ([train-124M] §2.1 GPT2Config, §2.6 MLP width)."""
+
+    vocab_size: int
+    block_size: int
+    n_layer: int
+    n_head: int
+    n_embd: int
+    mlp_hidden: int
+
+    @property
+    def head_dim(self) -> int:
+        return self.n_embd // self.n_head
+
+
+def param_specs(cfg: Config):
+    """Parameter names and shapes, following the HF listing in [train-124M] §2.
+
+    Linear weights are stored [out, in] (nn.Linear, as in the page's own
+    modules, §2.4 and §2.6), so c_attn.weight is [3C, C].  lm_head is not a
+    separate tensor: it is wte ([train-124M] §4, weight tying).
+    """
+    V, T, C, F = cfg.vocab_size, cfg.block_size, cfg.n_embd, cfg.mlp_hidden
+    specs = [("transformer.wte.weight", (V, C)), ("transformer.wpe.weight", (T, C))]
+    for layer in range(cfg.n_layer):
+        p = f"transformer.h.{layer}."
+        specs += [
+            (p + "ln_1.weight", (C,)),
+            (p + "ln_1.bias", (C,)),
+            (p + "attn.c_attn.weight", (3 * C, C)),
+            (p + "attn.c_attn.bias", (3 * C,)),
+            (p + "attn.c_proj.weight", (C, C)),
+            (p + "attn.c_proj.bias", (C,)),
+            (p + "ln_2.weight", (C,)),
+            (p + "ln_2.bias", (C,)),
+            (p + "mlp.c_fc.weight", (F, C)),
+            (p + "mlp.c_fc.bias", (F,)),
+            (p + "mlp.c_proj.weight", (C, F)),
+            (p + "mlp.c_proj.bias", (C,)),
+        ]
+    specs += [("transformer.ln_f.weight", (C,)), ("transformer.ln_f.bias", (C,))]
+    return specs
+
+
+def n_params(cfg: Config) -> int:
+    return int(sum(np.prod(s) for _, s in param_specs(cfg)))
+
+
+def is_decayed(shape) -> bool:
+    """Weight decay applies to tensors with dim >= 2 only ([train-124M] §6,
+    configure_optimizers)."""
+    return len(shape) >= 2
+
+
+# ----------------------------------------------------------------------------
+# elementwise pieces
+# ----------------------------------------------------------------------------
+
+def gelu_tanh(u):
+    """GELU, tanh approximation ([train-124M] §2.13):
+    0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    k = float(np.sqrt(2.0 / np.pi))
+    return 0.5 * u * (1.0 + np.tanh(k * (u + GELU_C * u * u * u)))
+
+
+def gelu_tanh_grad(u):
+    """d/du of gelu_tanh, by the product and chain rules."""
+    k = float(np.sqrt(2.0 / np.pi))
+    inner = k * (u + GELU_C * u * u * u)
+    th = np.tanh(inner)
+    dinner = k * (1.0 + 3.0 * GELU_C * u * u)
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * dinner
+
+
+def layernorm_fwd(x, w, b, eps=LN_EPS):
+    """LayerNorm over the last axis ([train-124M] §2.3 nn.LayerNorm(n_embd)).
+
+    Returns y and the cache (xhat, rstd) the backward needs."""
+    mu = x.mean(axis=-1, keepdims=True)
+    xc = x - mu
+    var = (xc * xc).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = xc * rstd
+    return xhat * w + b, (xhat, rstd)
+
+
+def layernorm_bwd(dy, cache, w):
+    """Backward of layernorm_fwd.  dx = rstd (g - mean(g) - xhat mean(g xhat))
+    with g = dy * w; dw = sum over rows of dy xhat; db = sum over rows of dy."""
+    xhat, rstd = cache
+    rows = dy.reshape(-1, dy.shape[-1])
+    xh = xhat.reshape(-1, xhat.shape[-1])
+    dw = (rows * xh).sum(axis=0)
+    db = rows.sum(axis=0)
+    g = dy * w
+    dx = rstd * (g - g.mean(axis=-1, keepdims=True) - xhat * (g * xhat).mean(axis=-1, keepdims=True))
+    return dx, dw, db
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+
+def attention_fwd(q, k, v):
+    """Causal softmax attention for one (batch, head): q, k, v are [T, hd].
+
+    S = q k^T / sqrt(hd), S[t, s] = -inf for s > t, P = softmax over s,
+    o = P v ([train-124M] §2.12 and §5).  Returns o and P."""
+    T, hd = q.shape
+    s = (q @ k.T) / np.sqrt(hd)
+    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    s = np.where(mask, -np.inf, s)
+    smax = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - smax)
+    p = e / e.sum(axis=-1, keepdims=True)
+    return p @ v, p
+
+
+def attention_bwd(do, q, k, v, p):
+    """Backward of attention_fwd for one (batch, head).
+
+    dP = dO v^T, dv = P^T dO, dS = P (dP - rowsum(dP P)), dq = dS k / sqrt(hd),
+    dk = dS^T q / sqrt(hd)."""
+    hd = q.shape[1]
+    dp = do @ v.T
+    dv = p.T @ do
+    ds = p * (dp - (dp * p).sum(axis=-1, keepdims=True))
+    dq = (ds @ k) / np.sqrt(hd)
+    dk = (ds.T @ q) / np.sqrt(hd)
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# loss
+# ----------------------------------------------------------------------------
+
+def cross_entropy_fwd_bwd(logits, targets, n_valid, scale):
+    """Cross-entropy rows ([train-124M] §4): softmax, pick the target, -log.
+
+    Returns per-row losses (0 for ignored rows) and dlogits of
+    scale * (sum of valid row losses) / n_valid.  Rows with target -1 are
+    ignored."""
+    valid = targets >= 0
+    m = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    se = e.sum(axis=-1, keepdims=True)
+    lse = (m + np.log(se))[:, 0]
+    tsafe = np.where(valid, targets, 0)
+    zt = logits[np.arange(logits.shape[0]), tsafe]
+    row_loss = np.where(valid, lse - zt, 0.0).astype(logits.dtype)
+    prob = e / se
+    dlogits = prob
+    dlogits[np.arange(logits.shape[0]), tsafe] -= 1.0
+    dlogits *= np.where(valid, scale / max(n_valid, 1), 0.0).astype(logits.dtype)[:, None]
+    return row_loss, dlogits
+
+
+def lmhead_ce(hidden, weight, targets, chunk=1024):
+    """Tied lm_head + mean cross-entropy, forward and backward, for the
+    isolated lm_head workload: logits = hidden @ weight^T (no bias), loss =
+    mean over valid targets, dHidden and dWeight of that mean.
+
+    Rows are processed in chunks so the dense logits never exceed
+    chunk x V; the arithmetic is the dense definition.
+    Returns (loss, row_loss, dhidden, dweight)."""
+    M = hidden.shape[0]
+    n_valid = int((targets >= 0).sum())
+    dhidden = np.zeros_like(hidden)
+    dweight = np.zeros_like(weight)
+    row_loss = np.zeros(M, dtype=hidden.dtype)
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        logits = hidden[r0:r1] @ weight.T
+        rl, dl = cross_entropy_fwd_bwd(logits, targets[r0:r1], n_valid, 1.0)
+        row_loss[r0:r1] = rl
+        dhidden[r0:r1] = dl @ weight
+        dweight += dl.T @ hidden[r0:r1]
+    loss = row_loss.astype(np.float64).sum() / n_valid if n_valid > 0 else float("nan")
+    return loss, row_loss, dhidden, dweight
+
+
+# ----------------------------------------------------------------------------
+# model
+# ----------------------------------------------------------------------------
+
+def _split_heads(x, n_head):
+    B, T, C = x.shape
+    return x.reshape(B, T, n_head, C // n_head).transpose(0, 2, 1, 3)
+
+
+def _merge_heads(x):
+    B, H, T, hd = x.shape
+    return x.transpose(0, 2, 1, 3).reshape(B, T, H * hd)
+
+
+def forward(cfg: Config, params, idx, targets, scale=1.0, chunk=1024, want_logits=False, n_valid=None):
+    """Forward pass with every activation the backward needs.
+
+    idx, targets: int [B, T].  Position ids are 0..T-1 in every row
+    ([train-124M] §2.10).  Returns (loss, row_loss [B*T], cache)."""
+    B, T = idx.shape
+    H, L = cfg.n_head, cfg.n_layer
+    wte = params["transformer.wte.weight"]
+    wpe = params["transformer.wpe.weight"]
+    dt = wte.dtype
+    if idx.min() < 0 or idx.max() >= cfg.vocab_size:
+        raise ValueError("token id out of range")
+    if T > cfg.block_size:
+        raise ValueError("T exceeds block_size")
+
+    # token + position embedding ([train-124M] §2.2, §2.10)
+    h = wte[idx] + wpe[np.arange(T)][None, :, :]
+    cache = {"idx": idx, "targets": targets, "layers": []}
+    for layer in range(L):
+        p = f"transformer.h.{layer}."
+        lc = {"h_in": h}
+        a1, lc["ln1"] = layernorm_fwd(h, params[p + "ln_1.weight"], params[p + "ln_1.bias"])
+        lc["a1"] = a1
+        qkv = a1 @ params[p + "attn.c_attn.weight"].T + params[p + "attn.c_attn.bias"]
+        C = cfg.n_embd
+        q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+        qh, kh, vh = _split_heads(q, H), _split_heads(k, H), _split_heads(v, H)
+        oh = np.empty_like(qh)
+        ps = np.empty((B, H, T, T), dtype=dt)
+        for b in range(B):
+            for j in range(H):
+                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j], vh[b, j])
+        y = _merge_heads(oh)
+        lc.update(qh=qh, kh=kh, vh=vh, p=ps, y=y)
+        h = h + (y @ params[p + "attn.c_proj.weight"].T + params[p + "attn.c_proj.bias"])
+        lc["h_mid"] = h
+        a2, lc["ln2"] = layernorm_fwd(h, params[p + "ln_2.weight"], params[p + "ln_2.bias"])
+        lc["a2"] = a2
+        u = a2 @ params[p + "mlp.c_fc.weight"].T + params[p + "mlp.c_fc.bias"]
+        g = gelu_tanh(u)
+        lc.update(u=u, g=g)
+        h = h + (g @ params[p + "mlp.c_proj.weight"].T + params[p + "mlp.c_proj.bias"])
+        cache["layers"].append(lc)
+
+    z, cache["lnf"] = layernorm_fwd(h, params["transformer.ln_f.weight"], params["transformer.ln_f.bias"])
+    cache["z"] = z
+    zf = z.reshape(B * T, -1)
+    tf = targets.reshape(B * T)
+    if n_valid is None:
+        n_valid = int((tf >= 0).sum())
+    cache["n_valid"] = n_valid
+
+    # tied lm_head + cross-entropy in row chunks ([train-124M] §4)
+    row_loss = np.zeros(B * T, dtype=dt)
+    dz = np.zeros_like(zf)
+    dwte_head = np.zeros_like(wte)
+    logits_all = np.empty((B * T, wte.shape[0]), dtype=dt) if want_logits else None
+    for r0 in range(0, B * T, chunk):
+        r1 = min(B * T, r0 + chunk)
+        logits = zf[r0:r1] @ wte.T
+        if want_logits:
+            logits_all[r0:r1] = logits
+        rl, dl = cross_entropy_fwd_bwd(logits, tf[r0:r1], n_valid, scale)
+        row_loss[r0:r1] = rl
+        dz[r0:r1] = dl @ wte
+        dwte_head += dl.T @ zf[r0:r1]
+    cache["dz"] = dz.reshape(B, T, -1)
+    cache["dwte_head"] = dwte_head
+    cache["logits"] = logits_all
+    loss = row_loss.astype(np.float64).sum() / n_valid if n_valid > 0 else float("nan")
+    return loss, row_loss, cache
+
+
+def backward(cfg: Config, params, cache):
+    """Hand-written backward of forward(); the loss scale and 1/n_valid are
+    already folded into cache['dz'] and cache['dwte_head'].  Returns a dict of
+    gradients keyed like params."""
+    H, L = cfg.n_head, cfg.n_layer
+    grads = {name: np.zeros_like(params[name]) for name, _ in param_specs(cfg)}
+    grads["transformer.wte.weight"] += cache["dwte_head"]
+
+    dh, dw, db = layernorm_bwd(cache["dz"], cache["lnf"], params["transformer.ln_f.weight"])
+    grads["transformer.ln_f.weight"] += dw
+    grads["transformer.ln_f.bias"] += db
+
+    for layer in reversed(range(L)):
+        p = f"transformer.h.{layer}."
+        lc = cache["layers"][layer]
+        C = cfg.n_embd
+        # MLP branch: h_out = h_mid + g Wmp^T + bmp
+        dflat = dh.reshape(-1, C)
+        gflat = lc["g"].reshape(-1, lc["g"].shape[-1])
+        grads[p + "mlp.c_proj.weight"] += dflat.T @ gflat
+        grads[p + "mlp.c_proj.bias"] += dflat.sum(axis=0)
+        dg = dh @ params[p + "mlp.c_proj.weight"]
+        du = dg * gelu_tanh_grad(lc["u"])
+        duflat = du.reshape(-1, du.shape[-1])
+        grads[p + "mlp.c_fc.weight"] += duflat.T @ lc["a2"].reshape(-1, C)
+        grads[p + "mlp.c_fc.bias"] += duflat.sum(axis=0)
+        da2 = du @ params[p + "mlp.c_fc.weight"]
+        dx, dw, db = layernorm_bwd(da2, lc["ln2"], params[p + "ln_2.weight"])
+        grads[p + "ln_2.weight"] += dw
+        grads[p + "ln_2.bias"] += db
+        dh = dh + dx
+        # attention branch: h_mid = h_in + y Wo^T + bo
+        dflat = dh.reshape(-1, C)
+        grads[p + "attn.c_proj.weight"] += dflat.T @ lc["y"].reshape(-1, C)
+        grads[p + "attn.c_proj.bias"] += dflat.sum(axis=0)
+        dy = dh @ params[p + "attn.c_proj.weight"]
+        doh = _split_heads(dy, H)
+        dqh = np.empty_like(doh)
+        dkh = np.empty_like(doh)
+        dvh = np.empty_like(doh)
+        B = doh.shape[0]
+        for b in range(B):
+            for j in range(H):
+                dqh[b, j], dkh[b, j], dvh[b, j] = attention_bwd(
+                    doh[b, j], lc["qh"][b, j], lc["kh"][b, j], lc["vh"][b, j], lc["p"][b, j])
+        dqkv = np.concatenate([_merge_heads(dqh), _merge_heads(dkh), _merge_heads(dvh)], axis=-1)
+        dqflat = dqkv.reshape(-1, 3 * C)
+        grads[p + "attn.c_attn.weight"] += dqflat.T @ lc["a1"].reshape(-1, C)
+        grads[p + "attn.c_attn.bias"] += dqflat.sum(axis=0)
+        da1 = dqkv @ params[p + "attn.c_attn.weight"]
+        dx, dw, db = layernorm_bwd(da1, lc["ln1"], params[p + "ln_1.weight"])
+        grads[p + "ln_1.weight"] += dw
+        grads[p + "ln_1.bias"] += db
+        dh = dh + dx
+
+    # embeddings: wte receives the scattered rows on top of its lm_head part
+    # (the tied weight, [train-124M] §4); wpe sums over the batch.
+    idx = cache["idx"]
+    T = idx.shape[1]
+    np.add.at(grads["transformer.wte.weight"], idx.reshape(-1), dh.reshape(-1, dh.shape[-1]))
+    grads["transformer.wpe.weight"][:T] += dh.sum(axis=0)
+    return grads
+
+
+def fwd_bwd(cfg: Config, params, idx, targets, scale=1.0, grads=None, chunk=1024, n_valid=None):
+    """One micro-step: loss of the micro-batch (unscaled mean over its valid
+    targets) and the gradient of scale * loss added into ``grads``
+    ([train-124M] §8.1: loss / grad_accum_steps, then backward).
+
+    Returns (loss, row_loss, grads)."""
+    loss, row_loss, cache = forward(cfg, params, idx, targets, scale=scale, chunk=chunk, n_valid=n_valid)
+    g = backward(cfg, params, cache)
+    if cache["n_valid"] == 0:
+        g = {k: np.zeros_like(v) for k, v in g.items()}
+    if grads is None:
+        return loss, row_loss, g
+    for k in grads:
+        grads[k] += g[k]
+    return loss, row_loss, grads

@@ -1,0 +1,205 @@
+"""Throughput of the GPT-2 124M training step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--no-cpu-baseline]
+
+One step is the pages' full optimizer step: zero_grad, 32 micro-steps of
+B=16 x T=1024 tokens with loss / 32, global-norm clipping at 1.0 and AdamW
+(lr 6e-4, betas 0.9/0.95, eps 1e-8, wd 0.1 on 2-D tensors) -- 524,288 tokens
+("How I trained my own GPT-2 124M on FineWeb-Edu" sections 8.1 and 9; the
+timing protocol of "Making Training Fast on One GPU": warm-up, then timed
+full steps with a device synchronisation on both sides, the loss read back
+once per step).  Inputs are a synthetic Zipf token stream resident in HBM
+before timing starts; weights are the library's own N(0, 0.02) init.
+
+Prints one JSON line with tokens/s, MFU, the roofline of the dominant kernel
+(measured with HIP events on the library's stream during the timed steps),
+and the CPU oracle timed on a bounded sample on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec + MFU %, GPT-2 124M B=16 T=1024 step, 1 MI355X"
+PEAK_BF16 = 2.5e15          # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
+B, T, G = 16, 1024, 32
+
+
+def flops_per_token(n_params: int, L=12, H=12, hd=64, T_=1024) -> int:
+    # "Making Training Fast on One GPU", MFU defined: 6N + 12 L H Q T
+    return 6 * n_params + 12 * L * H * hd * T_
+
+
+def gemm_site_flops():
+    """Algorithmic FLOPs of one launch at each GEMM site of the micro-step
+    (B*T = 16384 rows, C = 768, F = 3072, V = 50304, lm_head chunk 4096 rows)."""
+    M, C, F, V, CH = B * T, 768, 3072, 50304, 4096
+    return {
+        "gemm.qkv": 2 * M * 3 * C * C,
+        "gemm.attn_proj": 2 * M * C * C,
+        "gemm.fc": 2 * M * F * C,
+        "gemm.mlp_proj": 2 * M * C * F,
+        "gemm.lm_head": 2 * CH * V * C,
+        "gemm.lm_head_dx": 2 * CH * V * C,
+        "gemm.lm_head_dw": 2 * CH * V * C,
+        "gemm.mlp_proj_dw": 2 * M * C * F,
+        "gemm.mlp_proj_dx": 2 * M * C * F,
+        "gemm.fc_dw": 2 * M * F * C,
+        "gemm.fc_dx": 2 * M * F * C,
+        "gemm.attn_proj_dw": 2 * M * C * C,
+        "gemm.attn_proj_dx": 2 * M * C * C,
+        "gemm.qkv_dw": 2 * M * 3 * C * C,
+        "gemm.qkv_dx": 2 * M * 3 * C * C,
+    }
+
+
+def cpu_baseline(seconds_hint: float = 20.0):
+    """The CPU oracle (NumPy float32) on a bounded sample: one micro-step of the
+    same model on a single 1024-token sequence of the same token stream."""
+    import numpy as np
+    import synthetic
+    from oracle import model as OM
+    cores = len(os.sched_getaffinity(0))
+    cfg = OM.Config(50304, 1024, 12, 12, 768, 3072)
+    params = synthetic.random_params(OM.param_specs(cfg), seed=42)
+    stream = synthetic.token_stream(1025, seed=1337)
+    x, y = synthetic.micro_batch(stream, 0, 1, 1024)
+    t0 = time.perf_counter()
+    OM.fwd_bwd(cfg, params, x, y, scale=1.0 / G)
+    dt = time.perf_counter() - t0
+    return {"value": round(1024 / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "one micro-step (forward + backward, float32 NumPy) of GPT-2 124M on 1 x 1024 tokens of the "
+                      "synthetic stream; %.1f s" % dt}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--grad-accum", type=int, default=G)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="do not bracket launches with events")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import gpt_pretraining_step_amd as g
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ga = args.grad_accum
+    model = g.GPT2(g.GPT2_124M)
+    model.init_params(seed=42)
+    n_params = model.sizes.n_params
+    stream = synthetic.token_stream(ga * B * T + 1, seed=1337)
+    xs, ys = [], []
+    for k in range(ga):
+        x, y = synthetic.micro_batch(stream, k, B, T)
+        xs.append(torch.from_numpy(x).cuda())
+        ys.append(torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    losses = torch.zeros(ga, dtype=torch.float32, device="cuda")
+
+    def step():
+        model.zero_grad()
+        for k in range(ga):
+            model.fwd_bwd(xs[k], ys[k], loss_scale=1.0 / ga, loss_out=losses[k:k + 1])
+        norm = model.clip_adamw_step(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0)
+        # the loss is read back once per step, as a logger would
+        return float(losses.mean().item()), float(norm.item())
+
+    for _ in range(args.warmup):
+        step()
+    st = model.status()
+    if st != 0:
+        raise RuntimeError(f"device status {st} after warm-up")
+    print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    if not args.no_profile:
+        model.profile(True)
+        model.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_times, log = [], []
+    for i in range(args.steps):
+        s0 = time.perf_counter()
+        loss, norm = step()
+        step_times.append(time.perf_counter() - s0)
+        log.append((loss, norm))
+        print(f"[bench] step {i}: loss {loss:.4f} grad-norm {norm:.4f} {step_times[-1] * 1e3:.1f} ms",
+              file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = model.status()
+    if st != 0:
+        raise RuntimeError(f"device status {st} after timed steps")
+    prof = model.profile_entries() if not args.no_profile else {}
+    model.profile(False)
+
+    tokens = args.steps * ga * B * T
+    tps = tokens / elapsed
+    fpt = flops_per_token(n_params)
+    result = {
+        "metric": METRIC,
+        "value": round(tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Zipf token stream, EOT-prefixed documents; random N(0,0.02) init)",
+        "config": {"workload": f"gpt2-124m optimizer step: {ga} x micro-batch B={B} T={T} + clip 1.0 + AdamW",
+                   "global_batch_tokens": ga * B * T, "micro_batch": B, "seq_len": T, "grad_accum": ga,
+                   "vocab": 50304, "parallelism": "none (1 GPU)"},
+        "mfu": round(tps * fpt / PEAK_BF16, 4),
+        "flops_per_token": fpt,
+        "loss_last_step": round(log[-1][0], 5),
+        "grad_norm_last_step": round(log[-1][1], 5),
+    }
+
+    # dominant kernel: the launch site with the largest summed time
+    if prof:
+        total_ms = sum(ms for _, ms in prof.values())
+        site, (cnt, ms) = max(prof.items(), key=lambda kv: kv[1][1])
+        avg_s = ms / cnt / 1e3
+        fl = gemm_site_flops()
+        gemm_sites = {k: v for k, v in prof.items() if k in fl}
+        gsite, (gcnt, gms) = max(gemm_sites.items(), key=lambda kv: kv[1][1])
+        gavg = gms / gcnt / 1e3
+        result["roofline"] = {
+            "kernel": gsite, "bound": "mfma", "achieved": round(fl[gsite] / gavg / 1e12, 2),
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": round(fl[gsite] / gavg / PEAK_BF16, 4), "traffic": None,
+            "avg_launch_us": round(gavg * 1e6, 2), "flops_per_launch": fl[gsite],
+        }
+        result["time_breakdown_ms_per_step"] = {
+            k: round(v[1] / args.steps, 3) for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
+        result["top_site"] = {"site": site, "share": round(ms / total_ms, 4)}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline()
+    model.close()
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,277 @@
+"""One GPT-2 training micro-step and optimizer step on an MI355X (gfx950).
+
+A thin Python layer over libgpt2hip.so (include/gpt2.h).  PyTorch provides the
+device buffers and the stream; every step of the computation runs in the
+library's HIP kernels.  The calls mirror the training loop of "How I trained
+my own GPT-2 124M on FineWeb-Edu" (sections 8.1 and 9):
+
+    m = GPT2(GPT2_124M)                      # buffers sized for B <= max_batch
+    m.init_params(seed=42)
+    m.zero_grad()
+    for k in range(grad_accum_steps):
+        m.fwd_bwd(x_k, y_k, loss_scale=1 / grad_accum_steps)
+    norm = m.clip_adamw_step(lr=6e-4)
+"""
+
+from __future__ import annotations
+
+import ctypes as ct
+from dataclasses import dataclass
+
+from . import _ffi
+from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noqa: F401
+                   EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE)
+
+__all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm",
+           "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum",
+           "query_sizes", "param_table"]
+
+
+@dataclass(frozen=True)
+class ModelConfig:
+    vocab_size: int
+    block_size: int
+    n_layer: int
+    n_head: int
+    n_embd: int
+    mlp_hidden: int
+    max_batch: int
+    precision: int  # PRECISION_FP32 or PRECISION_BF16
+
+    def c(self) -> _ffi.Config:
+        return _ffi.Config(self.vocab_size, self.block_size, self.n_layer, self.n_head, self.n_embd,
+                           self.mlp_hidden, self.max_batch, self.precision)
+
+
+# The tiny character-level GPT in float32 (vocab 66, 2 layers, 64 wide, 4 heads, MLP 256, T 64, B 4).
+TINY_CHAR_FP32 = ModelConfig(66, 64, 2, 4, 64, 256, 4, PRECISION_FP32)
+# GPT-2 124M with the padded vocabulary, bf16 compute with float32 master weights, micro-batch 16.
+GPT2_124M = ModelConfig(50304, 1024, 12, 12, 768, 3072, 16, PRECISION_BF16)
+
+
+def query_sizes(cfg: ModelConfig) -> _ffi.Sizes:
+    s = _ffi.Sizes()
+    c = cfg.c()
+    check(lib().gpt2_query_sizes(ct.byref(c), ct.byref(s)), "gpt2_query_sizes")
+    return s
+
+
+def param_table(cfg: ModelConfig):
+    """[(name, offset, shape, decayed)] in table order (host only)."""
+    s = query_sizes(cfg)
+    c = cfg.c()
+    out = []
+    for i in range(s.n_tensors):
+        d = _ffi.ParamDesc()
+        check(lib().gpt2_param_info(ct.byref(c), i, ct.byref(d)), "gpt2_param_info")
+        shape = (d.shape[0], d.shape[1]) if d.ndim == 2 else (d.shape[0],)
+        out.append((d.name.decode(), int(d.offset), shape, bool(d.decayed)))
+    return out
+
+
+def _stream_ptr(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class GPT2:
+    """A model instance: caller-owned (torch) device buffers bound to a
+    library context."""
+
+    def __init__(self, cfg: ModelConfig, device: str = "cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.sizes = query_sizes(cfg)
+        s = self.sizes
+        n = s.n_elems
+
+        def buf(nbytes, dtype=torch.uint8):
+            return torch.zeros(max(nbytes, 1), dtype=dtype, device=self.device)
+
+        self.params = torch.zeros(n, dtype=torch.float32, device=self.device)
+        self.grads = torch.zeros(n, dtype=torch.float32, device=self.device)
+        self.adam_m = torch.zeros(n, dtype=torch.float32, device=self.device)
+        self.adam_v = torch.zeros(n, dtype=torch.float32, device=self.device)
+        self.shadow = torch.zeros(n, dtype=torch.bfloat16, device=self.device) if s.shadow_bytes else None
+        self.activations = buf(s.activations_bytes)
+        self.scratch = buf(s.scratch_bytes)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=self.device)
+        self.grad_norm = torch.zeros(1, dtype=torch.float32, device=self.device)
+        b = _ffi.Buffers(self.params.data_ptr(), self.grads.data_ptr(), self.adam_m.data_ptr(),
+                         self.adam_v.data_ptr(), _ptr(self.shadow), self.activations.data_ptr(),
+                         self.scratch.data_ptr())
+        c = cfg.c()
+        h = ct.c_void_p()
+        torch.cuda.synchronize(self.device)
+        check(lib().gpt2_create(ct.byref(c), ct.byref(b), _stream_ptr(stream), ct.byref(h)), "gpt2_create")
+        self._h = h
+        self.table = param_table(cfg)
+        self.index = {name: (off, shape, dec) for name, off, shape, dec in self.table}
+
+    # -- parameter views ---------------------------------------------------
+    def view(self, flat, name: str):
+        off, shape, _ = self.index[name]
+        n = 1
+        for d in shape:
+            n *= d
+        return flat[off:off + n].view(*shape)
+
+    def param(self, name):
+        return self.view(self.params, name)
+
+    def grad(self, name):
+        return self.view(self.grads, name)
+
+    # -- the training step ---------------------------------------------------
+    def init_params(self, seed: int = 42):
+        check(lib().gpt2_init_params(self._h, seed), "gpt2_init_params")
+
+    def sync_shadow(self):
+        check(lib().gpt2_sync_shadow(self._h), "gpt2_sync_shadow")
+
+    def zero_grad(self):
+        check(lib().gpt2_zero_grad(self._h), "gpt2_zero_grad")
+
+    def fwd_bwd(self, tokens, targets, loss_scale: float = 1.0, token_loss=None, loss_out=None):
+        """tokens, targets: int32 device tensors [B, T].  Returns the device
+        loss tensor (unscaled micro-batch mean)."""
+        import torch
+        assert tokens.dtype == torch.int32 and targets.dtype == torch.int32
+        assert tokens.is_contiguous() and targets.is_contiguous() and tokens.shape == targets.shape
+        B, T = tokens.shape
+        out = self.loss if loss_out is None else loss_out
+        check(lib().gpt2_fwd_bwd(self._h, tokens.data_ptr(), targets.data_ptr(), B, T, float(loss_scale),
+                                 out.data_ptr(), _ptr(token_loss)), "gpt2_fwd_bwd")
+        return out
+
+    def clip_adamw_step(self, lr: float, beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-8,
+                        weight_decay: float = 0.1, max_norm: float = 1.0, norm_out=None):
+        hp = _ffi.AdamW(lr, beta1, beta2, eps, weight_decay, max_norm)
+        out = self.grad_norm if norm_out is None else norm_out
+        check(lib().gpt2_clip_adamw_step(self._h, ct.byref(hp), out.data_ptr()), "gpt2_clip_adamw_step")
+        return out
+
+    @property
+    def step(self) -> int:
+        t = ct.c_int64()
+        check(lib().gpt2_get_step(self._h, ct.byref(t)), "gpt2_get_step")
+        return t.value
+
+    @step.setter
+    def step(self, t: int):
+        check(lib().gpt2_set_step(self._h, t), "gpt2_set_step")
+
+    def status(self) -> int:
+        """Synchronise and return (and clear) the device flag."""
+        return lib().gpt2_get_status(self._h)
+
+    # -- measurement ---------------------------------------------------------
+    def profile(self, on: bool = True):
+        check(lib().gpt2_profile_enable(self._h, 1 if on else 0), "gpt2_profile_enable")
+
+    def profile_reset(self):
+        check(lib().gpt2_profile_reset(self._h), "gpt2_profile_reset")
+
+    def profile_entries(self):
+        n = lib().gpt2_profile_count(self._h)
+        out = {}
+        for i in range(n):
+            name = ct.c_char_p()
+            cnt = ct.c_int64()
+            ms = ct.c_double()
+            check(lib().gpt2_profile_entry(self._h, i, ct.byref(name), ct.byref(cnt), ct.byref(ms)), "profile")
+            out[name.value.decode()] = (cnt.value, ms.value)
+        return out
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().gpt2_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------ single ops
+
+def lmhead_ce(hidden, weight, targets, dweight, stream=None, flag=None):
+    """Isolated tied lm_head + mean cross-entropy (bf16 hidden [M, C], bf16
+    weight [V, C], int32 targets [M]); dweight (float32 [V, C]) is added to.
+    Returns (loss [1] float32, dhidden bf16 [M, C])."""
+    import torch
+    M, C = hidden.shape
+    V = weight.shape[0]
+    nbytes = lib().gpt2_lmhead_ce_scratch_bytes(M, C, V)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=hidden.device)
+    loss = torch.empty(1, dtype=torch.float32, device=hidden.device)
+    dh = torch.empty_like(hidden)
+    check(lib().gpt2_lmhead_ce(_stream_ptr(stream), hidden.data_ptr(), weight.data_ptr(), targets.data_ptr(), M, C, V,
+                               loss.data_ptr(), dh.data_ptr(), dweight.data_ptr(), scratch.data_ptr(), _ptr(flag)),
+          "gpt2_lmhead_ce")
+    return loss, dh
+
+
+def op_gemm(A, B, C, M, N, K, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, ldc=None, epilogue=EPI_STORE,
+            C2=None, R=None, U=None, bias=None, alpha=1.0, stream=None):
+    import torch
+    dtype = PRECISION_BF16 if A.dtype == torch.bfloat16 else PRECISION_FP32
+    a = _ffi.GemmArgs()
+    a.M, a.N, a.K, a.dtype = M, N, K, dtype
+    a.a_kmajor, a.b_kmajor = int(a_kmajor), int(b_kmajor)
+    a.lda = lda if lda is not None else (K if a_kmajor else M)
+    a.ldb = ldb if ldb is not None else (K if b_kmajor else N)
+    a.ldc = ldc if ldc is not None else N
+    a.A, a.B, a.C = A.data_ptr(), B.data_ptr(), C.data_ptr()
+    a.C2, a.R, a.U, a.bias = _ptr(C2), _ptr(R), _ptr(U), _ptr(bias)
+    a.alpha = alpha
+    a.epilogue = epilogue
+    a.out_bf16 = int(C.dtype == torch.bfloat16)
+    check(lib().gpt2_op_gemm(_stream_ptr(stream), ct.byref(a)), "gpt2_op_gemm")
+
+
+def op_colsum(Y, db, stream=None):
+    import torch
+    M, N = Y.shape
+    check(lib().gpt2_op_colsum(_stream_ptr(stream), Y.data_ptr(), int(Y.dtype == torch.bfloat16), M, N, Y.stride(0),
+                               db.data_ptr()), "gpt2_op_colsum")
+
+
+def op_layernorm_fwd(x, w, b, y, mean, rstd, stream=None):
+    import torch
+    rows, C = x.shape
+    check(lib().gpt2_op_layernorm_fwd(_stream_ptr(stream), x.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(),
+                                      int(y.dtype == torch.bfloat16), mean.data_ptr(), rstd.data_ptr(), rows, C),
+          "gpt2_op_layernorm_fwd")
+
+
+def op_layernorm_bwd(dy, x, mean, rstd, w, dx, dw, db, stream=None):
+    rows, C = x.shape
+    check(lib().gpt2_op_layernorm_bwd(_stream_ptr(stream), dy.data_ptr(), x.data_ptr(), mean.data_ptr(),
+                                      rstd.data_ptr(), w.data_ptr(), dx.data_ptr(), dw.data_ptr(), db.data_ptr(),
+                                      rows, C), "gpt2_op_layernorm_bwd")
+
+
+def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None):
+    import torch
+    dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
+    check(lib().gpt2_op_attention_fwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
+                                      lse.data_ptr()), "gpt2_op_attention_fwd")
+
+
+def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None):
+    import torch
+    dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
+    nbytes = lib().gpt2_attention_bwd_scratch_bytes(B, T, H)
+    scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qkv.device)
+    check(lib().gpt2_op_attention_bwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
+                                      dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr()),
+          "gpt2_op_attention_bwd")

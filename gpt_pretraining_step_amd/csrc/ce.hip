@@ -1,0 +1,136 @@
+// Cross-entropy over the tied lm_head's logits, one row chunk at a time
+// ("How I trained my own GPT-2 124M on FineWeb-Edu" section 4: softmax, pick
+// the target's probability, -log, mean over positions).  Rows whose target is
+// -1 are ignored and the mean divides by the valid count ("Multi-GPU
+// calculation of gradients for accelerated training", "Cross-entropy averages
+// within one micro-batch").  The softmax runs over every padded column.
+#include "common.h"
+
+namespace g2 {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bool target_valid(int t, int V) { return t >= 0 && t < V; }
+
+// count[0] = number of targets in [0, V); ids outside [0, V) other than -1
+// raise GPT2_ERR_BAD_ID (and are then treated as ignored).  One block.
+__global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __restrict__ tgt, int n, int V,
+                                                             int* __restrict__ count, int* flag) {
+  __shared__ int red[1024];
+  int c = 0, bad = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int t = tgt[i];
+    c += target_valid(t, V);
+    bad |= (t != -1 && !target_valid(t, V));
+  }
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) count[0] = red[0];
+  if (bad) raise_flag(flag, GPT2_ERR_BAD_ID);
+}
+
+// One block per row: online (max, sum of exp) over the row, then
+// loss_row = lse - z[target], dlogits = scale / count * (softmax - onehot).
+template <typename LT, typename DT>
+__global__ __launch_bounds__(256) void ce_rows_kernel(const LT* __restrict__ logits, int64_t ld_l, DT* __restrict__ dl,
+                                                      int64_t ld_d, const int32_t* __restrict__ tgt, int V,
+                                                      const int* __restrict__ count, float scale,
+                                                      float* __restrict__ row_loss) {
+  const int r = blockIdx.x;
+  const LT* z = logits + (int64_t)r * ld_l;
+  float m = -INFINITY, s = 0.f;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    const float x = to_f<LT>(z[v]) * LOG2E;
+    if (x > m) {
+      s = s * exp2f(m - x) + 1.f;
+      m = x;
+    } else {
+      s += exp2f(x - m);
+    }
+  }
+  __shared__ float sm[256], ss[256];
+  sm[threadIdx.x] = m;
+  ss[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) {
+      const float m1 = sm[threadIdx.x], m2 = sm[threadIdx.x + k];
+      const float mm = fmaxf(m1, m2);
+      const float s1 = ss[threadIdx.x] * (m1 == -INFINITY ? 0.f : exp2f(m1 - mm));
+      const float s2 = ss[threadIdx.x + k] * (m2 == -INFINITY ? 0.f : exp2f(m2 - mm));
+      sm[threadIdx.x] = mm;
+      ss[threadIdx.x] = s1 + s2;
+    }
+    __syncthreads();
+  }
+  const float lse2 = sm[0] + log2f(ss[0]);  // log2-domain log-sum-exp
+  const int t = tgt[r];
+  const bool valid = target_valid(t, V);
+  const int n = count[0];
+  if (threadIdx.x == 0) row_loss[r] = valid ? (lse2 * LN2 - to_f<LT>(z[t])) : 0.f;
+  const float coef = (valid && n > 0) ? scale / (float)n : 0.f;
+  DT* d = dl + (int64_t)r * ld_d;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    const float p = exp2f(to_f<LT>(z[v]) * LOG2E - lse2);
+    d[v] = from_f<DT>(coef * (p - (v == t ? 1.f : 0.f)));
+  }
+}
+
+// loss = sum(row_loss) / count, or NaN with GPT2_WARN_NO_TARGETS if count = 0.
+__global__ __launch_bounds__(1024) void ce_finish_kernel(const float* __restrict__ row_loss, int n,
+                                                         const int* __restrict__ count, float* __restrict__ loss,
+                                                         int* flag) {
+  __shared__ float red[1024];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s += row_loss[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 512; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int c = count[0];
+    if (c > 0) {
+      loss[0] = red[0] / (float)c;
+    } else {
+      loss[0] = __builtin_nanf("");
+      raise_flag(flag, GPT2_WARN_NO_TARGETS);
+    }
+  }
+}
+
+hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int* count, int* flag) {
+  prof_begin(L);
+  count_targets_kernel<<<1, 1024, 0, L.stream>>>(tgt, n, V, count, flag);
+  prof_end(L);
+  return hipGetLastError();
+}
+
+template <typename LT, typename DT>
+hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, DT* dlogits, int64_t ld_d,
+                          const int32_t* tgt, int rows, int V, const int* count, float scale, float* /*loss_sum*/,
+                          float* row_loss) {
+  prof_begin(L);
+  ce_rows_kernel<LT, DT><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, count, scale, row_loss);
+  prof_end(L);
+  return hipGetLastError();
+}
+template hipError_t launch_ce_rows<float, bf16>(const Launch&, const float*, int64_t, bf16*, int64_t, const int32_t*,
+                                               int, int, const int*, float, float*, float*);
+template hipError_t launch_ce_rows<float, float>(const Launch&, const float*, int64_t, float*, int64_t, const int32_t*,
+                                                int, int, const int*, float, float*, float*);
+
+hipError_t launch_ce_finish_n(const Launch& L, const float* row_loss, int n, const int* count, float* loss, int* flag) {
+  prof_begin(L);
+  ce_finish_kernel<<<1, 1024, 0, L.stream>>>(row_loss, n, count, loss, flag);
+  prof_end(L);
+  return hipGetLastError();
+}
+
+}  // namespace g2

@@ -1,0 +1,117 @@
+// Internal declarations shared by the HIP kernels and the host runtime of
+// libgpt2hip.so.  Not part of the public C-ABI (see include/gpt2.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/gpt2.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace g2 {
+
+// Device error flag values (the most severe wins: lower is more severe).
+__host__ __device__ inline int flag_rank(int s) {
+  return s == GPT2_OK ? 0 : (s == GPT2_WARN_NO_TARGETS ? 1 : (s == GPT2_ERR_BAD_ID ? 2 : 3));
+}
+
+// Raise the device flag to `code` unless it already holds something more
+// severe.  Uses a vector-memory atomic.
+__device__ inline void raise_flag(int* flag, int code) {
+  if (!flag) return;
+  int old = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (flag_rank(code) > flag_rank(old)) {
+    int prev = atomicCAS(flag, old, code);
+    if (prev == old) break;
+    old = prev;
+  }
+}
+
+__device__ __forceinline__ float bf2f(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ bf16 f2bf(float x) { return static_cast<bf16>(x); }
+
+// Element type helpers for kernels templated on float / bf16 storage.
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<bf16>(bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
+
+// GELU, tanh form ("How I trained my own GPT-2 124M on FineWeb-Edu" 2.13),
+// and its derivative.
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float k = 0.7978845608028654f;  // sqrt(2/pi)
+  float inner = k * (u + 0.044715f * u * u * u);
+  return 0.5f * u * (1.0f + tanhf(inner));
+}
+__device__ __forceinline__ float gelu_tanh_grad(float u) {
+  const float k = 0.7978845608028654f;
+  float inner = k * (u + 0.044715f * u * u * u);
+  float th = tanhf(inner);
+  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * k * (1.0f + 3.0f * 0.044715f * u * u);
+}
+
+// Kernel launch bookkeeping: the runtime passes a Launch to every launcher,
+// which records HIP events around the kernel when profiling is on.
+struct Prof;
+struct Launch {
+  hipStream_t stream;
+  Prof* prof;      // may be null
+  const char* site;
+};
+void prof_begin(const Launch& L);
+void prof_end(const Launch& L);
+
+// ---------------------------------------------------------------- launchers
+// Each returns a hipError_t from the launch (hipSuccess when fine) after
+// host-side shape checks done by the caller.
+
+hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, int* flag);
+hipError_t launch_colsum(const Launch& L, const void* y, int y_bf16, int M, int N, int64_t ld, float* db);
+
+hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y,
+                                int y_bf16, float* mean, float* rstd, int rows, int C);
+// dx is added into `dx`; when dxb is non-null it also receives bf16(dx_new).
+hipError_t launch_layernorm_bwd_b(const Launch& L, const float* dy, const float* x, const float* mean,
+                                  const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
+                                  int rows, int C);
+
+hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
+                                void* y, float* lse);
+hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
+                                const void* y, const void* dy, const float* lse, void* dqkv, void* scratch);
+size_t attention_bwd_scratch(int B, int T, int H);
+
+hipError_t launch_embed_fwd(const Launch& L, const int32_t* tok, const float* wte, const float* wpe, float* out,
+                            int B, int T, int C, int V, int* flag);
+hipError_t launch_embed_bwd(const Launch& L, const int32_t* tok, const float* dr, float* dwte, float* dwpe, int B,
+                            int T, int C, int V);
+
+// Cross-entropy helpers for the chunked lm_head.
+hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int* count, int* flag);
+template <typename LT, typename DT>
+hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, DT* dlogits, int64_t ld_d,
+                          const int32_t* tgt, int rows, int V, const int* count, float scale, float* loss_sum,
+                          float* token_loss);
+hipError_t launch_ce_finish_n(const Launch& L, const float* row_loss, int n, const int* count, float* loss,
+                              int* flag);
+
+// Optimizer.
+hipError_t launch_sumsq_partials(const Launch& L, const float* g, size_t n, float* partials, int nparts);
+hipError_t launch_adamw(const Launch& L, float* p, const float* g, float* m, float* v, bf16* shadow, size_t n,
+                        size_t decay_end, const float* partials, int nparts, float lr, float b1, float b2,
+                        float eps, float wd, float max_norm, float bc1, float bc2, float* norm_out, int* flag);
+hipError_t launch_fill_f32(const Launch& L, float* p, size_t n, float value);
+hipError_t launch_fill_i32(const Launch& L, int* p, size_t n, int value);
+hipError_t launch_to_bf16(const Launch& L, const float* src, bf16* dst, size_t n);
+hipError_t launch_init_normal(const Launch& L, float* dst, size_t n, uint32_t tensor_index, uint64_t seed,
+                              float std);
+
+}  // namespace g2

@@ -1,0 +1,851 @@
+// Host runtime of libgpt2hip.so: configuration checks, the parameter table,
+// the activation/scratch layout, the launch sequence of one micro-step and
+// of the optimizer step, and the C-ABI of include/gpt2.h.
+//
+// The micro-step follows "How I trained my own GPT-2 124M on FineWeb-Edu":
+// embedding (2.2, 2.10), n_layer pre-LN blocks x + attn(ln_1(x)),
+// x + mlp(ln_2(x)) (2.3-2.13; the residual reading of the page's garbled
+// Block.forward), ln_f (2.8), the tied lm_head and mean cross-entropy (4), and
+// the backward pass (8.1: the gradient of loss / grad_accum_steps is added to
+// the gradients).  Everything is enqueued on the context's stream.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace g2 {
+
+// ------------------------------------------------------------- profiling
+
+struct Prof {
+  bool on = false;
+  std::vector<std::string> names;
+  std::vector<int64_t> counts;
+  std::vector<double> ms;
+  struct Pending {
+    int site;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t cur = nullptr;
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  int site(const char* n) {
+    for (size_t i = 0; i < names.size(); ++i)
+      if (names[i] == n) return (int)i;
+    names.emplace_back(n);
+    counts.push_back(0);
+    ms.push_back(0.0);
+    return (int)names.size() - 1;
+  }
+  void resolve() {
+    for (auto& p : pending) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, p.a, p.b) == hipSuccess) {
+        counts[p.site] += 1;
+        ms[p.site] += t;
+      }
+      pool.push_back(p.a);
+      pool.push_back(p.b);
+    }
+    pending.clear();
+  }
+  ~Prof() {
+    for (auto& p : pending) {
+      (void)hipEventDestroy(p.a);
+      (void)hipEventDestroy(p.b);
+    }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+void prof_begin(const Launch& L) {
+  if (!L.prof || !L.prof->on) return;
+  L.prof->cur = L.prof->get();
+  if (L.prof->cur) (void)hipEventRecord(L.prof->cur, L.stream);
+}
+void prof_end(const Launch& L) {
+  if (!L.prof || !L.prof->on || !L.prof->cur) return;
+  hipEvent_t b = L.prof->get();
+  if (!b) return;
+  (void)hipEventRecord(b, L.stream);
+  L.prof->pending.push_back({L.prof->site(L.site), L.prof->cur, b});
+  L.prof->cur = nullptr;
+}
+
+}  // namespace g2
+
+using namespace g2;
+
+// ------------------------------------------------------------ param table
+
+namespace {
+
+constexpr size_t kAlignElems = 64;  // 256 B for float32 tensors
+constexpr int kNormParts = 1024;
+constexpr int kCeChunk = 4096;
+
+struct Desc {
+  std::string name;
+  int ndim;
+  int shape[2];
+  int hf_index;  // position in the page's named_parameters order
+  int decayed;
+  size_t offset;
+  size_t numel() const { return (size_t)shape[0] * (ndim == 2 ? (size_t)shape[1] : 1); }
+};
+
+// Kinds of per-layer tensors, for lookups.
+enum Kind { LN1_W, LN1_B, QKV_W, QKV_B, PROJ_W, PROJ_B, LN2_W, LN2_B, FC_W, FC_B, MLP_W, MLP_B, N_KINDS };
+
+struct Table {
+  std::vector<Desc> d;
+  size_t n_elems = 0, n_params = 0, decay_end = 0;
+  int n_decayed = 0;
+  int wte = -1, wpe = -1, lnf_w = -1, lnf_b = -1;
+  std::vector<int> layer;  // [n_layer * N_KINDS] -> index into d
+};
+
+bool check_config(const gpt2_config* c) {
+  if (!c) return false;
+  if (c->vocab_size < 1 || c->block_size < 1 || c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1 ||
+      c->mlp_hidden < 1 || c->max_batch < 1)
+    return false;
+  if (c->precision != GPT2_PRECISION_FP32 && c->precision != GPT2_PRECISION_BF16) return false;
+  if (c->n_embd % c->n_head) return false;
+  const int hd = c->n_embd / c->n_head;
+  if (c->n_embd > 1024) return false;  // LayerNorm keeps a row in one wave's registers
+  if (c->precision == GPT2_PRECISION_BF16) {
+    if (hd != 64) return false;
+    if (c->vocab_size % 8 || c->n_embd % 8 || c->mlp_hidden % 8) return false;
+  } else {
+    if (hd > 64) return false;
+  }
+  if ((int64_t)c->max_batch * c->block_size > (1 << 30) / 4) return false;
+  return true;
+}
+
+Table build_table(const gpt2_config& c) {
+  const int V = c.vocab_size, T = c.block_size, C = c.n_embd, F = c.mlp_hidden, L = c.n_layer;
+  std::vector<Desc> hf;
+  auto add = [&](const std::string& n, int nd, int s0, int s1) {
+    Desc x;
+    x.name = n;
+    x.ndim = nd;
+    x.shape[0] = s0;
+    x.shape[1] = s1;
+    x.hf_index = (int)hf.size();
+    x.decayed = nd >= 2;
+    x.offset = 0;
+    hf.push_back(x);
+  };
+  add("transformer.wte.weight", 2, V, C);
+  add("transformer.wpe.weight", 2, T, C);
+  for (int l = 0; l < L; ++l) {
+    const std::string p = "transformer.h." + std::to_string(l) + ".";
+    add(p + "ln_1.weight", 1, C, 1);
+    add(p + "ln_1.bias", 1, C, 1);
+    add(p + "attn.c_attn.weight", 2, 3 * C, C);
+    add(p + "attn.c_attn.bias", 1, 3 * C, 1);
+    add(p + "attn.c_proj.weight", 2, C, C);
+    add(p + "attn.c_proj.bias", 1, C, 1);
+    add(p + "ln_2.weight", 1, C, 1);
+    add(p + "ln_2.bias", 1, C, 1);
+    add(p + "mlp.c_fc.weight", 2, F, C);
+    add(p + "mlp.c_fc.bias", 1, F, 1);
+    add(p + "mlp.c_proj.weight", 2, C, F);
+    add(p + "mlp.c_proj.bias", 1, C, 1);
+  }
+  add("transformer.ln_f.weight", 1, C, 1);
+  add("transformer.ln_f.bias", 1, C, 1);
+
+  Table t;
+  // decayed (dim >= 2) tensors first, each group in the page's order
+  for (auto& x : hf)
+    if (x.decayed) t.d.push_back(x);
+  t.n_decayed = (int)t.d.size();
+  for (auto& x : hf)
+    if (!x.decayed) t.d.push_back(x);
+  size_t off = 0;
+  for (size_t i = 0; i < t.d.size(); ++i) {
+    t.d[i].offset = off;
+    off += (t.d[i].numel() + kAlignElems - 1) / kAlignElems * kAlignElems;
+    t.n_params += t.d[i].numel();
+    if ((int)i == t.n_decayed - 1) t.decay_end = off;
+  }
+  t.n_elems = off;
+  t.layer.assign((size_t)L * N_KINDS, -1);
+  for (size_t i = 0; i < t.d.size(); ++i) {
+    const std::string& n = t.d[i].name;
+    if (n == "transformer.wte.weight") t.wte = (int)i;
+    else if (n == "transformer.wpe.weight") t.wpe = (int)i;
+    else if (n == "transformer.ln_f.weight") t.lnf_w = (int)i;
+    else if (n == "transformer.ln_f.bias") t.lnf_b = (int)i;
+    else {
+      int l = 0;
+      char rest[64];
+      if (sscanf(n.c_str(), "transformer.h.%d.%63s", &l, rest) == 2) {
+        static const char* kinds[N_KINDS] = {"ln_1.weight",       "ln_1.bias",       "attn.c_attn.weight",
+                                             "attn.c_attn.bias",  "attn.c_proj.weight", "attn.c_proj.bias",
+                                             "ln_2.weight",       "ln_2.bias",       "mlp.c_fc.weight",
+                                             "mlp.c_fc.bias",     "mlp.c_proj.weight", "mlp.c_proj.bias"};
+        for (int k = 0; k < N_KINDS; ++k)
+          if (strcmp(rest, kinds[k]) == 0) t.layer[(size_t)l * N_KINDS + k] = (int)i;
+      }
+    }
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------- layout
+
+struct Layout {
+  int rows = 0, chunk = 0;
+  size_t es = 4;  // bytes of an "activation" element (bf16 or float32)
+  // activations
+  std::vector<size_t> Rin, Rmid, A1, mean1, rstd1, QKV, Y, LSE, A2, mean2, rstd2, U, G;
+  size_t Z = 0, meanf = 0, rstdf = 0, act_bytes = 0;
+  // scratch
+  size_t dR = 0, dRb = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
+  size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, scratch_bytes = 0;
+};
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    off = (off + 255) / 256 * 256;
+    size_t r = off;
+    off += bytes;
+    return r;
+  }
+};
+
+Layout build_layout(const gpt2_config& c) {
+  Layout y;
+  const size_t rows = (size_t)c.max_batch * c.block_size;
+  const size_t C = c.n_embd, F = c.mlp_hidden, H = c.n_head, V = c.vocab_size;
+  const int L = c.n_layer;
+  y.rows = (int)rows;
+  y.es = c.precision == GPT2_PRECISION_BF16 ? 2 : 4;
+  y.chunk = (int)std::min<size_t>(rows, kCeChunk);
+  Bump a;
+  for (int l = 0; l <= L; ++l) y.Rin.push_back(a.take(rows * C * 4));
+  for (int l = 0; l < L; ++l) {
+    y.Rmid.push_back(a.take(rows * C * 4));
+    y.A1.push_back(a.take(rows * C * y.es));
+    y.mean1.push_back(a.take(rows * 4));
+    y.rstd1.push_back(a.take(rows * 4));
+    y.QKV.push_back(a.take(rows * 3 * C * y.es));
+    y.Y.push_back(a.take(rows * C * y.es));
+    y.LSE.push_back(a.take(rows * H * 4));
+    y.A2.push_back(a.take(rows * C * y.es));
+    y.mean2.push_back(a.take(rows * 4));
+    y.rstd2.push_back(a.take(rows * 4));
+    y.U.push_back(a.take(rows * F * y.es));
+    y.G.push_back(a.take(rows * F * y.es));
+  }
+  y.Z = a.take(rows * C * y.es);
+  y.meanf = a.take(rows * 4);
+  y.rstdf = a.take(rows * 4);
+  y.act_bytes = (a.off + 255) / 256 * 256;
+
+  Bump s;
+  y.flag = s.take(256);
+  y.count = s.take(256);
+  y.loss = s.take(256);
+  y.norm = s.take(256);
+  y.parts = s.take(kNormParts * 4);
+  y.dR = s.take(rows * C * 4);
+  y.dRb = s.take(rows * C * y.es);
+  y.dA = s.take(rows * C * 4);
+  y.dQKV = s.take(rows * 3 * C * y.es);
+  y.dY = s.take(rows * C * y.es);
+  y.dU = s.take(rows * F * y.es);
+  y.attnD = s.take(rows * H * 4);
+  y.logits = s.take((size_t)y.chunk * V * 4);
+  y.dlogits = s.take((size_t)y.chunk * V * y.es);
+  y.rowloss = s.take(rows * 4);
+  y.scratch_bytes = (s.off + 255) / 256 * 256;
+  return y;
+}
+
+}  // namespace
+
+struct gpt2_ctx {
+  gpt2_config cfg;
+  Table tab;
+  Layout lay;
+  gpt2_buffers buf;
+  hipStream_t stream;
+  int64_t t = 0;
+  Prof prof;
+
+  bool bf() const { return cfg.precision == GPT2_PRECISION_BF16; }
+  Launch at(const char* site) { return Launch{stream, &prof, site}; }
+  float* P(int i) const { return static_cast<float*>(buf.params) + tab.d[i].offset; }
+  float* Gr(int i) const { return static_cast<float*>(buf.grads) + tab.d[i].offset; }
+  // GEMM operand view of a weight: the bf16 shadow in BF16 mode, else float32.
+  const void* W(int i) const {
+    if (bf()) return static_cast<const bf16*>(buf.shadow) + tab.d[i].offset;
+    return static_cast<const float*>(buf.params) + tab.d[i].offset;
+  }
+  int L(int l, int k) const { return tab.layer[(size_t)l * N_KINDS + k]; }
+  template <typename T = void>
+  T* act(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(buf.activations) + off); }
+  template <typename T = void>
+  T* scr(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(buf.scratch) + off); }
+  int* flag() const { return scr<int>(lay.flag); }
+};
+
+// --------------------------------------------------------------- helpers
+
+#define HIP_TRY(...)                            \
+  do {                                          \
+    hipError_t e__ = (__VA_ARGS__);             \
+    if (e__ != hipSuccess) return GPT2_ERR_HIP; \
+  } while (0)
+
+static gpt2_gemm_args gemm_base(int dtype) {
+  gpt2_gemm_args a;
+  memset(&a, 0, sizeof(a));
+  a.dtype = dtype;
+  a.alpha = 1.f;
+  return a;
+}
+
+// y[M,N] = x[M,K] W[N,K]^T (+bias) with the given epilogue: a forward Linear.
+static hipError_t linear_fwd(gpt2_ctx* c, const char* site, const void* x, int M, int K, int wi, int N, int bi,
+                             int epi, void* out, void* out2, const float* resid) {
+  gpt2_gemm_args a = gemm_base(c->cfg.precision);
+  a.M = M; a.N = N; a.K = K;
+  a.a_kmajor = 1; a.b_kmajor = 1;
+  a.lda = K; a.ldb = K; a.ldc = N;
+  a.A = x; a.B = c->W(wi); a.C = out; a.C2 = out2; a.R = resid;
+  a.bias = bi >= 0 ? c->P(bi) : nullptr;
+  a.epilogue = epi;
+  a.out_bf16 = c->bf() && (epi == GPT2_EPI_STORE || epi == GPT2_EPI_GELU || epi == GPT2_EPI_DGELU);
+  return launch_gemm(c->at(site), a, c->flag());
+}
+
+// dx[M,K] = dy[M,N] W[N,K] (a Linear's input gradient), epilogue STORE or DGELU.
+static hipError_t linear_dx(gpt2_ctx* c, const char* site, const void* dy, int M, int N, int wi, int K, int epi,
+                            bool out_act, void* out, const void* u) {
+  gpt2_gemm_args a = gemm_base(c->cfg.precision);
+  a.M = M; a.N = K; a.K = N;
+  a.a_kmajor = 1; a.b_kmajor = 0;
+  a.lda = N; a.ldb = K; a.ldc = K;
+  a.A = dy; a.B = c->W(wi); a.C = out; a.U = u;
+  a.epilogue = epi;
+  a.out_bf16 = c->bf() && out_act;
+  return launch_gemm(c->at(site), a, c->flag());
+}
+
+// dW[N,K] += dy[M,N]^T x[M,K] (a Linear's weight gradient, reduced over tokens).
+static hipError_t linear_dw(gpt2_ctx* c, const char* site, const void* dy, int M, int N, const void* x, int K,
+                            int wi) {
+  gpt2_gemm_args a = gemm_base(c->cfg.precision);
+  a.M = N; a.N = K; a.K = M;
+  a.a_kmajor = 0; a.b_kmajor = 0;
+  a.lda = N; a.ldb = K; a.ldc = K;
+  a.A = dy; a.B = x; a.C = c->Gr(wi);
+  a.epilogue = GPT2_EPI_ACCUMULATE;
+  return launch_gemm(c->at(site), a, c->flag());
+}
+
+// ------------------------------------------------------------- the step
+
+static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int B, int T, float scale, float* loss,
+                        float* token_loss) {
+  const gpt2_config& g = c->cfg;
+  const Layout& y = c->lay;
+  const int M = B * T, C = g.n_embd, F = g.mlp_hidden, V = g.vocab_size, H = g.n_head, hd = C / H;
+  const int dt = g.precision;
+  const bool bf = c->bf();
+  int* flag = c->flag();
+  int* count = c->scr<int>(y.count);
+  float* rowloss = token_loss ? token_loss : c->scr<float>(y.rowloss);
+
+  HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, count, flag));
+  HIP_TRY(launch_embed_fwd(c->at("embed.fwd"), tok, c->P(c->tab.wte), c->P(c->tab.wpe), c->act<float>(y.Rin[0]), B,
+                           T, C, V, flag));
+  // ---- forward
+  for (int l = 0; l < g.n_layer; ++l) {
+    float* rin = c->act<float>(y.Rin[l]);
+    float* rmid = c->act<float>(y.Rmid[l]);
+    HIP_TRY(launch_layernorm_fwd(c->at("ln.fwd"), rin, c->P(c->L(l, LN1_W)), c->P(c->L(l, LN1_B)), c->act(y.A1[l]),
+                                 bf, c->act<float>(y.mean1[l]), c->act<float>(y.rstd1[l]), M, C));
+    HIP_TRY(linear_fwd(c, "gemm.qkv", c->act(y.A1[l]), M, C, c->L(l, QKV_W), 3 * C, c->L(l, QKV_B), GPT2_EPI_STORE,
+                       c->act(y.QKV[l]), nullptr, nullptr));
+    HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
+                                 c->act<float>(y.LSE[l])));
+    HIP_TRY(linear_fwd(c, "gemm.attn_proj", c->act(y.Y[l]), M, C, c->L(l, PROJ_W), C, c->L(l, PROJ_B),
+                       GPT2_EPI_RESIDUAL, rmid, nullptr, rin));
+    HIP_TRY(launch_layernorm_fwd(c->at("ln.fwd"), rmid, c->P(c->L(l, LN2_W)), c->P(c->L(l, LN2_B)), c->act(y.A2[l]),
+                                 bf, c->act<float>(y.mean2[l]), c->act<float>(y.rstd2[l]), M, C));
+    HIP_TRY(linear_fwd(c, "gemm.fc", c->act(y.A2[l]), M, C, c->L(l, FC_W), F, c->L(l, FC_B), GPT2_EPI_GELU,
+                       c->act(y.U[l]), c->act(y.G[l]), nullptr));
+    HIP_TRY(linear_fwd(c, "gemm.mlp_proj", c->act(y.G[l]), M, F, c->L(l, MLP_W), C, c->L(l, MLP_B),
+                       GPT2_EPI_RESIDUAL, c->act<float>(y.Rin[l + 1]), nullptr, rmid));
+  }
+  float* rlast = c->act<float>(y.Rin[g.n_layer]);
+  HIP_TRY(launch_layernorm_fwd(c->at("ln.fwd"), rlast, c->P(c->tab.lnf_w), c->P(c->tab.lnf_b), c->act(y.Z), bf,
+                               c->act<float>(y.meanf), c->act<float>(y.rstdf), M, C));
+
+  // ---- tied lm_head + cross-entropy, in row chunks
+  float* dZ = c->scr<float>(y.dA);
+  HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
+  const size_t es = y.es;
+  for (int r0 = 0; r0 < M; r0 += y.chunk) {
+    const int rows = std::min(y.chunk, M - r0);
+    const char* z_c = c->act<char>(y.Z) + (size_t)r0 * C * es;
+    float* logits = c->scr<float>(y.logits);
+    void* dlog = c->scr(y.dlogits);
+    {
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = rows; a.N = V; a.K = C;
+      a.a_kmajor = 1; a.b_kmajor = 1;
+      a.lda = C; a.ldb = C; a.ldc = V;
+      a.A = z_c; a.B = c->W(c->tab.wte); a.C = logits;
+      a.epilogue = GPT2_EPI_STORE; a.out_bf16 = 0;
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head"), a, flag));
+    }
+    if (bf)
+      HIP_TRY(launch_ce_rows<float, bf16>(c->at("ce.rows"), logits, V, static_cast<bf16*>(dlog), V, tgt + r0, rows, V,
+                                          count, scale, nullptr, rowloss + r0));
+    else
+      HIP_TRY(launch_ce_rows<float, float>(c->at("ce.rows"), logits, V, static_cast<float*>(dlog), V, tgt + r0, rows,
+                                           V, count, scale, nullptr, rowloss + r0));
+    {  // dZ_c += dlogits_c wte
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = rows; a.N = C; a.K = V;
+      a.a_kmajor = 1; a.b_kmajor = 0;
+      a.lda = V; a.ldb = C; a.ldc = C;
+      a.A = dlog; a.B = c->W(c->tab.wte); a.C = dZ + (size_t)r0 * C;
+      a.epilogue = GPT2_EPI_ACCUMULATE;
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dx"), a, flag));
+    }
+    {  // dwte += dlogits_c^T Z_c
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = V; a.N = C; a.K = rows;
+      a.a_kmajor = 0; a.b_kmajor = 0;
+      a.lda = V; a.ldb = C; a.ldc = C;
+      a.A = dlog; a.B = z_c; a.C = c->Gr(c->tab.wte);
+      a.epilogue = GPT2_EPI_ACCUMULATE;
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dw"), a, flag));
+    }
+  }
+  HIP_TRY(launch_ce_finish_n(c->at("ce.finish"), rowloss, M, count, loss, flag));
+
+  // ---- backward through the blocks
+  float* dR = c->scr<float>(y.dR);
+  bf16* dRb = bf ? c->scr<bf16>(y.dRb) : nullptr;
+  const void* dRop = bf ? static_cast<const void*>(dRb) : static_cast<const void*>(dR);
+  float* dA = c->scr<float>(y.dA);  // dZ lives here first; LN bwd consumes it before reuse
+  HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
+  HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dZ, rlast, c->act<float>(y.meanf), c->act<float>(y.rstdf),
+                                 c->P(c->tab.lnf_w), dR, dRb, c->Gr(c->tab.lnf_w), c->Gr(c->tab.lnf_b), M, C));
+  void* dU = c->scr(y.dU);
+  void* dY = c->scr(y.dY);
+  void* dQKV = c->scr(y.dQKV);
+  for (int l = g.n_layer - 1; l >= 0; --l) {
+    // MLP branch: R_{l+1} = Rmid + G Wmp^T + b
+    HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRop, M, C, c->act(y.G[l]), F, c->L(l, MLP_W)));
+    HIP_TRY(launch_colsum(c->at("colsum"), dR, 0, M, C, C, c->Gr(c->L(l, MLP_B))));
+    HIP_TRY(linear_dx(c, "gemm.mlp_proj_dx", dRop, M, C, c->L(l, MLP_W), F, GPT2_EPI_DGELU, true, dU,
+                      c->act(y.U[l])));
+    HIP_TRY(linear_dw(c, "gemm.fc_dw", dU, M, F, c->act(y.A2[l]), C, c->L(l, FC_W)));
+    HIP_TRY(launch_colsum(c->at("colsum"), dU, bf, M, F, F, c->Gr(c->L(l, FC_B))));
+    HIP_TRY(linear_dx(c, "gemm.fc_dx", dU, M, F, c->L(l, FC_W), C, GPT2_EPI_STORE, false, dA, nullptr));
+    HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, c->act<float>(y.Rmid[l]), c->act<float>(y.mean2[l]),
+                                   c->act<float>(y.rstd2[l]), c->P(c->L(l, LN2_W)), dR, dRb, c->Gr(c->L(l, LN2_W)),
+                                   c->Gr(c->L(l, LN2_B)), M, C));
+    // attention branch: Rmid = R_l + Y Wo^T + b
+    HIP_TRY(linear_dw(c, "gemm.attn_proj_dw", dRop, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W)));
+    HIP_TRY(launch_colsum(c->at("colsum"), dR, 0, M, C, C, c->Gr(c->L(l, PROJ_B))));
+    HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRop, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
+    HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
+                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
+    HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W)));
+    HIP_TRY(launch_colsum(c->at("colsum"), dQKV, bf, M, 3 * C, 3 * C, c->Gr(c->L(l, QKV_B))));
+    HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, false, dA, nullptr));
+    HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, c->act<float>(y.Rin[l]), c->act<float>(y.mean1[l]),
+                                   c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb, c->Gr(c->L(l, LN1_W)),
+                                   c->Gr(c->L(l, LN1_B)), M, C));
+  }
+  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V));
+  return GPT2_OK;
+}
+
+// ================================================================== C-ABI
+
+extern "C" {
+
+int gpt2_query_sizes(const gpt2_config* cfg, gpt2_sizes* out) {
+  if (!cfg || !out) return GPT2_ERR_ARG;
+  if (!check_config(cfg)) return GPT2_ERR_SHAPE;
+  Table t = build_table(*cfg);
+  Layout y = build_layout(*cfg);
+  out->n_params = t.n_params;
+  out->n_elems = t.n_elems;
+  out->n_tensors = (int32_t)t.d.size();
+  out->n_decayed = t.n_decayed;
+  out->params_bytes = t.n_elems * 4;
+  out->grads_bytes = t.n_elems * 4;
+  out->adam_m_bytes = t.n_elems * 4;
+  out->adam_v_bytes = t.n_elems * 4;
+  out->shadow_bytes = cfg->precision == GPT2_PRECISION_BF16 ? t.n_elems * 2 : 0;
+  out->activations_bytes = y.act_bytes;
+  out->scratch_bytes = y.scratch_bytes;
+  return GPT2_OK;
+}
+
+int gpt2_param_info(const gpt2_config* cfg, int idx, gpt2_param_desc* out) {
+  if (!cfg || !out) return GPT2_ERR_ARG;
+  if (!check_config(cfg)) return GPT2_ERR_SHAPE;
+  Table t = build_table(*cfg);
+  if (idx < 0 || idx >= (int)t.d.size()) return GPT2_ERR_ARG;
+  const Desc& d = t.d[idx];
+  memset(out, 0, sizeof(*out));
+  snprintf(out->name, sizeof(out->name), "%s", d.name.c_str());
+  out->offset = d.offset;
+  out->ndim = d.ndim;
+  out->shape[0] = d.shape[0];
+  out->shape[1] = d.ndim == 2 ? d.shape[1] : 0;
+  out->decayed = d.decayed;
+  return GPT2_OK;
+}
+
+int gpt2_create(const gpt2_config* cfg, const gpt2_buffers* bufs, void* stream, gpt2_ctx** out) {
+  if (!cfg || !bufs || !out) return GPT2_ERR_ARG;
+  if (!check_config(cfg)) return GPT2_ERR_SHAPE;
+  if (!bufs->params || !bufs->grads || !bufs->adam_m || !bufs->adam_v || !bufs->activations || !bufs->scratch)
+    return GPT2_ERR_UNBOUND;
+  if (cfg->precision == GPT2_PRECISION_BF16 && !bufs->shadow) return GPT2_ERR_UNBOUND;
+  gpt2_ctx* c = new gpt2_ctx();
+  c->cfg = *cfg;
+  c->tab = build_table(*cfg);
+  c->lay = build_layout(*cfg);
+  c->buf = *bufs;
+  c->stream = static_cast<hipStream_t>(stream);
+  c->t = 0;
+  if (launch_fill_i32(c->at("fill"), c->flag(), 1, GPT2_OK) != hipSuccess) {
+    delete c;
+    return GPT2_ERR_HIP;
+  }
+  *out = c;
+  return GPT2_OK;
+}
+
+int gpt2_destroy(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  (void)hipStreamSynchronize(c->stream);
+  delete c;
+  return GPT2_OK;
+}
+
+int gpt2_set_stream(gpt2_ctx* c, void* stream) {
+  if (!c) return GPT2_ERR_ARG;
+  c->stream = static_cast<hipStream_t>(stream);
+  return GPT2_OK;
+}
+
+int gpt2_sync_shadow(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (!c->bf()) return GPT2_OK;
+  HIP_TRY(launch_to_bf16(c->at("shadow"), static_cast<const float*>(c->buf.params), static_cast<bf16*>(c->buf.shadow),
+                         c->tab.n_elems));
+  return GPT2_OK;
+}
+
+int gpt2_init_params(gpt2_ctx* c, uint64_t seed) {
+  if (!c) return GPT2_ERR_ARG;
+  const size_t n = c->tab.n_elems;
+  HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.params), n, 0.f));
+  const double resid_std = 0.02 / sqrt(2.0 * c->cfg.n_layer);
+  for (size_t i = 0; i < c->tab.d.size(); ++i) {
+    const Desc& d = c->tab.d[i];
+    float* p = c->P((int)i);
+    if (d.ndim == 2) {
+      const bool resid = d.name.size() > 13 && d.name.compare(d.name.size() - 13, 13, "c_proj.weight") == 0;
+      HIP_TRY(launch_init_normal(c->at("init"), p, d.numel(), (uint32_t)d.hf_index, seed,
+                                 (float)(resid ? resid_std : 0.02)));
+    } else {
+      const bool ln_w = d.name.find("ln_") != std::string::npos && d.name.compare(d.name.size() - 6, 6, "weight") == 0;
+      HIP_TRY(launch_fill_f32(c->at("fill"), p, d.numel(), ln_w ? 1.f : 0.f));
+    }
+  }
+  HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.grads), n, 0.f));
+  HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.adam_m), n, 0.f));
+  HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.adam_v), n, 0.f));
+  c->t = 0;
+  return gpt2_sync_shadow(c);
+}
+
+int gpt2_zero_grad(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  HIP_TRY(launch_fill_f32(c->at("zero_grad"), static_cast<float*>(c->buf.grads), c->tab.n_elems, 0.f));
+  return GPT2_OK;
+}
+
+int gpt2_fwd_bwd(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets, int B, int T, float loss_scale,
+                 float* d_loss, float* d_token_loss) {
+  if (!c || !d_tokens || !d_targets || !d_loss) return GPT2_ERR_ARG;
+  if (B < 1 || B > c->cfg.max_batch || T < 1 || T > c->cfg.block_size) return GPT2_ERR_SHAPE;
+  if (!isfinite(loss_scale)) return GPT2_ERR_ARG;
+  return fwd_bwd_impl(c, d_tokens, d_targets, B, T, loss_scale, d_loss, d_token_loss);
+}
+
+int gpt2_clip_adamw_step(gpt2_ctx* c, const gpt2_adamw* hp, float* d_grad_norm) {
+  if (!c || !hp) return GPT2_ERR_ARG;
+  if (!(hp->lr >= 0.f) || !(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f) ||
+      !(hp->eps > 0.f) || !(hp->max_norm > 0.f) || !isfinite(hp->weight_decay))
+    return GPT2_ERR_ARG;
+  c->t += 1;
+  const double bc1 = 1.0 - pow((double)hp->beta1, (double)c->t);
+  const double bc2 = 1.0 - pow((double)hp->beta2, (double)c->t);
+  const Layout& y = c->lay;
+  float* parts = c->scr<float>(y.parts);
+  float* norm = d_grad_norm ? d_grad_norm : c->scr<float>(y.norm);
+  HIP_TRY(launch_sumsq_partials(c->at("opt.sumsq"), static_cast<const float*>(c->buf.grads), c->tab.n_elems, parts,
+                                kNormParts));
+  HIP_TRY(launch_adamw(c->at("opt.adamw"), static_cast<float*>(c->buf.params), static_cast<const float*>(c->buf.grads),
+                       static_cast<float*>(c->buf.adam_m), static_cast<float*>(c->buf.adam_v),
+                       c->bf() ? static_cast<bf16*>(c->buf.shadow) : nullptr, c->tab.n_elems, c->tab.decay_end, parts,
+                       kNormParts, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_norm, (float)bc1,
+                       (float)bc2, norm, c->flag()));
+  return GPT2_OK;
+}
+
+int gpt2_get_step(gpt2_ctx* c, int64_t* t) {
+  if (!c || !t) return GPT2_ERR_ARG;
+  *t = c->t;
+  return GPT2_OK;
+}
+
+int gpt2_set_step(gpt2_ctx* c, int64_t t) {
+  if (!c || t < 0) return GPT2_ERR_ARG;
+  c->t = t;
+  return GPT2_OK;
+}
+
+int gpt2_get_status(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+  int f = 0;
+  if (hipMemcpy(&f, c->flag(), sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return GPT2_ERR_HIP;
+  c->prof.resolve();
+  if (f != GPT2_OK) {
+    if (launch_fill_i32(c->at("fill"), c->flag(), 1, GPT2_OK) != hipSuccess) return GPT2_ERR_HIP;
+    if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+    c->prof.resolve();
+  }
+  return f;
+}
+
+const char* gpt2_strerror(int s) {
+  switch (s) {
+    case GPT2_OK: return "ok";
+    case GPT2_WARN_NO_TARGETS: return "no valid target in the micro-batch (loss is NaN, no gradient added)";
+    case GPT2_ERR_ARG: return "invalid argument";
+    case GPT2_ERR_SHAPE: return "unsupported shape or configuration";
+    case GPT2_ERR_HIP: return "HIP runtime error";
+    case GPT2_ERR_UNBOUND: return "required buffer not bound";
+    case GPT2_ERR_BAD_ID: return "token or target id out of range";
+    case GPT2_ERR_NONFINITE: return "non-finite gradient norm: update skipped";
+    default: return "unknown status";
+  }
+}
+
+// ---------------------------------------------------- isolated lm_head + CE
+
+static size_t lmhead_chunk(int M) { return (size_t)std::min(M, kCeChunk); }
+
+size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V) {
+  if (M < 1 || C < 1 || V < 1) return 0;
+  (void)C;
+  const size_t ch = lmhead_chunk(M);
+  Bump s;
+  s.take(256);                    // count
+  s.take((size_t)M * 4);          // row losses
+  s.take(ch * (size_t)V * 4);     // logits chunk
+  s.take(ch * (size_t)V * 2);     // dlogits chunk
+  s.take((size_t)M * C * 4);      // dhidden (float32 accumulation)
+  return (s.off + 255) / 256 * 256;
+}
+
+int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, const int32_t* d_targets, int M, int C,
+                   int V, float* d_loss, void* d_dhidden, float* d_dweight, void* d_scratch, int32_t* d_flag) {
+  if (!d_hidden || !d_weight || !d_targets || !d_loss || !d_dhidden || !d_dweight || !d_scratch) return GPT2_ERR_ARG;
+  if (M < 1 || C < 8 || V < 8 || C % 8 || V % 8) return GPT2_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Launch L{st, nullptr, ""};
+  const size_t ch = lmhead_chunk(M);
+  Bump s;
+  char* base = static_cast<char*>(d_scratch);
+  int* count = reinterpret_cast<int*>(base + s.take(256));
+  float* rowloss = reinterpret_cast<float*>(base + s.take((size_t)M * 4));
+  float* logits = reinterpret_cast<float*>(base + s.take(ch * (size_t)V * 4));
+  bf16* dlog = reinterpret_cast<bf16*>(base + s.take(ch * (size_t)V * 2));
+  float* dh32 = reinterpret_cast<float*>(base + s.take((size_t)M * C * 4));
+  int* flag = reinterpret_cast<int*>(d_flag);
+  HIP_TRY(launch_count_targets(L, d_targets, M, V, count, flag));
+  HIP_TRY(launch_fill_f32(L, dh32, (size_t)M * C, 0.f));
+  const bf16* H = static_cast<const bf16*>(d_hidden);
+  for (int r0 = 0; r0 < M; r0 += (int)ch) {
+    const int rows = std::min((int)ch, M - r0);
+    gpt2_gemm_args a = gemm_base(GPT2_PRECISION_BF16);
+    a.M = rows; a.N = V; a.K = C;
+    a.a_kmajor = 1; a.b_kmajor = 1;
+    a.lda = C; a.ldb = C; a.ldc = V;
+    a.A = H + (size_t)r0 * C; a.B = d_weight; a.C = logits;
+    a.epilogue = GPT2_EPI_STORE;
+    HIP_TRY(launch_gemm(L, a, flag));
+    HIP_TRY(launch_ce_rows<float, bf16>(L, logits, V, dlog, V, d_targets + r0, rows, V, count, 1.f, nullptr,
+                                        rowloss + r0));
+    a = gemm_base(GPT2_PRECISION_BF16);
+    a.M = rows; a.N = C; a.K = V;
+    a.a_kmajor = 1; a.b_kmajor = 0;
+    a.lda = V; a.ldb = C; a.ldc = C;
+    a.A = dlog; a.B = d_weight; a.C = dh32 + (size_t)r0 * C;
+    a.epilogue = GPT2_EPI_ACCUMULATE;
+    HIP_TRY(launch_gemm(L, a, flag));
+    a = gemm_base(GPT2_PRECISION_BF16);
+    a.M = V; a.N = C; a.K = rows;
+    a.a_kmajor = 0; a.b_kmajor = 0;
+    a.lda = V; a.ldb = C; a.ldc = C;
+    a.A = dlog; a.B = H + (size_t)r0 * C; a.C = d_dweight;
+    a.epilogue = GPT2_EPI_ACCUMULATE;
+    HIP_TRY(launch_gemm(L, a, flag));
+  }
+  HIP_TRY(launch_ce_finish_n(L, rowloss, M, count, d_loss, flag));
+  HIP_TRY(launch_to_bf16(L, dh32, static_cast<bf16*>(d_dhidden), (size_t)M * C));
+  return GPT2_OK;
+}
+
+// ------------------------------------------------------------ single ops
+
+static bool gemm_args_ok(const gpt2_gemm_args* a) {
+  if (!a || !a->A || !a->B || !a->C) return false;
+  if (a->M < 1 || a->N < 1 || a->K < 1) return false;
+  if (a->dtype != GPT2_PRECISION_BF16 && a->dtype != GPT2_PRECISION_FP32) return false;
+  if (a->epilogue < GPT2_EPI_STORE || a->epilogue > GPT2_EPI_ACCUMULATE) return false;
+  if (a->epilogue == GPT2_EPI_RESIDUAL && !a->R) return false;
+  if (a->epilogue == GPT2_EPI_GELU && !a->C2) return false;
+  if (a->epilogue == GPT2_EPI_DGELU && !a->U) return false;
+  if (a->epilogue == GPT2_EPI_ACCUMULATE && a->bias) return false;
+  const int64_t need_a = a->a_kmajor ? a->K : a->M;
+  const int64_t need_b = a->b_kmajor ? a->K : a->N;
+  if (a->lda < need_a || a->ldb < need_b || a->ldc < a->N) return false;
+  if (a->dtype == GPT2_PRECISION_BF16) {
+    if (a->M % 8 && !a->a_kmajor) return false;
+    if (a->N % 8 && !a->b_kmajor) return false;
+    if ((a->a_kmajor && a->K % 8) || (a->b_kmajor && a->K % 8)) return false;
+    if (a->lda % 8 || a->ldb % 8) return false;
+    if (((uintptr_t)a->A | (uintptr_t)a->B) & 15) return false;
+  }
+  return true;
+}
+
+int gpt2_op_gemm(void* stream, const gpt2_gemm_args* a) {
+  if (!gemm_args_ok(a)) return GPT2_ERR_ARG;
+  HIP_TRY(launch_gemm(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, *a, nullptr));
+  return GPT2_OK;
+}
+
+int gpt2_op_colsum(void* stream, const void* d_y, int y_bf16, int M, int N, int64_t ld, float* d_db) {
+  if (!d_y || !d_db || M < 1 || N < 1 || ld < N) return GPT2_ERR_ARG;
+  HIP_TRY(launch_colsum(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_y, y_bf16, M, N, ld, d_db));
+  return GPT2_OK;
+}
+
+int gpt2_op_layernorm_fwd(void* stream, const float* d_x, const float* d_w, const float* d_b, void* d_y, int y_bf16,
+                          float* d_mean, float* d_rstd, int rows, int C) {
+  if (!d_x || !d_w || !d_b || !d_y || !d_mean || !d_rstd) return GPT2_ERR_ARG;
+  if (rows < 1 || C < 1 || C > 1024) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_layernorm_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_x, d_w, d_b, d_y, y_bf16,
+                               d_mean, d_rstd, rows, C));
+  return GPT2_OK;
+}
+
+int gpt2_op_layernorm_bwd(void* stream, const float* d_dy, const float* d_x, const float* d_mean, const float* d_rstd,
+                          const float* d_w, float* d_dx, float* d_dw, float* d_db, int rows, int C) {
+  if (!d_dy || !d_x || !d_mean || !d_rstd || !d_w || !d_dx || !d_dw || !d_db) return GPT2_ERR_ARG;
+  if (rows < 1 || C < 1 || C > 1024) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_layernorm_bwd_b(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_dy, d_x, d_mean, d_rstd,
+                                 d_w, d_dx, nullptr, d_dw, d_db, rows, C));
+  return GPT2_OK;
+}
+
+static bool attn_shape_ok(int dtype, int B, int T, int H, int hd) {
+  if (B < 1 || T < 1 || H < 1) return false;
+  if (dtype == GPT2_PRECISION_BF16) return hd == 64;
+  if (dtype == GPT2_PRECISION_FP32) return hd >= 1 && hd <= 64;
+  return false;
+}
+
+int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv, void* d_y,
+                          float* d_lse) {
+  if (!d_qkv || !d_y || !d_lse) return GPT2_ERR_ARG;
+  if (!attn_shape_ok(dtype, B, T, H, hd)) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_attention_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, hd, d_qkv, d_y,
+                               d_lse));
+  return GPT2_OK;
+}
+
+size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H) { return attention_bwd_scratch(B, T, H); }
+
+int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv, const void* d_y,
+                          const void* d_dy, const float* d_lse, void* d_dqkv, void* d_scratch) {
+  if (!d_qkv || !d_y || !d_dy || !d_lse || !d_dqkv || !d_scratch) return GPT2_ERR_ARG;
+  if (!attn_shape_ok(dtype, B, T, H, hd)) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_attention_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, hd, d_qkv, d_y,
+                               d_dy, d_lse, d_dqkv, d_scratch));
+  return GPT2_OK;
+}
+
+// ------------------------------------------------------------ profiling
+
+int gpt2_profile_enable(gpt2_ctx* c, int on) {
+  if (!c) return GPT2_ERR_ARG;
+  c->prof.on = on != 0;
+  return GPT2_OK;
+}
+
+int gpt2_profile_reset(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  (void)hipStreamSynchronize(c->stream);
+  c->prof.resolve();
+  std::fill(c->prof.counts.begin(), c->prof.counts.end(), 0);
+  std::fill(c->prof.ms.begin(), c->prof.ms.end(), 0.0);
+  return GPT2_OK;
+}
+
+int gpt2_profile_count(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  return (int)c->prof.names.size();
+}
+
+int gpt2_profile_entry(gpt2_ctx* c, int i, const char** name, int64_t* launches, double* total_ms) {
+  if (!c || i < 0 || i >= (int)c->prof.names.size()) return GPT2_ERR_ARG;
+  if (name) *name = c->prof.names[i].c_str();
+  if (launches) *launches = c->prof.counts[i];
+  if (total_ms) *total_ms = c->prof.ms[i];
+  return GPT2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,315 @@
+/*
+ * gpt2.h -- C-ABI of libgpt2hip.so: one GPT-2 training micro-step and
+ * optimizer step on an AMD Instinct MI355X (gfx950).
+ *
+ * The calls mirror the training loop the pages print:
+ *   optimizer.zero_grad(); for each micro-step { loss = model(x, y) / G;
+ *   loss.backward(); } clip_grad_norm_(params, 1.0); optimizer.step()
+ *   ("How I trained my own GPT-2 124M on FineWeb-Edu", sections 8.1 and 9;
+ *    "Reproduce GPT-2 124M 复盘", training-optimisation list: clipping;
+ *    "Making Training Fast on One GPU", "How the measurements were taken").
+ *
+ * Conventions shared by every entry point
+ *  - Memory: every device buffer is allocated and owned by the caller.  The
+ *    library allocates no device memory; it keeps the pointers it is given,
+ *    which must stay valid until gpt2_destroy.  Sizes come from
+ *    gpt2_query_sizes.  Pointers named d_* are device pointers.
+ *  - Streams: `stream` arguments are hipStream_t values passed as void*
+ *    (NULL = the default stream).  Every call is asynchronous on its stream;
+ *    only gpt2_get_status synchronises.
+ *  - Layouts: row-major.  Tokens and targets are int32 [B, T].  Linear
+ *    weights are [out, in] (nn.Linear).  The parameter table (order, offsets,
+ *    shapes) is given by gpt2_param_info.
+ *  - Errors: host-checkable problems (null pointers, shapes, limits) are
+ *    returned immediately as a negative gpt2_status and nothing is enqueued.
+ *    Device-detected problems (an out-of-range token or target id, a
+ *    non-finite gradient norm) set a flag in the context: kernels clamp the
+ *    offending index so no access leaves its buffer, and the flag is
+ *    reported (and cleared) by gpt2_get_status.
+ *  - Threads: one context is used by one host thread at a time.
+ */
+#ifndef GPT2_HIP_H
+#define GPT2_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT2_OK = 0,
+  GPT2_WARN_NO_TARGETS = 1, /* a micro-batch had no valid target: loss is NaN, no gradient added */
+  GPT2_ERR_ARG = -1,        /* null pointer, bad enum or out-of-range scalar */
+  GPT2_ERR_SHAPE = -2,      /* B, T, M, N, K or config not supported */
+  GPT2_ERR_HIP = -3,        /* a HIP runtime call failed */
+  GPT2_ERR_UNBOUND = -4,    /* a required buffer was not given */
+  GPT2_ERR_BAD_ID = -5,     /* a token id outside [0, V) or a target outside [0, V) and not -1 */
+  GPT2_ERR_NONFINITE = -6   /* the global gradient norm was not finite: the update was skipped */
+} gpt2_status;
+
+enum { GPT2_PRECISION_FP32 = 0, GPT2_PRECISION_BF16 = 1 };
+
+/* Model and capacity.  GPT2Config of "How I trained my own GPT-2 124M on
+ * FineWeb-Edu" section 2.1 plus the MLP width (section 2.6, 4 * n_embd for
+ * GPT-2), the largest micro-batch the buffers are sized for, and the compute
+ * precision:
+ *   FP32: every tensor and every product in float32.
+ *   BF16: bfloat16 operands for the matrix products and attention, with
+ *         float32 accumulation, float32 master weights, gradients, optimizer
+ *         state, residual streams, norm and softmax statistics and loss
+ *         ("Making Training Fast on One GPU", Step 1, BF16 autocast).
+ * Limits: n_embd % n_head == 0; head_dim = n_embd / n_head must be 64 in
+ * BF16 mode and at most 64 in FP32 mode; in BF16 mode vocab_size, n_embd and
+ * mlp_hidden must be multiples of 8 (the page pads the vocabulary to 50304
+ * for the same alignment reason, section 8.3). */
+typedef struct {
+  int32_t vocab_size;
+  int32_t block_size;
+  int32_t n_layer;
+  int32_t n_head;
+  int32_t n_embd;
+  int32_t mlp_hidden;
+  int32_t max_batch;
+  int32_t precision;
+} gpt2_config;
+
+/* Byte sizes of the caller-owned buffers. */
+typedef struct {
+  size_t n_params;          /* number of parameters (tied wte counted once) */
+  size_t n_elems;           /* elements of the flat parameter buffer (with alignment padding) */
+  int32_t n_tensors;        /* entries of the parameter table */
+  int32_t n_decayed;        /* leading entries with weight decay (dim >= 2) */
+  size_t params_bytes;      /* float32 [n_elems] master weights */
+  size_t grads_bytes;       /* float32 [n_elems] gradients */
+  size_t adam_m_bytes;      /* float32 [n_elems] first moment */
+  size_t adam_v_bytes;      /* float32 [n_elems] second moment */
+  size_t shadow_bytes;      /* bfloat16 [n_elems] copy of the weights (0 in FP32 mode) */
+  size_t activations_bytes; /* activations kept for the backward, for max_batch x block_size */
+  size_t scratch_bytes;     /* per-call temporaries */
+} gpt2_sizes;
+
+typedef struct {
+  void *params, *grads, *adam_m, *adam_v, *shadow, *activations, *scratch;
+} gpt2_buffers;
+
+/* AdamW hyper-parameters ("How I trained my own GPT-2 124M on FineWeb-Edu"
+ * section 6: betas (0.9, 0.95), eps 1e-8, decay only on dim >= 2;
+ * clip max_norm 1.0 from "Reproduce GPT-2 124M 复盘"). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay, max_norm;
+} gpt2_adamw;
+
+/* One entry of the parameter table: HF-style name, element offset into the
+ * flat buffers (params, grads, adam_m, adam_v, shadow share offsets), shape
+ * ([out, in] for Linear weights), and whether AdamW decays it. */
+typedef struct {
+  char name[64];
+  size_t offset;
+  int32_t ndim;
+  int32_t shape[2];
+  int32_t decayed;
+} gpt2_param_desc;
+
+typedef struct gpt2_ctx gpt2_ctx;
+
+/* ---------------------------------------------------------------- setup -- */
+
+/* Validate cfg and report buffer sizes.  Host only; no GPU needed.
+ * Returns GPT2_ERR_ARG / GPT2_ERR_SHAPE for an unsupported config. */
+int gpt2_query_sizes(const gpt2_config* cfg, gpt2_sizes* out);
+
+/* Entry idx (0 <= idx < n_tensors) of the parameter table: the GPT-2
+ * parameters of the named_parameters listing in "How I trained my own GPT-2
+ * 124M on FineWeb-Edu" section 2 (lm_head is wte, section 4), ordered with
+ * the decayed 2-D tensors first.  Host only. */
+int gpt2_param_info(const gpt2_config* cfg, int idx, gpt2_param_desc* out);
+
+/* Bind the caller's buffers (sizes from gpt2_query_sizes; shadow may be NULL
+ * in FP32 mode) and a stream.  *out receives the context.  The step counter
+ * starts at 0 and the device error flag is cleared. */
+int gpt2_create(const gpt2_config* cfg, const gpt2_buffers* bufs, void* stream, gpt2_ctx** out);
+int gpt2_destroy(gpt2_ctx* ctx);
+int gpt2_set_stream(gpt2_ctx* ctx, void* stream);
+
+/* Initialise every parameter: Linear weights and both embeddings ~ N(0,
+ * 0.02), the two residual projections (attn.c_proj, mlp.c_proj) ~ N(0, 0.02 /
+ * sqrt(2 n_layer)), biases 0, LayerNorm weight 1 and bias 0 ("How I trained
+ * my own GPT-2 124M on FineWeb-Edu" section 7).  Normals come from
+ * Philox4x32-10 (Salmon et al., SC 2011) with the Box-Muller transform:
+ * element j of table entry k under seed s uses counter (j/4 low, j/4 high,
+ * k, 0x6770), key (s low, s high), and takes output pair j%4/2 of the four
+ * words.  Also zeroes grads and both moments, refreshes the bf16 shadow and
+ * sets the step counter to 0. */
+int gpt2_init_params(gpt2_ctx* ctx, uint64_t seed);
+
+/* Refresh the bf16 shadow from the float32 master weights (after the caller
+ * wrote params directly).  No-op in FP32 mode. */
+int gpt2_sync_shadow(gpt2_ctx* ctx);
+
+/* ----------------------------------------------------------- train step -- */
+
+/* grads <- 0 (optimizer.zero_grad with set_to_none=False, the form "Making
+ * Training Fast on One GPU" found necessary under graph replay). */
+int gpt2_zero_grad(gpt2_ctx* ctx);
+
+/* One micro-step ("How I trained my own GPT-2 124M on FineWeb-Edu" sections
+ * 2.10-2.13, 4, 5, 8.1): the forward pass of the B x T tokens, the mean
+ * cross-entropy of the logits over all vocab_size columns against the
+ * targets (targets equal to -1 are ignored; the mean divides by the number
+ * of valid targets of this call: "Multi-GPU calculation of gradients for
+ * accelerated training", "Cross-entropy averages within one micro-batch"),
+ * and the backward pass, which ADDS d(loss_scale * loss)/d(theta) into
+ * grads (loss_scale = 1 / grad_accum_steps reproduces loss / grad_accum_steps).
+ *   d_tokens, d_targets: int32 [B, T] device arrays; tokens in [0, V),
+ *     targets in [0, V) or -1.  Out-of-range ids set GPT2_ERR_BAD_ID in the
+ *     context flag and are clamped.
+ *   1 <= B <= max_batch, 1 <= T <= block_size.
+ *   d_loss: device float, receives the UNSCALED mean loss of this micro-batch
+ *     (NaN if no target is valid; then nothing is added to grads and the flag
+ *     reports GPT2_WARN_NO_TARGETS).
+ *   d_token_loss: optional device float [B, T], per-position loss (0 where
+ *     the target is ignored).
+ * The logits are never stored whole: the tied lm_head and the loss run over
+ * row chunks. */
+int gpt2_fwd_bwd(gpt2_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targets, int B, int T,
+                 float loss_scale, float* d_loss, float* d_token_loss);
+
+/* Global-norm clipping then AdamW on every parameter, one fused pass
+ * ("Reproduce GPT-2 124M 复盘": clip_grad_norm_(params, 1.0) and fused AdamW;
+ * "How I trained my own GPT-2 124M on FineWeb-Edu" section 6: betas, eps, and
+ * decay only on dim >= 2).  Increments the step counter t, then
+ *   norm = ||grads||_2 over every parameter;  coef = min(1, max_norm / (norm + 1e-6))
+ *   g = coef * grad;  p *= 1 - lr*wd (decayed tensors only)
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2
+ *   p -= lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ * and refreshes the bf16 shadow.  grads are left as they were (unclipped).
+ * d_grad_norm (optional device float) receives the pre-clip norm.  A
+ * non-finite norm leaves params, m and v unchanged and sets
+ * GPT2_ERR_NONFINITE in the context flag (t is still incremented). */
+int gpt2_clip_adamw_step(gpt2_ctx* ctx, const gpt2_adamw* hp, float* d_grad_norm);
+
+int gpt2_get_step(gpt2_ctx* ctx, int64_t* t);
+int gpt2_set_step(gpt2_ctx* ctx, int64_t t);
+
+/* Synchronise the context's stream, then return (and clear) the device
+ * flag: GPT2_OK, GPT2_WARN_NO_TARGETS, GPT2_ERR_BAD_ID or
+ * GPT2_ERR_NONFINITE (the most severe seen since the last call), or
+ * GPT2_ERR_HIP if the stream reported an error. */
+int gpt2_get_status(gpt2_ctx* ctx);
+
+const char* gpt2_strerror(int status);
+
+/* --------------------------------------------- isolated lm_head + loss -- */
+
+/* Bytes of scratch gpt2_lmhead_ce needs for M rows, width C, vocab V. */
+size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V);
+
+/* Tied lm_head and mean cross-entropy, forward and backward, for M rows
+ * ("How I trained my own GPT-2 124M on FineWeb-Edu" section 4: logits =
+ * hidden @ weight^T without bias, cross-entropy over every column; rows with
+ * target -1 ignored, the mean divides by the valid count).
+ *   d_hidden: bf16 [M, C]; d_weight: bf16 [V, C]; d_targets: int32 [M].
+ *   d_loss: device float, the mean loss (NaN if no target is valid).
+ *   d_dhidden: bf16 [M, C], written: d(loss)/d(hidden).
+ *   d_dweight: float32 [V, C], d(loss)/d(weight) is ADDED to it.
+ *   d_scratch: gpt2_lmhead_ce_scratch_bytes(M, C, V) bytes.
+ *   d_flag: optional device int32, receives GPT2_ERR_BAD_ID if a target is
+ *     out of range (else left unchanged).
+ * C and V must be multiples of 8, M >= 1.  Logits are formed one row chunk
+ * at a time and never stored whole. */
+int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, const int32_t* d_targets,
+                   int M, int C, int V, float* d_loss, void* d_dhidden, float* d_dweight,
+                   void* d_scratch, int32_t* d_flag);
+
+/* ------------------------------------------------------- single kernels -- */
+/* The building blocks of the step, exposed for kernel-level parity tests and
+ * measurement.  All are asynchronous on `stream`. */
+
+/* Matrix product C = alpha * op(A) op(B)^T with an epilogue.
+ * op(A) is [M, K]: a_kmajor=1 means A is stored [M][lda] (K contiguous),
+ *   a_kmajor=0 means A is stored [K][lda] (M contiguous).
+ * op(B) is [N, K]: b_kmajor=1 means B is stored [N][ldb] (K contiguous),
+ *   b_kmajor=0 means B is stored [K][ldb] (N contiguous).
+ * dtype: GPT2_PRECISION_BF16 (A, B bf16, MFMA with float32 accumulation) or
+ *   GPT2_PRECISION_FP32 (A, B float32).
+ * epilogue, with v = alpha * acc + (bias ? bias[n] : 0):
+ *   GPT2_EPI_STORE:      C[m][n] = v                        (C in out_bf16 ? bf16 : float32)
+ *   GPT2_EPI_RESIDUAL:   C[m][n] = R[m][n] + v              (float32; R may equal C)
+ *   GPT2_EPI_GELU:       C[m][n] = v, C2[m][n] = gelu_tanh(C[m][n])  (both out dtype)
+ *   GPT2_EPI_DGELU:      C[m][n] = v * gelu_tanh'(U[m][n])   (U in out dtype)
+ *   GPT2_EPI_ACCUMULATE: C[m][n] += v                       (float32)
+ * ldc is the row pitch of C, C2, R and U.  For bf16, M, N, K, lda, ldb, ldc
+ * must be multiples of 8 and pointers 16-byte aligned. */
+enum {
+  GPT2_EPI_STORE = 0,
+  GPT2_EPI_RESIDUAL = 1,
+  GPT2_EPI_GELU = 2,
+  GPT2_EPI_DGELU = 3,
+  GPT2_EPI_ACCUMULATE = 4
+};
+typedef struct {
+  int32_t M, N, K;
+  int32_t dtype;
+  int32_t a_kmajor, b_kmajor;
+  int64_t lda, ldb, ldc;
+  const void* A;
+  const void* B;
+  void* C;
+  void* C2;
+  const float* R;
+  const void* U;
+  const float* bias;
+  float alpha;
+  int32_t epilogue;
+  int32_t out_bf16;
+} gpt2_gemm_args;
+int gpt2_op_gemm(void* stream, const gpt2_gemm_args* args);
+
+/* Column sums: db[n] += sum_m Y[m][n], Y [M][ld] in bf16 (y_bf16=1) or float32. */
+int gpt2_op_colsum(void* stream, const void* d_y, int y_bf16, int M, int N, int64_t ld, float* d_db);
+
+/* LayerNorm over rows of x [rows, C] float32 ("How I trained my own GPT-2
+ * 124M on FineWeb-Edu" section 2.3, nn.LayerNorm defaults: eps 1e-5, biased
+ * variance): y = (x - mean) * rstd * w + b, y in bf16 (y_bf16=1) or float32;
+ * mean and rstd float32 [rows] are written for the backward. */
+int gpt2_op_layernorm_fwd(void* stream, const float* d_x, const float* d_w, const float* d_b, void* d_y,
+                          int y_bf16, float* d_mean, float* d_rstd, int rows, int C);
+/* Backward of the above for dy float32 [rows, C]: dx is ADDED to d_dx, and
+ * sum over rows of dy * xhat and of dy are ADDED to d_dw and d_db. */
+int gpt2_op_layernorm_bwd(void* stream, const float* d_dy, const float* d_x, const float* d_mean,
+                          const float* d_rstd, const float* d_w, float* d_dx, float* d_dw, float* d_db,
+                          int rows, int C);
+
+/* Causal multi-head attention ("How I trained my own GPT-2 124M on
+ * FineWeb-Edu" sections 2.12 and 5): qkv [B*T, 3*H*hd] holds q | k | v column
+ * thirds, head h at columns h*hd of each third; y [B*T, H*hd] receives the
+ * concatenated heads; lse float32 [B, H, T] the row log-sum-exp of the scaled
+ * scores (natural log).  dtype selects bf16 or float32 tensors. */
+int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv,
+                          void* d_y, float* d_lse);
+/* Backward: dqkv [B*T, 3*H*hd] is written.  d_scratch needs
+ * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes. */
+size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H);
+int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv,
+                          const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
+                          void* d_scratch);
+
+/* ---------------------------------------------------------- measurement -- */
+
+/* When enabled, the context brackets every kernel launch it makes with HIP
+ * events on its stream and accumulates, per launch site, the number of
+ * launches and their summed duration.  Site names are stable strings such
+ * as "gemm.fc_fwd" or "attn.fwd". */
+int gpt2_profile_enable(gpt2_ctx* ctx, int on);
+int gpt2_profile_reset(gpt2_ctx* ctx);
+int gpt2_profile_count(gpt2_ctx* ctx);
+/* Entry i: site name (static storage), launches, summed milliseconds.  Call
+ * after gpt2_get_status so the events have completed. */
+int gpt2_profile_entry(gpt2_ctx* ctx, int i, const char** name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_HIP_H */

@@ -113,10 +113,11 @@ def random_params(specs, seed: int = PARAM_SEED, matrix_std: float = 0.02, vecto
     rng = np.random.default_rng(seed)
     out = {}
     for name, shape in specs:
+        z = rng.standard_normal(shape, dtype=np.float32)
         if len(shape) >= 2:
-            out[name] = (matrix_std * rng.standard_normal(shape)).astype(np.float32)
+            out[name] = np.float32(matrix_std) * z
         elif "ln_" in name and name.endswith("weight"):
-            out[name] = (1.0 + vector_std * rng.standard_normal(shape)).astype(np.float32)
+            out[name] = np.float32(1.0) + np.float32(vector_std) * z
         else:
-            out[name] = (vector_std * rng.standard_normal(shape)).astype(np.float32)
+            out[name] = np.float32(vector_std) * z
     return out

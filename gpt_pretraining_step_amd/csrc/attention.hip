@@ -21,7 +21,7 @@
 //
 // float32 (FP32 precision mode, small heads): one thread per query (or key),
 // plain loops.
-#include "common.h"
+#include "tile_io.h"
 
 namespace g2 {
 
@@ -124,67 +124,37 @@ __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv, const fl
 }
 
 // ============================================================ bf16 kernels
+//
+// Tiles of 64 rows x 64 head dims (128-byte rows) are copied from HBM into
+// LDS by DMA, double-buffered: the next tile's copy is in flight while the
+// current one is multiplied, one barrier per tile.  Rows are stored with
+// their 16-byte chunks swizzled (tile_io.h).  Operands read along a row
+// (K, V, Q, dO rows) use 16-byte LDS reads; operands read along a column
+// (V^T, K^T, Q^T, dO^T) use the transposing LDS read, so no tile is ever
+// transposed in memory.
 
 constexpr int HD = 64;
-constexpr int RP = HD + 8;  // pitch of [row][d] tiles (elements)
-constexpr int TP = 64 + 8;  // pitch of [d][row] tiles (elements)
 
 union V8 {
   uint4 u;
   bf16x8 v;
   uint32_t w[4];
 };
-union V4 {
-  uint2 u;
-  bf16x4 v;
-};
 
-// rows row0..row0+63 of a [*, ld] bf16 matrix (columns 0..63 from g) -> LDS
-// [64][RP]; rows >= nrows are zero.
-__device__ __forceinline__ void load_rows64(bf16* lds, const bf16* __restrict__ g, int64_t ld, int row0, int nrows) {
-  for (int c = threadIdx.x; c < 64 * 8; c += 256) {
-    const int r = c >> 3, c8 = c & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < nrows) v = *reinterpret_cast<const uint4*>(g + (int64_t)(row0 + r) * ld + 8 * c8);
-    *reinterpret_cast<uint4*>(lds + r * RP + 8 * c8) = v;
-  }
+// MFMA operand: row `row` of a swizzled tile, k-slots 16kk + 8lg .. +7.
+__device__ __forceinline__ bf16x8 rowfrag(const bf16* t, int row, int kk, int lg) {
+  return *reinterpret_cast<const bf16x8*>(t + row * HD + 8 * swz_chunk<64>(row, 2 * kk + lg));
 }
-
-// dst[d][r] = src[r][d] for a 64x64 tile; 64 threads, one 8x8 block each.
-__device__ __forceinline__ void transpose64(bf16* dst, const bf16* src, int tid) {
-  if (tid < 0 || tid >= 64) return;
-  const int rb = tid >> 3, db = tid & 7;
-  V8 in[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) in[j].u = *reinterpret_cast<const uint4*>(src + (8 * rb + j) * RP + 8 * db);
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int word = dd >> 1;
-    const bool hi = dd & 1;
-    V8 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = in[2 * q].w[word], b = in[2 * q + 1].w[word];
-      o.w[q] = hi ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-    *reinterpret_cast<uint4*>(dst + (8 * db + dd) * TP + 8 * rb) = o.u;
-  }
-}
-
-// MFMA operand holding row (base + lane%32), k-slots 16kk + 8g .. +7 of a
-// [row][d] tile.
-__device__ __forceinline__ bf16x8 row_frag(const bf16* t, int base, int kk, int lr, int lg) {
-  return *reinterpret_cast<const bf16x8*>(t + (base + lr) * RP + 16 * kk + 8 * lg);
-}
-// MFMA operand from a [d][row] tile: row d, k-slots mapped to rows
-// kbase + 8*(e/4) + 4g + e%4 (the accumulator row order).
-__device__ __forceinline__ bf16x8 tr_frag(const bf16* t, int d, int kbase, int lg) {
-  V4 a, b;
-  a.u = *reinterpret_cast<const uint2*>(t + d * TP + kbase + 4 * lg);
-  b.u = *reinterpret_cast<const uint2*>(t + d * TP + kbase + 8 + 4 * lg);
+// MFMA operand: column d = d0 + lane%32 of a swizzled tile, with k-slots in
+// the accumulator row order: slots 0..3 <-> rows r0 + 4lg + 0..3, slots
+// 4..7 <-> rows r0 + 8 + 4lg + 0..3.
+__device__ __forceinline__ bf16x8 colfrag(const bf16* t, int r0, int d0, int lg) {
+  const int h = (threadIdx.x >> 4) & 1;
+  const bf16x4 a = tr_read4(t, r0 + 4 * lg, d0 + 16 * h);
+  const bf16x4 b = tr_read4(t, r0 + 8 + 4 * lg, d0 + 16 * h);
   bf16x8 r;
-  r[0] = a.v[0]; r[1] = a.v[1]; r[2] = a.v[2]; r[3] = a.v[3];
-  r[4] = b.v[0]; r[5] = b.v[1]; r[6] = b.v[2]; r[7] = b.v[3];
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
 }
 // registers 8s..8s+7 of an accumulator, as a bf16 operand
@@ -209,13 +179,19 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
-// Forward: block = 4 waves x 32 queries; loop over 64-key blocks.
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
-                                                            float* __restrict__ lse, int T, int H, float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * RP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * RP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[64 * TP];
-  const int nqb = (T + 127) / 128;
+// Wait for this wave's outstanding DMA and LDS writes, then meet the other
+// waves (no fence: later tiles' copies are not in flight at this point).
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Forward.  Block = NW waves x 32 queries; loop over 64-key tiles.  Each lane
+// owns one query (S^T = K Q^T, O^T = V^T P^T), so the online-softmax state is
+// per lane, shared with the partner lane 32 away.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+                                                                float* __restrict__ lse, int T, int H, float sl2) {
+  constexpr int BQ = 32 * NW;
+  __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][K, V]
+  const int nqb = (T + BQ - 1) / BQ;
   const int qb = nqb - 1 - blockIdx.x;  // longest rows first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
@@ -224,7 +200,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16* __restri
   const bf16* Vg = Qg + 2 * C;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int q0 = qb * 128 + wave * 32;
+  const int q0 = qb * BQ + wave * 32;
   const int qi = q0 + lr;
 
   bf16x8 qf[4];
@@ -232,30 +208,38 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16* __restri
   for (int kk = 0; kk < 4; ++kk) qf[kk] = (qi < T) ? load8(Qg + (int64_t)qi * C3 + 16 * kk + 8 * lg) : zero8();
   f32x16 oT[2] = {zero16(), zero16()};
   float m = -1e30f, l = 0.f;
-  const int kv_end = min(T, qb * 128 + 128);
-  for (int kb = 0; kb < kv_end; kb += 64) {
-    __syncthreads();
-    load_rows64(Ks, Kg, C3, kb, T);
-    load_rows64(Vs, Vg, C3, kb, T);
-    __syncthreads();
-    transpose64(Vt, Vs, threadIdx.x);
-    __syncthreads();
+  const int kv_end = min(T, qb * BQ + BQ);
+  const int ntiles = (kv_end + 63) / 64;
+  auto issue = [&](int st, int tile) {
+    dma_rows<64, 64, NW>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
+    dma_rows<64, 64, NW>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
+  };
+  issue(0, 0);
+  for (int jt = 0; jt < ntiles; ++jt) {
+    tile_barrier();
+    if (jt + 1 < ntiles) issue((jt + 1) & 1, jt + 1);
+    const int kb = jt * 64;
     if (q0 >= T || kb > q0 + 31) continue;
+    const bf16* Ks = sm[jt & 1][0];
+    const bf16* Vs = sm[jt & 1][1];
     f32x16 sT[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       sT[c] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sT[c] = MFMA(row_frag(Ks, 32 * c, kk, lr, lg), qf[kk], sT[c]);
+      for (int kk = 0; kk < 4; ++kk) sT[c] = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT[c]);
     }
+    const bool edge = (kb + 63 > q0) || (kb + 63 >= T);
     float mx = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
         float v = sT[c][r] * sl2;
-        if (key > qi || key >= T) v = -INFINITY;
+        if (edge) {
+          const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (key > qi || key >= T) v = -INFINITY;
+        }
         sT[c][r] = v;
         mx = fmaxf(mx, v);
       }
@@ -283,7 +267,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16* __restri
       for (int s = 0; s < 2; ++s) {
         const bf16x8 pb = acc_frag(sT[c], s);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) oT[dt] = MFMA(tr_frag(Vt, 32 * dt + lr, 32 * c + 16 * s, lg), pb, oT[dt]);
+        for (int dt = 0; dt < 2; ++dt) oT[dt] = MFMA(colfrag(Vs, 32 * c + 16 * s, 32 * dt, lg), pb, oT[dt]);
       }
   }
   l += __shfl_xor(l, 32);
@@ -304,15 +288,16 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16* __restri
 }
 
 // Backward, pass 1: D = rowsum(dO o O) and dQ.  Same tiling as the forward.
-__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(const bf16* __restrict__ qkv,
-                                                               const bf16* __restrict__ y, const bf16* __restrict__ dy,
-                                                               const float* __restrict__ lse, bf16* __restrict__ dqkv,
-                                                               float* __restrict__ Dbuf, int T, int H, float scale,
-                                                               float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * RP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * RP];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[64 * TP];
-  const int nqb = (T + 127) / 128;
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* __restrict__ qkv,
+                                                                   const bf16* __restrict__ y,
+                                                                   const bf16* __restrict__ dy,
+                                                                   const float* __restrict__ lse,
+                                                                   bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
+                                                                   int T, int H, float scale, float sl2) {
+  constexpr int BQ = 32 * NW;
+  __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][K, V]
+  const int nqb = (T + BQ - 1) / BQ;
   const int qb = nqb - 1 - blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
@@ -323,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(const bf16* __res
   const bf16* dOg = dy + (int64_t)b * T * C + h * HD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int q0 = qb * 128 + wave * 32;
+  const int q0 = qb * BQ + wave * 32;
   const int qi = q0 + lr;
   const bool qv = qi < T;
 
@@ -348,15 +333,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(const bf16* __res
   const float lse2 = qv ? lse[(int64_t)bh * T + qi] * kLOG2E : 0.f;
 
   f32x16 dqT[2] = {zero16(), zero16()};
-  const int kv_end = min(T, qb * 128 + 128);
-  for (int kb = 0; kb < kv_end; kb += 64) {
-    __syncthreads();
-    load_rows64(Ks, Kg, C3, kb, T);
-    load_rows64(Vs, Vg, C3, kb, T);
-    __syncthreads();
-    transpose64(Kt, Ks, threadIdx.x);
-    __syncthreads();
+  const int kv_end = min(T, qb * BQ + BQ);
+  const int ntiles = (kv_end + 63) / 64;
+  auto issue = [&](int st, int tile) {
+    dma_rows<64, 64, NW>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
+    dma_rows<64, 64, NW>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
+  };
+  issue(0, 0);
+  for (int jt = 0; jt < ntiles; ++jt) {
+    tile_barrier();
+    if (jt + 1 < ntiles) issue((jt + 1) & 1, jt + 1);
+    const int kb = jt * 64;
     if (q0 >= T || kb > q0 + 31) continue;
+    const bf16* Ks = sm[jt & 1][0];
+    const bf16* Vs = sm[jt & 1][1];
     f32x16 sT[2], dpT[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -364,16 +354,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(const bf16* __res
       dpT[c] = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        sT[c] = MFMA(row_frag(Ks, 32 * c, kk, lr, lg), qf[kk], sT[c]);
-        dpT[c] = MFMA(row_frag(Vs, 32 * c, kk, lr, lg), dof[kk], dpT[c]);
+        sT[c] = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT[c]);
+        dpT[c] = MFMA(rowfrag(Vs, 32 * c + lr, kk, lg), dof[kk], dpT[c]);
       }
     }
+    const bool edge = (kb + 63 > q0) || (kb + 63 >= T);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
-        const float p = (key <= qi && key < T) ? exp2f(sT[c][r] * sl2 - lse2) : 0.f;
+        float p = exp2f(sT[c][r] * sl2 - lse2);
+        if (edge) {
+          const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (key > qi || key >= T) p = 0.f;
+        }
         sT[c][r] = p * (dpT[c][r] - D);
       }
 #pragma unroll
@@ -382,7 +376,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(const bf16* __res
       for (int s = 0; s < 2; ++s) {
         const bf16x8 db = acc_frag(sT[c], s);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) dqT[dt] = MFMA(tr_frag(Kt, 32 * dt + lr, 32 * c + 16 * s, lg), db, dqT[dt]);
+        for (int dt = 0; dt < 2; ++dt) dqT[dt] = MFMA(colfrag(Ks, 32 * c + 16 * s, 32 * dt, lg), db, dqT[dt]);
       }
   }
   if (qv) {
@@ -399,20 +393,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(const bf16* __res
   }
 }
 
-// Backward, pass 2: dK and dV.  Block = 4 waves x 32 keys; loop over 64-query
-// blocks from the block's diagonal to T.
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(const bf16* __restrict__ qkv,
-                                                                 const bf16* __restrict__ dy,
-                                                                 const float* __restrict__ lse,
-                                                                 const float* __restrict__ Dbuf,
-                                                                 bf16* __restrict__ dqkv, int T, int H, float scale,
-                                                                 float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[64 * RP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[64 * RP];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[64 * TP];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[64 * TP];
-  __shared__ __attribute__((aligned(16))) float lse_s[64];
-  __shared__ __attribute__((aligned(16))) float D_s[64];
+// Backward, pass 2: dK and dV.  Block = NW waves x 32 keys; loop over 64-query
+// tiles from the block's diagonal to T.  Each lane owns one key (S = Q K^T).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_bf16_kernel(const bf16* __restrict__ qkv,
+                                                                     const bf16* __restrict__ dy,
+                                                                     const float* __restrict__ lse,
+                                                                     const float* __restrict__ Dbuf,
+                                                                     bf16* __restrict__ dqkv, int T, int H,
+                                                                     float scale, float sl2) {
+  constexpr int BK = 32 * NW;
+  __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse, D]
   const int kblk = blockIdx.x;  // smallest keys (most queries) first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
@@ -420,9 +412,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(const bf16* __r
   const bf16* Kg = Qg + C;
   const bf16* Vg = Qg + 2 * C;
   const bf16* dOg = dy + (int64_t)b * T * C + h * HD;
+  const float* lseg = lse + (int64_t)bh * T;
+  const float* Dg = Dbuf + (int64_t)bh * T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int k0 = kblk * 128 + wave * 32;
+  const int k0 = kblk * BK + wave * 32;
   const int kj = k0 + lr;
   const bool kvld = kj < T;
 
@@ -433,21 +427,43 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(const bf16* __r
     vf[kk] = kvld ? load8(Vg + (int64_t)kj * C3 + 16 * kk + 8 * lg) : zero8();
   }
   f32x16 dvT[2] = {zero16(), zero16()}, dkT[2] = {zero16(), zero16()};
-  for (int qs = kblk * 128; qs < T; qs += 64) {
-    __syncthreads();
-    load_rows64(Qs, Qg, C3, qs, T);
-    load_rows64(dOs, dOg, C, qs, T);
-    if (threadIdx.x < 64) {
-      const int q = qs + threadIdx.x;
-      lse_s[threadIdx.x] = (q < T) ? lse[(int64_t)bh * T + q] * kLOG2E : INFINITY;
-      D_s[threadIdx.x] = (q < T) ? Dbuf[(int64_t)bh * T + q] : 0.f;
+  const int qstart = kblk * BK;
+  const int ntiles = (T - qstart + 63) / 64;
+  // Q and dO tiles by DMA; the tile's 64 lse and D values through registers
+  // of wave 0, written to LDS after the current tile's compute.
+  float lse_r = 0.f, d_r = 0.f;
+  const bool w0 = __builtin_amdgcn_readfirstlane(wave) == 0;
+  auto issue = [&](int st, int tile) {
+    const int q0t = qstart + tile * 64;
+    dma_rows<64, 64, NW>(sm[st][0], Qg, C3, q0t, T, 0, HD);
+    dma_rows<64, 64, NW>(sm[st][1], dOg, C, q0t, T, 0, HD);
+    if (w0) {
+      const int q = q0t + lane;
+      lse_r = (q < T) ? lseg[q] : 0.f;
+      d_r = (q < T) ? Dg[q] : 0.f;
     }
-    __syncthreads();
-    transpose64(Qt, Qs, threadIdx.x);
-    transpose64(dOt, dOs, threadIdx.x - 64);
-    __syncthreads();
-    if (k0 >= T) continue;
-    if (qs + 63 < k0) continue;
+  };
+  auto commit = [&](int st) {
+    if (w0) {
+      rowst[st][0][lane] = lse_r;
+      rowst[st][1][lane] = d_r;
+    }
+  };
+  issue(0, 0);
+  commit(0);
+  for (int jt = 0; jt < ntiles; ++jt) {
+    tile_barrier();
+    const bool more = jt + 1 < ntiles;
+    if (more) issue((jt + 1) & 1, jt + 1);
+    const int qs = qstart + jt * 64;
+    if (k0 >= T || qs + 63 < k0) {
+      if (more) commit((jt + 1) & 1);
+      continue;
+    }
+    const bf16* Qs = sm[jt & 1][0];
+    const bf16* dOs = sm[jt & 1][1];
+    const float* Ls = rowst[jt & 1][0];
+    const float* Ds = rowst[jt & 1][1];
     f32x16 sc[2], dp[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -455,26 +471,30 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(const bf16* __r
       dp[c] = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        sc[c] = MFMA(row_frag(Qs, 32 * c, kk, lr, lg), kf[kk], sc[c]);
-        dp[c] = MFMA(row_frag(dOs, 32 * c, kk, lr, lg), vf[kk], dp[c]);
+        sc[c] = MFMA(rowfrag(Qs, 32 * c + lr, kk, lg), kf[kk], sc[c]);
+        dp[c] = MFMA(rowfrag(dOs, 32 * c + lr, kk, lg), vf[kk], dp[c]);
       }
     }
+    const bool edge = (qs < k0 + 31) || (qs + 63 >= T);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int ql = 32 * c + 8 * a + 4 * lg;
-        const float4 L4 = *reinterpret_cast<const float4*>(lse_s + ql);
-        const float4 D4 = *reinterpret_cast<const float4*>(D_s + ql);
-        const float Ls[4] = {L4.x, L4.y, L4.z, L4.w};
-        const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+        const float4 L4 = *reinterpret_cast<const float4*>(Ls + ql);
+        const float4 D4 = *reinterpret_cast<const float4*>(Ds + ql);
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+        const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          const int q = qs + ql + e;
-          const float p = (kj <= q && q < T) ? exp2f(sc[c][r] * sl2 - Ls[e]) : 0.f;
+          float p = exp2f(sc[c][r] * sl2 - Lv[e] * kLOG2E);
+          if (edge) {
+            const int q = qs + ql + e;
+            if (kj > q || q >= T) p = 0.f;
+          }
           sc[c][r] = p;
-          dp[c][r] = p * (dp[c][r] - Ds[e]);
+          dp[c][r] = p * (dp[c][r] - Dv[e]);
         }
       }
 #pragma unroll
@@ -485,10 +505,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(const bf16* __r
         const bf16x8 db = acc_frag(dp[c], s);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          dvT[dt] = MFMA(tr_frag(dOt, 32 * dt + lr, 32 * c + 16 * s, lg), pb, dvT[dt]);
-          dkT[dt] = MFMA(tr_frag(Qt, 32 * dt + lr, 32 * c + 16 * s, lg), db, dkT[dt]);
+          dvT[dt] = MFMA(colfrag(dOs, 32 * c + 16 * s, 32 * dt, lg), pb, dvT[dt]);
+          dkT[dt] = MFMA(colfrag(Qs, 32 * c + 16 * s, 32 * dt, lg), db, dkT[dt]);
         }
       }
+    if (more) commit((jt + 1) & 1);
   }
   if (kvld) {
     bf16* ok = dqkv + ((int64_t)b * T + kj) * C3 + C + h * HD;
@@ -516,8 +537,9 @@ hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H,
   const float scale = 1.f / sqrtf((float)hd);
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
-    dim3 grid((T + 127) / 128, B * H);
-    attn_fwd_bf16_kernel<<<grid, 256, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<bf16*>(y), lse, T, H,
+    constexpr int NW = 4;
+    dim3 grid((T + 32 * NW - 1) / (32 * NW), B * H);
+    attn_fwd_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<bf16*>(y), lse, T, H,
                                                      scale * kLOG2E);
   } else {
     const int n = B * H * T;
@@ -536,11 +558,12 @@ hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H,
   float* Dbuf = static_cast<float*>(scratch);
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
-    dim3 grid((T + 127) / 128, B * H);
-    attn_bwd_dq_bf16_kernel<<<grid, 256, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(y),
+    constexpr int NW = 4;
+    dim3 grid((T + 32 * NW - 1) / (32 * NW), B * H);
+    attn_bwd_dq_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(y),
                                                         static_cast<const bf16*>(dy), lse, static_cast<bf16*>(dqkv),
                                                         Dbuf, T, H, scale, scale * kLOG2E);
-    attn_bwd_dkdv_bf16_kernel<<<grid, 256, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(dy),
+    attn_bwd_dkdv_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(dy),
                                                           lse, Dbuf, static_cast<bf16*>(dqkv), T, H, scale,
                                                           scale * kLOG2E);
   } else {

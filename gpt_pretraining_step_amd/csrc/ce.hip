@@ -36,7 +36,8 @@ __global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __re
 
 // One block per row: online (max, sum of exp) over the row, then
 // loss_row = lse - z[target], dlogits = scale / count * (softmax - onehot).
-template <typename LT, typename DT>
+// VEC: V % 4 == 0 and float32 logits, read as float4.
+template <typename LT, typename DT, bool VEC>
 __global__ __launch_bounds__(256) void ce_rows_kernel(const LT* __restrict__ logits, int64_t ld_l, DT* __restrict__ dl,
                                                       int64_t ld_d, const int32_t* __restrict__ tgt, int V,
                                                       const int* __restrict__ count, float scale,
@@ -44,14 +45,29 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const LT* __restrict__ log
   const int r = blockIdx.x;
   const LT* z = logits + (int64_t)r * ld_l;
   float m = -INFINITY, s = 0.f;
-  for (int v = threadIdx.x; v < V; v += 256) {
-    const float x = to_f<LT>(z[v]) * LOG2E;
+  auto upd = [&](float x) {
+    x *= LOG2E;
     if (x > m) {
       s = s * exp2f(m - x) + 1.f;
       m = x;
     } else {
       s += exp2f(x - m);
     }
+  };
+  if constexpr (VEC) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    for (int v = threadIdx.x; v < V / 4; v += 256) {
+      const float4 q = z4[v];
+      // one max per group of four, then the four exponentials
+      const float mx = fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)) * LOG2E;
+      if (mx > m) {
+        s *= exp2f(m - mx);
+        m = mx;
+      }
+      s += exp2f(q.x * LOG2E - m) + exp2f(q.y * LOG2E - m) + exp2f(q.z * LOG2E - m) + exp2f(q.w * LOG2E - m);
+    }
+  } else {
+    for (int v = threadIdx.x; v < V; v += 256) upd(to_f<LT>(z[v]));
   }
   __shared__ float sm[256], ss[256];
   sm[threadIdx.x] = m;
@@ -75,9 +91,27 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const LT* __restrict__ log
   if (threadIdx.x == 0) row_loss[r] = valid ? (lse2 * LN2 - to_f<LT>(z[t])) : 0.f;
   const float coef = (valid && n > 0) ? scale / (float)n : 0.f;
   DT* d = dl + (int64_t)r * ld_d;
-  for (int v = threadIdx.x; v < V; v += 256) {
-    const float p = exp2f(to_f<LT>(z[v]) * LOG2E - lse2);
-    d[v] = from_f<DT>(coef * (p - (v == t ? 1.f : 0.f)));
+  if constexpr (VEC) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    for (int v = threadIdx.x; v < V / 4; v += 256) {
+      const float4 q = z4[v];
+      float o[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = coef * (exp2f(o[e] * LOG2E - lse2) - (4 * v + e == t ? 1.f : 0.f));
+      if constexpr (sizeof(DT) == 2) {
+        bf16x4 ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = f2bf(o[e]);
+        *reinterpret_cast<bf16x4*>(d + 4 * v) = ob;
+      } else {
+        *reinterpret_cast<float4*>(d + 4 * v) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  } else {
+    for (int v = threadIdx.x; v < V; v += 256) {
+      const float p = exp2f(to_f<LT>(z[v]) * LOG2E - lse2);
+      d[v] = from_f<DT>(coef * (p - (v == t ? 1.f : 0.f)));
+    }
   }
 }
 
@@ -117,7 +151,13 @@ hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, 
                           const int32_t* tgt, int rows, int V, const int* count, float scale, float* /*loss_sum*/,
                           float* row_loss) {
   prof_begin(L);
-  ce_rows_kernel<LT, DT><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, count, scale, row_loss);
+  const bool vec = sizeof(LT) == 4 && V % 4 == 0 && ld_logits % 4 == 0 && ld_d % 4 == 0;
+  if (vec)
+    ce_rows_kernel<LT, DT, true><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, count, scale,
+                                                             row_loss);
+  else
+    ce_rows_kernel<LT, DT, false><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, count, scale,
+                                                              row_loss);
   prof_end(L);
   return hipGetLastError();
 }

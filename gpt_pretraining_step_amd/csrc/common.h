@@ -44,18 +44,23 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
 
-// GELU, tanh form ("How I trained my own GPT-2 124M on FineWeb-Edu" 2.13),
-// and its derivative.
-__device__ __forceinline__ float gelu_tanh(float u) {
-  const float k = 0.7978845608028654f;  // sqrt(2/pi)
-  float inner = k * (u + 0.044715f * u * u * u);
-  return 0.5f * u * (1.0f + tanhf(inner));
+// GELU, tanh form ("How I trained my own GPT-2 124M on FineWeb-Edu" 2.13):
+// 0.5 u (1 + tanh(z/2)) with z = 2 sqrt(2/pi) (u + 0.044715 u^3), which is
+// u * sigmoid(z) since 1 + tanh(z/2) = 2 sigmoid(z); evaluated with the
+// hardware exp2 and reciprocal.  The derivative is
+// sigmoid(z) + u sigmoid(z) (1 - sigmoid(z)) dz/du.
+__device__ __forceinline__ float gelu_sigmoid_arg(float u) {
+  const float k2 = 1.5957691216057308f;  // 2 sqrt(2/pi)
+  return k2 * fmaf(0.044715f * u, u * u, u);
 }
+__device__ __forceinline__ float fast_sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2f(-1.4426950408889634f * z));
+}
+__device__ __forceinline__ float gelu_tanh(float u) { return u * fast_sigmoid(gelu_sigmoid_arg(u)); }
 __device__ __forceinline__ float gelu_tanh_grad(float u) {
-  const float k = 0.7978845608028654f;
-  float inner = k * (u + 0.044715f * u * u * u);
-  float th = tanhf(inner);
-  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * k * (1.0f + 3.0f * 0.044715f * u * u);
+  const float s = fast_sigmoid(gelu_sigmoid_arg(u));
+  const float dz = 1.5957691216057308f * fmaf(3.0f * 0.044715f, u * u, 1.0f);
+  return s + u * s * (1.0f - s) * dz;
 }
 
 // Kernel launch bookkeeping: the runtime passes a Launch to every launcher,
@@ -73,7 +78,9 @@ void prof_end(const Launch& L);
 // Each returns a hipError_t from the launch (hipSuccess when fine) after
 // host-side shape checks done by the caller.
 
-hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, int* flag);
+// row_sum (optional): row_sum[m] += alpha * sum_k A(m, k) -- the bias gradient of
+// a weight-gradient product (bf16 only).
+hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum = nullptr);
 hipError_t launch_colsum(const Launch& L, const void* y, int y_bf16, int M, int N, int64_t ld, float* db);
 
 hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y,

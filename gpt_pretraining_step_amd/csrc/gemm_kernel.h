@@ -1,0 +1,373 @@
+// bf16 MFMA GEMM kernel template (dispatch in gemm.hip).
+//
+// C[m][n] = alpha * sum_k A(m,k) B(n,k), then a fused epilogue.  Block tile
+// BM x BN, K step BK, WGM x WGN waves, each wave owning a (BM/WGM) x (BN/WGN)
+// sub-tile of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, float32
+// accumulators).  STAGES LDS buffers form a pipeline: operands stored with K
+// contiguous ("K-major") are copied from global memory straight into LDS by
+// DMA (global_load_lds_dwordx4), so the loads of later K steps are in flight
+// while the current one is multiplied; operands whose K index is the slow one
+// in memory (the backward products) are loaded as 8x8 blocks, transposed in
+// registers and written to LDS.  In LDS every row holds BK elements with its
+// 16-byte chunks XOR-swizzled, which keeps both the DMA writes (1 KB of
+// consecutive bytes per wave instruction) and the 32-row MFMA operand reads
+// free of bank conflicts.
+#pragma once
+
+#include "tile_io.h"
+
+namespace g2 {
+
+struct GemmP {
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  const void* A;
+  const void* B;
+  void* C;
+  void* C2;
+  const float* R;
+  const void* U;
+  const float* bias;
+  float* row_sum;  // optional: row_sum[m] += sum over this product's K of A(m, k) (one column-tile adds it)
+  float alpha;
+  int tiles_m, tiles_n, splits, k_per_split;
+};
+
+template <int EPI, bool OUT_BF16, bool ATOMIC>
+__device__ __forceinline__ void epi_store(const GemmP& p, int m, int n, float acc) {
+  float v = p.alpha * acc;
+  if (p.bias) v += p.bias[n];
+  const int64_t idx = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == GPT2_EPI_STORE) {
+    if constexpr (OUT_BF16) static_cast<bf16*>(p.C)[idx] = f2bf(v);
+    else static_cast<float*>(p.C)[idx] = v;
+  } else if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+    static_cast<float*>(p.C)[idx] = p.R[idx] + v;
+  } else if constexpr (EPI == GPT2_EPI_GELU) {
+    if constexpr (OUT_BF16) {
+      bf16 u = f2bf(v);
+      static_cast<bf16*>(p.C)[idx] = u;
+      static_cast<bf16*>(p.C2)[idx] = f2bf(gelu_tanh(bf2f(u)));
+    } else {
+      static_cast<float*>(p.C)[idx] = v;
+      static_cast<float*>(p.C2)[idx] = gelu_tanh(v);
+    }
+  } else if constexpr (EPI == GPT2_EPI_DGELU) {
+    if constexpr (OUT_BF16) {
+      float u = bf2f(static_cast<const bf16*>(p.U)[idx]);
+      static_cast<bf16*>(p.C)[idx] = f2bf(v * gelu_tanh_grad(u));
+    } else {
+      float u = static_cast<const float*>(p.U)[idx];
+      static_cast<float*>(p.C)[idx] = v * gelu_tanh_grad(u);
+    }
+  } else {  // ACCUMULATE
+    float* c = static_cast<float*>(p.C) + idx;
+    if constexpr (ATOMIC) unsafeAtomicAdd(c, v);
+    else *c += v;
+  }
+}
+
+
+// Epilogue for 4 consecutive columns n..n+3 of row m (n % 4 == 0, all < N).
+template <int EPI, bool OUT_BF16, bool ATOMIC>
+__device__ __forceinline__ void epi_store4(const GemmP& p, int m, int n, const float* acc) {
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[e];
+  if (p.bias) {
+    const float4 b = *reinterpret_cast<const float4*>(p.bias + n);
+    v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+  }
+  const int64_t idx = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == GPT2_EPI_STORE) {
+    if constexpr (OUT_BF16) {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f2bf(v[e]);
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = o;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.C) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+    const float4 r = *reinterpret_cast<const float4*>(p.R + idx);
+    *reinterpret_cast<float4*>(static_cast<float*>(p.C) + idx) = make_float4(r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]);
+  } else if constexpr (EPI == GPT2_EPI_GELU) {
+    bf16x4 u, g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = f2bf(v[e]);
+      g[e] = f2bf(gelu_tanh(bf2f(u[e])));
+    }
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = u;
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C2) + idx) = g;
+  } else if constexpr (EPI == GPT2_EPI_DGELU) {
+    const bf16x4 u = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(p.U) + idx);
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = f2bf(v[e] * gelu_tanh_grad(bf2f(u[e])));
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = o;
+  } else {  // ACCUMULATE
+    float* c = static_cast<float*>(p.C) + idx;
+    if constexpr (ATOMIC) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) unsafeAtomicAdd(c + e, v[e]);
+    } else {
+      float4 o = *reinterpret_cast<float4*>(c);
+      o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
+      *reinterpret_cast<float4*>(c) = o;
+    }
+  }
+}
+
+// Tile -> block mapping.  Blocks are handed to the 8 XCDs round-robin; the
+// remap makes consecutive logical tiles run on one XCD (sharing its L2), and
+// the grouped order walks GROUP_M row tiles per column panel.
+__device__ __forceinline__ void tile_of_block(const GemmP& p, int& tm, int& tn, int& split) {
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int per_split = p.tiles_m * p.tiles_n;
+  split = bid / per_split;
+  int t = bid - split * per_split;
+  const int GROUP_M = 8;
+  const int in_group = GROUP_M * p.tiles_n;
+  const int group = t / in_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(p.tiles_m - first_m, GROUP_M);
+  const int r = t - group * in_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+union GV8 {
+  uint4 u;
+  bf16x8 v;
+  uint32_t w[4];
+};
+
+// Operand whose K index is the slow one in memory: 8(k) x 8(row) blocks are
+// loaded to registers, transposed, and written as 16-byte row chunks into
+// the swizzled layout.  Consecutive lanes take consecutive K blocks of one
+// row block, so the 8 lanes of a write phase cover one 128-byte row span.
+template <int ROWS, int BK, int NT>
+struct TLoader {
+  static constexpr int KB = BK / 8;
+  static constexpr int BLOCKS = ROWS * BK / 64;
+  static constexpr int PER = (BLOCKS + NT - 1) / NT;
+  GV8 r[PER * 8];
+  __device__ __forceinline__ void load(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, int K) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int id = threadIdx.x + NT * i;
+      const int kb = id % KB, rb = id / KB;
+      const int gr = row0 + 8 * rb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int gk = k0 + 8 * kb + j;
+        if (id < BLOCKS && gr < nrows && gk < K)
+          r[8 * i + j].u = *reinterpret_cast<const uint4*>(src + (int64_t)gk * ld + gr);
+        else
+          r[8 * i + j].u = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16* lds) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int id = threadIdx.x + NT * i;
+      if (id >= BLOCKS) break;
+      const int kb = id % KB, rb = id / KB;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int word = rr >> 1;
+        const bool hi = rr & 1;
+        GV8 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a = r[8 * i + 2 * q].w[word];
+          const uint32_t b = r[8 * i + 2 * q + 1].w[word];
+          o.w[q] = hi ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        }
+        const int row = 8 * rb + rr;
+        *reinterpret_cast<uint4*>(lds + row * BK + 8 * swz_chunk<BK>(row, kb)) = o.u;
+      }
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
+          bool ATOMIC, bool SWAP>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int NT = 64 * NW;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = (BM + BN) * BK;  // elements per stage
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+
+  int tm, tn, split;
+  tile_of_block(p, tm, tn, split);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  const int lr = lane & 31, lg = lane >> 5;
+  const bool do_rowsum = p.row_sum != nullptr && tn == 0;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  float rsum = 0.f;
+
+  const bf16* Ag = static_cast<const bf16*>(p.A);
+  const bf16* Bg = static_cast<const bf16*>(p.B);
+  TLoader<BM, BK, NT> ta;
+  TLoader<BN, BK, NT> tb;
+
+  auto issue = [&](int stage, int kstep) {
+    bf16* as = smem + stage * STAGE;
+    bf16* bs = as + BM * BK;
+    const int k0 = kbeg + kstep * BK;
+    if constexpr (!A_K) ta.load(Ag, p.lda, m0, p.M, k0, kend);
+    if constexpr (!B_K) tb.load(Bg, p.ldb, n0, p.N, k0, kend);
+    if constexpr (A_K) dma_rows<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
+    if constexpr (B_K) dma_rows<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+  };
+  auto commit = [&](int stage) {
+    bf16* as = smem + stage * STAGE;
+    bf16* bs = as + BM * BK;
+    if constexpr (!A_K) ta.store(as);
+    if constexpr (!B_K) tb.store(bs);
+  };
+  // DMA instructions each wave issues per K step (the wait depth below)
+  constexpr int DMA_PER_STEP = (A_K ? BM * BK / 512 / NW : 0) + (B_K ? BN * BK / 512 / NW : 0);
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < nk) {
+      issue(s, s);
+      commit(s);
+    }
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // Wait for this wave's DMA of step kt (later steps stay in flight) and
+    // its LDS writes, then meet the other waves.  A plain __syncthreads()
+    // would also drain the later steps' DMA (its release fence waits for
+    // every outstanding load).  The asm statements are compiler memory
+    // barriers, so no LDS access moves across them.
+    if (kt + STAGES - 2 < nk) {
+      if constexpr (STAGES == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if constexpr (STAGES == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STEP) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_STEP) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int nxt = kt + STAGES - 1;
+    if (nxt < nk) issue(nxt % STAGES, nxt);
+    const bf16* as = smem + (kt % STAGES) * STAGE;
+    const bf16* bs = as + BM * BK;
+    // Fragments of the next 16-wide K slice are read from LDS while the
+    // current slice's MFMAs issue.  With SWAP the MFMA takes B's fragment as
+    // its first operand, so each lane's accumulator holds 4 consecutive
+    // output columns of one row (vector loads and stores in the epilogue);
+    // without it a lane holds one column of 4 consecutive rows and the 32
+    // lanes of a row cover 32 consecutive columns (coalesced scalar stores
+    // and atomics).
+    bf16x8 a[2][TM], b[2][TN];
+    auto frag = [&](int kk, bf16x8* fa, bf16x8* fb) {
+      const int c = 2 * kk + lg;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm0 + 32 * i + lr;
+        fa[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + 8 * swz_chunk<BK>(row, c));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn0 + 32 * j + lr;
+        fb[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + 8 * swz_chunk<BK>(row, c));
+      }
+    };
+    frag(0, a[0], b[0]);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cb = kk & 1;
+      if (kk + 1 < BK / 16) frag(kk + 1, a[cb ^ 1], b[cb ^ 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cb][j], a[cb][i], acc[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
+    }
+    if (do_rowsum && threadIdx.x < BM) {
+      const bf16* row = as + threadIdx.x * BK;
+#pragma unroll
+      for (int c = 0; c < BK / 8; ++c) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rsum += bf2f(v[e]);
+      }
+    }
+    if (nxt < nk) commit(nxt % STAGES);
+  }
+  if (do_rowsum && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
+    unsafeAtomicAdd(p.row_sum + m0 + threadIdx.x, p.alpha * rsum);
+
+  if constexpr (SWAP) {
+    // accumulator (i, j), register 4q + e: row m = wm0 + 32i + lr, column
+    // n = wn0 + 32j + 8q + 4lg + e
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm0 + 32 * i + lr;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn0 + 32 * j + 8 * q + 4 * lg;
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (n + 3 < p.N) {
+            epi_store4<EPI, OUT_BF16, ATOMIC>(p, m, n, v);
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n + e, v[e]);
+          }
+        }
+    }
+  } else {
+    // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn0 + 32 * j + lr;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (m < p.M) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int BK, int STAGES>
+constexpr size_t gemm2_lds_bytes() {
+  return (size_t)STAGES * (BM + BN) * BK * sizeof(bf16);
+}
+
+
+
+}  // namespace g2

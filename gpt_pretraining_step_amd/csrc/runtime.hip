@@ -339,7 +339,7 @@ static hipError_t linear_fwd(gpt2_ctx* c, const char* site, const void* x, int M
   a.bias = bi >= 0 ? c->P(bi) : nullptr;
   a.epilogue = epi;
   a.out_bf16 = c->bf() && (epi == GPT2_EPI_STORE || epi == GPT2_EPI_GELU || epi == GPT2_EPI_DGELU);
-  return launch_gemm(c->at(site), a, c->flag());
+  return launch_gemm(c->at(site), a);
 }
 
 // dx[M,K] = dy[M,N] W[N,K] (a Linear's input gradient), epilogue STORE or DGELU.
@@ -352,19 +352,25 @@ static hipError_t linear_dx(gpt2_ctx* c, const char* site, const void* dy, int M
   a.A = dy; a.B = c->W(wi); a.C = out; a.U = u;
   a.epilogue = epi;
   a.out_bf16 = c->bf() && out_act;
-  return launch_gemm(c->at(site), a, c->flag());
+  return launch_gemm(c->at(site), a);
 }
 
-// dW[N,K] += dy[M,N]^T x[M,K] (a Linear's weight gradient, reduced over tokens).
+// dW[N,K] += dy[M,N]^T x[M,K] (a Linear's weight gradient, reduced over
+// tokens) and db[N] += sum over tokens of dy.  In bf16 mode the bias gradient
+// is summed inside the product from its first operand; in float32 mode by a
+// column-sum kernel over dy_f32.
 static hipError_t linear_dw(gpt2_ctx* c, const char* site, const void* dy, int M, int N, const void* x, int K,
-                            int wi) {
+                            int wi, int bi, const float* dy_f32) {
   gpt2_gemm_args a = gemm_base(c->cfg.precision);
   a.M = N; a.N = K; a.K = M;
   a.a_kmajor = 0; a.b_kmajor = 0;
   a.lda = N; a.ldb = K; a.ldc = K;
   a.A = dy; a.B = x; a.C = c->Gr(wi);
   a.epilogue = GPT2_EPI_ACCUMULATE;
-  return launch_gemm(c->at(site), a, c->flag());
+  if (c->bf()) return launch_gemm(c->at(site), a, c->Gr(bi));
+  hipError_t e = launch_gemm(c->at(site), a);
+  if (e != hipSuccess) return e;
+  return launch_colsum(c->at("colsum"), dy_f32, 0, M, N, N, c->Gr(bi));
 }
 
 // ------------------------------------------------------------- the step
@@ -422,7 +428,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
       a.lda = C; a.ldb = C; a.ldc = V;
       a.A = z_c; a.B = c->W(c->tab.wte); a.C = logits;
       a.epilogue = GPT2_EPI_STORE; a.out_bf16 = 0;
-      HIP_TRY(launch_gemm(c->at("gemm.lm_head"), a, flag));
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head"), a));
     }
     if (bf)
       HIP_TRY(launch_ce_rows<float, bf16>(c->at("ce.rows"), logits, V, static_cast<bf16*>(dlog), V, tgt + r0, rows, V,
@@ -437,7 +443,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
       a.lda = V; a.ldb = C; a.ldc = C;
       a.A = dlog; a.B = c->W(c->tab.wte); a.C = dZ + (size_t)r0 * C;
       a.epilogue = GPT2_EPI_ACCUMULATE;
-      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dx"), a, flag));
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dx"), a));
     }
     {  // dwte += dlogits_c^T Z_c
       gpt2_gemm_args a = gemm_base(dt);
@@ -446,7 +452,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
       a.lda = V; a.ldb = C; a.ldc = C;
       a.A = dlog; a.B = z_c; a.C = c->Gr(c->tab.wte);
       a.epilogue = GPT2_EPI_ACCUMULATE;
-      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dw"), a, flag));
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dw"), a));
     }
   }
   HIP_TRY(launch_ce_finish_n(c->at("ce.finish"), rowloss, M, count, loss, flag));
@@ -464,24 +470,22 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   void* dQKV = c->scr(y.dQKV);
   for (int l = g.n_layer - 1; l >= 0; --l) {
     // MLP branch: R_{l+1} = Rmid + G Wmp^T + b
-    HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRop, M, C, c->act(y.G[l]), F, c->L(l, MLP_W)));
-    HIP_TRY(launch_colsum(c->at("colsum"), dR, 0, M, C, C, c->Gr(c->L(l, MLP_B))));
+    HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRop, M, C, c->act(y.G[l]), F, c->L(l, MLP_W), c->L(l, MLP_B), dR));
     HIP_TRY(linear_dx(c, "gemm.mlp_proj_dx", dRop, M, C, c->L(l, MLP_W), F, GPT2_EPI_DGELU, true, dU,
                       c->act(y.U[l])));
-    HIP_TRY(linear_dw(c, "gemm.fc_dw", dU, M, F, c->act(y.A2[l]), C, c->L(l, FC_W)));
-    HIP_TRY(launch_colsum(c->at("colsum"), dU, bf, M, F, F, c->Gr(c->L(l, FC_B))));
+    HIP_TRY(linear_dw(c, "gemm.fc_dw", dU, M, F, c->act(y.A2[l]), C, c->L(l, FC_W), c->L(l, FC_B),
+                      static_cast<const float*>(dU)));
     HIP_TRY(linear_dx(c, "gemm.fc_dx", dU, M, F, c->L(l, FC_W), C, GPT2_EPI_STORE, false, dA, nullptr));
     HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, c->act<float>(y.Rmid[l]), c->act<float>(y.mean2[l]),
                                    c->act<float>(y.rstd2[l]), c->P(c->L(l, LN2_W)), dR, dRb, c->Gr(c->L(l, LN2_W)),
                                    c->Gr(c->L(l, LN2_B)), M, C));
     // attention branch: Rmid = R_l + Y Wo^T + b
-    HIP_TRY(linear_dw(c, "gemm.attn_proj_dw", dRop, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W)));
-    HIP_TRY(launch_colsum(c->at("colsum"), dR, 0, M, C, C, c->Gr(c->L(l, PROJ_B))));
+    HIP_TRY(linear_dw(c, "gemm.attn_proj_dw", dRop, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRop, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
                                  c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
-    HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W)));
-    HIP_TRY(launch_colsum(c->at("colsum"), dQKV, bf, M, 3 * C, 3 * C, c->Gr(c->L(l, QKV_B))));
+    HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
+                      static_cast<const float*>(dQKV)));
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, false, dA, nullptr));
     HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, c->act<float>(y.Rin[l]), c->act<float>(y.mean1[l]),
                                    c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb, c->Gr(c->L(l, LN1_W)),
@@ -714,7 +718,7 @@ int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, con
     a.lda = C; a.ldb = C; a.ldc = V;
     a.A = H + (size_t)r0 * C; a.B = d_weight; a.C = logits;
     a.epilogue = GPT2_EPI_STORE;
-    HIP_TRY(launch_gemm(L, a, flag));
+    HIP_TRY(launch_gemm(L, a));
     HIP_TRY(launch_ce_rows<float, bf16>(L, logits, V, dlog, V, d_targets + r0, rows, V, count, 1.f, nullptr,
                                         rowloss + r0));
     a = gemm_base(GPT2_PRECISION_BF16);
@@ -723,14 +727,14 @@ int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, con
     a.lda = V; a.ldb = C; a.ldc = C;
     a.A = dlog; a.B = d_weight; a.C = dh32 + (size_t)r0 * C;
     a.epilogue = GPT2_EPI_ACCUMULATE;
-    HIP_TRY(launch_gemm(L, a, flag));
+    HIP_TRY(launch_gemm(L, a));
     a = gemm_base(GPT2_PRECISION_BF16);
     a.M = V; a.N = C; a.K = rows;
     a.a_kmajor = 0; a.b_kmajor = 0;
     a.lda = V; a.ldb = C; a.ldc = C;
     a.A = dlog; a.B = H + (size_t)r0 * C; a.C = d_dweight;
     a.epilogue = GPT2_EPI_ACCUMULATE;
-    HIP_TRY(launch_gemm(L, a, flag));
+    HIP_TRY(launch_gemm(L, a));
   }
   HIP_TRY(launch_ce_finish_n(L, rowloss, M, count, d_loss, flag));
   HIP_TRY(launch_to_bf16(L, dh32, static_cast<bf16*>(d_dhidden), (size_t)M * C));
@@ -755,7 +759,7 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
     if (a->M % 8 && !a->a_kmajor) return false;
     if (a->N % 8 && !a->b_kmajor) return false;
     if ((a->a_kmajor && a->K % 8) || (a->b_kmajor && a->K % 8)) return false;
-    if (a->lda % 8 || a->ldb % 8) return false;
+    if (a->lda % 8 || a->ldb % 8 || a->ldc % 8) return false;
     if (((uintptr_t)a->A | (uintptr_t)a->B) & 15) return false;
   }
   return true;
@@ -763,7 +767,7 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
 
 int gpt2_op_gemm(void* stream, const gpt2_gemm_args* a) {
   if (!gemm_args_ok(a)) return GPT2_ERR_ARG;
-  HIP_TRY(launch_gemm(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, *a, nullptr));
+  HIP_TRY(launch_gemm(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, *a));
   return GPT2_OK;
 }
 

@@ -1,0 +1,69 @@
+// Tile movement between HBM and LDS shared by the MFMA kernels.
+//
+//  * DMA: global_load_lds_dwordx4 copies 16 bytes per lane straight into LDS;
+//    one wave instruction fills 1 KB of consecutive LDS bytes (lane l at byte
+//    16 l from the wave's base).
+//  * Swizzle: a tile row of BK bf16 elements is stored without padding, its
+//    16-byte chunk c at position c ^ swz(row).  The 32 rows touched by one
+//    MFMA operand fetch then fall on distinct banks.
+//  * Transposed operand reads: ds_read_b64_tr_b16 (gfx950).  Within each
+//    group of 16 lanes, source lane j supplies the 8 bytes at its address and
+//    result lane i receives element i%4 of the vectors of source lanes i/4,
+//    i/4+4, i/4+8, i/4+12.  If source lane j points at row r0 + j/4, columns
+//    c0 + 4 (j%4) .. +3 of a row-major tile, result lane i holds column c0 + i
+//    of rows r0 .. r0+3: a column read of the tile.
+#pragma once
+
+#include "common.h"
+
+namespace g2 {
+
+// Out-of-range DMA lanes copy from this block of zeros, so ragged M, N and K
+// tails read as zeros.
+
+__device__ __attribute__((aligned(16))) static const uint4 g2_zero16[4] = {};
+
+template <int BK>
+__device__ __forceinline__ int swz_chunk(int row, int c) {
+  if constexpr (BK == 64) return c ^ (row & 7);
+  else return c ^ ((row >> 1) & 3);  // BK == 32: 4 chunks per 64-byte row
+}
+
+// K-major tile [ROWS][BK] (source rows row0.., K columns k0..) -> LDS, by DMA.
+template <int ROWS, int BK, int NWAVES>
+__device__ __forceinline__ void dma_rows(bf16* lds, const bf16* __restrict__ src, int64_t ld, int row0, int nrows,
+                                         int k0, int K) {
+  constexpr int CPR = BK / 8;              // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;            // rows per wave instruction
+  constexpr int INSTR = ROWS / RPI;        // instructions per tile
+  static_assert(INSTR % NWAVES == 0, "tile rows must split evenly over the waves");
+  constexpr int IPW = INSTR / NWAVES;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane / CPR, pc = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int ins = wave * IPW + i;
+    const int r = ins * RPI + rl;
+    const int c = swz_chunk<BK>(r, pc);
+    const int gr = row0 + r, gk = k0 + 8 * c;
+    const bf16* g = (gr < nrows && gk < K) ? src + (int64_t)gr * ld + gk : reinterpret_cast<const bf16*>(g2_zero16);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), lds + ins * RPI * BK, 16, 0, 0);
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Column read of a swizzled [rows][64] tile (128-byte rows): returns for
+// this lane column c0 + (lane % 16) of rows r0..r0+3 (r0 % 4 == 0, c0 % 16 == 0).
+__device__ __forceinline__ bf16x4 tr_read4(const bf16* tile, int r0, int c0) {
+  const int j = threadIdx.x & 15;
+  const int row = r0 + (j >> 2);
+  const int col = c0 + 4 * (j & 3);
+  const int byte = row * 128 + ((((col >> 3) ^ (row & 7))) << 4) + ((col & 7) << 1);
+  auto base = (__attribute__((address_space(3))) char*)(tile);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + byte));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+}  // namespace g2

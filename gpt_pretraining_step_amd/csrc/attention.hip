@@ -347,37 +347,31 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
     if (q0 >= T || kb > q0 + 31) continue;
     const bf16* Ks = sm[jt & 1][0];
     const bf16* Vs = sm[jt & 1][1];
-    f32x16 sT[2], dpT[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      sT[c] = zero16();
-      dpT[c] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        sT[c] = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT[c]);
-        dpT[c] = MFMA(rowfrag(Vs, 32 * c + lr, kk, lg), dof[kk], dpT[c]);
-      }
-    }
     const bool edge = (kb + 63 > q0) || (kb + 63 >= T);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c) {
+      f32x16 sT = zero16(), dpT = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        sT = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT);
+        dpT = MFMA(rowfrag(Vs, 32 * c + lr, kk, lg), dof[kk], dpT);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2f(sT[c][r] * sl2 - lse2);
+        float p = exp2f(sT[r] * sl2 - lse2);
         if (edge) {
           const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
           if (key > qi || key >= T) p = 0.f;
         }
-        sT[c][r] = p * (dpT[c][r] - D);
+        sT[r] = p * (dpT[r] - D);
       }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 db = acc_frag(sT[c], s);
+        const bf16x8 db = acc_frag(sT, s);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) dqT[dt] = MFMA(colfrag(Ks, 32 * c + 16 * s, 32 * dt, lg), db, dqT[dt]);
       }
+    }
   }
   if (qv) {
     bf16* o = dqkv + ((int64_t)b * T + qi) * C3 + h * HD;
@@ -396,7 +390,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
 // Backward, pass 2: dK and dV.  Block = NW waves x 32 keys; loop over 64-query
 // tiles from the block's diagonal to T.  Each lane owns one key (S = Q K^T).
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_bf16_kernel(const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf16* __restrict__ qkv,
                                                                      const bf16* __restrict__ dy,
                                                                      const float* __restrict__ lse,
                                                                      const float* __restrict__ Dbuf,
@@ -464,20 +458,17 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_bf16_kernel(const bf16*
     const bf16* dOs = sm[jt & 1][1];
     const float* Ls = rowst[jt & 1][0];
     const float* Ds = rowst[jt & 1][1];
-    f32x16 sc[2], dp[2];
-#pragma unroll
+    const bool edge = (qs < k0 + 31) || (qs + 63 >= T);
+    // the two 32-query halves of the tile one after the other (fewer live
+    // accumulators and operand fragments)
+#pragma unroll 1
     for (int c = 0; c < 2; ++c) {
-      sc[c] = zero16();
-      dp[c] = zero16();
+      f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        sc[c] = MFMA(rowfrag(Qs, 32 * c + lr, kk, lg), kf[kk], sc[c]);
-        dp[c] = MFMA(rowfrag(dOs, 32 * c + lr, kk, lg), vf[kk], dp[c]);
+        sc = MFMA(rowfrag(Qs, 32 * c + lr, kk, lg), kf[kk], sc);
+        dp = MFMA(rowfrag(dOs, 32 * c + lr, kk, lg), vf[kk], dp);
       }
-    }
-    const bool edge = (qs < k0 + 31) || (qs + 63 >= T);
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int ql = 32 * c + 8 * a + 4 * lg;
@@ -488,27 +479,26 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_bf16_kernel(const bf16*
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          float p = exp2f(sc[c][r] * sl2 - Lv[e] * kLOG2E);
+          float p = exp2f(sc[r] * sl2 - Lv[e] * kLOG2E);
           if (edge) {
             const int q = qs + ql + e;
             if (kj > q || q >= T) p = 0.f;
           }
-          sc[c][r] = p;
-          dp[c][r] = p * (dp[c][r] - Dv[e]);
+          sc[r] = p;
+          dp[r] = p * (dp[r] - Dv[e]);
         }
       }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 pb = acc_frag(sc[c], s);
-        const bf16x8 db = acc_frag(dp[c], s);
+        const bf16x8 pb = acc_frag(sc, s);
+        const bf16x8 db = acc_frag(dp, s);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           dvT[dt] = MFMA(colfrag(dOs, 32 * c + 16 * s, 32 * dt, lg), pb, dvT[dt]);
           dkT[dt] = MFMA(colfrag(Qs, 32 * c + 16 * s, 32 * dt, lg), db, dkT[dt]);
         }
       }
+    }
     if (more) commit((jt + 1) & 1);
   }
   if (kvld) {

@@ -162,11 +162,13 @@ static hipError_t dispatch_f32(const Launch& L, GemmP p, int epi) {
   return hipGetLastError();
 }
 
-// Number of K splits for accumulate-into products whose output has too few
-// tiles to fill 256 CUs (the weight gradients: few output tiles, K = tokens).
-static int choose_splits(int tiles, int K, int BK) {
+// Number of K splits for accumulate-into products whose output has few tiles
+// (the weight gradients: small outputs, K = tokens).  Partial products are
+// added with float32 atomics, whose cost grows with the split count, so the
+// grid is filled to about one block per CU and no further.
+static int choose_splits(int tiles, int K, int BK, int target_blocks) {
   int splits = 1;
-  while (tiles * splits < 512 && K / (splits * 2) >= 4 * BK) splits *= 2;
+  while (tiles * splits * 2 <= target_blocks && K / (splits * 2) >= 4 * BK) splits *= 2;
   return splits;
 }
 
@@ -177,7 +179,7 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
   if (a.dtype == GPT2_PRECISION_FP32) {
     if (a.epilogue == GPT2_EPI_ACCUMULATE) {
       const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
-      p.splits = choose_splits(tiles, a.K, 16);
+      p.splits = choose_splits(tiles, a.K, 16, 512);
       p.k_per_split = ((a.K + p.splits * 16 - 1) / (p.splits * 16)) * 16;
       p.splits = (a.K + p.k_per_split - 1) / p.k_per_split;
     }
@@ -189,7 +191,7 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
   constexpr int BK = 64;
   if (a.epilogue == GPT2_EPI_ACCUMULATE) {
     const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    p.splits = choose_splits(tiles, a.K, BK);
+    p.splits = choose_splits(tiles, a.K, BK, 256);
     p.k_per_split = ((a.K + p.splits * BK - 1) / (p.splits * BK)) * BK;
     p.splits = (a.K + p.k_per_split - 1) / p.k_per_split;
   }

@@ -3,15 +3,16 @@
 // C[m][n] = alpha * sum_k A(m,k) B(n,k), then a fused epilogue.  Block tile
 // BM x BN, K step BK, WGM x WGN waves, each wave owning a (BM/WGM) x (BN/WGN)
 // sub-tile of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, float32
-// accumulators).  STAGES LDS buffers form a pipeline: operands stored with K
-// contiguous ("K-major") are copied from global memory straight into LDS by
-// DMA (global_load_lds_dwordx4), so the loads of later K steps are in flight
-// while the current one is multiplied; operands whose K index is the slow one
-// in memory (the backward products) are loaded as 8x8 blocks, transposed in
-// registers and written to LDS.  In LDS every row holds BK elements with its
-// 16-byte chunks XOR-swizzled, which keeps both the DMA writes (1 KB of
-// consecutive bytes per wave instruction) and the 32-row MFMA operand reads
-// free of bank conflicts.
+// accumulators).  STAGES LDS buffers form a pipeline: every operand tile is
+// copied from global memory straight into LDS by DMA (global_load_lds_dwordx4),
+// so the loads of later K steps are in flight while the current one is
+// multiplied.  Operands stored with K contiguous ("K-major") are kept as
+// [rows][BK] and fetched with 16-byte LDS reads; operands whose K index is the
+// slow one in memory (the backward products) are kept in their memory layout,
+// [BK][rows], and fetched with the transposing LDS read (ds_read_b64_tr_b16).
+// Tiles carry no padding: 16-byte chunks are XOR-swizzled per row, which keeps
+// the DMA writes (1 KB of consecutive bytes per wave instruction) and the
+// operand reads free of bank conflicts.
 #pragma once
 
 #include "tile_io.h"
@@ -145,56 +146,6 @@ union GV8 {
   uint32_t w[4];
 };
 
-// Operand whose K index is the slow one in memory: 8(k) x 8(row) blocks are
-// loaded to registers, transposed, and written as 16-byte row chunks into
-// the swizzled layout.  Consecutive lanes take consecutive K blocks of one
-// row block, so the 8 lanes of a write phase cover one 128-byte row span.
-template <int ROWS, int BK, int NT>
-struct TLoader {
-  static constexpr int KB = BK / 8;
-  static constexpr int BLOCKS = ROWS * BK / 64;
-  static constexpr int PER = (BLOCKS + NT - 1) / NT;
-  GV8 r[PER * 8];
-  __device__ __forceinline__ void load(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, int K) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int id = threadIdx.x + NT * i;
-      const int kb = id % KB, rb = id / KB;
-      const int gr = row0 + 8 * rb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + 8 * kb + j;
-        if (id < BLOCKS && gr < nrows && gk < K)
-          r[8 * i + j].u = *reinterpret_cast<const uint4*>(src + (int64_t)gk * ld + gr);
-        else
-          r[8 * i + j].u = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16* lds) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int id = threadIdx.x + NT * i;
-      if (id >= BLOCKS) break;
-      const int kb = id % KB, rb = id / KB;
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int word = rr >> 1;
-        const bool hi = rr & 1;
-        GV8 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a = r[8 * i + 2 * q].w[word];
-          const uint32_t b = r[8 * i + 2 * q + 1].w[word];
-          o.w[q] = hi ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-        }
-        const int row = 8 * rb + rr;
-        *reinterpret_cast<uint4*>(lds + row * BK + 8 * swz_chunk<BK>(row, kb)) = o.u;
-      }
-    }
-  }
-};
-
 template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
           bool ATOMIC, bool SWAP>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
@@ -231,34 +182,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
 
   const bf16* Ag = static_cast<const bf16*>(p.A);
   const bf16* Bg = static_cast<const bf16*>(p.B);
-  TLoader<BM, BK, NT> ta;
-  TLoader<BN, BK, NT> tb;
 
+  // Every operand tile is copied into LDS by DMA: K-major ones as [rows][BK]
+  // (row-swizzled), K-slow ones in their memory layout as [BK][rows].
   auto issue = [&](int stage, int kstep) {
     bf16* as = smem + stage * STAGE;
     bf16* bs = as + BM * BK;
     const int k0 = kbeg + kstep * BK;
-    if constexpr (!A_K) ta.load(Ag, p.lda, m0, p.M, k0, kend);
-    if constexpr (!B_K) tb.load(Bg, p.ldb, n0, p.N, k0, kend);
     if constexpr (A_K) dma_rows<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
+    else dma_kr<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
     if constexpr (B_K) dma_rows<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+    else dma_kr<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
   };
-  auto commit = [&](int stage) {
-    bf16* as = smem + stage * STAGE;
-    bf16* bs = as + BM * BK;
-    if constexpr (!A_K) ta.store(as);
-    if constexpr (!B_K) tb.store(bs);
-  };
-  // DMA instructions each wave issues per K step (the wait depth below)
-  constexpr int DMA_PER_STEP = (A_K ? BM * BK / 512 / NW : 0) + (B_K ? BN * BK / 512 / NW : 0);
+  constexpr int DMA_PER_STEP = (BM + BN) * BK / 512 / NW;  // DMA instructions per wave per K step
 
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < nk) {
-      issue(s, s);
-      commit(s);
-    }
-  }
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
 
   for (int kt = 0; kt < nk; ++kt) {
     // Wait for this wave's DMA of step kt (later steps stay in flight) and
@@ -288,15 +228,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
     bf16x8 a[2][TM], b[2][TN];
     auto frag = [&](int kk, bf16x8* fa, bf16x8* fb) {
       const int c = 2 * kk + lg;
+      const int h = (lane >> 4) & 1;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int row = wm0 + 32 * i + lr;
-        fa[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + 8 * swz_chunk<BK>(row, c));
+        if constexpr (A_K) {
+          const int row = wm0 + 32 * i + lr;
+          fa[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + 8 * swz_chunk<BK>(row, c));
+        } else {
+          const bf16x4 lo = tr_read4_kr<BM>(as, 16 * kk + 8 * lg, wm0 + 32 * i + 16 * h);
+          const bf16x4 hi = tr_read4_kr<BM>(as, 16 * kk + 8 * lg + 4, wm0 + 32 * i + 16 * h);
+          fa[i] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int row = wn0 + 32 * j + lr;
-        fb[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + 8 * swz_chunk<BK>(row, c));
+        if constexpr (B_K) {
+          const int row = wn0 + 32 * j + lr;
+          fb[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + 8 * swz_chunk<BK>(row, c));
+        } else {
+          const bf16x4 lo = tr_read4_kr<BN>(bs, 16 * kk + 8 * lg, wn0 + 32 * j + 16 * h);
+          const bf16x4 hi = tr_read4_kr<BN>(bs, 16 * kk + 8 * lg + 4, wn0 + 32 * j + 16 * h);
+          fb[j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
     };
     frag(0, a[0], b[0]);
@@ -312,15 +265,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
     }
     if (do_rowsum && threadIdx.x < BM) {
-      const bf16* row = as + threadIdx.x * BK;
+      // row sums of this block's A tile (K values past kend read as zeros)
+      const int t = threadIdx.x;
+      if constexpr (A_K) {
+        const bf16* row = as + t * BK;
 #pragma unroll
-      for (int c = 0; c < BK / 8; ++c) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+        for (int c = 0; c < BK / 8; ++c) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + 8 * c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rsum += bf2f(v[e]);
+          for (int e = 0; e < 8; ++e) rsum += bf2f(v[e]);
+        }
+      } else {
+#pragma unroll 8
+        for (int k = 0; k < BK; ++k) rsum += bf2f(as[k * BM + 8 * kr_chunk<BM>(k, t >> 3) + (t & 7)]);
       }
     }
-    if (nxt < nk) commit(nxt % STAGES);
   }
   if (do_rowsum && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
     unsafeAtomicAdd(p.row_sum + m0 + threadIdx.x, p.alpha * rsum);

@@ -66,4 +66,49 @@ __device__ __forceinline__ bf16x4 tr_read4(const bf16* tile, int r0, int c0) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// ---- tiles stored with K as the row index: [BK rows][R columns], R bf16 per
+// row (the output rows of a product whose operand is K-slow in memory).
+// 16-byte chunk c of row k sits at c ^ ((k & 3) << 1), so the 4 rows of one
+// transposing read fall on distinct banks.
+template <int R>
+__device__ __forceinline__ int kr_chunk(int k, int c) {
+  return c ^ ((k & 3) << 1);
+}
+
+// [BK][R] tile (source rows k0.. of a [K][ld] matrix, columns col0..col0+R)
+// -> LDS by DMA; rows past K and columns past ncols read as zeros.
+template <int R, int BK, int NWAVES>
+__device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, int64_t ld, int col0, int ncols,
+                                       int k0, int K) {
+  constexpr int CPR = R / 8;             // 16-byte chunks per row
+  constexpr int INSTR = BK * CPR / 64;   // 64 chunks per wave instruction
+  static_assert(CPR <= 64 && 64 % CPR == 0, "a wave instruction covers whole rows");
+  static_assert(INSTR % NWAVES == 0, "tile must split evenly over the waves");
+  constexpr int RPI = 64 / CPR;          // rows per instruction
+  constexpr int IPW = INSTR / NWAVES;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int ins = wave * IPW + i;
+    const int k = ins * RPI + lane / CPR;
+    const int c = kr_chunk<R>(k, lane % CPR);
+    const int gk = k0 + k, gc = col0 + 8 * c;
+    const bf16* g = (gk < K && gc < ncols) ? src + (int64_t)gk * ld + gc : reinterpret_cast<const bf16*>(g2_zero16);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), lds + ins * RPI * R, 16, 0, 0);
+  }
+}
+
+// Column read of a [rows][R] kr-swizzled tile: this lane gets column
+// c0 + (lane % 16) of rows r0 .. r0+3 (r0 % 4 == 0, c0 % 16 == 0).
+template <int R>
+__device__ __forceinline__ bf16x4 tr_read4_kr(const bf16* tile, int r0, int c0) {
+  const int j = threadIdx.x & 15;
+  const int row = r0 + (j >> 2);
+  const int col = c0 + 4 * (j & 3);
+  const int byte = row * (2 * R) + (kr_chunk<R>(row, col >> 3) << 4) + ((col & 7) << 1);
+  auto base = (__attribute__((address_space(3))) char*)(tile);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + byte));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 }  // namespace g2

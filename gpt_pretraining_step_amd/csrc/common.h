@@ -46,21 +46,29 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return stati
 
 // GELU, tanh form ("How I trained my own GPT-2 124M on FineWeb-Edu" 2.13):
 // 0.5 u (1 + tanh(z/2)) with z = 2 sqrt(2/pi) (u + 0.044715 u^3), which is
-// u * sigmoid(z) since 1 + tanh(z/2) = 2 sigmoid(z); evaluated with the
-// hardware exp2 and reciprocal.  The derivative is
-// sigmoid(z) + u sigmoid(z) (1 - sigmoid(z)) dz/du.
-__device__ __forceinline__ float gelu_sigmoid_arg(float u) {
-  const float k2 = 1.5957691216057308f;  // 2 sqrt(2/pi)
-  return k2 * fmaf(0.044715f * u, u * u, u);
+// u * sigmoid(z) since 1 + tanh(z/2) = 2 sigmoid(z).  sigmoid(z) is
+// 1 / (1 + 2^(-z log2 e)), evaluated with the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32; a result that would be denormal flushes to zero,
+// which only moves sigmoid by less than 2^-126).  The derivative is
+// sigmoid(z) + u sigmoid(z) (1 - sigmoid(z)) dz/du with
+// dz/du = 2 sqrt(2/pi) (1 + 3 * 0.044715 u^2).
+namespace gelu_k {
+constexpr float K2 = 1.5957691216057308f;            // 2 sqrt(2/pi)
+constexpr float C1 = -K2 * 1.4426950408889634f;      // -z / u at u = 0, in log2 units
+constexpr float C3 = C1 * 0.044715f;                 // cubic term of the same
+constexpr float D0 = K2, D2 = K2 * 3.0f * 0.044715f;  // dz/du = D0 + D2 u^2
+}  // namespace gelu_k
+// sigmoid(z(u)), given u and u^2
+__device__ __forceinline__ float gelu_sig(float u, float u2) {
+  const float a = u * fmaf(gelu_k::C3, u2, gelu_k::C1);  // -z log2 e
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
 }
-__device__ __forceinline__ float fast_sigmoid(float z) {
-  return __builtin_amdgcn_rcpf(1.0f + exp2f(-1.4426950408889634f * z));
-}
-__device__ __forceinline__ float gelu_tanh(float u) { return u * fast_sigmoid(gelu_sigmoid_arg(u)); }
+__device__ __forceinline__ float gelu_tanh(float u) { return u * gelu_sig(u, u * u); }
 __device__ __forceinline__ float gelu_tanh_grad(float u) {
-  const float s = fast_sigmoid(gelu_sigmoid_arg(u));
-  const float dz = 1.5957691216057308f * fmaf(3.0f * 0.044715f, u * u, 1.0f);
-  return s + u * s * (1.0f - s) * dz;
+  const float u2 = u * u;
+  const float s = gelu_sig(u, u2);
+  const float dz = fmaf(gelu_k::D2, u2, gelu_k::D0);
+  return fmaf(u * fmaf(-s, s, s), dz, s);
 }
 
 // Kernel launch bookkeeping: the runtime passes a Launch to every launcher,

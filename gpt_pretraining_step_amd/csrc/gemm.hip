@@ -89,7 +89,7 @@ static GemmP make_params(const gpt2_gemm_args& a) {
 
 // Launch one instantiation of the multi-stage bf16 kernel, raising its
 // dynamic-LDS limit once.
-template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool A_K, bool B_K, int EPI, bool OB, bool AT, bool SW>
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool A_K, bool B_K, int EPI, bool OB, bool AT, bool SW = false>
 static hipError_t launch_v2(const Launch& L, const GemmP& p) {
   auto kern = gemm2_kernel<BM, BN, BK, WGM, WGN, ST, A_K, B_K, EPI, OB, AT, SW>;
   constexpr size_t lds = gemm2_lds_bytes<BM, BN, BK, ST>();
@@ -120,21 +120,21 @@ static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
   prof_begin(L);
   switch (epi) {
     case GPT2_EPI_STORE:
-      e = ob ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_STORE, true, false, false>(L, p)
-             : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_STORE, false, false, false>(L, p);
+      e = ob ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_STORE, true, false>(L, p)
+             : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_STORE, false, false>(L, p);
       break;
     case GPT2_EPI_RESIDUAL:
       e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_RESIDUAL, false, false, true>(L, p);
       break;
     case GPT2_EPI_GELU:
-      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_GELU, true, false, false>(L, p);
+      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_GELU, true, false>(L, p);
       break;
     case GPT2_EPI_DGELU:
       e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_DGELU, true, false, true>(L, p);
       break;
     default:
-      e = at ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, true, false>(L, p)
-             : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, false, false>(L, p);
+      e = at ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, true>(L, p)
+             : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, false>(L, p);
       break;
   }
   prof_end(L);

@@ -69,54 +69,129 @@ __device__ __forceinline__ void epi_store(const GemmP& p, int m, int n, float ac
 }
 
 
-// Epilogue for 4 consecutive columns n..n+3 of row m (n % 4 == 0, all < N).
-template <int EPI, bool OUT_BF16, bool ATOMIC>
-__device__ __forceinline__ void epi_store4(const GemmP& p, int m, int n, const float* acc) {
-  float v[4];
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2 f2bf2(float a, float b) { return __builtin_convertvector((f32x2){a, b}, bf16x2); }
+
+// Epilogue of a tile that lies wholly inside C (no bounds checks): this lane
+// holds column ncol + 32 j of rows
+// mrow + 32 i + 8 (q / 4) + q % 4.  Rows q and q + 1 are converted to bf16
+// together (one packed conversion for two rows).
+template <int EPI, bool OUT_BF16, bool ATOMIC, int TM, int TN>
+__device__ __forceinline__ void epi_tile(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN]) {
+  float bj[TN];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[e];
-  if (p.bias) {
-    const float4 b = *reinterpret_cast<const float4*>(p.bias + n);
-    v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
-  }
-  const int64_t idx = (int64_t)m * p.ldc + n;
-  if constexpr (EPI == GPT2_EPI_STORE) {
-    if constexpr (OUT_BF16) {
-      bf16x4 o;
+  for (int j = 0; j < TN; ++j) bj[j] = p.bias ? p.bias[ncol + 32 * j] : 0.f;
+  const int ldc = (int)p.ldc;
+  const int64_t base = (int64_t)mrow * p.ldc + ncol;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = f2bf(v[e]);
-      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = o;
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(p.C) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) {
+      const int64_t r0 = base + (int64_t)((32 * i + 8 * (q >> 2) + (q & 3)) * ldc);
+      const int64_t r1 = r0 + ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t i0 = r0 + 32 * j, i1 = r1 + 32 * j;
+        const float v0 = fmaf(p.alpha, acc[i][j][q], bj[j]);
+        const float v1 = fmaf(p.alpha, acc[i][j][q + 1], bj[j]);
+        if constexpr (EPI == GPT2_EPI_STORE) {
+          if constexpr (OUT_BF16) {
+            const bf16x2 o = f2bf2(v0, v1);
+            static_cast<bf16*>(p.C)[i0] = o[0];
+            static_cast<bf16*>(p.C)[i1] = o[1];
+          } else {
+            static_cast<float*>(p.C)[i0] = v0;
+            static_cast<float*>(p.C)[i1] = v1;
+          }
+        } else if constexpr (EPI == GPT2_EPI_GELU) {
+          if constexpr (OUT_BF16) {
+            const bf16x2 u = f2bf2(v0, v1);
+            const float u0 = bf2f(u[0]), u1 = bf2f(u[1]);
+            const bf16x2 g = f2bf2(gelu_tanh(u0), gelu_tanh(u1));
+            static_cast<bf16*>(p.C)[i0] = u[0];
+            static_cast<bf16*>(p.C)[i1] = u[1];
+            static_cast<bf16*>(p.C2)[i0] = g[0];
+            static_cast<bf16*>(p.C2)[i1] = g[1];
+          } else {
+            static_cast<float*>(p.C)[i0] = v0;
+            static_cast<float*>(p.C)[i1] = v1;
+            static_cast<float*>(p.C2)[i0] = gelu_tanh(v0);
+            static_cast<float*>(p.C2)[i1] = gelu_tanh(v1);
+          }
+        } else if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+          static_cast<float*>(p.C)[i0] = p.R[i0] + v0;
+          static_cast<float*>(p.C)[i1] = p.R[i1] + v1;
+        } else if constexpr (EPI == GPT2_EPI_DGELU) {
+          if constexpr (OUT_BF16) {
+            const float u0 = bf2f(static_cast<const bf16*>(p.U)[i0]);
+            const float u1 = bf2f(static_cast<const bf16*>(p.U)[i1]);
+            const bf16x2 o = f2bf2(v0 * gelu_tanh_grad(u0), v1 * gelu_tanh_grad(u1));
+            static_cast<bf16*>(p.C)[i0] = o[0];
+            static_cast<bf16*>(p.C)[i1] = o[1];
+          } else {
+            static_cast<float*>(p.C)[i0] = v0 * gelu_tanh_grad(static_cast<const float*>(p.U)[i0]);
+            static_cast<float*>(p.C)[i1] = v1 * gelu_tanh_grad(static_cast<const float*>(p.U)[i1]);
+          }
+        } else {  // ACCUMULATE
+          float* c = static_cast<float*>(p.C);
+          if constexpr (ATOMIC) {
+            unsafeAtomicAdd(c + i0, v0);
+            unsafeAtomicAdd(c + i1, v1);
+          } else {
+            c[i0] += v0;
+            c[i1] += v1;
+          }
+        }
+      }
     }
-  } else if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+}
+
+// Stores 4 consecutive outputs C[idx .. idx+3] whose values v already carry
+// alpha and the bias (idx % 4 == 0); the epilogues of the swapped layout.
+template <int EPI>
+__device__ __forceinline__ void epi_put4(const GemmP& p, int64_t idx, const float* v) {
+  static_assert(EPI == GPT2_EPI_RESIDUAL || EPI == GPT2_EPI_DGELU, "swapped layout: residual or dGELU");
+  if constexpr (EPI == GPT2_EPI_RESIDUAL) {
     const float4 r = *reinterpret_cast<const float4*>(p.R + idx);
-    *reinterpret_cast<float4*>(static_cast<float*>(p.C) + idx) = make_float4(r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]);
-  } else if constexpr (EPI == GPT2_EPI_GELU) {
-    bf16x4 u, g;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u[e] = f2bf(v[e]);
-      g[e] = f2bf(gelu_tanh(bf2f(u[e])));
-    }
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = u;
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C2) + idx) = g;
-  } else if constexpr (EPI == GPT2_EPI_DGELU) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.C) + idx) =
+        make_float4(r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]);
+  } else {
     const bf16x4 u = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(p.U) + idx);
-    bf16x4 o;
+    const bf16x2 o0 = f2bf2(v[0] * gelu_tanh_grad(bf2f(u[0])), v[1] * gelu_tanh_grad(bf2f(u[1])));
+    const bf16x2 o1 = f2bf2(v[2] * gelu_tanh_grad(bf2f(u[2])), v[3] * gelu_tanh_grad(bf2f(u[3])));
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = bf16x4{o0[0], o0[1], o1[0], o1[1]};
+  }
+}
+
+// Swapped layout (the MFMA takes B's fragment first): this lane holds row
+// mrow + 32 i, columns ncol + 32 j + 8 q .. +3 (ncol includes 4 * (lane / 32)),
+// so the epilogue reads and writes 16-byte vectors.  With CHECK, rows at or
+// past M and columns at or past N are skipped (a group of 4 that straddles N
+// is stored element by element).
+template <int EPI, bool OUT_BF16, int TM, int TN, bool CHECK>
+__device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = f2bf(v[e] * gelu_tanh_grad(bf2f(u[e])));
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = o;
-  } else {  // ACCUMULATE
-    float* c = static_cast<float*>(p.C) + idx;
-    if constexpr (ATOMIC) {
+  for (int i = 0; i < TM; ++i) {
+    const int m = mrow + 32 * i;
+    if (CHECK && m >= p.M) continue;
+    const int64_t rb = (int64_t)m * p.ldc + ncol;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) unsafeAtomicAdd(c + e, v[e]);
-    } else {
-      float4 o = *reinterpret_cast<float4*>(c);
-      o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
-      *reinterpret_cast<float4*>(c) = o;
-    }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int co = 32 * j + 8 * q;
+        if (CHECK && ncol + co >= p.N) continue;
+        if (CHECK && ncol + co + 4 > p.N) {
+          for (int e = 0; ncol + co + e < p.N; ++e) epi_store<EPI, OUT_BF16, false>(p, m, ncol + co + e, acc[i][j][4 * q + e]);
+          continue;
+        }
+        float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.bias) b = *reinterpret_cast<const float4*>(p.bias + ncol + co);
+        const float v[4] = {fmaf(p.alpha, acc[i][j][4 * q + 0], b.x), fmaf(p.alpha, acc[i][j][4 * q + 1], b.y),
+                            fmaf(p.alpha, acc[i][j][4 * q + 2], b.z), fmaf(p.alpha, acc[i][j][4 * q + 3], b.w)};
+        epi_put4<EPI>(p, rb + co, v);
+      }
   }
 }
 
@@ -219,12 +294,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
     const bf16* as = smem + (kt % STAGES) * STAGE;
     const bf16* bs = as + BM * BK;
     // Fragments of the next 16-wide K slice are read from LDS while the
-    // current slice's MFMAs issue.  With SWAP the MFMA takes B's fragment as
-    // its first operand, so each lane's accumulator holds 4 consecutive
-    // output columns of one row (vector loads and stores in the epilogue);
-    // without it a lane holds one column of 4 consecutive rows and the 32
-    // lanes of a row cover 32 consecutive columns (coalesced scalar stores
-    // and atomics).
+    // current slice's MFMAs issue.  Without SWAP a lane's accumulator holds
+    // one output column of 4 consecutive rows per register group, and the 32
+    // lanes of a row cover 32 consecutive columns (coalesced stores and
+    // atomics); with SWAP the MFMA takes B's fragment first and a lane holds
+    // 4 consecutive columns of one row (16-byte reads of the residual or the
+    // GELU input).
     bf16x8 a[2][TM], b[2][TN];
     auto frag = [&](int kk, bf16x8* fa, bf16x8* fb) {
       const int c = 2 * kk + lg;
@@ -284,42 +359,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   if (do_rowsum && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
     unsafeAtomicAdd(p.row_sum + m0 + threadIdx.x, p.alpha * rsum);
 
+  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
   if constexpr (SWAP) {
-    // accumulator (i, j), register 4q + e: row m = wm0 + 32i + lr, column
-    // n = wn0 + 32j + 8q + 4lg + e
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm0 + 32 * i + lr;
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn0 + 32 * j + 8 * q + 4 * lg;
-          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (n + 3 < p.N) {
-            epi_store4<EPI, OUT_BF16, ATOMIC>(p, m, n, v);
-          } else {
-            for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n + e, v[e]);
-          }
-        }
-    }
-  } else {
-    // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn0 + 32 * j + lr;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (m < p.M) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
-        }
-      }
+    if (interior) epi_tile_swap<EPI, OUT_BF16, TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    else epi_tile_swap<EPI, OUT_BF16, TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    return;
   }
+  if (interior) {
+    epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+    return;
+  }
+  // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn0 + 32 * j + lr;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+        if (m < p.M) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
+      }
+    }
 }
 
 template <int BM, int BN, int BK, int STAGES>

@@ -90,9 +90,11 @@ def test_gemm_bf16_accumulate_split_k_exact(g, ak, bk):
     assert np.array_equal(host(C), ref)
 
 
-def test_gemm_bf16_epilogues(g):
+@pytest.mark.parametrize("M,N,K", [(264, 392, 328), (776, 520, 200)])
+def test_gemm_bf16_epilogues(g, M, N, K):
+    """Every fused epilogue, on tiles wholly inside C (the unchecked store
+    path) and on ragged edge tiles."""
     import torch
-    M, N, K = 264, 392, 328
     announce(f"gemm bf16 epilogues M={M} N={N} K={K}")
     rng = np.random.default_rng(3)
     A = bf16_round(rng.standard_normal((M, K)).astype(np.float32))

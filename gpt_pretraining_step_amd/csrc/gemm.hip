@@ -13,6 +13,8 @@
 // gradient of the same Linear.
 #include "gemm_kernel.h"
 
+#include <algorithm>
+
 namespace g2 {
 
 // ------------------------------------------------------- float32 SIMT GEMM
@@ -105,14 +107,14 @@ static hipError_t launch_v2(const Launch& L, const GemmP& p) {
   return hipGetLastError();
 }
 
-// bf16 products: 256x256 block tiles, 8 waves of 128x64, K step 64, two LDS
-// stages fed by DMA.  Residual and dGELU epilogues use the accumulator
-// layout with 4 consecutive columns per lane (vector loads of R / U);
-// the others keep 32 consecutive columns per row per instruction
-// (coalesced scalar stores and atomics).
-template <bool A_K, bool B_K>
-static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
-  constexpr int BM = 256, BN = 256, BK = 64, WGM = 2, WGN = 4, ST = 2;
+// bf16 products: 256 x BN block tiles (BN = 256: 8 waves of 128x64; BN =
+// 192: 8 waves of 64x96), K step 64, two LDS stages fed by DMA.  Residual
+// and dGELU epilogues use the accumulator layout with 4 consecutive columns
+// per lane (vector loads of R / U); the others keep 32 consecutive columns
+// per row per instruction (coalesced scalar stores and atomics).
+template <int BN, int WGM, int WGN, bool A_K, bool B_K>
+static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
+  constexpr int BM = 256, BK = 64, ST = 2;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const bool at = p.splits > 1;
@@ -141,6 +143,21 @@ static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
   return e;
 }
 
+// Rounds of one block per compute unit that a 256 x bn tiling needs, times
+// the tile width: the relative time of the product under that tiling.
+static long tiling_cost(int M, int N, int bn, int splits) {
+  const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn) * splits;
+  return (tiles + 255) / 256 * bn;
+}
+
+template <bool A_K, bool B_K>
+static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
+  // the narrower tile re-reads A more often: take it only for a clear gain
+  if (epi != GPT2_EPI_ACCUMULATE && 10 * tiling_cost(p.M, p.N, 192, 1) < 9 * tiling_cost(p.M, p.N, 256, 1))
+    return dispatch_tile<192, 4, 2, A_K, B_K>(L, p, epi, ob);
+  return dispatch_tile<256, 2, 4, A_K, B_K>(L, p, epi, ob);
+}
+
 template <bool A_K, bool B_K>
 static hipError_t dispatch_f32(const Launch& L, GemmP p, int epi) {
   p.tiles_m = (p.M + 63) / 64;
@@ -166,10 +183,14 @@ static hipError_t dispatch_f32(const Launch& L, GemmP p, int epi) {
 // (the weight gradients: small outputs, K = tokens).  Partial products are
 // added with float32 atomics, whose cost grows with the split count, so the
 // grid is filled to about one block per CU and no further.
-static int choose_splits(int tiles, int K, int BK, int target_blocks) {
-  int splits = 1;
-  while (tiles * splits * 2 <= target_blocks && K / (splits * 2) >= 4 * BK) splits *= 2;
-  return splits;
+// Split-K count for an accumulating product with few output tiles: as many
+// splits as fill one round of blocks over the compute units, keeping at least
+// 16 K steps per split (each split adds its partial sums atomically).
+static int choose_splits(int tiles, int K, int BK, int units) {
+  if (tiles >= units) return 1;
+  const int by_units = units / tiles;
+  const int by_k = K / (16 * BK);
+  return std::max(1, std::min(by_units, by_k));
 }
 
 hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum) {
@@ -191,7 +212,7 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
   constexpr int BK = 64;
   if (a.epilogue == GPT2_EPI_ACCUMULATE) {
     const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    p.splits = choose_splits(tiles, a.K, BK, 256);
+    p.splits = choose_splits(tiles, a.K, BK, 256);  // 256 compute units
     p.k_per_split = ((a.K + p.splits * BK - 1) / (p.splits * BK)) * BK;
     p.splits = (a.K + p.k_per_split - 1) / p.k_per_split;
   }

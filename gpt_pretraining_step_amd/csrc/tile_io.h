@@ -69,32 +69,37 @@ __device__ __forceinline__ bf16x4 tr_read4(const bf16* tile, int r0, int c0) {
 // ---- tiles stored with K as the row index: [BK rows][R columns], R bf16 per
 // row (the output rows of a product whose operand is K-slow in memory).
 // 16-byte chunk c of row k sits at c ^ ((k & 3) << 1), so the 4 rows of one
-// transposing read fall on distinct banks.
+// transposing read fall on distinct banks.  The XOR flips only bits 1 and 2
+// of c, so it stays inside the row whenever R / 8 is a multiple of 8 (R = 64,
+// 128, 192, 256).
 template <int R>
 __device__ __forceinline__ int kr_chunk(int k, int c) {
+  static_assert(R % 64 == 0, "rows of whole 8-chunk groups");
   return c ^ ((k & 3) << 1);
 }
 
 // [BK][R] tile (source rows k0.. of a [K][ld] matrix, columns col0..col0+R)
-// -> LDS by DMA; rows past K and columns past ncols read as zeros.
+// -> LDS by DMA; rows past K and columns past ncols read as zeros.  Wave
+// instruction i fills LDS chunks 64 i .. 64 i + 63 of the tile (chunk g is
+// row g / (R/8), position g % (R/8)); the lane whose destination is position
+// p of row k fetches the logical chunk that the swizzle puts there.
 template <int R, int BK, int NWAVES>
 __device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, int64_t ld, int col0, int ncols,
                                        int k0, int K) {
   constexpr int CPR = R / 8;             // 16-byte chunks per row
-  constexpr int INSTR = BK * CPR / 64;   // 64 chunks per wave instruction
-  static_assert(CPR <= 64 && 64 % CPR == 0, "a wave instruction covers whole rows");
-  static_assert(INSTR % NWAVES == 0, "tile must split evenly over the waves");
-  constexpr int RPI = 64 / CPR;          // rows per instruction
-  constexpr int IPW = INSTR / NWAVES;
+  constexpr int TOTAL = BK * CPR;        // chunks per tile
+  static_assert(TOTAL % (64 * NWAVES) == 0, "tile must split evenly over the waves");
+  constexpr int IPW = TOTAL / 64 / NWAVES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int ins = wave * IPW + i;
-    const int k = ins * RPI + lane / CPR;
-    const int c = kr_chunk<R>(k, lane % CPR);
+    const int g = ins * 64 + lane;
+    const int k = g / CPR;
+    const int c = kr_chunk<R>(k, g % CPR);
     const int gk = k0 + k, gc = col0 + 8 * c;
-    const bf16* g = (gk < K && gc < ncols) ? src + (int64_t)gk * ld + gc : reinterpret_cast<const bf16*>(g2_zero16);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), lds + ins * RPI * R, 16, 0, 0);
+    const bf16* gp = (gk < K && gc < ncols) ? src + (int64_t)gk * ld + gc : reinterpret_cast<const bf16*>(g2_zero16);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp), lds + ins * 512, 16, 0, 0);
   }
 }
 

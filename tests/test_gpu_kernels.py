@@ -90,10 +90,11 @@ def test_gemm_bf16_accumulate_split_k_exact(g, ak, bk):
     assert np.array_equal(host(C), ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(264, 392, 328), (776, 520, 200)])
+@pytest.mark.parametrize("M,N,K", [(264, 392, 328), (776, 520, 200), (4096, 4096, 72)])
 def test_gemm_bf16_epilogues(g, M, N, K):
     """Every fused epilogue, on tiles wholly inside C (the unchecked store
-    path) and on ragged edge tiles."""
+    path) and on ragged edge tiles; the small shapes take 256x192 block
+    tiles, 4096 x 4096 the 256x256 ones."""
     import torch
     announce(f"gemm bf16 epilogues M={M} N={N} K={K}")
     rng = np.random.default_rng(3)

@@ -10,6 +10,8 @@ namespace g2 {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bool target_valid(int t, int V) { return t >= 0 && t < V; }
 
@@ -139,6 +141,91 @@ __global__ __launch_bounds__(1024) void ce_finish_kernel(const float* __restrict
   }
 }
 
+// One block per row of the fused path.  From the per-tile statistics
+// (mx_t, s_t) of row r: lse = max_t mx_t + log(sum_t s_t exp(mx_t - max)).
+// The target logit is recomputed in float32 as hidden[r] . wte[target], and
+// loss_r = lse - z_target.  Then y[r][n] = z - mx_t(n) is overwritten with
+// dlogits = scale / count * (exp(z - lse) - [n == target]), the target entry
+// from the float32 logit.  Rows with an ignored target get zeros.
+__global__ __launch_bounds__(256) void ce_apply_kernel(bf16* __restrict__ y, const float2* __restrict__ stats,
+                                                       int tiles, const bf16* __restrict__ hidden,
+                                                       const bf16* __restrict__ wte, const int32_t* __restrict__ tgt,
+                                                       int V, int C, const int* __restrict__ count, float scale,
+                                                       float* __restrict__ row_loss) {
+  extern __shared__ float shift[];  // [tiles]: mx_t - lse, then scratch
+  __shared__ float red[256 / 64];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float2* st = stats + (int64_t)r * tiles;
+  auto block_max = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return v;
+  };
+  auto block_sum = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return v;
+  };
+  float mx = -INFINITY;
+  for (int t = tid; t < tiles; t += 256) mx = fmaxf(mx, st[t].x);
+  mx = block_max(mx);
+  float sm = 0.f;
+  for (int t = tid; t < tiles; t += 256) {
+    const float2 s2 = st[t];
+    sm += s2.y * exp2f((s2.x - mx) * LOG2E);
+  }
+  sm = block_sum(sm);
+  const float lse = mx + log2f(sm) * LN2;
+  for (int t = tid; t < tiles; t += 256) shift[t] = (st[t].x - lse) * LOG2E;
+  const int t = tgt[r];
+  const bool valid = target_valid(t, V);
+  float zt = 0.f;
+  if (valid) {
+    const bf16* h = hidden + (int64_t)r * C;
+    const bf16* w = wte + (int64_t)t * C;
+    for (int c = tid; c < C; c += 256) zt = fmaf(bf2f(h[c]), bf2f(w[c]), zt);
+  }
+  zt = block_sum(zt);  // also orders the shift[] writes before their reads
+  const int n = count[0];
+  const float coef = (valid && n > 0) ? scale / (float)n : 0.f;
+  if (tid == 0) row_loss[r] = valid ? lse - zt : 0.f;
+  const float dt = coef * (exp2f((zt - lse) * LOG2E) - 1.f);
+  bf16* yr = y + (int64_t)r * V;
+  for (int c8 = tid; c8 < V / 8; c8 += 256) {
+    const int n0 = 8 * c8;
+    const float sh = shift[n0 / kCeTile];
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(yr + n0);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = coef * __builtin_amdgcn_exp2f(fmaf(bf2f(v[e]), LOG2E, sh));
+    if (valid && t >= n0 && t < n0 + 8) o[t - n0] = dt;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2v pr = __builtin_convertvector((f32x2v){o[e], o[e + 1]}, bf16x2v);
+      v[e] = pr[0];
+      v[e + 1] = pr[1];
+    }
+    *reinterpret_cast<bf16x8*>(yr + n0) = v;
+  }
+}
+
+hipError_t launch_ce_apply(const Launch& L, bf16* y, const float2* stats, const bf16* hidden, const bf16* wte,
+                           const int32_t* tgt, int rows, int V, int C, const int* count, float scale,
+                           float* row_loss) {
+  const int tiles = ce_stat_tiles(V);
+  prof_begin(L);
+  ce_apply_kernel<<<rows, 256, tiles * sizeof(float), L.stream>>>(y, stats, tiles, hidden, wte, tgt, V, C, count,
+                                                                   scale, row_loss);
+  prof_end(L);
+  return hipGetLastError();
+}
+
 hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int* count, int* flag) {
   prof_begin(L);
   count_targets_kernel<<<1, 1024, 0, L.stream>>>(tgt, n, V, count, flag);
@@ -161,8 +248,6 @@ hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, 
   prof_end(L);
   return hipGetLastError();
 }
-template hipError_t launch_ce_rows<float, bf16>(const Launch&, const float*, int64_t, bf16*, int64_t, const int32_t*,
-                                               int, int, const int*, float, float*, float*);
 template hipError_t launch_ce_rows<float, float>(const Launch&, const float*, int64_t, float*, int64_t, const int32_t*,
                                                 int, int, const int*, float, float*, float*);
 

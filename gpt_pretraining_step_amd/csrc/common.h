@@ -118,6 +118,17 @@ hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, 
 hipError_t launch_ce_finish_n(const Launch& L, const float* row_loss, int n, const int* count, float* loss,
                               int* flag);
 
+// Fused lm_head + cross-entropy (bf16): the logits product writes per-tile
+// softmax statistics and bf16 logits offset by their tile maximum (ld = V),
+// then one pass per row turns them into dlogits in place.
+constexpr int kCeTile = 256;  // columns per statistics tile
+inline int ce_stat_tiles(int V) { return (V + kCeTile - 1) / kCeTile; }
+hipError_t launch_gemm_ce_stats(const Launch& L, const bf16* hidden, const bf16* wte, bf16* y, float2* stats, int M,
+                                int V, int C);
+hipError_t launch_ce_apply(const Launch& L, bf16* y, const float2* stats, const bf16* hidden, const bf16* wte,
+                           const int32_t* tgt, int rows, int V, int C, const int* count, float scale,
+                           float* row_loss);
+
 // Optimizer.
 hipError_t launch_sumsq_partials(const Launch& L, const float* g, size_t n, float* partials, int nparts);
 hipError_t launch_adamw(const Launch& L, float* p, const float* g, float* m, float* v, bf16* shadow, size_t n,

@@ -143,18 +143,45 @@ static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
   return e;
 }
 
-// Rounds of one block per compute unit that a 256 x bn tiling needs, times
-// the tile width: the relative time of the product under that tiling.
-static long tiling_cost(int M, int N, int bn, int splits) {
-  const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn) * splits;
-  return (tiles + 255) / 256 * bn;
+constexpr int kUnits = 256;  // compute units: one block each per round
+
+// Split-K count for an accumulating product (each split adds its partial
+// sums atomically): the count that minimises the rounds of blocks over the
+// compute units per unit of work, keeping at least 16 K steps per split; a
+// larger count must save at least 3%.
+static int choose_splits(long tiles, int K, int BK) {
+  int best = 1;
+  double best_cost = (double)((tiles + kUnits - 1) / kUnits);
+  for (int s = 2; s <= 32 && K / s >= 16 * BK; ++s) {
+    const double cost = (double)((tiles * s + kUnits - 1) / kUnits) / s;
+    if (cost < 0.97 * best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+// Relative time of a product under 256 x bn block tiles: rounds of blocks
+// per split times the tile width.
+static double tiling_cost(int M, int N, int K, int bn, bool accumulate, int* splits) {
+  const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+  *splits = accumulate ? choose_splits(tiles, K, 64) : 1;
+  return (double)((tiles * *splits + kUnits - 1) / kUnits) / *splits * bn;
 }
 
 template <bool A_K, bool B_K>
 static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
+  const bool acc = epi == GPT2_EPI_ACCUMULATE;
+  int s256 = 1, s192 = 1;
+  const double c256 = tiling_cost(p.M, p.N, p.K, 256, acc, &s256);
+  const double c192 = tiling_cost(p.M, p.N, p.K, 192, acc, &s192);
   // the narrower tile re-reads A more often: take it only for a clear gain
-  if (epi != GPT2_EPI_ACCUMULATE && 10 * tiling_cost(p.M, p.N, 192, 1) < 9 * tiling_cost(p.M, p.N, 256, 1))
-    return dispatch_tile<192, 4, 2, A_K, B_K>(L, p, epi, ob);
+  const bool narrow = c192 < 0.9 * c256;
+  const int splits = narrow ? s192 : s256;
+  p.k_per_split = (p.K + splits * 64 - 1) / (splits * 64) * 64;
+  p.splits = (p.K + p.k_per_split - 1) / p.k_per_split;
+  if (narrow) return dispatch_tile<192, 4, 2, A_K, B_K>(L, p, epi, ob);
   return dispatch_tile<256, 2, 4, A_K, B_K>(L, p, epi, ob);
 }
 
@@ -183,14 +210,23 @@ static hipError_t dispatch_f32(const Launch& L, GemmP p, int epi) {
 // (the weight gradients: small outputs, K = tokens).  Partial products are
 // added with float32 atomics, whose cost grows with the split count, so the
 // grid is filled to about one block per CU and no further.
-// Split-K count for an accumulating product with few output tiles: as many
-// splits as fill one round of blocks over the compute units, keeping at least
-// 16 K steps per split (each split adds its partial sums atomically).
-static int choose_splits(int tiles, int K, int BK, int units) {
-  if (tiles >= units) return 1;
-  const int by_units = units / tiles;
-  const int by_k = K / (16 * BK);
-  return std::max(1, std::min(by_units, by_k));
+hipError_t launch_gemm_ce_stats(const Launch& L, const bf16* hidden, const bf16* wte, bf16* y, float2* stats, int M,
+                                int V, int C) {
+  constexpr int BM = 256, BN = kCeTile, BK = 64, WGM = 2, WGN = 4, ST = 2;
+  GemmP p{};
+  p.M = M; p.N = V; p.K = C;
+  p.lda = C; p.ldb = C; p.ldc = V;
+  p.A = hidden; p.B = wte; p.C = y;
+  p.stats = stats;
+  p.alpha = 1.f;
+  p.splits = 1;
+  p.k_per_split = C;
+  p.tiles_m = (M + BM - 1) / BM;
+  p.tiles_n = (V + BN - 1) / BN;
+  prof_begin(L);
+  const hipError_t e = launch_v2<BM, BN, BK, WGM, WGN, ST, true, true, EPI_CE_STATS, true, false, true>(L, p);
+  prof_end(L);
+  return e;
 }
 
 hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum) {
@@ -200,7 +236,8 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
   if (a.dtype == GPT2_PRECISION_FP32) {
     if (a.epilogue == GPT2_EPI_ACCUMULATE) {
       const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
-      p.splits = choose_splits(tiles, a.K, 16, 512);
+      p.splits = 1;
+      while (tiles * p.splits * 2 <= 2 * kUnits && a.K / (p.splits * 2) >= 64) p.splits *= 2;
       p.k_per_split = ((a.K + p.splits * 16 - 1) / (p.splits * 16)) * 16;
       p.splits = (a.K + p.k_per_split - 1) / p.k_per_split;
     }
@@ -208,13 +245,6 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
     if (ak && !bk) return dispatch_f32<true, false>(L, p, a.epilogue);
     if (!ak && bk) return dispatch_f32<false, true>(L, p, a.epilogue);
     return dispatch_f32<false, false>(L, p, a.epilogue);
-  }
-  constexpr int BK = 64;
-  if (a.epilogue == GPT2_EPI_ACCUMULATE) {
-    const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    p.splits = choose_splits(tiles, a.K, BK, 256);  // 256 compute units
-    p.k_per_split = ((a.K + p.splits * BK - 1) / (p.splits * BK)) * BK;
-    p.splits = (a.K + p.k_per_split - 1) / p.k_per_split;
   }
   const bool ob = a.out_bf16 != 0;
   if (ak && bk) return dispatch_bf16<true, true>(L, p, a.epilogue, ob);

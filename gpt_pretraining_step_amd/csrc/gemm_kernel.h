@@ -30,6 +30,7 @@ struct GemmP {
   const void* U;
   const float* bias;
   float* row_sum;  // optional: row_sum[m] += sum over this product's K of A(m, k) (one column-tile adds it)
+  float2* stats;   // EPI_CE_STATS: per (row, column tile) softmax statistics, [M][tiles_n]
   float alpha;
   int tiles_m, tiles_n, splits, k_per_split;
 };
@@ -191,6 +192,80 @@ __device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol
         const float v[4] = {fmaf(p.alpha, acc[i][j][4 * q + 0], b.x), fmaf(p.alpha, acc[i][j][4 * q + 1], b.y),
                             fmaf(p.alpha, acc[i][j][4 * q + 2], b.z), fmaf(p.alpha, acc[i][j][4 * q + 3], b.w)};
         epi_put4<EPI>(p, rb + co, v);
+      }
+  }
+}
+
+// Internal epilogue of the lm_head product (logits = hidden wte^T), swapped
+// layout only.  For every row m and column tile tn it stores the tile's
+// softmax statistics stats[m][tn] = (mx, sum over the tile's columns n < N of
+// exp(z[m][n] - mx)) with mx the tile's largest logit, all from the float32
+// accumulators, and writes C[m][n] = bf16(z[m][n] - mx).  Entries near the
+// row's maximum, the ones that carry the softmax, keep nearly full precision.
+constexpr int EPI_CE_STATS = 16;
+
+template <int BM, int WGN, int TM, int TN>
+__device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int tn, int wm0, int wn0, int wave,
+                                             int lr, int lg, const f32x16 (&acc)[TM][TN], float* red) {
+  constexpr float L2E = 1.4426950408889634f;
+  const int wn = wave % WGN;
+  // per row: this wave's 64 columns (32 in each lane half) -> (max, sum of exp)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int col = n0 + wn0 + 32 * j + 8 * (e >> 2) + 4 * lg + (e & 3);
+        if (col < p.N) mx = fmaxf(mx, acc[i][j][e]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int col = n0 + wn0 + 32 * j + 8 * (e >> 2) + 4 * lg + (e & 3);
+        if (col < p.N) sm += __builtin_amdgcn_exp2f((acc[i][j][e] - mx) * L2E);
+      }
+    sm += __shfl_xor(sm, 32);
+    const int row = wm0 + 32 * i + lr;
+    if (lg == 0) {
+      red[2 * (wn * BM + row)] = mx;
+      red[2 * (wn * BM + row) + 1] = sm;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = wm0 + 32 * i + lr;
+    const int m = m0 + row;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WGN; ++w) mx = fmaxf(mx, red[2 * (w * BM + row)]);
+    float sm = 0.f;
+#pragma unroll
+    for (int w = 0; w < WGN; ++w) {
+      const float mw = red[2 * (w * BM + row)];
+      if (mw != -INFINITY) sm += red[2 * (w * BM + row) + 1] * __builtin_amdgcn_exp2f((mw - mx) * L2E);
+    }
+    if (m >= p.M) continue;
+    if (wn == 0 && lg == 0) p.stats[(int64_t)m * p.tiles_n + tn] = make_float2(mx, sm);
+    bf16* crow = static_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn0 + 32 * j + 8 * q + 4 * lg;
+        const bf16x2 lo = f2bf2(acc[i][j][4 * q] - mx, acc[i][j][4 * q + 1] - mx);
+        const bf16x2 hi = f2bf2(acc[i][j][4 * q + 2] - mx, acc[i][j][4 * q + 3] - mx);
+        if (col + 4 <= p.N) {
+          *reinterpret_cast<bf16x4*>(crow + col) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          const bf16 v4[4] = {lo[0], lo[1], hi[0], hi[1]};
+          for (int e = 0; e < 4 && col + e < p.N; ++e) crow[col + e] = v4[e];
+        }
       }
   }
 }
@@ -359,29 +434,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   if (do_rowsum && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
     unsafeAtomicAdd(p.row_sum + m0 + threadIdx.x, p.alpha * rsum);
 
-  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
-  if constexpr (SWAP) {
-    if (interior) epi_tile_swap<EPI, OUT_BF16, TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
-    else epi_tile_swap<EPI, OUT_BF16, TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
-    return;
-  }
-  if (interior) {
-    epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
-    return;
-  }
-  // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
+  if constexpr (EPI == EPI_CE_STATS) {
+    static_assert(SWAP && WN == 64, "statistics epilogue: swapped layout, 64 columns per wave");
+    // every wave is done with the operand stages: reuse them for the
+    // cross-wave reduction
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    epi_ce_stats<BM, WGN, TM, TN>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, reinterpret_cast<float*>(smem));
+  } else {
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
+    if constexpr (SWAP) {
+      if (interior) epi_tile_swap<EPI, OUT_BF16, TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+      else epi_tile_swap<EPI, OUT_BF16, TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    } else if (interior) {
+      epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+    } else {
+      // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn0 + 32 * j + lr;
-      if (n >= p.N) continue;
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn0 + 32 * j + lr;
+          if (n >= p.N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (m < p.M) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
-      }
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+            if (m < p.M) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
+          }
+        }
     }
+  }
 }
 
 template <int BM, int BN, int BK, int STAGES>

@@ -222,6 +222,7 @@ struct Layout {
   size_t Z = 0, meanf = 0, rstdf = 0, act_bytes = 0;
   // scratch
   size_t dR = 0, dRb = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
+  size_t ce_stats = 0;
   size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, scratch_bytes = 0;
 };
 
@@ -277,8 +278,16 @@ Layout build_layout(const gpt2_config& c) {
   y.dY = s.take(rows * C * y.es);
   y.dU = s.take(rows * F * y.es);
   y.attnD = s.take(rows * H * 4);
-  y.logits = s.take((size_t)y.chunk * V * 4);
-  y.dlogits = s.take((size_t)y.chunk * V * y.es);
+  if (c.precision == GPT2_PRECISION_BF16) {
+    // fused lm_head + cross-entropy over all rows at once: bf16 logits (then
+    // dlogits, in place) and per-tile softmax statistics
+    y.chunk = (int)rows;
+    y.dlogits = s.take(rows * V * 2);
+    y.ce_stats = s.take(rows * (size_t)ce_stat_tiles((int)V) * sizeof(float2));
+  } else {
+    y.logits = s.take((size_t)y.chunk * V * 4);
+    y.dlogits = s.take((size_t)y.chunk * V * y.es);
+  }
   y.rowloss = s.take(rows * 4);
   y.scratch_bytes = (s.off + 255) / 256 * 256;
   return y;
@@ -412,11 +421,38 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   HIP_TRY(launch_layernorm_fwd(c->at("ln.fwd"), rlast, c->P(c->tab.lnf_w), c->P(c->tab.lnf_b), c->act(y.Z), bf,
                                c->act<float>(y.meanf), c->act<float>(y.rstdf), M, C));
 
-  // ---- tied lm_head + cross-entropy, in row chunks
+  // ---- tied lm_head + cross-entropy
   float* dZ = c->scr<float>(y.dA);
   HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
   const size_t es = y.es;
-  for (int r0 = 0; r0 < M; r0 += y.chunk) {
+  if (bf) {
+    // all rows at once: statistics-epilogue product, then dlogits in place
+    bf16* dlog = c->scr<bf16>(y.dlogits);
+    float2* stats = c->scr<float2>(y.ce_stats);
+    const bf16* Zb = c->act<bf16>(y.Z);
+    const bf16* Wb = static_cast<const bf16*>(c->W(c->tab.wte));
+    HIP_TRY(launch_gemm_ce_stats(c->at("gemm.lm_head"), Zb, Wb, dlog, stats, M, V, C));
+    HIP_TRY(launch_ce_apply(c->at("ce.rows"), dlog, stats, Zb, Wb, tgt, M, V, C, count, scale, rowloss));
+    {  // dZ += dlogits wte
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = M; a.N = C; a.K = V;
+      a.a_kmajor = 1; a.b_kmajor = 0;
+      a.lda = V; a.ldb = C; a.ldc = C;
+      a.A = dlog; a.B = Wb; a.C = dZ;
+      a.epilogue = GPT2_EPI_ACCUMULATE;
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dx"), a));
+    }
+    {  // dwte += dlogits^T Z
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = V; a.N = C; a.K = M;
+      a.a_kmajor = 0; a.b_kmajor = 0;
+      a.lda = V; a.ldb = C; a.ldc = C;
+      a.A = dlog; a.B = Zb; a.C = c->Gr(c->tab.wte);
+      a.epilogue = GPT2_EPI_ACCUMULATE;
+      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dw"), a));
+    }
+  }
+  for (int r0 = 0; !bf && r0 < M; r0 += y.chunk) {
     const int rows = std::min(y.chunk, M - r0);
     const char* z_c = c->act<char>(y.Z) + (size_t)r0 * C * es;
     float* logits = c->scr<float>(y.logits);
@@ -430,12 +466,8 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
       a.epilogue = GPT2_EPI_STORE; a.out_bf16 = 0;
       HIP_TRY(launch_gemm(c->at("gemm.lm_head"), a));
     }
-    if (bf)
-      HIP_TRY(launch_ce_rows<float, bf16>(c->at("ce.rows"), logits, V, static_cast<bf16*>(dlog), V, tgt + r0, rows, V,
-                                          count, scale, nullptr, rowloss + r0));
-    else
-      HIP_TRY(launch_ce_rows<float, float>(c->at("ce.rows"), logits, V, static_cast<float*>(dlog), V, tgt + r0, rows,
-                                           V, count, scale, nullptr, rowloss + r0));
+    HIP_TRY(launch_ce_rows<float, float>(c->at("ce.rows"), logits, V, static_cast<float*>(dlog), V, tgt + r0, rows, V,
+                                         count, scale, nullptr, rowloss + r0));
     {  // dZ_c += dlogits_c wte
       gpt2_gemm_args a = gemm_base(dt);
       a.M = rows; a.N = C; a.K = V;
@@ -677,18 +709,14 @@ const char* gpt2_strerror(int s) {
 
 // ---------------------------------------------------- isolated lm_head + CE
 
-static size_t lmhead_chunk(int M) { return (size_t)std::min(M, kCeChunk); }
-
 size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V) {
   if (M < 1 || C < 1 || V < 1) return 0;
-  (void)C;
-  const size_t ch = lmhead_chunk(M);
   Bump s;
-  s.take(256);                    // count
-  s.take((size_t)M * 4);          // row losses
-  s.take(ch * (size_t)V * 4);     // logits chunk
-  s.take(ch * (size_t)V * 2);     // dlogits chunk
-  s.take((size_t)M * C * 4);      // dhidden (float32 accumulation)
+  s.take(256);                                            // count
+  s.take((size_t)M * 4);                                  // row losses
+  s.take((size_t)M * V * 2);                              // bf16 logits, then dlogits
+  s.take((size_t)M * ce_stat_tiles(V) * sizeof(float2));  // per-tile softmax statistics
+  s.take((size_t)M * C * 4);                              // dhidden (float32 accumulation)
   return (s.off + 255) / 256 * 256;
 }
 
@@ -698,44 +726,34 @@ int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, con
   if (M < 1 || C < 8 || V < 8 || C % 8 || V % 8) return GPT2_ERR_SHAPE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Launch L{st, nullptr, ""};
-  const size_t ch = lmhead_chunk(M);
   Bump s;
   char* base = static_cast<char*>(d_scratch);
   int* count = reinterpret_cast<int*>(base + s.take(256));
   float* rowloss = reinterpret_cast<float*>(base + s.take((size_t)M * 4));
-  float* logits = reinterpret_cast<float*>(base + s.take(ch * (size_t)V * 4));
-  bf16* dlog = reinterpret_cast<bf16*>(base + s.take(ch * (size_t)V * 2));
+  bf16* dlog = reinterpret_cast<bf16*>(base + s.take((size_t)M * V * 2));
+  float2* stats = reinterpret_cast<float2*>(base + s.take((size_t)M * ce_stat_tiles(V) * sizeof(float2)));
   float* dh32 = reinterpret_cast<float*>(base + s.take((size_t)M * C * 4));
   int* flag = reinterpret_cast<int*>(d_flag);
+  const bf16* H = static_cast<const bf16*>(d_hidden);
+  const bf16* W = static_cast<const bf16*>(d_weight);
   HIP_TRY(launch_count_targets(L, d_targets, M, V, count, flag));
   HIP_TRY(launch_fill_f32(L, dh32, (size_t)M * C, 0.f));
-  const bf16* H = static_cast<const bf16*>(d_hidden);
-  for (int r0 = 0; r0 < M; r0 += (int)ch) {
-    const int rows = std::min((int)ch, M - r0);
-    gpt2_gemm_args a = gemm_base(GPT2_PRECISION_BF16);
-    a.M = rows; a.N = V; a.K = C;
-    a.a_kmajor = 1; a.b_kmajor = 1;
-    a.lda = C; a.ldb = C; a.ldc = V;
-    a.A = H + (size_t)r0 * C; a.B = d_weight; a.C = logits;
-    a.epilogue = GPT2_EPI_STORE;
-    HIP_TRY(launch_gemm(L, a));
-    HIP_TRY(launch_ce_rows<float, bf16>(L, logits, V, dlog, V, d_targets + r0, rows, V, count, 1.f, nullptr,
-                                        rowloss + r0));
-    a = gemm_base(GPT2_PRECISION_BF16);
-    a.M = rows; a.N = C; a.K = V;
-    a.a_kmajor = 1; a.b_kmajor = 0;
-    a.lda = V; a.ldb = C; a.ldc = C;
-    a.A = dlog; a.B = d_weight; a.C = dh32 + (size_t)r0 * C;
-    a.epilogue = GPT2_EPI_ACCUMULATE;
-    HIP_TRY(launch_gemm(L, a));
-    a = gemm_base(GPT2_PRECISION_BF16);
-    a.M = V; a.N = C; a.K = rows;
-    a.a_kmajor = 0; a.b_kmajor = 0;
-    a.lda = V; a.ldb = C; a.ldc = C;
-    a.A = dlog; a.B = H + (size_t)r0 * C; a.C = d_dweight;
-    a.epilogue = GPT2_EPI_ACCUMULATE;
-    HIP_TRY(launch_gemm(L, a));
-  }
+  HIP_TRY(launch_gemm_ce_stats(L, H, W, dlog, stats, M, V, C));
+  HIP_TRY(launch_ce_apply(L, dlog, stats, H, W, d_targets, M, V, C, count, 1.f, rowloss));
+  gpt2_gemm_args a = gemm_base(GPT2_PRECISION_BF16);
+  a.M = M; a.N = C; a.K = V;
+  a.a_kmajor = 1; a.b_kmajor = 0;
+  a.lda = V; a.ldb = C; a.ldc = C;
+  a.A = dlog; a.B = W; a.C = dh32;
+  a.epilogue = GPT2_EPI_ACCUMULATE;
+  HIP_TRY(launch_gemm(L, a));
+  a = gemm_base(GPT2_PRECISION_BF16);
+  a.M = V; a.N = C; a.K = M;
+  a.a_kmajor = 0; a.b_kmajor = 0;
+  a.lda = V; a.ldb = C; a.ldc = C;
+  a.A = dlog; a.B = H; a.C = d_dweight;
+  a.epilogue = GPT2_EPI_ACCUMULATE;
+  HIP_TRY(launch_gemm(L, a));
   HIP_TRY(launch_ce_finish_n(L, rowloss, M, count, d_loss, flag));
   HIP_TRY(launch_to_bf16(L, dh32, static_cast<bf16*>(d_dhidden), (size_t)M * C));
   return GPT2_OK;

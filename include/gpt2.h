@@ -217,8 +217,12 @@ size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V);
  *   d_scratch: gpt2_lmhead_ce_scratch_bytes(M, C, V) bytes.
  *   d_flag: optional device int32, receives GPT2_ERR_BAD_ID if a target is
  *     out of range (else left unchanged).
- * C and V must be multiples of 8, M >= 1.  Logits are formed one row chunk
- * at a time and never stored whole. */
+ * C and V must be multiples of 8, M >= 1.  The logits product keeps, per
+ * row and 256-column tile, the float32 maximum and sum of exponentials and
+ * stores the logits in bf16 as offsets from that tile maximum; one pass per
+ * row then forms the log-sum-exp, the loss (target logit recomputed in
+ * float32) and the bf16 logit gradient in place, and the two products of the
+ * backward read it.  Scratch grows as M * V * 2 bytes. */
 int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, const int32_t* d_targets,
                    int M, int C, int V, float* d_loss, void* d_dhidden, float* d_dweight,
                    void* d_scratch, int32_t* d_flag);

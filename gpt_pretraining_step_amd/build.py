@@ -36,9 +36,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file extras.  attention.hip: MFMA accumulators in ordinary VGPRs (the
+# softmax rescales and reads them every tile; the AGPR form would copy them
+# out and back).
+EXTRA = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CXXFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *CXXFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -229,38 +229,46 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) sT[c] = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT[c]);
     }
-    const bool edge = (kb + 63 > q0) || (kb + 63 >= T);
+    // keys after the query (and past T) only occur in the diagonal and
+    // ragged tiles; the branch is uniform over the wave
+    if ((kb + 63 > q0) || (kb + 63 >= T)) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
+          sT[c][r] = (key > qi || key >= T) ? -INFINITY : sT[c][r];
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sT[c][r] * sl2;
-        if (edge) {
-          const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (key > qi || key >= T) v = -INFINITY;
-        }
-        sT[c][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
-    m = mn;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sT[c][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;  // log2 units (sl2 > 0)
+    // The running maximum m moves only when some query of the wave sees a
+    // score more than 2^8 above it; otherwise p = 2^(s - m) <= 256 and O, l
+    // keep their scale.  The normalisation O / l is exact either way.
+    if (__any(mx > m + 8.f)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oT[dt][r] *= alpha;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sT[c][r] - mn);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sT[c][r], sl2, -m));
         sT[c][r] = p;
         ls += p;
       }
-    l = l * alpha + ls;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oT[dt][r] *= alpha;
+    l += ls;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
         for (int e = 0; e < 4; ++e) o4[e] = f2bf(oT[dt][4 * a + e] * inv);
         *reinterpret_cast<bf16x4*>(yo + 32 * dt + 8 * a + 4 * lg) = o4;
       }
-    if (lg == 0) lse[(int64_t)bh * T + qi] = (m + log2f(l)) * kLN2;
+    if (lg == 0) lse[(int64_t)bh * T + qi] = (m + __log2f(l)) * kLN2;
   }
 }
 
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
     if (q0 >= T || kb > q0 + 31) continue;
     const bf16* Ks = sm[jt & 1][0];
     const bf16* Vs = sm[jt & 1][1];
-    const bool edge = (kb + 63 > q0) || (kb + 63 >= T);
+    const bool edge = (kb + 63 > q0) || (kb + 63 >= T);  // uniform over the wave
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       f32x16 sT = zero16(), dpT = zero16();
@@ -356,15 +364,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
         sT = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT);
         dpT = MFMA(rowfrag(Vs, 32 * c + lr, kk, lg), dof[kk], dpT);
       }
+      if (edge) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2f(sT[r] * sl2 - lse2);
-        if (edge) {
+        for (int r = 0; r < 16; ++r) {
           const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (key > qi || key >= T) p = 0.f;
+          sT[r] = (key > qi || key >= T) ? -INFINITY : sT[r];
         }
-        sT[r] = p * (dpT[r] - D);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[r] = __builtin_amdgcn_exp2f(fmaf(sT[r], sl2, -lse2)) * (dpT[r] - D);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bf16x8 db = acc_frag(sT, s);
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
                                                                      float scale, float sl2) {
   constexpr int BK = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse, D]
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse * log2 e, D]
   const int kblk = blockIdx.x;  // smallest keys (most queries) first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
@@ -433,7 +441,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     dma_rows<64, 64, NW>(sm[st][1], dOg, C, q0t, T, 0, HD);
     if (w0) {
       const int q = q0t + lane;
-      lse_r = (q < T) ? lseg[q] : 0.f;
+      lse_r = (q < T) ? lseg[q] * kLOG2E : 0.f;
       d_r = (q < T) ? Dg[q] : 0.f;
     }
   };
@@ -479,11 +487,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          float p = exp2f(sc[r] * sl2 - Lv[e] * kLOG2E);
+          float x = sc[r];
           if (edge) {
             const int q = qs + ql + e;
-            if (kj > q || q >= T) p = 0.f;
+            x = (kj > q || q >= T) ? -INFINITY : x;
           }
+          const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, -Lv[e]));
           sc[r] = p;
           dp[r] = p * (dp[r] - Dv[e]);
         }

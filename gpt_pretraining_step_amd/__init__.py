@@ -175,6 +175,10 @@ class GPT2:
     def profile(self, on: bool = True):
         check(lib().gpt2_profile_enable(self._h, 1 if on else 0), "gpt2_profile_enable")
 
+    def profile_only(self, site=None):
+        """Time only launches from `site` (None: every site)."""
+        check(lib().gpt2_profile_only(self._h, site.encode() if site else None), "gpt2_profile_only")
+
     def profile_reset(self):
         check(lib().gpt2_profile_reset(self._h), "gpt2_profile_reset")
 

@@ -24,6 +24,7 @@ namespace g2 {
 
 struct Prof {
   bool on = false;
+  std::string only;  // when non-empty, only launches from this site are timed
   std::vector<std::string> names;
   std::vector<int64_t> counts;
   std::vector<double> ms;
@@ -76,6 +77,7 @@ struct Prof {
 
 void prof_begin(const Launch& L) {
   if (!L.prof || !L.prof->on) return;
+  if (!L.prof->only.empty() && L.prof->only != L.site) return;
   L.prof->cur = L.prof->get();
   if (L.prof->cur) (void)hipEventRecord(L.prof->cur, L.stream);
 }
@@ -845,6 +847,12 @@ int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, 
 int gpt2_profile_enable(gpt2_ctx* c, int on) {
   if (!c) return GPT2_ERR_ARG;
   c->prof.on = on != 0;
+  return GPT2_OK;
+}
+
+int gpt2_profile_only(gpt2_ctx* c, const char* site) {
+  if (!c) return GPT2_ERR_ARG;
+  c->prof.only = site ? site : "";
   return GPT2_OK;
 }
 

@@ -307,6 +307,9 @@ int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, 
  * launches and their summed duration.  Site names are stable strings such
  * as "gemm.fc_fwd" or "attn.fwd". */
 int gpt2_profile_enable(gpt2_ctx* ctx, int on);
+/* Restrict the timing to launches from one site (site == NULL: all sites),
+ * so that a measurement of one kernel adds no events around the others. */
+int gpt2_profile_only(gpt2_ctx* ctx, const char* site);
 int gpt2_profile_reset(gpt2_ctx* ctx);
 int gpt2_profile_count(gpt2_ctx* ctx);
 /* Entry i: site name (static storage), launches, summed milliseconds.  Call

@@ -219,7 +219,9 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
     tile_barrier();
     if (jt + 1 < ntiles) issue((jt + 1) & 1, jt + 1);
     const int kb = jt * 64;
-    if (q0 >= T || kb > q0 + 31) continue;
+    // a tile wholly after this wave's queries is computed anyway (every
+    // score masked, no contribution): a skip would make the compiler copy
+    // the accumulators around the branch on every tile
     const bf16* Ks = sm[jt & 1][0];
     const bf16* Vs = sm[jt & 1][1];
     f32x16 sT[2];
@@ -230,15 +232,17 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
       for (int kk = 0; kk < 4; ++kk) sT[c] = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT[c]);
     }
     // keys after the query (and past T) only occur in the diagonal and
-    // ragged tiles; the branch is uniform over the wave
+    // ragged tiles; the branch is uniform over the wave (the empty asm keeps
+    // the compiler from turning it into selects on every tile).  Element r
+    // of block c is key kb + 32 c + 4 lg + (8 (r / 4) + r % 4).
     if ((kb + 63 > q0) || (kb + 63 >= T)) {
+      asm volatile("");
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) {
+        const int lim = min(qi, T - 1) - kb - 32 * c - 4 * lg;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
-          sT[c][r] = (key > qi || key >= T) ? -INFINITY : sT[c][r];
-        }
+        for (int r = 0; r < 16; ++r) sT[c][r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : sT[c][r];
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -352,7 +356,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
     tile_barrier();
     if (jt + 1 < ntiles) issue((jt + 1) & 1, jt + 1);
     const int kb = jt * 64;
-    if (q0 >= T || kb > q0 + 31) continue;
+    // a tile wholly after this wave's queries is computed anyway (every
+    // score masked, no contribution): a skip would make the compiler copy
+    // the accumulators around the branch on every tile
     const bf16* Ks = sm[jt & 1][0];
     const bf16* Vs = sm[jt & 1][1];
     const bool edge = (kb + 63 > q0) || (kb + 63 >= T);  // uniform over the wave
@@ -365,11 +371,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
         dpT = MFMA(rowfrag(Vs, 32 * c + lr, kk, lg), dof[kk], dpT);
       }
       if (edge) {
+        asm volatile("");
+        const int lim = min(qi, T - 1) - kb - 32 * c - 4 * lg;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * c + 8 * (r >> 2) + 4 * lg + (r & 3);
-          sT[r] = (key > qi || key >= T) ? -INFINITY : sT[r];
-        }
+        for (int r = 0; r < 16; ++r) sT[r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : sT[r];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[r] = __builtin_amdgcn_exp2f(fmaf(sT[r], sl2, -lse2)) * (dpT[r] - D);
@@ -458,10 +463,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     const bool more = jt + 1 < ntiles;
     if (more) issue((jt + 1) & 1, jt + 1);
     const int qs = qstart + jt * 64;
-    if (k0 >= T || qs + 63 < k0) {
-      if (more) commit((jt + 1) & 1);
-      continue;
-    }
+    // a tile wholly before this wave's keys is computed anyway (every score
+    // masked, no contribution): a skip would make the compiler copy the
+    // accumulators around the branch on every tile
     const bf16* Qs = sm[jt & 1][0];
     const bf16* dOs = sm[jt & 1][1];
     const float* Ls = rowst[jt & 1][0];
@@ -469,13 +473,28 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     const bool edge = (qs < k0 + 31) || (qs + 63 >= T);
     // the two 32-query halves of the tile one after the other (fewer live
     // accumulators and operand fragments)
-#pragma unroll 1
+#pragma unroll
     for (int c = 0; c < 2; ++c) {
+      // no instruction moves between the halves (keeps one half's scores
+      // and gradients live at a time)
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         sc = MFMA(rowfrag(Qs, 32 * c + lr, kk, lg), kf[kk], sc);
         dp = MFMA(rowfrag(dOs, 32 * c + lr, kk, lg), vf[kk], dp);
+      }
+      if (edge) {
+        // element r is query qs + 32 c + 4 lg + (8 (r / 4) + r % 4): keep
+        // lo <= 8 (r / 4) + r % 4 <= hi (query >= key, query < T)
+        asm volatile("");
+        const int base = qs + 32 * c + 4 * lg;
+        const int lo = kj - base, hi = T - 1 - base;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = 8 * (r >> 2) + (r & 3);
+          sc[r] = (o < lo || o > hi) ? -INFINITY : sc[r];
+        }
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -487,12 +506,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          float x = sc[r];
-          if (edge) {
-            const int q = qs + ql + e;
-            x = (kj > q || q >= T) ? -INFINITY : x;
-          }
-          const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, -Lv[e]));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -Lv[e]));
           sc[r] = p;
           dp[r] = p * (dp[r] - Dv[e]);
         }

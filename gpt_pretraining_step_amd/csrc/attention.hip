@@ -186,14 +186,18 @@ __device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt vmcnt(0
 // Forward.  Block = NW waves x 32 queries; loop over 64-key tiles.  Each lane
 // owns one query (S^T = K Q^T, O^T = V^T P^T), so the online-softmax state is
 // per lane, shared with the partner lane 32 away.
-template <int NW>
+template <int NW, int ST>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
                                                                 float* __restrict__ lse, int T, int H, float sl2) {
   constexpr int BQ = 32 * NW;
-  __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][K, V]
+  constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
+  __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][64 * HD];  // [stage][K, V]
   const int nqb = (T + BQ - 1) / BQ;
-  const int qb = nqb - 1 - blockIdx.x;  // longest rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  // blocks are dispatched x-fastest: every head's longest (last) query
+  // block first, then the next longest, ... (longest work first balances the
+  // causal triangle over the compute units)
+  const int qb = nqb - 1 - blockIdx.y;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
   const bf16* Qg = qkv + (int64_t)b * T * C3 + h * HD;
   const bf16* Kg = Qg + C;
@@ -214,16 +218,28 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
     dma_rows<64, 64, NW>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
     dma_rows<64, 64, NW>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
   };
-  issue(0, 0);
+  // ST-stage ring: tiles jt+1 .. jt+ST-2 stay in flight while tile jt is
+  // used; tile jt+ST-1 goes into the buffer of tile jt-1 once every wave has
+  // passed this iteration's barrier.
+#pragma unroll
+  for (int t = 0; t < ST - 1; ++t)
+    if (t < ntiles) issue(t, t);
   for (int jt = 0; jt < ntiles; ++jt) {
-    tile_barrier();
-    if (jt + 1 < ntiles) issue((jt + 1) & 1, jt + 1);
+    if (jt + ST - 2 < ntiles) {
+      if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if constexpr (ST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_TILE) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_TILE) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (jt + ST - 1 < ntiles) issue((jt + ST - 1) % ST, jt + ST - 1);
     const int kb = jt * 64;
     // a tile wholly after this wave's queries is computed anyway (every
     // score masked, no contribution): a skip would make the compiler copy
     // the accumulators around the branch on every tile
-    const bf16* Ks = sm[jt & 1][0];
-    const bf16* Vs = sm[jt & 1][1];
+    const bf16* Ks = sm[jt % ST][0];
+    const bf16* Vs = sm[jt % ST][1];
     f32x16 sT[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -300,7 +316,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
 }
 
 // Backward, pass 1: D = rowsum(dO o O) and dQ.  Same tiling as the forward.
-template <int NW>
+template <int NW, int ST>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
@@ -308,10 +324,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
                                                                    bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
                                                                    int T, int H, float scale, float sl2) {
   constexpr int BQ = 32 * NW;
-  __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][K, V]
+  constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
+  __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][64 * HD];  // [stage][K, V]
   const int nqb = (T + BQ - 1) / BQ;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int qb = nqb - 1 - blockIdx.y;  // longest work first, over all heads
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
   const bf16* Qg = qkv + (int64_t)b * T * C3 + h * HD;
   const bf16* Kg = Qg + C;
@@ -351,16 +368,28 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
     dma_rows<64, 64, NW>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
     dma_rows<64, 64, NW>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
   };
-  issue(0, 0);
+  // ST-stage ring: tiles jt+1 .. jt+ST-2 stay in flight while tile jt is
+  // used; tile jt+ST-1 goes into the buffer of tile jt-1 once every wave has
+  // passed this iteration's barrier.
+#pragma unroll
+  for (int t = 0; t < ST - 1; ++t)
+    if (t < ntiles) issue(t, t);
   for (int jt = 0; jt < ntiles; ++jt) {
-    tile_barrier();
-    if (jt + 1 < ntiles) issue((jt + 1) & 1, jt + 1);
+    if (jt + ST - 2 < ntiles) {
+      if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if constexpr (ST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_TILE) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_TILE) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (jt + ST - 1 < ntiles) issue((jt + ST - 1) % ST, jt + ST - 1);
     const int kb = jt * 64;
     // a tile wholly after this wave's queries is computed anyway (every
     // score masked, no contribution): a skip would make the compiler copy
     // the accumulators around the branch on every tile
-    const bf16* Ks = sm[jt & 1][0];
-    const bf16* Vs = sm[jt & 1][1];
+    const bf16* Ks = sm[jt % ST][0];
+    const bf16* Vs = sm[jt % ST][1];
     const bool edge = (kb + 63 > q0) || (kb + 63 >= T);  // uniform over the wave
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -412,8 +441,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
   constexpr int BK = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
   __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse * log2 e, D]
-  const int kblk = blockIdx.x;  // smallest keys (most queries) first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int kblk = blockIdx.y;  // smallest keys (most queries) first, over all heads
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
   const bf16* Qg = qkv + (int64_t)b * T * C3 + h * HD;
   const bf16* Kg = Qg + C;
@@ -550,10 +579,10 @@ hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H,
   const float scale = 1.f / sqrtf((float)hd);
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
-    constexpr int NW = 4;
-    dim3 grid((T + 32 * NW - 1) / (32 * NW), B * H);
-    attn_fwd_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<bf16*>(y), lse, T, H,
-                                                     scale * kLOG2E);
+    constexpr int NW = 4, ST = 2;
+    dim3 grid(B * H, (T + 32 * NW - 1) / (32 * NW));
+    attn_fwd_bf16_kernel<NW, ST><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<bf16*>(y),
+                                                                 lse, T, H, scale * kLOG2E);
   } else {
     const int n = B * H * T;
     attn_fwd_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(static_cast<const float*>(qkv), static_cast<float*>(y),
@@ -572,8 +601,8 @@ hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H,
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
     constexpr int NW = 4;
-    dim3 grid((T + 32 * NW - 1) / (32 * NW), B * H);
-    attn_bwd_dq_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(y),
+    dim3 grid(B * H, (T + 32 * NW - 1) / (32 * NW));
+    attn_bwd_dq_bf16_kernel<NW, 2><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(y),
                                                         static_cast<const bf16*>(dy), lse, static_cast<bf16*>(dqkv),
                                                         Dbuf, T, H, scale, scale * kLOG2E);
     attn_bwd_dkdv_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(dy),

@@ -20,7 +20,7 @@ from dataclasses import dataclass
 
 from . import _ffi
 from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noqa: F401
-                   EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE)
+                   EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE, EPI_GELU_GRAD, EPI_MUL)
 
 __all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm",
            "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum",

@@ -29,6 +29,8 @@ EPI_RESIDUAL = 1
 EPI_GELU = 2
 EPI_DGELU = 3
 EPI_ACCUMULATE = 4
+EPI_GELU_GRAD = 5
+EPI_MUL = 6
 
 
 class Config(ct.Structure):

@@ -64,6 +64,13 @@ __device__ __forceinline__ float gelu_sig(float u, float u2) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
 }
 __device__ __forceinline__ float gelu_tanh(float u) { return u * gelu_sig(u, u * u); }
+// gelu(u) and gelu'(u) from one sigmoid evaluation
+__device__ __forceinline__ void gelu_tanh_and_grad(float u, float& g, float& dg) {
+  const float u2 = u * u;
+  const float s = gelu_sig(u, u2);
+  g = u * s;
+  dg = fmaf(u * fmaf(-s, s, s), fmaf(gelu_k::D2, u2, gelu_k::D0), s);
+}
 __device__ __forceinline__ float gelu_tanh_grad(float u) {
   const float u2 = u * u;
   const float s = gelu_sig(u, u2);

@@ -134,6 +134,12 @@ static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
     case GPT2_EPI_DGELU:
       e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_DGELU, true, false, true>(L, p);
       break;
+    case GPT2_EPI_GELU_GRAD:
+      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_GELU_GRAD, true, false>(L, p);
+      break;
+    case GPT2_EPI_MUL:
+      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_MUL, true, false, true>(L, p);
+      break;
     default:
       e = at ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, true>(L, p)
              : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, false>(L, p);
@@ -197,6 +203,8 @@ static hipError_t dispatch_f32(const Launch& L, GemmP p, int epi) {
     case GPT2_EPI_RESIDUAL: gemm_f32_kernel<A_K, B_K, GPT2_EPI_RESIDUAL, false><<<grid, block, 0, L.stream>>>(p); break;
     case GPT2_EPI_GELU: gemm_f32_kernel<A_K, B_K, GPT2_EPI_GELU, false><<<grid, block, 0, L.stream>>>(p); break;
     case GPT2_EPI_DGELU: gemm_f32_kernel<A_K, B_K, GPT2_EPI_DGELU, false><<<grid, block, 0, L.stream>>>(p); break;
+    case GPT2_EPI_GELU_GRAD: gemm_f32_kernel<A_K, B_K, GPT2_EPI_GELU_GRAD, false><<<grid, block, 0, L.stream>>>(p); break;
+    case GPT2_EPI_MUL: gemm_f32_kernel<A_K, B_K, GPT2_EPI_MUL, false><<<grid, block, 0, L.stream>>>(p); break;
     default:
       if (atomic) gemm_f32_kernel<A_K, B_K, GPT2_EPI_ACCUMULATE, true><<<grid, block, 0, L.stream>>>(p);
       else gemm_f32_kernel<A_K, B_K, GPT2_EPI_ACCUMULATE, false><<<grid, block, 0, L.stream>>>(p);

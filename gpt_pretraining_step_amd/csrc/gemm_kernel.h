@@ -62,6 +62,20 @@ __device__ __forceinline__ void epi_store(const GemmP& p, int m, int n, float ac
       float u = static_cast<const float*>(p.U)[idx];
       static_cast<float*>(p.C)[idx] = v * gelu_tanh_grad(u);
     }
+  } else if constexpr (EPI == GPT2_EPI_GELU_GRAD) {
+    float g, dg;
+    if constexpr (OUT_BF16) {
+      gelu_tanh_and_grad(bf2f(f2bf(v)), g, dg);
+      static_cast<bf16*>(p.C)[idx] = f2bf(g);
+      static_cast<bf16*>(p.C2)[idx] = f2bf(dg);
+    } else {
+      gelu_tanh_and_grad(v, g, dg);
+      static_cast<float*>(p.C)[idx] = g;
+      static_cast<float*>(p.C2)[idx] = dg;
+    }
+  } else if constexpr (EPI == GPT2_EPI_MUL) {
+    if constexpr (OUT_BF16) static_cast<bf16*>(p.C)[idx] = f2bf(v * bf2f(static_cast<const bf16*>(p.U)[idx]));
+    else static_cast<float*>(p.C)[idx] = v * static_cast<const float*>(p.U)[idx];
   } else {  // ACCUMULATE
     float* c = static_cast<float*>(p.C) + idx;
     if constexpr (ATOMIC) unsafeAtomicAdd(c, v);
@@ -120,6 +134,35 @@ __device__ __forceinline__ void epi_tile(const GemmP& p, int mrow, int ncol, con
             static_cast<float*>(p.C2)[i0] = gelu_tanh(v0);
             static_cast<float*>(p.C2)[i1] = gelu_tanh(v1);
           }
+        } else if constexpr (EPI == GPT2_EPI_GELU_GRAD) {
+          float g0, g1, d0, d1;
+          if constexpr (OUT_BF16) {
+            const bf16x2 u = f2bf2(v0, v1);
+            gelu_tanh_and_grad(bf2f(u[0]), g0, d0);
+            gelu_tanh_and_grad(bf2f(u[1]), g1, d1);
+            const bf16x2 g = f2bf2(g0, g1), d = f2bf2(d0, d1);
+            static_cast<bf16*>(p.C)[i0] = g[0];
+            static_cast<bf16*>(p.C)[i1] = g[1];
+            static_cast<bf16*>(p.C2)[i0] = d[0];
+            static_cast<bf16*>(p.C2)[i1] = d[1];
+          } else {
+            gelu_tanh_and_grad(v0, g0, d0);
+            gelu_tanh_and_grad(v1, g1, d1);
+            static_cast<float*>(p.C)[i0] = g0;
+            static_cast<float*>(p.C)[i1] = g1;
+            static_cast<float*>(p.C2)[i0] = d0;
+            static_cast<float*>(p.C2)[i1] = d1;
+          }
+        } else if constexpr (EPI == GPT2_EPI_MUL) {
+          if constexpr (OUT_BF16) {
+            const bf16* U = static_cast<const bf16*>(p.U);
+            const bf16x2 o = f2bf2(v0 * bf2f(U[i0]), v1 * bf2f(U[i1]));
+            static_cast<bf16*>(p.C)[i0] = o[0];
+            static_cast<bf16*>(p.C)[i1] = o[1];
+          } else {
+            static_cast<float*>(p.C)[i0] = v0 * static_cast<const float*>(p.U)[i0];
+            static_cast<float*>(p.C)[i1] = v1 * static_cast<const float*>(p.U)[i1];
+          }
         } else if constexpr (EPI == GPT2_EPI_RESIDUAL) {
           static_cast<float*>(p.C)[i0] = p.R[i0] + v0;
           static_cast<float*>(p.C)[i1] = p.R[i1] + v1;
@@ -149,11 +192,18 @@ __device__ __forceinline__ void epi_tile(const GemmP& p, int mrow, int ncol, con
 }
 
 // Stores 4 consecutive outputs C[idx .. idx+3] whose values v already carry
-// alpha and the bias (idx % 4 == 0); the epilogues of the swapped layout.
+// alpha and the bias (idx % 4 == 0); the epilogues of the swapped layout
+// (bf16 output for dGELU and the product).
 template <int EPI>
 __device__ __forceinline__ void epi_put4(const GemmP& p, int64_t idx, const float* v) {
-  static_assert(EPI == GPT2_EPI_RESIDUAL || EPI == GPT2_EPI_DGELU, "swapped layout: residual or dGELU");
-  if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+  static_assert(EPI == GPT2_EPI_RESIDUAL || EPI == GPT2_EPI_DGELU || EPI == GPT2_EPI_MUL,
+                "swapped layout: residual, dGELU or product");
+  if constexpr (EPI == GPT2_EPI_MUL) {
+    const bf16x4 u = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(p.U) + idx);
+    const bf16x2 o0 = f2bf2(v[0] * bf2f(u[0]), v[1] * bf2f(u[1]));
+    const bf16x2 o1 = f2bf2(v[2] * bf2f(u[2]), v[3] * bf2f(u[3]));
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + idx) = bf16x4{o0[0], o0[1], o1[0], o1[1]};
+  } else if constexpr (EPI == GPT2_EPI_RESIDUAL) {
     const float4 r = *reinterpret_cast<const float4*>(p.R + idx);
     *reinterpret_cast<float4*>(static_cast<float*>(p.C) + idx) =
         make_float4(r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]);

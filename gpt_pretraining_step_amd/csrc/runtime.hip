@@ -349,7 +349,7 @@ static hipError_t linear_fwd(gpt2_ctx* c, const char* site, const void* x, int M
   a.A = x; a.B = c->W(wi); a.C = out; a.C2 = out2; a.R = resid;
   a.bias = bi >= 0 ? c->P(bi) : nullptr;
   a.epilogue = epi;
-  a.out_bf16 = c->bf() && (epi == GPT2_EPI_STORE || epi == GPT2_EPI_GELU || epi == GPT2_EPI_DGELU);
+  a.out_bf16 = c->bf() && (epi == GPT2_EPI_STORE || epi == GPT2_EPI_GELU || epi == GPT2_EPI_GELU_GRAD);
   return launch_gemm(c->at(site), a);
 }
 
@@ -414,8 +414,9 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                        GPT2_EPI_RESIDUAL, rmid, nullptr, rin));
     HIP_TRY(launch_layernorm_fwd(c->at("ln.fwd"), rmid, c->P(c->L(l, LN2_W)), c->P(c->L(l, LN2_B)), c->act(y.A2[l]),
                                  bf, c->act<float>(y.mean2[l]), c->act<float>(y.rstd2[l]), M, C));
-    HIP_TRY(linear_fwd(c, "gemm.fc", c->act(y.A2[l]), M, C, c->L(l, FC_W), F, c->L(l, FC_B), GPT2_EPI_GELU,
-                       c->act(y.U[l]), c->act(y.G[l]), nullptr));
+    // G = gelu(u) for the next product, U = gelu'(u) for the backward
+    HIP_TRY(linear_fwd(c, "gemm.fc", c->act(y.A2[l]), M, C, c->L(l, FC_W), F, c->L(l, FC_B), GPT2_EPI_GELU_GRAD,
+                       c->act(y.G[l]), c->act(y.U[l]), nullptr));
     HIP_TRY(linear_fwd(c, "gemm.mlp_proj", c->act(y.G[l]), M, F, c->L(l, MLP_W), C, c->L(l, MLP_B),
                        GPT2_EPI_RESIDUAL, c->act<float>(y.Rin[l + 1]), nullptr, rmid));
   }
@@ -505,7 +506,8 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   for (int l = g.n_layer - 1; l >= 0; --l) {
     // MLP branch: R_{l+1} = Rmid + G Wmp^T + b
     HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRop, M, C, c->act(y.G[l]), F, c->L(l, MLP_W), c->L(l, MLP_B), dR));
-    HIP_TRY(linear_dx(c, "gemm.mlp_proj_dx", dRop, M, C, c->L(l, MLP_W), F, GPT2_EPI_DGELU, true, dU,
+    // dU = (dR W_mp) * gelu'(u), gelu'(u) kept by the forward
+    HIP_TRY(linear_dx(c, "gemm.mlp_proj_dx", dRop, M, C, c->L(l, MLP_W), F, GPT2_EPI_MUL, true, dU,
                       c->act(y.U[l])));
     HIP_TRY(linear_dw(c, "gemm.fc_dw", dU, M, F, c->act(y.A2[l]), C, c->L(l, FC_W), c->L(l, FC_B),
                       static_cast<const float*>(dU)));
@@ -767,7 +769,9 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
   if (!a || !a->A || !a->B || !a->C) return false;
   if (a->M < 1 || a->N < 1 || a->K < 1) return false;
   if (a->dtype != GPT2_PRECISION_BF16 && a->dtype != GPT2_PRECISION_FP32) return false;
-  if (a->epilogue < GPT2_EPI_STORE || a->epilogue > GPT2_EPI_ACCUMULATE) return false;
+  if (a->epilogue < GPT2_EPI_STORE || a->epilogue > GPT2_EPI_MUL) return false;
+  if (a->epilogue == GPT2_EPI_GELU_GRAD && !a->C2) return false;
+  if (a->epilogue == GPT2_EPI_MUL && !a->U) return false;
   if (a->epilogue == GPT2_EPI_RESIDUAL && !a->R) return false;
   if (a->epilogue == GPT2_EPI_GELU && !a->C2) return false;
   if (a->epilogue == GPT2_EPI_DGELU && !a->U) return false;
@@ -780,7 +784,14 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
     if (a->N % 8 && !a->b_kmajor) return false;
     if ((a->a_kmajor && a->K % 8) || (a->b_kmajor && a->K % 8)) return false;
     if (a->lda % 8 || a->ldb % 8 || a->ldc % 8) return false;
-    if (((uintptr_t)a->A | (uintptr_t)a->B) & 15) return false;
+    if (((uintptr_t)a->A | (uintptr_t)a->B | (uintptr_t)a->C | (uintptr_t)a->C2 | (uintptr_t)a->R |
+         (uintptr_t)a->U | (uintptr_t)a->bias) & 15)
+      return false;
+    // the output dtype each epilogue writes in bf16 mode
+    const bool bf_out = a->epilogue == GPT2_EPI_GELU || a->epilogue == GPT2_EPI_DGELU ||
+                        a->epilogue == GPT2_EPI_GELU_GRAD || a->epilogue == GPT2_EPI_MUL;
+    const bool f32_out = a->epilogue == GPT2_EPI_RESIDUAL || a->epilogue == GPT2_EPI_ACCUMULATE;
+    if ((bf_out && !a->out_bf16) || (f32_out && a->out_bf16)) return false;
   }
   return true;
 }

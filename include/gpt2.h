@@ -244,14 +244,24 @@ int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, con
  *   GPT2_EPI_GELU:       C[m][n] = v, C2[m][n] = gelu_tanh(C[m][n])  (both out dtype)
  *   GPT2_EPI_DGELU:      C[m][n] = v * gelu_tanh'(U[m][n])   (U in out dtype)
  *   GPT2_EPI_ACCUMULATE: C[m][n] += v                       (float32)
+ *   GPT2_EPI_GELU_GRAD:  u = v rounded to the out dtype; C[m][n] = gelu_tanh(u),
+ *                        C2[m][n] = gelu_tanh'(u)            (both out dtype)
+ *   GPT2_EPI_MUL:        C[m][n] = v * U[m][n]               (U in out dtype)
+ * ("How I trained my own GPT-2 124M on FineWeb-Edu" 2.13 for the tanh GELU;
+ * its derivative by the chain rule.)  GELU_GRAD feeds the MLP's second
+ * product with gelu(u) and keeps gelu'(u) so that the backward's input
+ * gradient is a MUL epilogue.
  * ldc is the row pitch of C, C2, R and U.  For bf16, M, N, K, lda, ldb, ldc
- * must be multiples of 8 and pointers 16-byte aligned. */
+ * must be multiples of 8, every pointer 16-byte aligned, and out_bf16 must
+ * be 1 for GELU, DGELU, GELU_GRAD and MUL and 0 for RESIDUAL and ACCUMULATE. */
 enum {
   GPT2_EPI_STORE = 0,
   GPT2_EPI_RESIDUAL = 1,
   GPT2_EPI_GELU = 2,
   GPT2_EPI_DGELU = 3,
-  GPT2_EPI_ACCUMULATE = 4
+  GPT2_EPI_ACCUMULATE = 4,
+  GPT2_EPI_GELU_GRAD = 5,
+  GPT2_EPI_MUL = 6
 };
 typedef struct {
   int32_t M, N, K;

@@ -125,6 +125,17 @@ def test_gemm_bf16_epilogues(g, M, N, K):
     g.op_gemm(dA, dB, D, M, N, K, alpha=0.75, epilogue=g.EPI_DGELU, U=U)
     ref = 0.75 * acc * OM.gelu_tanh_grad(u.astype(np.float64))
     np.testing.assert_allclose(host(D), ref, rtol=2e-2, atol=2e-2)
+    # GELU_GRAD: u = bf16(v); C = bf16(gelu(u)), C2 = bf16(gelu'(u))
+    Gg = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    Gd = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    g.op_gemm(dA, dB, Gg, M, N, K, bias=dev(bias), alpha=0.75, epilogue=g.EPI_GELU_GRAD, C2=Gd)
+    np.testing.assert_allclose(host(Gg), OM.gelu_tanh(u.astype(np.float64)), rtol=1e-2, atol=1e-2)
+    gd = host(Gd)
+    np.testing.assert_allclose(gd, OM.gelu_tanh_grad(u.astype(np.float64)), rtol=1e-2, atol=1e-2)
+    # MUL: out = bf16(v * U), here with U = gelu'(u): the backward's dGELU
+    P = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    g.op_gemm(dA, dB, P, M, N, K, alpha=0.75, epilogue=g.EPI_MUL, U=Gd)
+    np.testing.assert_allclose(host(P), 0.75 * acc * gd.astype(np.float64), rtol=2e-2, atol=2e-2)
 
 
 @pytest.mark.parametrize("ak,bk", LAYOUTS)
@@ -156,6 +167,10 @@ def test_gemm_rejects_bad_arguments(g):
         g.op_gemm(A, A, C, 16, 16, 16, lda=8)   # pitch smaller than K
     with pytest.raises(g.GPT2Error):
         g.op_gemm(A, A, C, 16, 16, 16, epilogue=g.EPI_RESIDUAL)  # residual without R
+    with pytest.raises(g.GPT2Error):
+        g.op_gemm(A, A, C, 16, 16, 16, epilogue=g.EPI_MUL)  # product without U
+    with pytest.raises(g.GPT2Error):
+        g.op_gemm(A, A, C, 16, 16, 16, epilogue=g.EPI_MUL, U=A)  # bf16 product into a float32 C
 
 
 def test_colsum(g):

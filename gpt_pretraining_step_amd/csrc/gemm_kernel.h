@@ -17,6 +17,8 @@
 
 #include "tile_io.h"
 
+#include <type_traits>
+
 namespace g2 {
 
 struct GemmP {
@@ -385,14 +387,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
 
   // Every operand tile is copied into LDS by DMA: K-major ones as [rows][BK]
   // (row-swizzled), K-slow ones in their memory layout as [BK][rows].
+  // full K steps: per-lane offsets fixed for the tile (tile_io.h); a ragged
+  // last step: the bounds-checked, zero-filling copy
+  std::conditional_t<A_K, RowsDma<BM, BK, NW>, KrDma<BM, BK, NW>> dma_a;
+  std::conditional_t<B_K, RowsDma<BN, BK, NW>, KrDma<BN, BK, NW>> dma_b;
+  dma_a.init(p.lda, m0, p.M);
+  dma_b.init(p.ldb, n0, p.N);
   auto issue = [&](int stage, int kstep) {
     bf16* as = smem + stage * STAGE;
     bf16* bs = as + BM * BK;
     const int k0 = kbeg + kstep * BK;
-    if constexpr (A_K) dma_rows<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
-    else dma_kr<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
-    if constexpr (B_K) dma_rows<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
-    else dma_kr<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+    if (k0 + BK <= kend) {
+      dma_a.issue(as, Ag, p.lda, m0, k0);
+      dma_b.issue(bs, Bg, p.ldb, n0, k0);
+    } else {
+      if constexpr (A_K) dma_rows<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
+      else dma_kr<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
+      if constexpr (B_K) dma_rows<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+      else dma_kr<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+    }
   };
   constexpr int DMA_PER_STEP = (BM + BN) * BK / 512 / NW;  // DMA instructions per wave per K step
 

@@ -103,6 +103,69 @@ __device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, 
   }
 }
 
+// ---- DMA with per-lane offsets computed once per tile.  For a K step that
+// lies wholly inside the matrix, a lane's source address is a uniform base
+// (matrix, tile origin and K step: scalar registers) plus a 32-bit byte
+// offset fixed for the whole tile, so each wave instruction costs one M0
+// write and the load itself.  Rows (K-major) or columns (K-slow) past the
+// matrix edge are clamped to the last valid one: they only feed output rows
+// or columns that are never stored.  The caller uses dma_rows / dma_kr (zero
+// fill) for a ragged last K step.
+template <int ROWS, int BK, int NWAVES>
+struct RowsDma {
+  static constexpr int CPR = BK / 8, RPI = 64 / CPR, INSTR = ROWS / RPI, IPW = INSTR / NWAVES;
+  static_assert(INSTR % NWAVES == 0, "tile rows must split evenly over the waves");
+  uint32_t off[IPW];
+  int ins0;
+  // tile rows row0 .. row0+ROWS of a [nrows][ld] matrix (row0 < nrows)
+  __device__ __forceinline__ void init(int64_t ld, int row0, int nrows) {
+    const int lane = threadIdx.x & 63;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    const int last = nrows - 1 - row0;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (ins0 + i) * RPI + lane / CPR;
+      const int c = swz_chunk<BK>(r, lane % CPR);
+      off[i] = (uint32_t)(((int64_t)min(r, last) * ld + 8 * c) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* lds, const bf16* src, int64_t ld, int row0, int k0) const {
+    const char* base = reinterpret_cast<const char*>(src + (int64_t)row0 * ld + k0);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]), lds + (ins0 + i) * RPI * BK, 16,
+                                       0, 0);
+  }
+};
+
+template <int R, int BK, int NWAVES>
+struct KrDma {
+  static constexpr int CPR = R / 8, TOTAL = BK * CPR, IPW = TOTAL / 64 / NWAVES;
+  static_assert(TOTAL % (64 * NWAVES) == 0, "tile must split evenly over the waves");
+  uint32_t off[IPW];
+  int ins0;
+  // tile columns col0 .. col0+R of a [K][ld] matrix (col0 < ncols, ncols % 8 == 0)
+  __device__ __forceinline__ void init(int64_t ld, int col0, int ncols) {
+    const int lane = threadIdx.x & 63;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    const int last = ncols - 8 - col0;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int g = (ins0 + i) * 64 + lane;
+      const int k = g / CPR;
+      const int c = kr_chunk<R>(k, g % CPR);
+      off[i] = (uint32_t)(((int64_t)k * ld + min(8 * c, last)) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* lds, const bf16* src, int64_t ld, int col0, int k0) const {
+    const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * ld + col0);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]), lds + (ins0 + i) * 512, 16, 0,
+                                       0);
+  }
+};
+
 // Column read of a [rows][R] kr-swizzled tile: this lane gets column
 // c0 + (lane % 16) of rows r0 .. r0+3 (r0 % 4 == 0, c0 % 16 == 0).
 template <int R>

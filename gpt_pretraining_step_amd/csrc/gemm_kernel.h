@@ -252,14 +252,16 @@ __device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol
 // layout only.  For every row m and column tile tn it stores the tile's
 // softmax statistics stats[m][tn] = (mx, sum over the tile's columns n < N of
 // exp(z[m][n] - mx)) with mx the tile's largest logit, all from the float32
-// accumulators, and writes C[m][n] = bf16(z[m][n] - mx).  Entries near the
-// row's maximum, the ones that carry the softmax, keep nearly full precision.
+// accumulators, and writes C[m][n] = bf16(z[m][n] - mx) (staged through LDS
+// so each row goes out in 512-byte pieces).  Entries near the row's
+// maximum, the ones that carry the softmax, keep nearly full precision.
 constexpr int EPI_CE_STATS = 16;
 
-template <int BM, int WGN, int TM, int TN>
+template <int BM, int BN, int WGN, int TM, int TN, bool EDGE>
 __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int tn, int wm0, int wn0, int wave,
-                                             int lr, int lg, const f32x16 (&acc)[TM][TN], float* red) {
+                                             int lr, int lg, const f32x16 (&acc)[TM][TN], float* red, char* stage) {
   constexpr float L2E = 1.4426950408889634f;
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   const int wn = wave % WGN;
   // per row: this wave's 64 columns (32 in each lane half) -> (max, sum of exp)
 #pragma unroll
@@ -270,7 +272,7 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int col = n0 + wn0 + 32 * j + 8 * (e >> 2) + 4 * lg + (e & 3);
-        if (col < p.N) mx = fmaxf(mx, acc[i][j][e]);
+        if (!EDGE || col < p.N) mx = fmaxf(mx, acc[i][j][e]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float sm = 0.f;
@@ -279,7 +281,7 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int col = n0 + wn0 + 32 * j + 8 * (e >> 2) + 4 * lg + (e & 3);
-        if (col < p.N) sm += __builtin_amdgcn_exp2f((acc[i][j][e] - mx) * L2E);
+        if (!EDGE || col < p.N) sm += __builtin_amdgcn_exp2f((acc[i][j][e] - mx) * L2E);
       }
     sm += __shfl_xor(sm, 32);
     const int row = wm0 + 32 * i + lr;
@@ -289,6 +291,8 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // the tile's row maxima and sums; the offsets z - max go to LDS as bf16,
+  // row-major with 16-byte chunk c of row r at c ^ (r % 32)
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int row = wm0 + 32 * i + lr;
@@ -302,23 +306,35 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
       const float mw = red[2 * (w * BM + row)];
       if (mw != -INFINITY) sm += red[2 * (w * BM + row) + 1] * __builtin_amdgcn_exp2f((mw - mx) * L2E);
     }
-    if (m >= p.M) continue;
-    if (wn == 0 && lg == 0) p.stats[(int64_t)m * p.tiles_n + tn] = make_float2(mx, sm);
-    bf16* crow = static_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+    if (wn == 0 && lg == 0 && m < p.M) p.stats[(int64_t)m * p.tiles_n + tn] = make_float2(mx, sm);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn0 + 32 * j + 8 * q + 4 * lg;
+        const int col = wn0 + 32 * j + 8 * q + 4 * lg;  // within the tile
         const bf16x2 lo = f2bf2(acc[i][j][4 * q] - mx, acc[i][j][4 * q + 1] - mx);
         const bf16x2 hi = f2bf2(acc[i][j][4 * q + 2] - mx, acc[i][j][4 * q + 3] - mx);
-        if (col + 4 <= p.N) {
-          *reinterpret_cast<bf16x4*>(crow + col) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          const bf16 v4[4] = {lo[0], lo[1], hi[0], hi[1]};
-          for (int e = 0; e < 4 && col + e < p.N; ++e) crow[col + e] = v4[e];
-        }
+        const int addr = row * (BN * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8;
+        *reinterpret_cast<bf16x4*>(stage + addr) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
       }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // copy out: each lane 16 bytes, 32 lanes a 512-byte row
+  bf16* C = static_cast<bf16*>(p.C);
+  constexpr int NT = 64 * (BM / (TM * 32)) * WGN;
+#pragma unroll 4
+  for (int idx = threadIdx.x; idx < BM * CPR; idx += NT) {
+    const int row = idx / CPR, c = idx % CPR;
+    const int m = m0 + row, n = n0 + 8 * c;
+    if (m >= p.M || (EDGE && n >= p.N)) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4));
+    bf16* d = C + (int64_t)m * p.ldc + n;
+    if (!EDGE || n + 8 <= p.N) {
+      *reinterpret_cast<uint4*>(d) = v;
+    } else {
+      const bf16* vv = reinterpret_cast<const bf16*>(&v);
+      for (int e = 0; n + e < p.N; ++e) d[e] = vv[e];
+    }
   }
 }
 
@@ -501,8 +517,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
     static_assert(SWAP && WN == 64, "statistics epilogue: swapped layout, 64 columns per wave");
     // every wave is done with the operand stages: reuse them for the
     // cross-wave reduction
+    static_assert(BM * BN * 2 <= STAGES * STAGE * 2, "the output tile fits in the operand stages");
+    __shared__ float red[2 * WGN * BM];
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    epi_ce_stats<BM, WGN, TM, TN>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, reinterpret_cast<float*>(smem));
+    if (n0 + BN <= p.N)
+      epi_ce_stats<BM, BN, WGN, TM, TN, false>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
+                                               reinterpret_cast<char*>(smem));
+    else
+      epi_ce_stats<BM, BN, WGN, TM, TN, true>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
+                                              reinterpret_cast<char*>(smem));
   } else {
     const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
     if constexpr (SWAP) {

@@ -248,6 +248,34 @@ __device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol
   }
 }
 
+// MUL epilogue of an interior tile, swapped layout, with the factors of the
+// first TMP accumulator rows already in registers (upre[i][j][q] = U at row
+// mrow + 32 i, columns ncol + 32 j + 8 q .. +3); the others are loaded here.
+template <int TM, int TN, int TMP>
+__device__ __forceinline__ void epi_tile_mul_pre(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN],
+                                                 const bf16x4 (&upre)[TMP][TN][4]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t rb = (int64_t)(mrow + 32 * i) * p.ldc + ncol;
+    bf16* crow = static_cast<bf16*>(p.C) + rb;
+    const bf16* urow = static_cast<const bf16*>(p.U) + rb;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int co = 32 * j + 8 * q;
+        float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.bias) b = *reinterpret_cast<const float4*>(p.bias + ncol + co);
+        const bf16x4 u = i < TMP ? upre[i < TMP ? i : 0][j][q] : *reinterpret_cast<const bf16x4*>(urow + co);
+        const f32x16& a = acc[i][j];
+        const bf16x2 o0 = f2bf2(fmaf(p.alpha, a[4 * q], b.x) * bf2f(u[0]), fmaf(p.alpha, a[4 * q + 1], b.y) * bf2f(u[1]));
+        const bf16x2 o1 =
+            f2bf2(fmaf(p.alpha, a[4 * q + 2], b.z) * bf2f(u[2]), fmaf(p.alpha, a[4 * q + 3], b.w) * bf2f(u[3]));
+        *reinterpret_cast<bf16x4*>(crow + co) = bf16x4{o0[0], o0[1], o1[0], o1[1]};
+      }
+  }
+}
+
 // Internal epilogue of the lm_head product (logits = hidden wte^T), swapped
 // layout only.  For every row m and column tile tn it stores the tile's
 // softmax statistics stats[m][tn] = (mx, sum over the tile's columns n < N of
@@ -424,6 +452,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
     }
   };
   constexpr int DMA_PER_STEP = (BM + BN) * BK / 512 / NW;  // DMA instructions per wave per K step
+  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
+  // MUL epilogue (swapped layout) of an interior tile: the factors this lane
+  // multiplies by are loaded during the first K step (64 registers), so
+  // their latency hides behind the main loop
+  constexpr bool PRE_U = SWAP && EPI == GPT2_EPI_MUL;
+  constexpr int TMP = (TM + 1) / 2;  // accumulator rows whose factors are prefetched (register budget)
+  bf16x4 upre[PRE_U ? TMP : 1][PRE_U ? TN : 1][PRE_U ? 4 : 1];
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -443,6 +478,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (PRE_U) {
+      // issued before the next step's DMA, so the next wait covers them
+      if (kt == 0 && interior) {
+        const bf16* U = static_cast<const bf16*>(p.U) + (int64_t)(m0 + wm0 + lr) * p.ldc + n0 + wn0 + 4 * lg;
+#pragma unroll
+        for (int i = 0; i < TMP; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              upre[i][j][q] = *reinterpret_cast<const bf16x4*>(U + (int64_t)(32 * i) * p.ldc + 32 * j + 8 * q);
+      }
+    }
     const int nxt = kt + STAGES - 1;
     if (nxt < nk) issue(nxt % STAGES, nxt);
     const bf16* as = smem + (kt % STAGES) * STAGE;
@@ -527,8 +575,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
       epi_ce_stats<BM, BN, WGN, TM, TN, true>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
                                               reinterpret_cast<char*>(smem));
   } else {
-    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
-    if constexpr (SWAP) {
+    if constexpr (PRE_U) {
+      if (interior) epi_tile_mul_pre<TM, TN, TMP>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc, upre);
+      else epi_tile_swap<EPI, OUT_BF16, TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    } else if constexpr (SWAP) {
       if (interior) epi_tile_swap<EPI, OUT_BF16, TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
       else epi_tile_swap<EPI, OUT_BF16, TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
     } else if (interior) {

@@ -1,6 +1,7 @@
 """Throughput of the GPT-2 124M training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--no-cpu-baseline]
+    python bench.py --traffic-probe SITE     (under rocprofv3 --pmc, see below)
 
 One step is the pages' full optimizer step: zero_grad, 32 micro-steps of
 B=16 x T=1024 tokens with loss / 32, global-norm clipping at 1.0 and AdamW
@@ -14,7 +15,11 @@ before timing starts; weights are the library's own N(0, 0.02) init.
 Prints one JSON line with tokens/s, MFU, the roofline of the dominant kernel
 (its launches timed with HIP events on the library's stream during the timed
 steps; the per-site breakdown comes from the first warm-up step), and the CPU
-oracle timed on a bounded sample on this host.
+oracle timed on a bounded sample on this host.  The roofline's `traffic`
+(HBM bytes per launch of the dominant kernel) is read from a record under
+profiles/ written by `python -m gpt_pretraining_step_amd.profiling traffic`
+from two counter runs of `--traffic-probe`, and is null when no record
+matches the kernel's current sources.
 """
 
 from __future__ import annotations
@@ -64,23 +69,57 @@ def gemm_site_flops():
     }
 
 
-def cpu_baseline(seconds_hint: float = 20.0):
+def cpu_baseline(rows: int = 8):
     """The CPU oracle (NumPy float32) on a bounded sample: one micro-step of the
-    same model on a single 1024-token sequence of the same token stream."""
-    import numpy as np
+    same model on `rows` 1024-token sequences of the same token stream (about
+    2 s of host time per sequence on 16 cores)."""
     import synthetic
     from oracle import model as OM
     cores = len(os.sched_getaffinity(0))
     cfg = OM.Config(50304, 1024, 12, 12, 768, 3072)
     params = synthetic.random_params(OM.param_specs(cfg), seed=42)
-    stream = synthetic.token_stream(1025, seed=1337)
-    x, y = synthetic.micro_batch(stream, 0, 1, 1024)
+    stream = synthetic.token_stream(rows * 1024 + 1, seed=1337)
+    x, y = synthetic.micro_batch(stream, 0, rows, 1024)
     t0 = time.perf_counter()
     OM.fwd_bwd(cfg, params, x, y, scale=1.0 / G)
     dt = time.perf_counter() - t0
-    return {"value": round(1024 / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "one micro-step (forward + backward, float32 NumPy) of GPT-2 124M on 1 x 1024 tokens of the "
-                      "synthetic stream; %.1f s" % dt}
+    return {"value": round(rows * 1024 / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one micro-step (forward + backward, float32 NumPy) of GPT-2 124M on {rows} x 1024 tokens of "
+                      f"the synthetic stream; {dt:.1f} s"}
+
+
+COPY_BYTES = 256 << 20
+
+
+def traffic_probe(site: str) -> int:
+    """One micro-step with the library's marker kernel launched before every
+    launch of `site`, then the marker and a plain device copy of COPY_BYTES
+    (read and written once) that calibrates the HBM byte counters.  Run under
+    `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc WRITE_SIZE`."""
+    import torch
+    import gpt_pretraining_step_amd as g
+    import synthetic
+    model = g.GPT2(g.GPT2_124M)
+    model.init_params(seed=42)
+    stream = synthetic.token_stream(B * T + 1, seed=1337)
+    x, y = synthetic.micro_batch(stream, 0, B, T)
+    x, y = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    model.zero_grad()
+    torch.cuda.synchronize()
+    model.profile(True)
+    model.profile_only(site)
+    model.profile_mark(True)
+    model.fwd_bwd(x, y, loss_scale=1.0 / G)
+    g.op_marker()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    st = model.status()
+    n = model.profile_entries().get(site, (0, 0.0))[0]
+    model.close()
+    print(f"[bench] traffic probe: site {site}, {n} marked launches, status {st}", file=sys.stderr, flush=True)
+    return 0 if st == 0 and n > 0 else 1
 
 
 def main(argv=None):
@@ -91,11 +130,14 @@ def main(argv=None):
     ap.add_argument("--grad-accum", type=int, default=G)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no HIP events at all (no roofline, no breakdown)")
+    ap.add_argument("--traffic-probe", metavar="SITE", help="one marked micro-step for an HBM counter run")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)",
               file=sys.stderr)
         return 2
+    if args.traffic_probe:
+        return traffic_probe(args.traffic_probe)
 
     import numpy as np
     import torch
@@ -200,12 +242,16 @@ def main(argv=None):
     # profiled warm-up step; its launches are timed with HIP events on the
     # library's stream during the timed steps
     if gsite is not None and gsite in prof and prof[gsite][0] > 0:
+        from gpt_pretraining_step_amd.profiling import load_traffic
         gcnt, gms = prof[gsite]
         gavg = gms / gcnt / 1e3
         result["roofline"] = {
             "kernel": gsite, "bound": "mfma", "achieved": round(fl[gsite] / gavg / 1e12, 2),
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-            "frac": round(fl[gsite] / gavg / PEAK_BF16, 4), "traffic": None,
+            "frac": round(fl[gsite] / gavg / PEAK_BF16, 4),
+            # HBM bytes per launch from the two counter runs recorded under
+            # profiles/ (null when none matches this kernel's current sources)
+            "traffic": load_traffic(os.path.join(ROOT, "profiles"), gsite),
             "avg_launch_us": round(gavg * 1e6, 2), "flops_per_launch": fl[gsite],
             "launches_timed": gcnt,
         }

@@ -23,7 +23,7 @@ from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noq
                    EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE, EPI_GELU_GRAD, EPI_MUL)
 
 __all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm",
-           "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum",
+           "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
            "query_sizes", "param_table"]
 
 
@@ -179,6 +179,10 @@ class GPT2:
         """Time only launches from `site` (None: every site)."""
         check(lib().gpt2_profile_only(self._h, site.encode() if site else None), "gpt2_profile_only")
 
+    def profile_mark(self, on: bool = True):
+        """Precede every timed launch with the empty marker kernel."""
+        check(lib().gpt2_profile_mark(self._h, 1 if on else 0), "gpt2_profile_mark")
+
     def profile_reset(self):
         check(lib().gpt2_profile_reset(self._h), "gpt2_profile_reset")
 
@@ -240,6 +244,12 @@ def op_gemm(A, B, C, M, N, K, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, 
     a.epilogue = epilogue
     a.out_bf16 = int(C.dtype == torch.bfloat16)
     check(lib().gpt2_op_gemm(_stream_ptr(stream), ct.byref(a)), "gpt2_op_gemm")
+
+
+def op_marker(stream=None):
+    """One launch of the library's empty marker kernel (delimits work in a
+    per-dispatch counter trace)."""
+    check(lib().gpt2_op_marker(_stream_ptr(stream)), "gpt2_op_marker")
 
 
 def op_colsum(Y, db, stream=None):

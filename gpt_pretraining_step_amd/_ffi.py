@@ -103,6 +103,8 @@ SIGNATURES = {
                                          ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p]),
     "gpt2_profile_enable": (ct.c_int, [ct.c_void_p, ct.c_int]),
     "gpt2_profile_only": (ct.c_int, [ct.c_void_p, ct.c_char_p]),
+    "gpt2_profile_mark": (ct.c_int, [ct.c_void_p, ct.c_int]),
+    "gpt2_op_marker": (ct.c_int, [ct.c_void_p]),
     "gpt2_profile_reset": (ct.c_int, [ct.c_void_p]),
     "gpt2_profile_count": (ct.c_int, [ct.c_void_p]),
     "gpt2_profile_entry": (ct.c_int, [ct.c_void_p, ct.c_int, ct.POINTER(ct.c_char_p), ct.POINTER(ct.c_int64),

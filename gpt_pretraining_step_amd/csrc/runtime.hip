@@ -24,6 +24,7 @@ namespace g2 {
 
 struct Prof {
   bool on = false;
+  bool mark = false;  // launch site_marker_kernel before each timed launch
   std::string only;  // when non-empty, only launches from this site are timed
   std::vector<std::string> names;
   std::vector<int64_t> counts;
@@ -75,9 +76,14 @@ struct Prof {
   }
 };
 
+// An empty kernel: in a per-dispatch counter trace, the dispatch that follows
+// it belongs to the marked launch site.
+__global__ void site_marker_kernel() {}
+
 void prof_begin(const Launch& L) {
   if (!L.prof || !L.prof->on) return;
   if (!L.prof->only.empty() && L.prof->only != L.site) return;
+  if (L.prof->mark) site_marker_kernel<<<1, 64, 0, L.stream>>>();
   L.prof->cur = L.prof->get();
   if (L.prof->cur) (void)hipEventRecord(L.prof->cur, L.stream);
 }
@@ -865,6 +871,17 @@ int gpt2_profile_only(gpt2_ctx* c, const char* site) {
   if (!c) return GPT2_ERR_ARG;
   c->prof.only = site ? site : "";
   return GPT2_OK;
+}
+
+int gpt2_profile_mark(gpt2_ctx* c, int on) {
+  if (!c) return GPT2_ERR_ARG;
+  c->prof.mark = on != 0;
+  return GPT2_OK;
+}
+
+int gpt2_op_marker(void* stream) {
+  site_marker_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>();
+  return hipGetLastError() == hipSuccess ? GPT2_OK : GPT2_ERR_HIP;
 }
 
 int gpt2_profile_reset(gpt2_ctx* c) {

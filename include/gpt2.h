@@ -320,6 +320,15 @@ int gpt2_profile_enable(gpt2_ctx* ctx, int on);
 /* Restrict the timing to launches from one site (site == NULL: all sites),
  * so that a measurement of one kernel adds no events around the others. */
 int gpt2_profile_only(gpt2_ctx* ctx, const char* site);
+/* When on, every timed launch is preceded by one launch of an empty kernel
+ * (g2::site_marker_kernel, 1 x 64 threads) on the context's stream, so that
+ * a per-dispatch hardware-counter trace can attribute the dispatch that
+ * follows each marker to the selected site.  Off by default; it adds one
+ * tiny launch per timed launch. */
+int gpt2_profile_mark(gpt2_ctx* ctx, int on);
+/* One launch of the same empty marker kernel on `stream` (NULL: the null
+ * stream), to delimit foreign work in such a trace. */
+int gpt2_op_marker(void* stream);
 int gpt2_profile_reset(gpt2_ctx* ctx);
 int gpt2_profile_count(gpt2_ctx* ctx);
 /* Entry i: site name (static storage), launches, summed milliseconds.  Call

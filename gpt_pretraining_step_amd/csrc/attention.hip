@@ -9,8 +9,8 @@
 // exchange with the partner lane 32 away) and the S^T accumulator feeds the
 // next product directly as its B operand.  The dK/dV pass works in the
 // direct orientation S = Q K^T so that each lane owns one key.  Operands whose
-// contraction index is the slow one in memory are transposed once per tile
-// in LDS (8x8 blocks through registers).  The MFMA k-slots of an accumulator
+// contraction index is the slow one in memory are read from LDS with the
+// transposing read.  The MFMA k-slots of an accumulator
 // used as an operand follow the accumulator's row order (row 8*(r/4) + 4*g +
 // r%4 of register r in lane group g); the matching operand is read in that
 // same order.

@@ -267,11 +267,15 @@ def op_layernorm_fwd(x, w, b, y, mean, rstd, stream=None):
           "gpt2_op_layernorm_fwd")
 
 
-def op_layernorm_bwd(dy, x, mean, rstd, w, dx, dw, db, stream=None):
+def op_layernorm_bwd(dy, x, mean, rstd, w, dx, dw, db, dx_bf16=None, stream=None):
+    """dy float32 or bf16; dx (float32) += the input gradient; dx_bf16 (optional)
+    receives bf16 of the updated dx."""
+    import torch
     rows, C = x.shape
-    check(lib().gpt2_op_layernorm_bwd(_stream_ptr(stream), dy.data_ptr(), x.data_ptr(), mean.data_ptr(),
-                                      rstd.data_ptr(), w.data_ptr(), dx.data_ptr(), dw.data_ptr(), db.data_ptr(),
-                                      rows, C), "gpt2_op_layernorm_bwd")
+    check(lib().gpt2_op_layernorm_bwd(_stream_ptr(stream), dy.data_ptr(), int(dy.dtype == torch.bfloat16),
+                                      x.data_ptr(), mean.data_ptr(), rstd.data_ptr(), w.data_ptr(), dx.data_ptr(),
+                                      _ptr(dx_bf16), dw.data_ptr(), db.data_ptr(), rows, C),
+          "gpt2_op_layernorm_bwd")
 
 
 def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None):

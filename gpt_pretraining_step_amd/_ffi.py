@@ -95,7 +95,7 @@ SIGNATURES = {
     "gpt2_op_colsum": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int64, ct.c_void_p]),
     "gpt2_op_layernorm_fwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
                                          ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int]),
-    "gpt2_op_layernorm_bwd": (ct.c_int, [ct.c_void_p] + [ct.c_void_p] * 8 + [ct.c_int, ct.c_int]),
+    "gpt2_op_layernorm_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int] + [ct.c_void_p] * 8 + [ct.c_int, ct.c_int]),
     "gpt2_op_attention_fwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
                                          ct.c_void_p, ct.c_void_p]),
     "gpt2_attention_bwd_scratch_bytes": (ct.c_size_t, [ct.c_int, ct.c_int, ct.c_int]),

@@ -101,7 +101,7 @@ hipError_t launch_colsum(const Launch& L, const void* y, int y_bf16, int M, int 
 hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y,
                                 int y_bf16, float* mean, float* rstd, int rows, int C);
 // dx is added into `dx`; when dxb is non-null it also receives bf16(dx_new).
-hipError_t launch_layernorm_bwd_b(const Launch& L, const float* dy, const float* x, const float* mean,
+hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* mean,
                                   const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
                                   int rows, int C);
 

@@ -3,8 +3,8 @@
 //
 // One wave (64 lanes) per row; the row lives in registers, statistics in
 // float32.  HBM-bound: the forward reads x (4 B) and writes y (2 or 4 B) per
-// element; the backward reads dy, x (8 B), read-modify-writes dx (8 B) and
-// writes its bf16 copy (2 B).
+// element; the backward reads dy (2 or 4 B) and x (4 B), read-modify-writes
+// dx (8 B) and writes its bf16 copy (2 B).
 #include "common.h"
 
 namespace g2 {
@@ -59,12 +59,10 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 // dx = rstd (g - mean(g) - xhat mean(g xhat)), g = dy w; dx is added into
 // dR; optionally dRb = bf16(dR) for the bf16 products that consume it.  The
 // weight and bias gradients are summed over the block's rows in registers,
-// then added with one atomic per column per block.
-//
-// VEC: C is a multiple of 256 and each lane owns float4 groups of columns
-// (lane*4 + 256*j); otherwise one column per lane (c = lane + 64*j).
-template <bool VEC, int ROWS_PER_WAVE>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+// then added with one atomic per column per block.  Any C <= 1024: one
+// column per lane (c = lane + 64 j); dy is float32 or bf16.
+template <typename DYT, int ROWS_PER_WAVE>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const DYT* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
                                                      const float* __restrict__ w, float* __restrict__ dR,
                                                      bf16* __restrict__ dRb, float* __restrict__ dw,
@@ -73,10 +71,9 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   const int wave = threadIdx.x >> 6;
   constexpr int NV = LN_MAXV;  // values per lane
   float gw[NV], gb[NV], wr[NV];
-  auto col = [&](int j) { return VEC ? (4 * lane + 256 * (j >> 2) + (j & 3)) : (lane + 64 * j); };
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int c = col(j);
+    const int c = lane + 64 * j;
     gw[j] = 0.f;
     gb[j] = 0.f;
     wr[j] = (c < C) ? w[c] : 0.f;
@@ -87,32 +84,18 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
     if (row >= rows) break;
     const float mu = mean[row], rs = rstd[row];
     const float* xr = x + (int64_t)row * C;
-    const float* dyr = dy + (int64_t)row * C;
+    const DYT* dyr = dy + (int64_t)row * C;
     float xh[NV], g[NV], d[NV];
-    if constexpr (VEC) {
 #pragma unroll
-      for (int q = 0; q < NV / 4; ++q) {
-        const int c = 4 * lane + 256 * q;
-        float4 dv = make_float4(0.f, 0.f, 0.f, 0.f), xv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < C) {
-          dv = *reinterpret_cast<const float4*>(dyr + c);
-          xv = *reinterpret_cast<const float4*>(xr + c);
-        }
-        d[4 * q] = dv.x; d[4 * q + 1] = dv.y; d[4 * q + 2] = dv.z; d[4 * q + 3] = dv.w;
-        xh[4 * q] = xv.x; xh[4 * q + 1] = xv.y; xh[4 * q + 2] = xv.z; xh[4 * q + 3] = xv.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int c = col(j);
-        d[j] = (c < C) ? dyr[c] : 0.f;
-        xh[j] = (c < C) ? xr[c] : 0.f;
-      }
+    for (int j = 0; j < NV; ++j) {
+      const int c = lane + 64 * j;
+      d[j] = (c < C) ? to_f<DYT>(dyr[c]) : 0.f;
+      xh[j] = (c < C) ? xr[c] : 0.f;
     }
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const bool in = col(j) < C;
+      const bool in = lane + 64 * j < C;
       const float xv = in ? (xh[j] - mu) * rs : 0.f;
       xh[j] = xv;
       g[j] = d[j] * wr[j];
@@ -124,33 +107,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
     sg = wave_sum(sg) / C;
     sgx = wave_sum(sgx) / C;
     float* dr = dR + (int64_t)row * C;
-    if constexpr (VEC) {
 #pragma unroll
-      for (int q = 0; q < NV / 4; ++q) {
-        const int c = 4 * lane + 256 * q;
-        if (c < C) {
-          float4 o = *reinterpret_cast<float4*>(dr + c);
-          o.x += rs * (g[4 * q] - sg - xh[4 * q] * sgx);
-          o.y += rs * (g[4 * q + 1] - sg - xh[4 * q + 1] * sgx);
-          o.z += rs * (g[4 * q + 2] - sg - xh[4 * q + 2] * sgx);
-          o.w += rs * (g[4 * q + 3] - sg - xh[4 * q + 3] * sgx);
-          *reinterpret_cast<float4*>(dr + c) = o;
-          if (dRb) {
-            bf16x4 ob;
-            ob[0] = f2bf(o.x); ob[1] = f2bf(o.y); ob[2] = f2bf(o.z); ob[3] = f2bf(o.w);
-            *reinterpret_cast<bf16x4*>(dRb + (int64_t)row * C + c) = ob;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int c = col(j);
-        if (c < C) {
-          const float nv = dr[c] + rs * (g[j] - sg - xh[j] * sgx);
-          dr[c] = nv;
-          if (dRb) dRb[(int64_t)row * C + c] = f2bf(nv);
-        }
+    for (int j = 0; j < NV; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C) {
+        const float nv = dr[c] + rs * (g[j] - sg - xh[j] * sgx);
+        dr[c] = nv;
+        if (dRb) dRb[(int64_t)row * C + c] = f2bf(nv);
       }
     }
   }
@@ -161,10 +124,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
     if (64 * j0 >= C) break;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      // position of value j0+jj within this 256-column slice
-      const int pos = VEC ? (4 * lane + jj) : (lane + 64 * jj);
-      red[wave][0][pos] = gw[j0 + jj];
-      red[wave][1][pos] = gb[j0 + jj];
+      red[wave][0][lane + 64 * jj] = gw[j0 + jj];
+      red[wave][1][lane + 64 * jj] = gb[j0 + jj];
     }
     __syncthreads();
     const int t = threadIdx.x;
@@ -179,28 +140,212 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   }
 }
 
+// ------------------------------------------------ vector kernels, C % 256 == 0
+//
+// Lane l owns the float4 column groups 4l + 256q (q < NQ = C/256), so every
+// load and store is 16 bytes (8 for bf16) per lane and a wave's access to a
+// row is contiguous.
+
+template <int NQ>
+__global__ __launch_bounds__(256) void ln_fwd_vec_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                         const float* __restrict__ b, bf16* __restrict__ y,
+                                                         float* __restrict__ mean, float* __restrict__ rstd,
+                                                         int rows, int C) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* xr = x + (int64_t)row * C + 4 * lane;
+  float4 v[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) v[q] = *reinterpret_cast<const float4*>(xr + 256 * q);
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
+  const float mu = wave_sum(s) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const float a = v[q].x - mu, bb = v[q].y - mu, c = v[q].z - mu, d = v[q].w - mu;
+    ss += (a * a + bb * bb) + (c * c + d * d);
+  }
+  const float rs = rsqrtf(wave_sum(ss) / C + LN_EPS);
+  bf16* yr = y + (int64_t)row * C + 4 * lane;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int c = 4 * lane + 256 * q;
+    const float4 ww = *reinterpret_cast<const float4*>(w + c);
+    const float4 bv = *reinterpret_cast<const float4*>(b + c);
+    bf16x4 o;
+    o[0] = f2bf((v[q].x - mu) * rs * ww.x + bv.x);
+    o[1] = f2bf((v[q].y - mu) * rs * ww.y + bv.y);
+    o[2] = f2bf((v[q].z - mu) * rs * ww.z + bv.z);
+    o[3] = f2bf((v[q].w - mu) * rs * ww.w + bv.w);
+    *reinterpret_cast<bf16x4*>(yr + 256 * q) = o;
+  }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16>(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4(bf2f(v[0]), bf2f(v[1]), bf2f(v[2]), bf2f(v[3]));
+}
+
+// Backward over RPW consecutive rows per wave; the next row's dy, x and dR
+// are loaded before the current row is reduced, so each wave keeps two
+// rows of loads in flight.  dy is float32 or bf16.
+template <typename DYT, int NQ, int RPW>
+__global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__ dy, const float* __restrict__ x,
+                                                         const float* __restrict__ mean,
+                                                         const float* __restrict__ rstd,
+                                                         const float* __restrict__ w, float* __restrict__ dR,
+                                                         bf16* __restrict__ dRb, float* __restrict__ dw,
+                                                         float* __restrict__ db, int rows, int C) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float4 wr[NQ], gw[NQ], gb[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    wr[q] = *reinterpret_cast<const float4*>(w + 4 * lane + 256 * q);
+    gw[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    gb[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const int nrows = min(RPW, rows - row0);
+  float4 d[NQ], xv[NQ], r[NQ];
+  float mu = 0.f, rs = 0.f;
+  auto load = [&](int row, float4 (&d_)[NQ], float4 (&x_)[NQ], float4 (&r_)[NQ], float& mu_, float& rs_) {
+    const int64_t o = (int64_t)row * C + 4 * lane;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      d_[q] = load4<DYT>(dy + o + 256 * q);
+      x_[q] = *reinterpret_cast<const float4*>(x + o + 256 * q);
+      r_[q] = *reinterpret_cast<const float4*>(dR + o + 256 * q);
+    }
+    mu_ = mean[row];
+    rs_ = rstd[row];
+  };
+  if (nrows > 0) load(row0, d, xv, r, mu, rs);
+#pragma unroll 1
+  for (int rr = 0; rr < nrows; ++rr) {
+    const int row = row0 + rr;
+    float4 nd[NQ], nx[NQ], nr[NQ];
+    float nmu = 0.f, nrs = 0.f;
+    if (rr + 1 < nrows) load(row + 1, nd, nx, nr, nmu, nrs);
+    float sg = 0.f, sgx = 0.f;
+    float4 g[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      xv[q] = make_float4((xv[q].x - mu) * rs, (xv[q].y - mu) * rs, (xv[q].z - mu) * rs, (xv[q].w - mu) * rs);
+      g[q] = make_float4(d[q].x * wr[q].x, d[q].y * wr[q].y, d[q].z * wr[q].z, d[q].w * wr[q].w);
+      gw[q].x += d[q].x * xv[q].x; gw[q].y += d[q].y * xv[q].y;
+      gw[q].z += d[q].z * xv[q].z; gw[q].w += d[q].w * xv[q].w;
+      gb[q].x += d[q].x; gb[q].y += d[q].y; gb[q].z += d[q].z; gb[q].w += d[q].w;
+      sg += (g[q].x + g[q].y) + (g[q].z + g[q].w);
+      sgx += (g[q].x * xv[q].x + g[q].y * xv[q].y) + (g[q].z * xv[q].z + g[q].w * xv[q].w);
+    }
+    sg = wave_sum(sg) / C;
+    sgx = wave_sum(sgx) / C;
+    const int64_t o = (int64_t)row * C + 4 * lane;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float4 v = r[q];
+      v.x += rs * (g[q].x - sg - xv[q].x * sgx);
+      v.y += rs * (g[q].y - sg - xv[q].y * sgx);
+      v.z += rs * (g[q].z - sg - xv[q].z * sgx);
+      v.w += rs * (g[q].w - sg - xv[q].w * sgx);
+      *reinterpret_cast<float4*>(dR + o + 256 * q) = v;
+      if (dRb) {
+        bf16x4 ob;
+        ob[0] = f2bf(v.x); ob[1] = f2bf(v.y); ob[2] = f2bf(v.z); ob[3] = f2bf(v.w);
+        *reinterpret_cast<bf16x4*>(dRb + o + 256 * q) = ob;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      d[q] = nd[q];
+      xv[q] = nx[q];
+      r[q] = nr[q];
+    }
+    mu = nmu;
+    rs = nrs;
+  }
+  // the 4 waves' column partials through LDS, then one atomic per column
+  // (consecutive threads, consecutive columns)
+  __shared__ float red[2][4][256 * NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    *reinterpret_cast<float4*>(&red[0][wave][4 * lane + 256 * q]) = gw[q];
+    *reinterpret_cast<float4*>(&red[1][wave][4 * lane + 256 * q]) = gb[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int c = threadIdx.x + 256 * q;
+    unsafeAtomicAdd(dw + c, (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]));
+    unsafeAtomicAdd(db + c, (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]));
+  }
+}
+
 hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y, int y_bf16,
                                 float* mean, float* rstd, int rows, int C) {
   dim3 grid((rows + 3) / 4), block(256);
   prof_begin(L);
-  if (y_bf16)
-    ln_fwd_kernel<bf16><<<grid, block, 0, L.stream>>>(x, w, b, static_cast<bf16*>(y), mean, rstd, rows, C);
-  else
+  bf16* yb = static_cast<bf16*>(y);
+  if (y_bf16 && C % 256 == 0) {
+    switch (C / 256) {
+      case 1: ln_fwd_vec_kernel<1><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      case 2: ln_fwd_vec_kernel<2><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      case 3: ln_fwd_vec_kernel<3><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      default: ln_fwd_vec_kernel<4><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+    }
+  } else if (y_bf16) {
+    ln_fwd_kernel<bf16><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C);
+  } else {
     ln_fwd_kernel<float><<<grid, block, 0, L.stream>>>(x, w, b, static_cast<float*>(y), mean, rstd, rows, C);
+  }
   prof_end(L);
   return hipGetLastError();
 }
 
-hipError_t launch_layernorm_bwd_b(const Launch& L, const float* dy, const float* x, const float* mean,
+template <typename DYT>
+static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const float* mean, const float* rstd,
+                            const float* w, float* dx, bf16* dxb, float* dw, float* db, int rows, int C) {
+  if (C % 256 == 0) {
+    // 16 rows per wave: few blocks, so few column atomics; the next row's
+    // loads in flight keep HBM busy
+    constexpr int RPW = 16;
+    const dim3 grid((rows + 4 * RPW - 1) / (4 * RPW));
+    switch (C / 256) {
+      case 1: ln_bwd_vec_kernel<DYT, 1, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 2: ln_bwd_vec_kernel<DYT, 2, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 3: ln_bwd_vec_kernel<DYT, 3, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      default: ln_bwd_vec_kernel<DYT, 4, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+    }
+  } else {
+    constexpr int RPW = 4;
+    const dim3 grid((rows + 4 * RPW - 1) / (4 * RPW));
+    ln_bwd_kernel<DYT, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+  }
+}
+
+hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* mean,
                                   const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
                                   int rows, int C) {
-  constexpr int RPW = 4;
-  dim3 grid((rows + 4 * RPW - 1) / (4 * RPW)), block(256);
   prof_begin(L);
-  if (C % 256 == 0)
-    ln_bwd_kernel<true, RPW><<<grid, block, 0, L.stream>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+  if (dy_bf16)
+    ln_bwd_dispatch<bf16>(L.stream, static_cast<const bf16*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows, C);
   else
-    ln_bwd_kernel<false, RPW><<<grid, block, 0, L.stream>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+    ln_bwd_dispatch<float>(L.stream, static_cast<const float*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows, C);
   prof_end(L);
   return hipGetLastError();
 }

@@ -502,9 +502,12 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   float* dR = c->scr<float>(y.dR);
   bf16* dRb = bf ? c->scr<bf16>(y.dRb) : nullptr;
   const void* dRop = bf ? static_cast<const void*>(dRb) : static_cast<const void*>(dR);
-  float* dA = c->scr<float>(y.dA);  // dZ lives here first; LN bwd consumes it before reuse
+  // gradient of an LN output: bf16 in BF16 mode (the products' output type,
+  // as under autocast), float32 otherwise; dZ (float32) lives here first and
+  // the final LN backward consumes it before the buffer is reused
+  void* dA = c->scr(y.dA);
   HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
-  HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dZ, rlast, c->act<float>(y.meanf), c->act<float>(y.rstdf),
+  HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dZ, 0, rlast, c->act<float>(y.meanf), c->act<float>(y.rstdf),
                                  c->P(c->tab.lnf_w), dR, dRb, c->Gr(c->tab.lnf_w), c->Gr(c->tab.lnf_b), M, C));
   void* dU = c->scr(y.dU);
   void* dY = c->scr(y.dY);
@@ -517,8 +520,8 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                       c->act(y.U[l])));
     HIP_TRY(linear_dw(c, "gemm.fc_dw", dU, M, F, c->act(y.A2[l]), C, c->L(l, FC_W), c->L(l, FC_B),
                       static_cast<const float*>(dU)));
-    HIP_TRY(linear_dx(c, "gemm.fc_dx", dU, M, F, c->L(l, FC_W), C, GPT2_EPI_STORE, false, dA, nullptr));
-    HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, c->act<float>(y.Rmid[l]), c->act<float>(y.mean2[l]),
+    HIP_TRY(linear_dx(c, "gemm.fc_dx", dU, M, F, c->L(l, FC_W), C, GPT2_EPI_STORE, true, dA, nullptr));
+    HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, bf, c->act<float>(y.Rmid[l]), c->act<float>(y.mean2[l]),
                                    c->act<float>(y.rstd2[l]), c->P(c->L(l, LN2_W)), dR, dRb, c->Gr(c->L(l, LN2_W)),
                                    c->Gr(c->L(l, LN2_B)), M, C));
     // attention branch: Rmid = R_l + Y Wo^T + b
@@ -528,8 +531,8 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                                  c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
     HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
                       static_cast<const float*>(dQKV)));
-    HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, false, dA, nullptr));
-    HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, c->act<float>(y.Rin[l]), c->act<float>(y.mean1[l]),
+    HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
+    HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, bf, c->act<float>(y.Rin[l]), c->act<float>(y.mean1[l]),
                                    c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb, c->Gr(c->L(l, LN1_W)),
                                    c->Gr(c->L(l, LN1_B)), M, C));
   }
@@ -818,17 +821,24 @@ int gpt2_op_layernorm_fwd(void* stream, const float* d_x, const float* d_w, cons
                           float* d_mean, float* d_rstd, int rows, int C) {
   if (!d_x || !d_w || !d_b || !d_y || !d_mean || !d_rstd) return GPT2_ERR_ARG;
   if (rows < 1 || C < 1 || C > 1024) return GPT2_ERR_SHAPE;
+  if (y_bf16 && C % 256 == 0 && (((uintptr_t)d_x | (uintptr_t)d_w | (uintptr_t)d_b | (uintptr_t)d_y) & 15))
+    return GPT2_ERR_ARG;
   HIP_TRY(launch_layernorm_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_x, d_w, d_b, d_y, y_bf16,
                                d_mean, d_rstd, rows, C));
   return GPT2_OK;
 }
 
-int gpt2_op_layernorm_bwd(void* stream, const float* d_dy, const float* d_x, const float* d_mean, const float* d_rstd,
-                          const float* d_w, float* d_dx, float* d_dw, float* d_db, int rows, int C) {
+int gpt2_op_layernorm_bwd(void* stream, const void* d_dy, int dy_bf16, const float* d_x, const float* d_mean,
+                          const float* d_rstd, const float* d_w, float* d_dx, void* d_dx_bf16, float* d_dw, float* d_db,
+                          int rows, int C) {
   if (!d_dy || !d_x || !d_mean || !d_rstd || !d_w || !d_dx || !d_dw || !d_db) return GPT2_ERR_ARG;
   if (rows < 1 || C < 1 || C > 1024) return GPT2_ERR_SHAPE;
-  HIP_TRY(launch_layernorm_bwd_b(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_dy, d_x, d_mean, d_rstd,
-                                 d_w, d_dx, nullptr, d_dw, d_db, rows, C));
+  // the vector kernels (C a multiple of 256) move 16 bytes per lane
+  if (C % 256 == 0 && (((uintptr_t)d_dy | (uintptr_t)d_x | (uintptr_t)d_w | (uintptr_t)d_dx |
+                        (uintptr_t)d_dx_bf16 | (uintptr_t)d_dw | (uintptr_t)d_db) & 15))
+    return GPT2_ERR_ARG;
+  HIP_TRY(launch_layernorm_bwd_b(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_dy, dy_bf16 != 0, d_x,
+                                 d_mean, d_rstd, d_w, d_dx, static_cast<bf16*>(d_dx_bf16), d_dw, d_db, rows, C));
   return GPT2_OK;
 }
 

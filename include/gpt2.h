@@ -290,11 +290,15 @@ int gpt2_op_colsum(void* stream, const void* d_y, int y_bf16, int M, int N, int6
  * mean and rstd float32 [rows] are written for the backward. */
 int gpt2_op_layernorm_fwd(void* stream, const float* d_x, const float* d_w, const float* d_b, void* d_y,
                           int y_bf16, float* d_mean, float* d_rstd, int rows, int C);
-/* Backward of the above for dy float32 [rows, C]: dx is ADDED to d_dx, and
- * sum over rows of dy * xhat and of dy are ADDED to d_dw and d_db. */
-int gpt2_op_layernorm_bwd(void* stream, const float* d_dy, const float* d_x, const float* d_mean,
-                          const float* d_rstd, const float* d_w, float* d_dx, float* d_dw, float* d_db,
-                          int rows, int C);
+/* Backward of the above for dy [rows, C] (float32, or bf16 when dy_bf16):
+ * dx is ADDED to the float32 d_dx; when d_dx_bf16 is not NULL it also
+ * receives bf16 of the updated d_dx; sum over rows of dy * xhat and of dy
+ * are ADDED to d_dw and d_db.  When C is a multiple of 256 every pointer
+ * (and, with y_bf16, those of the forward) must be 16-byte aligned
+ * (GPT2_ERR_ARG otherwise). */
+int gpt2_op_layernorm_bwd(void* stream, const void* d_dy, int dy_bf16, const float* d_x, const float* d_mean,
+                          const float* d_rstd, const float* d_w, float* d_dx, void* d_dx_bf16, float* d_dw,
+                          float* d_db, int rows, int C);
 
 /* Causal multi-head attention ("How I trained my own GPT-2 124M on
  * FineWeb-Edu" sections 2.12 and 5): qkv [B*T, 3*H*hd] holds q | k | v column

@@ -281,10 +281,17 @@ def test_attention_causality_bitwise(g):
 
 # ------------------------------------------------------------------ layernorm
 
-@pytest.mark.parametrize("rows,C,bf", [(1, 768, True), (1000, 768, True), (77, 64, False), (33, 100, False)])
-def test_layernorm_vs_oracle(g, rows, C, bf):
+@pytest.mark.parametrize("rows,C,bf,dyb", [(1, 768, True, False), (1000, 768, True, False), (1000, 768, True, True),
+                                           (129, 256, True, True), (70, 512, True, False), (65, 1024, True, True),
+                                           (77, 64, False, False), (33, 100, False, True)])
+def test_layernorm_vs_oracle(g, rows, C, bf, dyb):
+    """Forward and backward against the oracle.  C a multiple of 256 takes the
+    vector kernels (one float4 group per lane per 256 columns, 16 rows per
+    wave in the backward, ragged row counts); other C the generic ones.  dy is
+    float32 or bf16 (rounded on the host, so both sides see the same values);
+    the bf16 copy of the updated dx must equal bf16 of the float32 dx."""
     import torch
-    announce(f"layernorm rows={rows} C={C} bf16={bf}")
+    announce(f"layernorm rows={rows} C={C} bf16={bf} dy_bf16={dyb}")
     rng = np.random.default_rng(rows + C)
     x = (rng.standard_normal((rows, C)) * 2 + 0.5).astype(np.float32)
     w = (1 + 0.1 * rng.standard_normal(C)).astype(np.float32)
@@ -299,15 +306,20 @@ def test_layernorm_vs_oracle(g, rows, C, bf):
     np.testing.assert_allclose(host(y), y_ref, rtol=tol, atol=tol)
     np.testing.assert_allclose(host(rstd), cache[1][:, 0], rtol=1e-5)
     dy = rng.standard_normal((rows, C)).astype(np.float32)
+    if dyb:
+        dy = synthetic.round_to_bf16(dy)
     dx0 = rng.standard_normal((rows, C)).astype(np.float32)
     dxr, dwr, dbr = OM.layernorm_bwd(dy.astype(np.float64), cache, w.astype(np.float64))
     dx = dev(dx0)
+    dxb = torch.zeros((rows, C), dtype=torch.bfloat16, device="cuda")
     dw = dev(np.ones(C, dtype=np.float32))
     db = dev(np.zeros(C, dtype=np.float32))
-    g.op_layernorm_bwd(dev(dy), dx_, mean, rstd, dev(w), dx, dw, db)
+    g.op_layernorm_bwd(dev(dy, torch.bfloat16) if dyb else dev(dy), dx_, mean, rstd, dev(w), dx, dw, db,
+                       dx_bf16=dxb)
     np.testing.assert_allclose(host(dx), dx0 + dxr, rtol=1e-4, atol=1e-4)
     np.testing.assert_allclose(host(dw), 1 + dwr, rtol=1e-4, atol=1e-3)
     np.testing.assert_allclose(host(db), dbr, rtol=1e-4, atol=1e-3)
+    assert torch.equal(dxb, dx.to(torch.bfloat16))
 
 
 # ------------------------------------------------------------- lm_head + loss

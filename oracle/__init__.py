@@ -18,6 +18,10 @@ Sources (cited by page title and section throughout):
   [fast-1gpu]    "Build an LLM From Scratch: Making Training Fast on One GPU" (vidyal.ai)
   [grad-accum]   "Multi-GPU calculation of gradients for accelerated training" (joelfernandes.org)
 
+``oracle.modern`` holds the modern variant of the same model (RMSNorm,
+rotary position embedding, SwiGLU, no position table, no biases) that
+[repro-124M] trains; it reuses this package's attention and cross-entropy.
+
 Every function in this package is pinned by a ``-m "not gpu"`` test against
 something other than itself (finite differences, closed forms, invariants,
 the worked examples the pages print, published known-answer vectors).
@@ -42,3 +46,4 @@ from .model import (  # noqa: F401
 from .optim import global_grad_norm, clip_coef, adamw_update, clip_adamw_step  # noqa: F401
 from .init import philox4x32_10, normal_from_philox, init_params  # noqa: F401
 from .flops import flops_per_token, mfu  # noqa: F401
+from . import modern  # noqa: F401

@@ -20,11 +20,13 @@ from dataclasses import dataclass
 
 from . import _ffi
 from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noqa: F401
-                   EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE, EPI_GELU_GRAD, EPI_MUL)
+                   EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE, EPI_GELU_GRAD, EPI_MUL,
+                   EPI_ROPE, EPI_SWIGLU, EPI_SWIGLU_BWD, ARCH_GPT2, ARCH_ROTARY)
 
 __all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm",
            "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
-           "query_sizes", "param_table"]
+           "op_rope_table", "op_rope_bwd", "op_rmsnorm_fwd", "op_rmsnorm_bwd", "query_sizes", "param_table",
+           "GPT2_ROTARY_124M"]
 
 
 @dataclass(frozen=True)
@@ -37,16 +39,20 @@ class ModelConfig:
     mlp_hidden: int
     max_batch: int
     precision: int  # PRECISION_FP32 or PRECISION_BF16
+    arch: int = ARCH_GPT2  # ARCH_GPT2 or ARCH_ROTARY
 
     def c(self) -> _ffi.Config:
         return _ffi.Config(self.vocab_size, self.block_size, self.n_layer, self.n_head, self.n_embd,
-                           self.mlp_hidden, self.max_batch, self.precision)
+                           self.mlp_hidden, self.max_batch, self.precision, self.arch)
 
 
 # The tiny character-level GPT in float32 (vocab 66, 2 layers, 64 wide, 4 heads, MLP 256, T 64, B 4).
 TINY_CHAR_FP32 = ModelConfig(66, 64, 2, 4, 64, 256, 4, PRECISION_FP32)
 # GPT-2 124M with the padded vocabulary, bf16 compute with float32 master weights, micro-batch 16.
 GPT2_124M = ModelConfig(50304, 1024, 12, 12, 768, 3072, 16, PRECISION_BF16)
+# The rotary variant ("Reproduce GPT-2 124M": RMSNorm, RoPE, SwiGLU 2048, no
+# position table, no biases), bf16, micro-batch 64.
+GPT2_ROTARY_124M = ModelConfig(50304, 1024, 12, 12, 768, 2048, 64, PRECISION_BF16, ARCH_ROTARY)
 
 
 def query_sizes(cfg: ModelConfig) -> _ffi.Sizes:
@@ -229,7 +235,8 @@ def lmhead_ce(hidden, weight, targets, dweight, stream=None, flag=None):
 
 
 def op_gemm(A, B, C, M, N, K, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, ldc=None, epilogue=EPI_STORE,
-            C2=None, R=None, U=None, bias=None, alpha=1.0, stream=None):
+            C2=None, R=None, U=None, bias=None, alpha=1.0, rope=None, rope_period=0, rope_cols=0, ld2=None,
+            stream=None):
     import torch
     dtype = PRECISION_BF16 if A.dtype == torch.bfloat16 else PRECISION_FP32
     a = _ffi.GemmArgs()
@@ -237,13 +244,45 @@ def op_gemm(A, B, C, M, N, K, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, 
     a.a_kmajor, a.b_kmajor = int(a_kmajor), int(b_kmajor)
     a.lda = lda if lda is not None else (K if a_kmajor else M)
     a.ldb = ldb if ldb is not None else (K if b_kmajor else N)
-    a.ldc = ldc if ldc is not None else N
+    default_ldc = {EPI_SWIGLU: N // 2, EPI_SWIGLU_BWD: 2 * N}.get(epilogue, N)
+    a.ldc = ldc if ldc is not None else default_ldc
     a.A, a.B, a.C = A.data_ptr(), B.data_ptr(), C.data_ptr()
     a.C2, a.R, a.U, a.bias = _ptr(C2), _ptr(R), _ptr(U), _ptr(bias)
     a.alpha = alpha
     a.epilogue = epilogue
     a.out_bf16 = int(C.dtype == torch.bfloat16)
+    a.rope, a.rope_period, a.rope_cols = _ptr(rope), rope_period, rope_cols
+    a.ld2 = ld2 if ld2 is not None else {EPI_SWIGLU: N, EPI_SWIGLU_BWD: 2 * N}.get(epilogue, 0)
     check(lib().gpt2_op_gemm(_stream_ptr(stream), ct.byref(a)), "gpt2_op_gemm")
+
+
+def op_rope_table(T, base=10000.0, stream=None):
+    """(cos, sin) of the rotary angles for head dimension 64: float32 [T, 32, 2]."""
+    import torch
+    tab = torch.empty((T, 32, 2), dtype=torch.float32, device="cuda")
+    check(lib().gpt2_op_rope_table(_stream_ptr(stream), T, float(base), tab.data_ptr()), "gpt2_op_rope_table")
+    return tab
+
+
+def op_rope_bwd(dqkv, T, n_embd, tab, stream=None):
+    """Backward rotation, in place, of the q and k blocks of dqkv [rows, 3 C] (bf16)."""
+    rows = dqkv.shape[0]
+    check(lib().gpt2_op_rope_bwd(_stream_ptr(stream), dqkv.data_ptr(), rows, dqkv.stride(0), 2 * n_embd, T,
+                                 tab.data_ptr()), "gpt2_op_rope_bwd")
+
+
+def op_rmsnorm_fwd(x, w, y, rstd, stream=None):
+    rows, C = x.shape
+    check(lib().gpt2_op_rmsnorm_fwd(_stream_ptr(stream), x.data_ptr(), w.data_ptr(), y.data_ptr(), rstd.data_ptr(),
+                                    rows, C), "gpt2_op_rmsnorm_fwd")
+
+
+def op_rmsnorm_bwd(dy, x, rstd, w, dx, dw, dx_bf16=None, stream=None):
+    import torch
+    rows, C = x.shape
+    check(lib().gpt2_op_rmsnorm_bwd(_stream_ptr(stream), dy.data_ptr(), int(dy.dtype == torch.bfloat16), x.data_ptr(),
+                                    rstd.data_ptr(), w.data_ptr(), dx.data_ptr(), _ptr(dx_bf16), dw.data_ptr(),
+                                    rows, C), "gpt2_op_rmsnorm_bwd")
 
 
 def op_marker(stream=None):

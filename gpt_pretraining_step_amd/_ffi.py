@@ -31,11 +31,17 @@ EPI_DGELU = 3
 EPI_ACCUMULATE = 4
 EPI_GELU_GRAD = 5
 EPI_MUL = 6
+EPI_ROPE = 7
+EPI_SWIGLU = 8
+EPI_SWIGLU_BWD = 9
+
+ARCH_GPT2 = 0
+ARCH_ROTARY = 1
 
 
 class Config(ct.Structure):
     _fields_ = [(n, ct.c_int32) for n in (
-        "vocab_size", "block_size", "n_layer", "n_head", "n_embd", "mlp_hidden", "max_batch", "precision")]
+        "vocab_size", "block_size", "n_layer", "n_head", "n_embd", "mlp_hidden", "max_batch", "precision", "arch")]
 
 
 class Sizes(ct.Structure):
@@ -67,7 +73,8 @@ class GemmArgs(ct.Structure):
         ("lda", ct.c_int64), ("ldb", ct.c_int64), ("ldc", ct.c_int64),
         ("A", ct.c_void_p), ("B", ct.c_void_p), ("C", ct.c_void_p), ("C2", ct.c_void_p), ("R", ct.c_void_p),
         ("U", ct.c_void_p), ("bias", ct.c_void_p), ("alpha", ct.c_float), ("epilogue", ct.c_int32),
-        ("out_bf16", ct.c_int32),
+        ("out_bf16", ct.c_int32), ("rope", ct.c_void_p), ("rope_period", ct.c_int32), ("rope_cols", ct.c_int32),
+        ("ld2", ct.c_int64),
     ]
 
 
@@ -105,6 +112,10 @@ SIGNATURES = {
     "gpt2_profile_only": (ct.c_int, [ct.c_void_p, ct.c_char_p]),
     "gpt2_profile_mark": (ct.c_int, [ct.c_void_p, ct.c_int]),
     "gpt2_op_marker": (ct.c_int, [ct.c_void_p]),
+    "gpt2_op_rmsnorm_fwd": (ct.c_int, [ct.c_void_p] * 5 + [ct.c_int, ct.c_int]),
+    "gpt2_op_rmsnorm_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int] + [ct.c_void_p] * 6 + [ct.c_int, ct.c_int]),
+    "gpt2_op_rope_table": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_double, ct.c_void_p]),
+    "gpt2_op_rope_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int64, ct.c_int, ct.c_int, ct.c_void_p]),
     "gpt2_profile_reset": (ct.c_int, [ct.c_void_p]),
     "gpt2_profile_count": (ct.c_int, [ct.c_void_p]),
     "gpt2_profile_entry": (ct.c_int, [ct.c_void_p, ct.c_int, ct.POINTER(ct.c_char_p), ct.POINTER(ct.c_int64),

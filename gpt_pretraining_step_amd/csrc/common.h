@@ -104,6 +104,15 @@ hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w,
 hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* mean,
                                   const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
                                   int rows, int C);
+// Rotary embedding, head dimension 64: the (cos, sin) table [T][32] and the
+// backward rotation of the q and k blocks of dqkv in place.
+hipError_t launch_rope_table(const Launch& L, float2* tab, int T, double base);
+hipError_t launch_rope_bwd(const Launch& L, bf16* dqkv, int rows, int64_t ld, int cols, int period,
+                           const float2* tab);
+// RMSNorm of the rotary variant (C % 256 == 0, C <= 1024).
+hipError_t launch_rmsnorm_fwd(const Launch& L, const float* x, const float* w, bf16* y, float* rstd, int rows, int C);
+hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* rstd,
+                              const float* w, float* dx, bf16* dxb, float* dw, int rows, int C);
 
 hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
                                 void* y, float* lse);

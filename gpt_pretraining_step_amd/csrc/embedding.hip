@@ -1,6 +1,8 @@
 // Token + position embedding ("How I trained my own GPT-2 124M on
 // FineWeb-Edu" 2.2 and 2.10: x = wte[idx] + wpe[0..T-1]) and its backward.
 // The tied wte also receives the lm_head gradient elsewhere (section 4).
+// Without a position table (wpe == NULL: the rotary variant of "Reproduce
+// GPT-2 124M", whose model holds no wpe) x = wte[idx].
 #include "common.h"
 
 namespace g2 {
@@ -19,8 +21,12 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
   }
   const int t = row % T;
   const float* a = wte + (int64_t)id * C;
-  const float* p = wpe + (int64_t)t * C;
   float* o = out + (int64_t)row * C;
+  if (!wpe) {
+    for (int c = threadIdx.x; c < C; c += blockDim.x) o[c] = a[c];
+    return;
+  }
+  const float* p = wpe + (int64_t)t * C;
   if ((C & 3) == 0) {
     for (int c = 4 * threadIdx.x; c < C; c += 4 * blockDim.x) {
       float4 x = *reinterpret_cast<const float4*>(a + c);
@@ -69,7 +75,7 @@ hipError_t launch_embed_bwd(const Launch& L, const int32_t* tok, const float* dr
   prof_begin(L);
   embed_bwd_wte_kernel<<<B * T, 256, 0, L.stream>>>(tok, dr, dwte, B * T, C, V);
   const int64_t n = (int64_t)T * C;
-  embed_bwd_wpe_kernel<<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(dr, dwpe, B, T, C);
+  if (dwpe) embed_bwd_wpe_kernel<<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(dr, dwpe, B, T, C);
   prof_end(L);
   return hipGetLastError();
 }

@@ -84,6 +84,10 @@ static GemmP make_params(const gpt2_gemm_args& a) {
   p.lda = a.lda; p.ldb = a.ldb; p.ldc = a.ldc;
   p.A = a.A; p.B = a.B; p.C = a.C; p.C2 = a.C2; p.R = a.R; p.U = a.U; p.bias = a.bias;
   p.alpha = a.alpha;
+  p.rope = static_cast<const float2*>(a.rope);
+  p.rope_period = a.rope_period;
+  p.rope_cols = a.rope_cols;
+  p.ld2 = a.ld2;
   p.splits = 1;
   p.k_per_split = a.K;
   return p;
@@ -140,6 +144,20 @@ static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
     case GPT2_EPI_MUL:
       e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_MUL, true, false, true>(L, p);
       break;
+    case GPT2_EPI_ROPE:
+    case GPT2_EPI_SWIGLU:
+      // paired columns in one lane: 64 columns per wave (256-wide tiles), forward layout
+      if constexpr (BN == 256 && A_K && B_K) {
+        e = epi == GPT2_EPI_ROPE ? launch_v2<BM, BN, BK, WGM, WGN, ST, true, true, GPT2_EPI_ROPE, true, false, true>(L, p)
+                                 : launch_v2<BM, BN, BK, WGM, WGN, ST, true, true, GPT2_EPI_SWIGLU, true, false, true>(L, p);
+      } else {
+        e = hipErrorInvalidValue;
+      }
+      break;
+    case GPT2_EPI_SWIGLU_BWD:
+      if constexpr (A_K && !B_K) e = launch_v2<BM, BN, BK, WGM, WGN, ST, true, false, GPT2_EPI_SWIGLU_BWD, true, false, true>(L, p);
+      else e = hipErrorInvalidValue;
+      break;
     default:
       e = at ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, true>(L, p)
              : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_ACCUMULATE, false, false>(L, p);
@@ -182,8 +200,9 @@ static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
   int s256 = 1, s192 = 1;
   const double c256 = tiling_cost(p.M, p.N, p.K, 256, acc, &s256);
   const double c192 = tiling_cost(p.M, p.N, p.K, 192, acc, &s192);
-  // the narrower tile re-reads A more often: take it only for a clear gain
-  const bool narrow = c192 < 0.9 * c256;
+  // the narrower tile re-reads A more often: take it only for a clear gain;
+  // the paired epilogues need 64 columns per wave
+  const bool narrow = c192 < 0.9 * c256 && epi != GPT2_EPI_ROPE && epi != GPT2_EPI_SWIGLU;
   const int splits = narrow ? s192 : s256;
   p.k_per_split = (p.K + splits * 64 - 1) / (splits * 64) * 64;
   p.splits = (p.K + p.k_per_split - 1) / p.k_per_split;

@@ -33,6 +33,9 @@ struct GemmP {
   const float* bias;
   float* row_sum;  // optional: row_sum[m] += sum over this product's K of A(m, k) (one column-tile adds it)
   float2* stats;   // EPI_CE_STATS: per (row, column tile) softmax statistics, [M][tiles_n]
+  const float2* rope;  // ROPE: (cos, sin) [rope_period][32]
+  int rope_period, rope_cols;
+  int64_t ld2;  // SWIGLU: row pitch of C2; SWIGLU_BWD: row pitch of U
   float alpha;
   int tiles_m, tiles_n, splits, k_per_split;
 };
@@ -276,6 +279,134 @@ __device__ __forceinline__ void epi_tile_mul_pre(const GemmP& p, int mrow, int n
   }
 }
 
+// ------------------------------------------------ rotary and SwiGLU epilogues
+//
+// Swapped layout with 64 columns per wave (TN == 2): in accumulator j = 0 a
+// lane holds columns g + 8q + 4 lg + e of the wave's 64-column group g, in
+// j = 1 the columns 32 further on, so the two elements that a rotation or
+// the SwiGLU gate combine sit in the same lane and register.
+
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e))
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+// ROPE: rotary embedding of q and k ("Reproduce GPT-2 124M", x cos +
+// rotate_half(x) sin, dimension i of a 64-wide head paired with i + 32) on
+// the bf16 output of the qkv product.  Column groups g < rope_cols are
+// rotated with the angle table of position m % rope_period; the others
+// (v) are stored as they are.
+// SWIGLU: the product's columns are the interleaved rows of [W_gate; W_up]
+// (group g holds gate rows g/2 .. g/2+31 in j = 0 and the matching up rows
+// in j = 1): act = silu(gate) up goes to C at column g/2 + d, the bf16 gate
+// and up to C2 at columns g/2 + d and F + g/2 + d (F = N / 2).
+template <int EPI, int TM, bool CHECK>
+__device__ __forceinline__ void epi_tile_pair(const GemmP& p, int mrow, int gcol, int lg, const f32x16 (&acc)[TM][2]) {
+  if (CHECK && gcol >= p.N) return;  // N % 64 == 0: a group is wholly in or out
+  const bool rot = EPI == GPT2_EPI_ROPE && gcol < p.rope_cols;
+  const int F = p.N >> 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = mrow + 32 * i;
+    if (CHECK && m >= p.M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 8 * q + 4 * lg;
+      float v0[4], v1[4];
+      float4 b0 = make_float4(0.f, 0.f, 0.f, 0.f), b1 = b0;
+      if (EPI == GPT2_EPI_ROPE && p.bias) {
+        b0 = *reinterpret_cast<const float4*>(p.bias + gcol + d);
+        b1 = *reinterpret_cast<const float4*>(p.bias + gcol + 32 + d);
+      }
+      const float bb0[4] = {b0.x, b0.y, b0.z, b0.w}, bb1[4] = {b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[e] = fmaf(p.alpha, acc[i][0][4 * q + e], bb0[e]);
+        v1[e] = fmaf(p.alpha, acc[i][1][4 * q + e], bb1[e]);
+      }
+      if constexpr (EPI == GPT2_EPI_ROPE) {
+        bf16* crow = static_cast<bf16*>(p.C) + (int64_t)m * p.ldc + gcol;
+        float o0[4], o1[4];
+        if (rot) {
+          const float2* tab = p.rope + (int64_t)(m % p.rope_period) * 32 + d;
+          const float4 cs01 = *reinterpret_cast<const float4*>(tab);
+          const float4 cs23 = *reinterpret_cast<const float4*>(tab + 2);
+          const float cc[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o0[e] = v0[e] * cc[e] - v1[e] * sn[e];
+            o1[e] = v1[e] * cc[e] + v0[e] * sn[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o0[e] = v0[e];
+            o1[e] = v1[e];
+          }
+        }
+        const bf16x2 a01 = f2bf2(o0[0], o0[1]), a23 = f2bf2(o0[2], o0[3]);
+        const bf16x2 c01 = f2bf2(o1[0], o1[1]), c23 = f2bf2(o1[2], o1[3]);
+        *reinterpret_cast<bf16x4*>(crow + d) = bf16x4{a01[0], a01[1], a23[0], a23[1]};
+        *reinterpret_cast<bf16x4*>(crow + 32 + d) = bf16x4{c01[0], c01[1], c23[0], c23[1]};
+      } else {  // SWIGLU
+        const int f = (gcol >> 1) + d;
+        const bf16x2 g01 = f2bf2(v0[0], v0[1]), g23 = f2bf2(v0[2], v0[3]);
+        const bf16x2 u01 = f2bf2(v1[0], v1[1]), u23 = f2bf2(v1[2], v1[3]);
+        const bf16x4 g = bf16x4{g01[0], g01[1], g23[0], g23[1]}, u = bf16x4{u01[0], u01[1], u23[0], u23[1]};
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gf = bf2f(g[e]);
+          a[e] = gf * sigmoid_fast(gf) * bf2f(u[e]);
+        }
+        const bf16x2 a01 = f2bf2(a[0], a[1]), a23 = f2bf2(a[2], a[3]);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + (int64_t)m * p.ldc + f) =
+            bf16x4{a01[0], a01[1], a23[0], a23[1]};
+        bf16* c2 = static_cast<bf16*>(p.C2) + (int64_t)m * p.ld2 + f;
+        *reinterpret_cast<bf16x4*>(c2) = g;
+        *reinterpret_cast<bf16x4*>(c2 + F) = u;
+      }
+    }
+  }
+}
+
+// SWIGLU_BWD: the product is d(act) [M, F] (F = N); with gate g = U[m][f]
+// and up u = U[m][F + f] (row pitch ld2), C[m][f] = d(act) u silu'(g) and
+// C[m][F + f] = d(act) silu(g), silu'(g) = s (1 + g (1 - s)), s = sigmoid(g).
+// Swapped layout, any tile width; N % 4 == 0.
+template <int TM, int TN, bool CHECK>
+__device__ __forceinline__ void epi_tile_swiglu_bwd(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN]) {
+  const int F = p.N;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = mrow + 32 * i;
+    if (CHECK && m >= p.M) continue;
+    const bf16* urow = static_cast<const bf16*>(p.U) + (int64_t)m * p.ld2;
+    bf16* crow = static_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = ncol + 32 * j + 8 * q;
+        if (CHECK && f >= p.N) continue;
+        const bf16x4 g = *reinterpret_cast<const bf16x4*>(urow + f);
+        const bf16x4 u = *reinterpret_cast<const bf16x4*>(urow + F + f);
+        float dg[4], du[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = p.alpha * acc[i][j][4 * q + e];
+          const float gf = bf2f(g[e]), sg = sigmoid_fast(gf);
+          du[e] = v * gf * sg;
+          dg[e] = v * bf2f(u[e]) * sg * fmaf(gf, 1.f - sg, 1.f);
+        }
+        const bf16x2 g01 = f2bf2(dg[0], dg[1]), g23 = f2bf2(dg[2], dg[3]);
+        const bf16x2 u01 = f2bf2(du[0], du[1]), u23 = f2bf2(du[2], du[3]);
+        *reinterpret_cast<bf16x4*>(crow + f) = bf16x4{g01[0], g01[1], g23[0], g23[1]};
+        *reinterpret_cast<bf16x4*>(crow + F + f) = bf16x4{u01[0], u01[1], u23[0], u23[1]};
+      }
+  }
+}
+
 // Internal epilogue of the lm_head product (logits = hidden wte^T), swapped
 // layout only.  For every row m and column tile tn it stores the tile's
 // softmax statistics stats[m][tn] = (mx, sum over the tile's columns n < N of
@@ -435,15 +566,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   // last step: the bounds-checked, zero-filling copy
   std::conditional_t<A_K, RowsDma<BM, BK, NW>, KrDma<BM, BK, NW>> dma_a;
   std::conditional_t<B_K, RowsDma<BN, BK, NW>, KrDma<BN, BK, NW>> dma_b;
+  // SWIGLU reads B's rows interleaved (64-column group g: gate rows g/2 ..
+  // g/2+31, then the up rows F + g/2 ..), from absolute row offsets
+  constexpr bool MAP_B = EPI == GPT2_EPI_SWIGLU;
+  static_assert(!MAP_B || (B_K && SWAP && WN == 64), "SwiGLU: K-major B, swapped layout, 64 columns per wave");
+  const int b_row0 = MAP_B ? 0 : n0;
   dma_a.init(p.lda, m0, p.M);
-  dma_b.init(p.ldb, n0, p.N);
+  if constexpr (MAP_B) dma_b.init_swiglu(p.ldb, n0, p.N);
+  else dma_b.init(p.ldb, n0, p.N);
   auto issue = [&](int stage, int kstep) {
     bf16* as = smem + stage * STAGE;
     bf16* bs = as + BM * BK;
     const int k0 = kbeg + kstep * BK;
-    if (k0 + BK <= kend) {
+    if (MAP_B || k0 + BK <= kend) {  // SWIGLU: K % BK == 0, checked by the host
       dma_a.issue(as, Ag, p.lda, m0, k0);
-      dma_b.issue(bs, Bg, p.ldb, n0, k0);
+      dma_b.issue(bs, Bg, p.ldb, b_row0, k0);
     } else {
       if constexpr (A_K) dma_rows<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
       else dma_kr<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
@@ -574,6 +711,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
     else
       epi_ce_stats<BM, BN, WGN, TM, TN, true>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
                                               reinterpret_cast<char*>(smem));
+  } else if constexpr (EPI == GPT2_EPI_ROPE || EPI == GPT2_EPI_SWIGLU) {
+    static_assert(SWAP && WN == 64, "paired epilogues: swapped layout, 64 columns per wave");
+    if (interior) epi_tile_pair<EPI, TM, false>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
+    else epi_tile_pair<EPI, TM, true>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
+  } else if constexpr (EPI == GPT2_EPI_SWIGLU_BWD) {
+    static_assert(SWAP, "SwiGLU backward: swapped layout");
+    if (interior) epi_tile_swiglu_bwd<TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    else epi_tile_swiglu_bwd<TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
   } else {
     if constexpr (PRE_U) {
       if (interior) epi_tile_mul_pre<TM, TN, TMP>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc, upre);

@@ -11,6 +11,7 @@ namespace g2 {
 
 constexpr int LN_MAXV = 16;  // supports C <= 1024
 constexpr float LN_EPS = 1e-5f;
+constexpr float RMS_EPS = 1.1920928955078125e-07f;  // float32 machine epsilon, 2^-23
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -146,7 +147,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const DYT* __restrict__ dy,
 // load and store is 16 bytes (8 for bf16) per lane and a wave's access to a
 // row is contiguous.
 
-template <int NQ>
+// RMS: the RMSNorm of the rotary variant ("Reproduce GPT-2 124M", nn.RMSNorm
+// with its defaults): no centring, no bias, eps = float32 machine epsilon;
+// mean is not written.
+template <int NQ, bool RMS>
 __global__ __launch_bounds__(256) void ln_fwd_vec_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                          const float* __restrict__ b, bf16* __restrict__ y,
                                                          float* __restrict__ mean, float* __restrict__ rstd,
@@ -158,23 +162,26 @@ __global__ __launch_bounds__(256) void ln_fwd_vec_kernel(const float* __restrict
   float4 v[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) v[q] = *reinterpret_cast<const float4*>(xr + 256 * q);
-  float s = 0.f;
+  float mu = 0.f;
+  if constexpr (!RMS) {
+    float s = 0.f;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
-  const float mu = wave_sum(s) / C;
+    for (int q = 0; q < NQ; ++q) s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
+    mu = wave_sum(s) / C;
+  }
   float ss = 0.f;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const float a = v[q].x - mu, bb = v[q].y - mu, c = v[q].z - mu, d = v[q].w - mu;
     ss += (a * a + bb * bb) + (c * c + d * d);
   }
-  const float rs = rsqrtf(wave_sum(ss) / C + LN_EPS);
+  const float rs = rsqrtf(wave_sum(ss) / C + (RMS ? RMS_EPS : LN_EPS));
   bf16* yr = y + (int64_t)row * C + 4 * lane;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int c = 4 * lane + 256 * q;
     const float4 ww = *reinterpret_cast<const float4*>(w + c);
-    const float4 bv = *reinterpret_cast<const float4*>(b + c);
+    const float4 bv = RMS ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(b + c);
     bf16x4 o;
     o[0] = f2bf((v[q].x - mu) * rs * ww.x + bv.x);
     o[1] = f2bf((v[q].y - mu) * rs * ww.y + bv.y);
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(256) void ln_fwd_vec_kernel(const float* __restrict
     *reinterpret_cast<bf16x4*>(yr + 256 * q) = o;
   }
   if (lane == 0) {
-    mean[row] = mu;
+    if constexpr (!RMS) mean[row] = mu;
     rstd[row] = rs;
   }
 }
@@ -202,8 +209,9 @@ __device__ __forceinline__ float4 load4<bf16>(const bf16* p) {
 
 // Backward over RPW consecutive rows per wave; the next row's dy, x and dR
 // are loaded before the current row is reduced, so each wave keeps two
-// rows of loads in flight.  dy is float32 or bf16.
-template <typename DYT, int NQ, int RPW>
+// rows of loads in flight.  dy is float32 or bf16.  RMS: the RMSNorm
+// backward, dx = rstd (g - xhat mean(g xhat)) (no centring term), no db.
+template <typename DYT, int NQ, int RPW, bool RMS>
 __global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__ dy, const float* __restrict__ x,
                                                          const float* __restrict__ mean,
                                                          const float* __restrict__ rstd,
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__
       x_[q] = *reinterpret_cast<const float4*>(x + o + 256 * q);
       r_[q] = *reinterpret_cast<const float4*>(dR + o + 256 * q);
     }
-    mu_ = mean[row];
+    mu_ = RMS ? 0.f : mean[row];
     rs_ = rstd[row];
   };
   if (nrows > 0) load(row0, d, xv, r, mu, rs);
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__
       sg += (g[q].x + g[q].y) + (g[q].z + g[q].w);
       sgx += (g[q].x * xv[q].x + g[q].y * xv[q].y) + (g[q].z * xv[q].z + g[q].w * xv[q].w);
     }
-    sg = wave_sum(sg) / C;
+    sg = RMS ? 0.f : wave_sum(sg) / C;
     sgx = wave_sum(sgx) / C;
     const int64_t o = (int64_t)row * C + 4 * lane;
 #pragma unroll
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__
   for (int q = 0; q < NQ; ++q) {
     const int c = threadIdx.x + 256 * q;
     unsafeAtomicAdd(dw + c, (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]));
-    unsafeAtomicAdd(db + c, (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]));
+    if constexpr (!RMS) unsafeAtomicAdd(db + c, (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]));
   }
 }
 
@@ -303,10 +311,10 @@ hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w,
   bf16* yb = static_cast<bf16*>(y);
   if (y_bf16 && C % 256 == 0) {
     switch (C / 256) {
-      case 1: ln_fwd_vec_kernel<1><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
-      case 2: ln_fwd_vec_kernel<2><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
-      case 3: ln_fwd_vec_kernel<3><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
-      default: ln_fwd_vec_kernel<4><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      case 1: ln_fwd_vec_kernel<1, false><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      case 2: ln_fwd_vec_kernel<2, false><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      case 3: ln_fwd_vec_kernel<3, false><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
+      default: ln_fwd_vec_kernel<4, false><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C); break;
     }
   } else if (y_bf16) {
     ln_fwd_kernel<bf16><<<grid, block, 0, L.stream>>>(x, w, b, yb, mean, rstd, rows, C);
@@ -317,7 +325,7 @@ hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w,
   return hipGetLastError();
 }
 
-template <typename DYT>
+template <typename DYT, bool RMS>
 static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const float* mean, const float* rstd,
                             const float* w, float* dx, bf16* dxb, float* dw, float* db, int rows, int C) {
   if (C % 256 == 0) {
@@ -326,12 +334,12 @@ static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const
     constexpr int RPW = 16;
     const dim3 grid((rows + 4 * RPW - 1) / (4 * RPW));
     switch (C / 256) {
-      case 1: ln_bwd_vec_kernel<DYT, 1, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      case 2: ln_bwd_vec_kernel<DYT, 2, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      case 3: ln_bwd_vec_kernel<DYT, 3, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      default: ln_bwd_vec_kernel<DYT, 4, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      default: ln_bwd_vec_kernel<DYT, 4, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
     }
-  } else {
+  } else if constexpr (!RMS) {
     constexpr int RPW = 4;
     const dim3 grid((rows + 4 * RPW - 1) / (4 * RPW));
     ln_bwd_kernel<DYT, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C);
@@ -343,9 +351,39 @@ hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, 
                                   int rows, int C) {
   prof_begin(L);
   if (dy_bf16)
-    ln_bwd_dispatch<bf16>(L.stream, static_cast<const bf16*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+    ln_bwd_dispatch<bf16, false>(L.stream, static_cast<const bf16*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows, C);
   else
-    ln_bwd_dispatch<float>(L.stream, static_cast<const float*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+    ln_bwd_dispatch<float, false>(L.stream, static_cast<const float*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows,
+                                  C);
+  prof_end(L);
+  return hipGetLastError();
+}
+
+// RMSNorm (C % 256 == 0): y bf16, rstd float32 per row.
+hipError_t launch_rmsnorm_fwd(const Launch& L, const float* x, const float* w, bf16* y, float* rstd, int rows, int C) {
+  if (C % 256 != 0 || C > 1024) return hipErrorInvalidValue;
+  dim3 grid((rows + 3) / 4), block(256);
+  prof_begin(L);
+  switch (C / 256) {
+    case 1: ln_fwd_vec_kernel<1, true><<<grid, block, 0, L.stream>>>(x, w, nullptr, y, nullptr, rstd, rows, C); break;
+    case 2: ln_fwd_vec_kernel<2, true><<<grid, block, 0, L.stream>>>(x, w, nullptr, y, nullptr, rstd, rows, C); break;
+    case 3: ln_fwd_vec_kernel<3, true><<<grid, block, 0, L.stream>>>(x, w, nullptr, y, nullptr, rstd, rows, C); break;
+    default: ln_fwd_vec_kernel<4, true><<<grid, block, 0, L.stream>>>(x, w, nullptr, y, nullptr, rstd, rows, C); break;
+  }
+  prof_end(L);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* rstd,
+                              const float* w, float* dx, bf16* dxb, float* dw, int rows, int C) {
+  if (C % 256 != 0 || C > 1024) return hipErrorInvalidValue;
+  prof_begin(L);
+  if (dy_bf16)
+    ln_bwd_dispatch<bf16, true>(L.stream, static_cast<const bf16*>(dy), x, nullptr, rstd, w, dx, dxb, dw, nullptr,
+                                rows, C);
+  else
+    ln_bwd_dispatch<float, true>(L.stream, static_cast<const float*>(dy), x, nullptr, rstd, w, dx, dxb, dw, nullptr,
+                                 rows, C);
   prof_end(L);
   return hipGetLastError();
 }

@@ -145,6 +145,12 @@ bool check_config(const gpt2_config* c) {
     if (hd > 64) return false;
   }
   if ((int64_t)c->max_batch * c->block_size > (1 << 30) / 4) return false;
+  if (c->arch != GPT2_ARCH_GPT2 && c->arch != GPT2_ARCH_ROTARY) return false;
+  if (c->arch == GPT2_ARCH_ROTARY) {
+    // bf16 kernels only: vector RMSNorm (C % 256), paired rotary / SwiGLU
+    // epilogues (heads of 64, hidden width % 32)
+    if (c->precision != GPT2_PRECISION_BF16 || c->n_embd % 256 || c->mlp_hidden % 32) return false;
+  }
   return true;
 }
 
@@ -162,9 +168,22 @@ Table build_table(const gpt2_config& c) {
     x.offset = 0;
     hf.push_back(x);
   };
+  const bool rotary = c.arch == GPT2_ARCH_ROTARY;
   add("transformer.wte.weight", 2, V, C);
-  add("transformer.wpe.weight", 2, T, C);
-  for (int l = 0; l < L; ++l) {
+  if (rotary) {
+    for (int l = 0; l < L; ++l) {
+      const std::string p = "transformer.h." + std::to_string(l) + ".";
+      add(p + "ln_1.weight", 1, C, 1);
+      add(p + "attn.c_attn.weight", 2, 3 * C, C);
+      add(p + "attn.c_proj.weight", 2, C, C);
+      add(p + "ln_2.weight", 1, C, 1);
+      add(p + "mlp.c_fc.weight", 2, 2 * F, C);
+      add(p + "mlp.c_proj.weight", 2, C, F);
+    }
+    add("transformer.ln_f.weight", 1, C, 1);
+  }
+  if (!rotary) add("transformer.wpe.weight", 2, T, C);
+  for (int l = 0; !rotary && l < L; ++l) {
     const std::string p = "transformer.h." + std::to_string(l) + ".";
     add(p + "ln_1.weight", 1, C, 1);
     add(p + "ln_1.bias", 1, C, 1);
@@ -179,8 +198,10 @@ Table build_table(const gpt2_config& c) {
     add(p + "mlp.c_proj.weight", 2, C, F);
     add(p + "mlp.c_proj.bias", 1, C, 1);
   }
-  add("transformer.ln_f.weight", 1, C, 1);
-  add("transformer.ln_f.bias", 1, C, 1);
+  if (!rotary) {
+    add("transformer.ln_f.weight", 1, C, 1);
+    add("transformer.ln_f.bias", 1, C, 1);
+  }
 
   Table t;
   // decayed (dim >= 2) tensors first, each group in the page's order
@@ -230,7 +251,7 @@ struct Layout {
   size_t Z = 0, meanf = 0, rstdf = 0, act_bytes = 0;
   // scratch
   size_t dR = 0, dRb = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
-  size_t ce_stats = 0;
+  size_t ce_stats = 0, rope = 0;
   size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, scratch_bytes = 0;
 };
 
@@ -249,6 +270,9 @@ Layout build_layout(const gpt2_config& c) {
   const size_t rows = (size_t)c.max_batch * c.block_size;
   const size_t C = c.n_embd, F = c.mlp_hidden, H = c.n_head, V = c.vocab_size;
   const int L = c.n_layer;
+  // U / dU: gelu'(u) [rows, F] for GPT-2; [gate | up] [rows, 2F] for the
+  // rotary variant (G then holds silu(gate) up)
+  const size_t FU = c.arch == GPT2_ARCH_ROTARY ? 2 * F : F;
   y.rows = (int)rows;
   y.es = c.precision == GPT2_PRECISION_BF16 ? 2 : 4;
   y.chunk = (int)std::min<size_t>(rows, kCeChunk);
@@ -265,7 +289,7 @@ Layout build_layout(const gpt2_config& c) {
     y.A2.push_back(a.take(rows * C * y.es));
     y.mean2.push_back(a.take(rows * 4));
     y.rstd2.push_back(a.take(rows * 4));
-    y.U.push_back(a.take(rows * F * y.es));
+    y.U.push_back(a.take(rows * FU * y.es));
     y.G.push_back(a.take(rows * F * y.es));
   }
   y.Z = a.take(rows * C * y.es);
@@ -284,8 +308,9 @@ Layout build_layout(const gpt2_config& c) {
   y.dA = s.take(rows * C * 4);
   y.dQKV = s.take(rows * 3 * C * y.es);
   y.dY = s.take(rows * C * y.es);
-  y.dU = s.take(rows * F * y.es);
+  y.dU = s.take(rows * FU * y.es);
   y.attnD = s.take(rows * H * 4);
+  if (c.arch == GPT2_ARCH_ROTARY) y.rope = s.take((size_t)c.block_size * 32 * sizeof(float2));
   if (c.precision == GPT2_PRECISION_BF16) {
     // fused lm_head + cross-entropy over all rows at once: bf16 logits (then
     // dlogits, in place) and per-tile softmax statistics
@@ -384,10 +409,48 @@ static hipError_t linear_dw(gpt2_ctx* c, const char* site, const void* dy, int M
   a.lda = N; a.ldb = K; a.ldc = K;
   a.A = dy; a.B = x; a.C = c->Gr(wi);
   a.epilogue = GPT2_EPI_ACCUMULATE;
-  if (c->bf()) return launch_gemm(c->at(site), a, c->Gr(bi));
+  if (c->bf()) return launch_gemm(c->at(site), a, bi >= 0 ? c->Gr(bi) : nullptr);
   hipError_t e = launch_gemm(c->at(site), a);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || bi < 0) return e;
   return launch_colsum(c->at("colsum"), dy_f32, 0, M, N, N, c->Gr(bi));
+}
+
+// Tied lm_head + cross-entropy, bf16, all rows at once: the statistics
+// product (logit offsets + per-tile softmax statistics), the row pass that
+// turns them into the row losses and dlogits in place, then dZ += dlogits
+// wte and dwte += dlogits^T Z.  dZ must hold zeros (float32 [M, C]).
+static hipError_t lmhead_ce_bf16(gpt2_ctx* c, const int32_t* tgt, int M, const int* count, float scale,
+                                 float* rowloss, float* dZ) {
+  const Layout& y = c->lay;
+  const int C = c->cfg.n_embd, V = c->cfg.vocab_size, dt = c->cfg.precision;
+  bf16* dlog = c->scr<bf16>(y.dlogits);
+  float2* stats = c->scr<float2>(y.ce_stats);
+  const bf16* Zb = c->act<bf16>(y.Z);
+  const bf16* Wb = static_cast<const bf16*>(c->W(c->tab.wte));
+  hipError_t e = launch_gemm_ce_stats(c->at("gemm.lm_head"), Zb, Wb, dlog, stats, M, V, C);
+  if (e != hipSuccess) return e;
+  e = launch_ce_apply(c->at("ce.rows"), dlog, stats, Zb, Wb, tgt, M, V, C, count, scale, rowloss);
+  if (e != hipSuccess) return e;
+  {  // dZ += dlogits wte
+    gpt2_gemm_args a = gemm_base(dt);
+    a.M = M; a.N = C; a.K = V;
+    a.a_kmajor = 1; a.b_kmajor = 0;
+    a.lda = V; a.ldb = C; a.ldc = C;
+    a.A = dlog; a.B = Wb; a.C = dZ;
+    a.epilogue = GPT2_EPI_ACCUMULATE;
+    e = launch_gemm(c->at("gemm.lm_head_dx"), a);
+    if (e != hipSuccess) return e;
+  }
+  {  // dwte += dlogits^T Z
+    gpt2_gemm_args a = gemm_base(dt);
+    a.M = V; a.N = C; a.K = M;
+    a.a_kmajor = 0; a.b_kmajor = 0;
+    a.lda = V; a.ldb = C; a.ldc = C;
+    a.A = dlog; a.B = Zb; a.C = c->Gr(c->tab.wte);
+    a.epilogue = GPT2_EPI_ACCUMULATE;
+    e = launch_gemm(c->at("gemm.lm_head_dw"), a);
+  }
+  return e;
 }
 
 // ------------------------------------------------------------- the step
@@ -434,33 +497,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   float* dZ = c->scr<float>(y.dA);
   HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
   const size_t es = y.es;
-  if (bf) {
-    // all rows at once: statistics-epilogue product, then dlogits in place
-    bf16* dlog = c->scr<bf16>(y.dlogits);
-    float2* stats = c->scr<float2>(y.ce_stats);
-    const bf16* Zb = c->act<bf16>(y.Z);
-    const bf16* Wb = static_cast<const bf16*>(c->W(c->tab.wte));
-    HIP_TRY(launch_gemm_ce_stats(c->at("gemm.lm_head"), Zb, Wb, dlog, stats, M, V, C));
-    HIP_TRY(launch_ce_apply(c->at("ce.rows"), dlog, stats, Zb, Wb, tgt, M, V, C, count, scale, rowloss));
-    {  // dZ += dlogits wte
-      gpt2_gemm_args a = gemm_base(dt);
-      a.M = M; a.N = C; a.K = V;
-      a.a_kmajor = 1; a.b_kmajor = 0;
-      a.lda = V; a.ldb = C; a.ldc = C;
-      a.A = dlog; a.B = Wb; a.C = dZ;
-      a.epilogue = GPT2_EPI_ACCUMULATE;
-      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dx"), a));
-    }
-    {  // dwte += dlogits^T Z
-      gpt2_gemm_args a = gemm_base(dt);
-      a.M = V; a.N = C; a.K = M;
-      a.a_kmajor = 0; a.b_kmajor = 0;
-      a.lda = V; a.ldb = C; a.ldc = C;
-      a.A = dlog; a.B = Zb; a.C = c->Gr(c->tab.wte);
-      a.epilogue = GPT2_EPI_ACCUMULATE;
-      HIP_TRY(launch_gemm(c->at("gemm.lm_head_dw"), a));
-    }
-  }
+  if (bf) HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ));
   for (int r0 = 0; !bf && r0 < M; r0 += y.chunk) {
     const int rows = std::min(y.chunk, M - r0);
     const char* z_c = c->act<char>(y.Z) + (size_t)r0 * C * es;
@@ -537,6 +574,106 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                                    c->Gr(c->L(l, LN1_B)), M, C));
   }
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V));
+  return GPT2_OK;
+}
+
+// The rotary variant ("Reproduce GPT-2 124M 复盘": RMSNorm, rotary q/k,
+// SwiGLU, no position table, no biases), bf16.
+static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int B, int T, float scale, float* loss,
+                          float* token_loss) {
+  const gpt2_config& g = c->cfg;
+  const Layout& y = c->lay;
+  const int M = B * T, C = g.n_embd, F = g.mlp_hidden, V = g.vocab_size, H = g.n_head, hd = C / H;
+  const int dt = g.precision;
+  int* flag = c->flag();
+  int* count = c->scr<int>(y.count);
+  float* rowloss = token_loss ? token_loss : c->scr<float>(y.rowloss);
+  float2* rope = c->scr<float2>(y.rope);
+
+  HIP_TRY(launch_rope_table(c->at("rope.table"), rope, T, 10000.0));
+  HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, count, flag));
+  HIP_TRY(launch_embed_fwd(c->at("embed.fwd"), tok, c->P(c->tab.wte), nullptr, c->act<float>(y.Rin[0]), B, T, C, V,
+                           flag));
+  for (int l = 0; l < g.n_layer; ++l) {
+    float* rin = c->act<float>(y.Rin[l]);
+    float* rmid = c->act<float>(y.Rmid[l]);
+    HIP_TRY(launch_rmsnorm_fwd(c->at("norm.fwd"), rin, c->P(c->L(l, LN1_W)), c->act<bf16>(y.A1[l]),
+                               c->act<float>(y.rstd1[l]), M, C));
+    {  // qkv = a1 Wqkv^T, q and k rotated in the epilogue
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = M; a.N = 3 * C; a.K = C;
+      a.a_kmajor = 1; a.b_kmajor = 1;
+      a.lda = C; a.ldb = C; a.ldc = 3 * C;
+      a.A = c->act(y.A1[l]); a.B = c->W(c->L(l, QKV_W)); a.C = c->act(y.QKV[l]);
+      a.epilogue = GPT2_EPI_ROPE; a.out_bf16 = 1;
+      a.rope = rope; a.rope_period = T; a.rope_cols = 2 * C;
+      HIP_TRY(launch_gemm(c->at("gemm.qkv"), a));
+    }
+    HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
+                                 c->act<float>(y.LSE[l])));
+    HIP_TRY(linear_fwd(c, "gemm.attn_proj", c->act(y.Y[l]), M, C, c->L(l, PROJ_W), C, -1, GPT2_EPI_RESIDUAL, rmid,
+                       nullptr, rin));
+    HIP_TRY(launch_rmsnorm_fwd(c->at("norm.fwd"), rmid, c->P(c->L(l, LN2_W)), c->act<bf16>(y.A2[l]),
+                               c->act<float>(y.rstd2[l]), M, C));
+    {  // act = silu(a2 Wg^T) (a2 Wu^T); gate | up kept for the backward
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = M; a.N = 2 * F; a.K = C;
+      a.a_kmajor = 1; a.b_kmajor = 1;
+      a.lda = C; a.ldb = C; a.ldc = F; a.ld2 = 2 * F;
+      a.A = c->act(y.A2[l]); a.B = c->W(c->L(l, FC_W)); a.C = c->act(y.G[l]); a.C2 = c->act(y.U[l]);
+      a.epilogue = GPT2_EPI_SWIGLU; a.out_bf16 = 1;
+      HIP_TRY(launch_gemm(c->at("gemm.fc"), a));
+    }
+    HIP_TRY(linear_fwd(c, "gemm.mlp_proj", c->act(y.G[l]), M, F, c->L(l, MLP_W), C, -1, GPT2_EPI_RESIDUAL,
+                       c->act<float>(y.Rin[l + 1]), nullptr, rmid));
+  }
+  float* rlast = c->act<float>(y.Rin[g.n_layer]);
+  HIP_TRY(launch_rmsnorm_fwd(c->at("norm.fwd"), rlast, c->P(c->tab.lnf_w), c->act<bf16>(y.Z),
+                             c->act<float>(y.rstdf), M, C));
+
+  float* dZ = c->scr<float>(y.dA);
+  HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
+  HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ));
+  HIP_TRY(launch_ce_finish_n(c->at("ce.finish"), rowloss, M, count, loss, flag));
+
+  // ---- backward
+  float* dR = c->scr<float>(y.dR);
+  bf16* dRb = c->scr<bf16>(y.dRb);
+  void* dA = c->scr(y.dA);  // dZ (float32) first, then bf16 norm-output gradients
+  void* dGU = c->scr(y.dU);
+  void* dY = c->scr(y.dY);
+  bf16* dQKV = c->scr<bf16>(y.dQKV);
+  HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
+  HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dZ, 0, rlast, c->act<float>(y.rstdf), c->P(c->tab.lnf_w), dR, dRb,
+                             c->Gr(c->tab.lnf_w), M, C));
+  for (int l = g.n_layer - 1; l >= 0; --l) {
+    // feed-forward: R_{l+1} = Rmid + act Wd^T
+    HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRb, M, C, c->act(y.G[l]), F, c->L(l, MLP_W), -1, nullptr));
+    {  // d(act) = dR Wd; dgate, dup through the SwiGLU gate
+      gpt2_gemm_args a = gemm_base(dt);
+      a.M = M; a.N = F; a.K = C;
+      a.a_kmajor = 1; a.b_kmajor = 0;
+      a.lda = C; a.ldb = F; a.ldc = 2 * F; a.ld2 = 2 * F;
+      a.A = dRb; a.B = c->W(c->L(l, MLP_W)); a.C = dGU; a.U = c->act(y.U[l]);
+      a.epilogue = GPT2_EPI_SWIGLU_BWD; a.out_bf16 = 1;
+      HIP_TRY(launch_gemm(c->at("gemm.mlp_proj_dx"), a));
+    }
+    HIP_TRY(linear_dw(c, "gemm.fc_dw", dGU, M, 2 * F, c->act(y.A2[l]), C, c->L(l, FC_W), -1, nullptr));
+    HIP_TRY(linear_dx(c, "gemm.fc_dx", dGU, M, 2 * F, c->L(l, FC_W), C, GPT2_EPI_STORE, true, dA, nullptr));
+    HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rmid[l]), c->act<float>(y.rstd2[l]),
+                               c->P(c->L(l, LN2_W)), dR, dRb, c->Gr(c->L(l, LN2_W)), M, C));
+    // attention: Rmid = R_l + Y Wo^T
+    HIP_TRY(linear_dw(c, "gemm.attn_proj_dw", dRb, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1, nullptr));
+    HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRb, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
+    HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
+                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
+    HIP_TRY(launch_rope_bwd(c->at("rope.bwd"), dQKV, M, 3 * C, 2 * C, T, rope));
+    HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), -1, nullptr));
+    HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
+    HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rin[l]), c->act<float>(y.rstd1[l]),
+                               c->P(c->L(l, LN1_W)), dR, dRb, c->Gr(c->L(l, LN1_W)), M, C));
+  }
+  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V));
   return GPT2_OK;
 }
 
@@ -656,6 +793,8 @@ int gpt2_fwd_bwd(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
   if (!c || !d_tokens || !d_targets || !d_loss) return GPT2_ERR_ARG;
   if (B < 1 || B > c->cfg.max_batch || T < 1 || T > c->cfg.block_size) return GPT2_ERR_SHAPE;
   if (!isfinite(loss_scale)) return GPT2_ERR_ARG;
+  if (c->cfg.arch == GPT2_ARCH_ROTARY)
+    return fwd_bwd_rotary(c, d_tokens, d_targets, B, T, loss_scale, d_loss, d_token_loss);
   return fwd_bwd_impl(c, d_tokens, d_targets, B, T, loss_scale, d_loss, d_token_loss);
 }
 
@@ -778,7 +917,24 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
   if (!a || !a->A || !a->B || !a->C) return false;
   if (a->M < 1 || a->N < 1 || a->K < 1) return false;
   if (a->dtype != GPT2_PRECISION_BF16 && a->dtype != GPT2_PRECISION_FP32) return false;
-  if (a->epilogue < GPT2_EPI_STORE || a->epilogue > GPT2_EPI_MUL) return false;
+  if (a->epilogue < GPT2_EPI_STORE || a->epilogue > GPT2_EPI_SWIGLU_BWD) return false;
+  const bool rotary_family = a->epilogue >= GPT2_EPI_ROPE;
+  if (rotary_family) {
+    if (a->dtype != GPT2_PRECISION_BF16 || !a->out_bf16) return false;
+    if (a->epilogue == GPT2_EPI_ROPE) {
+      if (!a->a_kmajor || !a->b_kmajor || a->N % 64 || a->rope_cols % 64 || a->rope_cols < 0 ||
+          (a->rope_cols > 0 && (!a->rope || a->rope_period < 1)))
+        return false;
+      if ((uintptr_t)a->rope & 15) return false;
+    } else if (a->epilogue == GPT2_EPI_SWIGLU) {
+      if (!a->a_kmajor || !a->b_kmajor || a->N % 64 || a->K % 64 || !a->C2 || a->bias) return false;
+      if (a->ld2 < a->N || a->ld2 % 8 || a->ldc < a->N / 2) return false;
+      if ((int64_t)a->N * a->ldb * 2 >= ((int64_t)1 << 32)) return false;  // 32-bit row offsets of B
+    } else {  // SWIGLU_BWD
+      if (!a->a_kmajor || a->b_kmajor || a->N % 8 || !a->U || a->bias) return false;
+      if (a->ld2 < 2 * (int64_t)a->N || a->ld2 % 8 || a->ldc < 2 * (int64_t)a->N) return false;
+    }
+  }
   if (a->epilogue == GPT2_EPI_GELU_GRAD && !a->C2) return false;
   if (a->epilogue == GPT2_EPI_MUL && !a->U) return false;
   if (a->epilogue == GPT2_EPI_RESIDUAL && !a->R) return false;
@@ -787,7 +943,8 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
   if (a->epilogue == GPT2_EPI_ACCUMULATE && a->bias) return false;
   const int64_t need_a = a->a_kmajor ? a->K : a->M;
   const int64_t need_b = a->b_kmajor ? a->K : a->N;
-  if (a->lda < need_a || a->ldb < need_b || a->ldc < a->N) return false;
+  const int64_t need_c = a->epilogue == GPT2_EPI_SWIGLU ? a->N / 2 : (a->epilogue == GPT2_EPI_SWIGLU_BWD ? 2 * (int64_t)a->N : a->N);
+  if (a->lda < need_a || a->ldb < need_b || a->ldc < need_c) return false;
   if (a->dtype == GPT2_PRECISION_BF16) {
     if (a->M % 8 && !a->a_kmajor) return false;
     if (a->N % 8 && !a->b_kmajor) return false;
@@ -798,7 +955,7 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
       return false;
     // the output dtype each epilogue writes in bf16 mode
     const bool bf_out = a->epilogue == GPT2_EPI_GELU || a->epilogue == GPT2_EPI_DGELU ||
-                        a->epilogue == GPT2_EPI_GELU_GRAD || a->epilogue == GPT2_EPI_MUL;
+                        a->epilogue == GPT2_EPI_GELU_GRAD || a->epilogue == GPT2_EPI_MUL || rotary_family;
     const bool f32_out = a->epilogue == GPT2_EPI_RESIDUAL || a->epilogue == GPT2_EPI_ACCUMULATE;
     if ((bf_out && !a->out_bf16) || (f32_out && a->out_bf16)) return false;
   }
@@ -839,6 +996,44 @@ int gpt2_op_layernorm_bwd(void* stream, const void* d_dy, int dy_bf16, const flo
     return GPT2_ERR_ARG;
   HIP_TRY(launch_layernorm_bwd_b(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_dy, dy_bf16 != 0, d_x,
                                  d_mean, d_rstd, d_w, d_dx, static_cast<bf16*>(d_dx_bf16), d_dw, d_db, rows, C));
+  return GPT2_OK;
+}
+
+int gpt2_op_rmsnorm_fwd(void* stream, const float* d_x, const float* d_w, void* d_y, float* d_rstd, int rows, int C) {
+  if (!d_x || !d_w || !d_y || !d_rstd) return GPT2_ERR_ARG;
+  if (rows < 1 || C < 256 || C > 1024 || C % 256) return GPT2_ERR_SHAPE;
+  if (((uintptr_t)d_x | (uintptr_t)d_w | (uintptr_t)d_y) & 15) return GPT2_ERR_ARG;
+  HIP_TRY(launch_rmsnorm_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_x, d_w, static_cast<bf16*>(d_y),
+                             d_rstd, rows, C));
+  return GPT2_OK;
+}
+
+int gpt2_op_rmsnorm_bwd(void* stream, const void* d_dy, int dy_bf16, const float* d_x, const float* d_rstd,
+                        const float* d_w, float* d_dx, void* d_dx_bf16, float* d_dw, int rows, int C) {
+  if (!d_dy || !d_x || !d_rstd || !d_w || !d_dx || !d_dw) return GPT2_ERR_ARG;
+  if (rows < 1 || C < 256 || C > 1024 || C % 256) return GPT2_ERR_SHAPE;
+  if (((uintptr_t)d_dy | (uintptr_t)d_x | (uintptr_t)d_w | (uintptr_t)d_dx | (uintptr_t)d_dx_bf16 |
+       (uintptr_t)d_dw) & 15)
+    return GPT2_ERR_ARG;
+  HIP_TRY(launch_rmsnorm_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_dy, dy_bf16 != 0, d_x, d_rstd,
+                             d_w, d_dx, static_cast<bf16*>(d_dx_bf16), d_dw, rows, C));
+  return GPT2_OK;
+}
+
+int gpt2_op_rope_table(void* stream, int T, double base, float* d_table) {
+  if (!d_table || !(base > 0.0)) return GPT2_ERR_ARG;
+  if (T < 1) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_rope_table(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, reinterpret_cast<float2*>(d_table),
+                            T, base));
+  return GPT2_OK;
+}
+
+int gpt2_op_rope_bwd(void* stream, void* d_dqkv, int rows, int64_t ld, int cols, int T, const float* d_table) {
+  if (!d_dqkv || !d_table) return GPT2_ERR_ARG;
+  if (rows < 1 || T < 1 || cols < 64 || cols % 64 || ld < cols || ld % 4) return GPT2_ERR_SHAPE;
+  if (((uintptr_t)d_dqkv & 7) || ((uintptr_t)d_table & 7)) return GPT2_ERR_ARG;
+  HIP_TRY(launch_rope_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, static_cast<bf16*>(d_dqkv), rows, ld,
+                          cols, T, reinterpret_cast<const float2*>(d_table)));
   return GPT2_OK;
 }
 

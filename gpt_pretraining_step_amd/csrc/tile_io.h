@@ -129,6 +129,25 @@ struct RowsDma {
       off[i] = (uint32_t)(((int64_t)min(r, last) * ld + 8 * c) * 2);
     }
   }
+  // The SwiGLU row map: tile row r stands for virtual column v = row0 + r
+  // of a product whose 64-column groups pair gate and up rows of a stacked
+  // [2F][ld] matrix (F = nvirt / 2): v = 64 b + w reads row 32 b + w for
+  // w < 32 and F + 32 b + w - 32 otherwise.  Offsets are absolute (issue
+  // with row0 = 0); rows past nvirt are clamped to the last one.
+  __device__ __forceinline__ void init_swiglu(int64_t ld, int row0, int nvirt) {
+    const int lane = threadIdx.x & 63;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    const int F = nvirt >> 1;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (ins0 + i) * RPI + lane / CPR;
+      const int c = swz_chunk<BK>(r, lane % CPR);
+      const int v = min(row0 + r, nvirt - 1);
+      const int w = v & 63, f = ((v >> 6) << 5) + (w & 31);
+      const int row = w < 32 ? f : F + f;
+      off[i] = (uint32_t)(((int64_t)row * ld + 8 * c) * 2);
+    }
+  }
   __device__ __forceinline__ void issue(bf16* lds, const bf16* src, int64_t ld, int row0, int k0) const {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)row0 * ld + k0);
 #pragma unroll

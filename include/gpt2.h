@@ -50,6 +50,7 @@ typedef enum {
 } gpt2_status;
 
 enum { GPT2_PRECISION_FP32 = 0, GPT2_PRECISION_BF16 = 1 };
+enum { GPT2_ARCH_GPT2 = 0, GPT2_ARCH_ROTARY = 1 };
 
 /* Model and capacity.  GPT2Config of "How I trained my own GPT-2 124M on
  * FineWeb-Edu" section 2.1 plus the MLP width (section 2.6, 4 * n_embd for
@@ -63,7 +64,23 @@ enum { GPT2_PRECISION_FP32 = 0, GPT2_PRECISION_BF16 = 1 };
  * Limits: n_embd % n_head == 0; head_dim = n_embd / n_head must be 64 in
  * BF16 mode and at most 64 in FP32 mode; in BF16 mode vocab_size, n_embd and
  * mlp_hidden must be multiples of 8 (the page pads the vocabulary to 50304
- * for the same alignment reason, section 8.3). */
+ * for the same alignment reason, section 8.3).
+ * arch selects the model family:
+ *   GPT2_ARCH_GPT2:   the GPT-2 model above (LayerNorm, learned positions,
+ *                     GELU MLP of width mlp_hidden, biases).
+ *   GPT2_ARCH_ROTARY: the modern variant of "Reproduce GPT-2 124M 复盘"
+ *                     (its model listing and training improvements): no
+ *                     position table, RMSNorm (weight only, eps = float32
+ *                     machine epsilon) for the block norms and ln_f, rotary
+ *                     embedding (base 10000, rotate_half form) on q and k,
+ *                     a SwiGLU feed-forward silu(x W_gate^T) * (x W_up^T)
+ *                     W_down^T of hidden width mlp_hidden, no biases, lm_head
+ *                     tied to wte.  BF16 only; n_embd % 256 == 0, head_dim
+ *                     64, mlp_hidden % 32 == 0.  Its table: wte, per layer
+ *                     ln_1.weight, attn.c_attn.weight [3C, C],
+ *                     attn.c_proj.weight, ln_2.weight, mlp.c_fc.weight
+ *                     [2F, C] (rows 0..F-1 W_gate, F..2F-1 W_up),
+ *                     mlp.c_proj.weight [C, F], then ln_f.weight. */
 typedef struct {
   int32_t vocab_size;
   int32_t block_size;
@@ -73,6 +90,7 @@ typedef struct {
   int32_t mlp_hidden;
   int32_t max_batch;
   int32_t precision;
+  int32_t arch;
 } gpt2_config;
 
 /* Byte sizes of the caller-owned buffers. */
@@ -247,13 +265,31 @@ int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, con
  *   GPT2_EPI_GELU_GRAD:  u = v rounded to the out dtype; C[m][n] = gelu_tanh(u),
  *                        C2[m][n] = gelu_tanh'(u)            (both out dtype)
  *   GPT2_EPI_MUL:        C[m][n] = v * U[m][n]               (U in out dtype)
+ * The rotary variant ("Reproduce GPT-2 124M": RoPE in the rotate_half form,
+ * SwiGLU), bf16 only, A and B K-major unless noted, 256-wide block tiles:
+ *   GPT2_EPI_ROPE:       C = v in bf16, except that in every 64-column head
+ *                        below rope_cols, with t = m % rope_period and
+ *                        (c, s) = rope[t][i]: C[m][h+i] = v[h+i] c - v[h+i+32] s,
+ *                        C[m][h+i+32] = v[h+i+32] c + v[h+i] s (i < 32).
+ *                        N and rope_cols multiples of 64.
+ *   GPT2_EPI_SWIGLU:     B is the stacked [W_gate; W_up] ([2F][ldb], N = 2F,
+ *                        F % 32 == 0, K % 64 == 0, no bias); with
+ *                        g = bf16(v[m][f]), u = bf16(v[m][F+f]):
+ *                        C[m][f] = bf16(silu(g) u) (ldc), C2[m][f] = g and
+ *                        C2[m][F+f] = u (row pitch ld2 >= 2F).
+ *   GPT2_EPI_SWIGLU_BWD: A K-major, B not (a Linear's input gradient); N = F,
+ *                        U holds [gate | up] (row pitch ld2), v is d(act):
+ *                        C[m][f] = v u silu'(g), C[m][F+f] = v silu(g)
+ *                        (bf16, ldc >= 2F).  silu(g) = g sigmoid(g).
  * ("How I trained my own GPT-2 124M on FineWeb-Edu" 2.13 for the tanh GELU;
  * its derivative by the chain rule.)  GELU_GRAD feeds the MLP's second
  * product with gelu(u) and keeps gelu'(u) so that the backward's input
  * gradient is a MUL epilogue.
- * ldc is the row pitch of C, C2, R and U.  For bf16, M, N, K, lda, ldb, ldc
- * must be multiples of 8, every pointer 16-byte aligned, and out_bf16 must
- * be 1 for GELU, DGELU, GELU_GRAD and MUL and 0 for RESIDUAL and ACCUMULATE. */
+ * ldc is the row pitch of C, C2, R and U (but see ld2).  For bf16, M, N, K,
+ * lda, ldb, ldc must be multiples of 8, every pointer 16-byte aligned, and
+ * out_bf16 must be 1 for GELU, DGELU, GELU_GRAD, MUL, ROPE, SWIGLU and
+ * SWIGLU_BWD and 0 for RESIDUAL and ACCUMULATE.  The three rotary-variant
+ * epilogues exist in bf16 only. */
 enum {
   GPT2_EPI_STORE = 0,
   GPT2_EPI_RESIDUAL = 1,
@@ -261,7 +297,10 @@ enum {
   GPT2_EPI_DGELU = 3,
   GPT2_EPI_ACCUMULATE = 4,
   GPT2_EPI_GELU_GRAD = 5,
-  GPT2_EPI_MUL = 6
+  GPT2_EPI_MUL = 6,
+  GPT2_EPI_ROPE = 7,
+  GPT2_EPI_SWIGLU = 8,
+  GPT2_EPI_SWIGLU_BWD = 9
 };
 typedef struct {
   int32_t M, N, K;
@@ -278,6 +317,13 @@ typedef struct {
   float alpha;
   int32_t epilogue;
   int32_t out_bf16;
+  /* GPT2_EPI_ROPE: (cos, sin) float32 pairs [rope_period][32] (see
+   * gpt2_op_rope_table); row m is at position m % rope_period; columns
+   * below rope_cols are rotated. */
+  const void* rope;
+  int32_t rope_period, rope_cols;
+  /* GPT2_EPI_SWIGLU: row pitch of C2; GPT2_EPI_SWIGLU_BWD: row pitch of U. */
+  int64_t ld2;
 } gpt2_gemm_args;
 int gpt2_op_gemm(void* stream, const gpt2_gemm_args* args);
 
@@ -299,6 +345,27 @@ int gpt2_op_layernorm_fwd(void* stream, const float* d_x, const float* d_w, cons
 int gpt2_op_layernorm_bwd(void* stream, const void* d_dy, int dy_bf16, const float* d_x, const float* d_mean,
                           const float* d_rstd, const float* d_w, float* d_dx, void* d_dx_bf16, float* d_dw,
                           float* d_db, int rows, int C);
+
+/* RMSNorm of the rotary variant: y = x rstd w (bf16), rstd = (mean(x^2) +
+ * eps)^-1/2 per row (float32), eps = 2^-23.  C % 256 == 0, C <= 1024,
+ * pointers 16-byte aligned. */
+int gpt2_op_rmsnorm_fwd(void* stream, const float* d_x, const float* d_w, void* d_y, float* d_rstd, int rows, int C);
+/* Its backward for dy float32 or bf16 (dy_bf16): dx (float32) += rstd (g -
+ * xhat mean(g xhat)) with g = dy w and xhat = x rstd; d_dx_bf16 (nullable)
+ * receives bf16 of the updated dx; dw += sum over rows of dy xhat. */
+int gpt2_op_rmsnorm_bwd(void* stream, const void* d_dy, int dy_bf16, const float* d_x, const float* d_rstd,
+                        const float* d_w, float* d_dx, void* d_dx_bf16, float* d_dw, int rows, int C);
+
+/* Rotary embedding, head dimension 64 ("Reproduce GPT-2 124M 复盘": x cos +
+ * rotate_half(x) sin, dimension i paired with i + 32):
+ * gpt2_op_rope_table writes (cos, sin) of t base^(-2i/64) as float32 pairs
+ * [T][32] (angles in double precision); gpt2_op_rope_bwd applies, in place,
+ * the transpose of the rotation to the first `cols` columns (q and k, heads
+ * of 64) of the bf16 matrix d_dqkv [rows][ld], row r at position r % T:
+ * z_i' = z_i c + z_{i+32} s, z_{i+32}' = z_{i+32} c - z_i s.
+ * cols % 64 == 0, ld % 4 == 0, d_dqkv 8-byte aligned. */
+int gpt2_op_rope_table(void* stream, int T, double base, float* d_table);
+int gpt2_op_rope_bwd(void* stream, void* d_dqkv, int rows, int64_t ld, int cols, int T, const float* d_table);
 
 /* Causal multi-head attention ("How I trained my own GPT-2 124M on
  * FineWeb-Edu" sections 2.12 and 5): qkv [B*T, 3*H*hd] holds q | k | v column

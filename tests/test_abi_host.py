@@ -44,10 +44,35 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header_sizes():
     from gpt_pretraining_step_amd import _ffi
-    assert ct.sizeof(_ffi.Config) == 8 * 4
+    assert ct.sizeof(_ffi.Config) == 9 * 4
     assert ct.sizeof(_ffi.AdamW) == 6 * 4
     assert ct.sizeof(_ffi.Buffers) == 7 * 8
     assert ct.sizeof(_ffi.ParamDesc) == 64 + 8 + 4 + 8 + 4
+
+
+def test_rotary_param_table_matches_oracle_specs():
+    """The rotary variant's table: the oracle's names and shapes, decayed 2-D
+    tensors first, 123,587,328 parameters at the full size; configurations
+    the kernels do not cover are rejected."""
+    _lib()
+    import gpt_pretraining_step_amd as g
+    from oracle import modern as MM
+    for cfg in (g.GPT2_ROTARY_124M,
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY)):
+        oc = MM.ModernConfig(cfg.vocab_size, cfg.block_size, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.mlp_hidden)
+        table = g.param_table(cfg)
+        assert {n: tuple(s) for n, _, s, _ in table} == dict(MM.param_specs(oc))
+        decayed = [d for _, _, _, d in table]
+        assert decayed == sorted(decayed, reverse=True)
+        assert all(d == (len(s) == 2) for _, _, s, d in table)
+        assert g.query_sizes(cfg).n_params == MM.n_params(oc)
+    assert g.query_sizes(g.GPT2_ROTARY_124M).n_params == 123_587_328
+    for bad in (g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_FP32, g.ARCH_ROTARY),  # bf16 only
+                g.ModelConfig(1024, 256, 2, 2, 128, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY),   # C % 256
+                g.ModelConfig(1024, 256, 2, 4, 256, 150, 3, g.PRECISION_BF16, g.ARCH_ROTARY),   # F % 32
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, 7)):
+        with pytest.raises(g.GPT2Error):
+            g.query_sizes(bad)
 
 
 def _cfgs():

@@ -34,10 +34,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-METRIC = "train tokens/sec + MFU %, GPT-2 124M B=16 T=1024 step, 1 MI355X"
 PEAK_BF16 = 2.5e15          # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
-B, T, G = 16, 1024, 32
+
+# The two measured workloads.  "gpt2" is the headline: the GPT-2 124M
+# optimizer step of "How I trained my own GPT-2 124M on FineWeb-Edu" (32 x
+# B=16, lr 6e-4).  "rotary" is the modern variant that "Reproduce GPT-2 124M
+# 复盘" runs on one H100 (RMSNorm, RoPE, SwiGLU 2048; 8 x B=64, lr 1.5e-3).
+WORKLOADS = {
+    "gpt2": dict(metric="train tokens/sec + MFU %, GPT-2 124M B=16 T=1024 step, 1 MI355X", B=16, G=32, lr=6e-4,
+                 F=3072, name="gpt2-124m optimizer step"),
+    "rotary": dict(metric="train tokens/sec + MFU %, GPT-2 124M rotary variant B=64 T=1024 step, 1 MI355X", B=64,
+                   G=8, lr=1.5e-3, F=2048, name="gpt2-124m rotary variant (RMSNorm, RoPE, SwiGLU 2048) optimizer step"),
+}
+T = 1024
+B, G = WORKLOADS["gpt2"]["B"], WORKLOADS["gpt2"]["G"]
+METRIC = WORKLOADS["gpt2"]["metric"]
 
 
 def flops_per_token(n_params: int, L=12, H=12, hd=64, T_=1024) -> int:
@@ -45,23 +57,25 @@ def flops_per_token(n_params: int, L=12, H=12, hd=64, T_=1024) -> int:
     return 6 * n_params + 12 * L * H * hd * T_
 
 
-def gemm_site_flops():
+def gemm_site_flops(rows=B * T, F=3072, FC=None):
     """Algorithmic FLOPs of one launch at each GEMM site of the micro-step
-    (B*T = 16384 rows, C = 768, F = 3072, V = 50304; the lm_head products take
-    all 16384 rows in one launch)."""
-    M, C, F, V, CH = B * T, 768, 3072, 50304, B * T
+    (rows = B*T, C = 768, MLP width F, V = 50304; the lm_head products take
+    all rows in one launch).  FC is the fc product's output width: F for
+    GPT-2, 2F (gate and up) for the rotary variant."""
+    M, C, V = rows, 768, 50304
+    FC = F if FC is None else FC
     return {
         "gemm.qkv": 2 * M * 3 * C * C,
         "gemm.attn_proj": 2 * M * C * C,
-        "gemm.fc": 2 * M * F * C,
+        "gemm.fc": 2 * M * FC * C,
         "gemm.mlp_proj": 2 * M * C * F,
-        "gemm.lm_head": 2 * CH * V * C,
-        "gemm.lm_head_dx": 2 * CH * V * C,
-        "gemm.lm_head_dw": 2 * CH * V * C,
+        "gemm.lm_head": 2 * M * V * C,
+        "gemm.lm_head_dx": 2 * M * V * C,
+        "gemm.lm_head_dw": 2 * M * V * C,
         "gemm.mlp_proj_dw": 2 * M * C * F,
         "gemm.mlp_proj_dx": 2 * M * C * F,
-        "gemm.fc_dw": 2 * M * F * C,
-        "gemm.fc_dx": 2 * M * F * C,
+        "gemm.fc_dw": 2 * M * FC * C,
+        "gemm.fc_dx": 2 * M * FC * C,
         "gemm.attn_proj_dw": 2 * M * C * C,
         "gemm.attn_proj_dx": 2 * M * C * C,
         "gemm.qkv_dw": 2 * M * 3 * C * C,
@@ -69,22 +83,28 @@ def gemm_site_flops():
     }
 
 
-def cpu_baseline(rows: int = 8):
+def cpu_baseline(rows: int = 8, workload: str = "gpt2"):
     """The CPU oracle (NumPy float32) on a bounded sample: one micro-step of the
     same model on `rows` 1024-token sequences of the same token stream (about
     2 s of host time per sequence on 16 cores)."""
     import synthetic
-    from oracle import model as OM
+    if workload == "rotary":
+        from oracle import modern as OM
+        cfg = OM.ModernConfig(50304, 1024, 12, 12, 768, 2048)
+        what = "the GPT-2 124M rotary variant"
+    else:
+        from oracle import model as OM
+        cfg = OM.Config(50304, 1024, 12, 12, 768, 3072)
+        what = "GPT-2 124M"
     cores = len(os.sched_getaffinity(0))
-    cfg = OM.Config(50304, 1024, 12, 12, 768, 3072)
     params = synthetic.random_params(OM.param_specs(cfg), seed=42)
     stream = synthetic.token_stream(rows * 1024 + 1, seed=1337)
     x, y = synthetic.micro_batch(stream, 0, rows, 1024)
     t0 = time.perf_counter()
-    OM.fwd_bwd(cfg, params, x, y, scale=1.0 / G)
+    OM.fwd_bwd(cfg, params, x, y, scale=1.0 / WORKLOADS[workload]["G"])
     dt = time.perf_counter() - t0
     return {"value": round(rows * 1024 / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one micro-step (forward + backward, float32 NumPy) of GPT-2 124M on {rows} x 1024 tokens of "
+            "sample": f"one micro-step (forward + backward, float32 NumPy) of {what} on {rows} x 1024 tokens of "
                       f"the synthetic stream; {dt:.1f} s"}
 
 
@@ -127,10 +147,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--grad-accum", type=int, default=G)
+    ap.add_argument("--grad-accum", type=int, default=None, help="micro-steps per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no HIP events at all (no roofline, no breakdown)")
     ap.add_argument("--traffic-probe", metavar="SITE", help="one marked micro-step for an HBM counter run")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2",
+                    help="gpt2 (the headline step, default) or rotary (the modern variant)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)",
@@ -145,8 +167,10 @@ def main(argv=None):
     import synthetic
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    ga = args.grad_accum
-    model = g.GPT2(g.GPT2_124M)
+    wl = WORKLOADS[args.workload]
+    B = wl["B"]
+    ga = args.grad_accum if args.grad_accum is not None else wl["G"]
+    model = g.GPT2(g.GPT2_124M if args.workload == "gpt2" else g.GPT2_ROTARY_124M)
     model.init_params(seed=42)
     n_params = model.sizes.n_params
     stream = synthetic.token_stream(ga * B * T + 1, seed=1337)
@@ -162,14 +186,14 @@ def main(argv=None):
         model.zero_grad()
         for k in range(ga):
             model.fwd_bwd(xs[k], ys[k], loss_scale=1.0 / ga, loss_out=losses[k:k + 1])
-        norm = model.clip_adamw_step(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0)
+        norm = model.clip_adamw_step(lr=wl["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0)
         # the loss is read back once per step, as a logger would
         return float(losses.mean().item()), float(norm.item())
 
     # Warm-up.  The first warm-up step is also the per-site breakdown: every
     # launch bracketed with events (that adds about 6% to its wall time, so
     # the timed steps below bracket only the dominant kernel).
-    fl = gemm_site_flops()
+    fl = gemm_site_flops(B * T, wl["F"], 2 * wl["F"] if args.workload == "rotary" else wl["F"])
     breakdown, gsite = {}, None
     for w in range(max(1, args.warmup)):
         if w == 0 and not args.no_profile:
@@ -217,7 +241,7 @@ def main(argv=None):
     tps = tokens / elapsed
     fpt = flops_per_token(n_params)
     result = {
-        "metric": METRIC,
+        "metric": wl["metric"],
         "value": round(tps, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -229,7 +253,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (Zipf token stream, EOT-prefixed documents; random N(0,0.02) init)",
-        "config": {"workload": f"gpt2-124m optimizer step: {ga} x micro-batch B={B} T={T} + clip 1.0 + AdamW",
+        "config": {"workload": f"{wl['name']}: {ga} x micro-batch B={B} T={T} + clip 1.0 + AdamW lr {wl['lr']:g}",
                    "global_batch_tokens": ga * B * T, "micro_batch": B, "seq_len": T, "grad_accum": ga,
                    "vocab": 50304, "parallelism": "none (1 GPU)"},
         "mfu": round(tps * fpt / PEAK_BF16, 4),
@@ -263,7 +287,7 @@ def main(argv=None):
         result["top_site"] = {"site": site, "share": round(ms / total_ms, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"] = cpu_baseline(workload=args.workload)
     model.close()
     print(json.dumps(result))
     return 0

@@ -225,6 +225,51 @@ __device__ __forceinline__ void epi_put4(const GemmP& p, int64_t idx, const floa
 // so the epilogue reads and writes 16-byte vectors.  With CHECK, rows at or
 // past M and columns at or past N are skipped (a group of 4 that straddles N
 // is stored element by element).
+//
+// Interior tiles gather a row group's operands (bias, and R or U) into
+// registers before the first store: the compiler must assume that C may
+// alias them, so loads interleaved with stores would each wait out the full
+// memory latency in turn.  Every lane reads only the elements it writes, so
+// R == C (in place) stays correct.
+template <int EPI, int TN>
+__device__ __forceinline__ void epi_row_gathered(const GemmP& p, int64_t rb, int ncol, int i,
+                                                 const f32x16 (&acc)[TN]) {
+  using Op = std::conditional_t<EPI == GPT2_EPI_RESIDUAL, float4, bf16x4>;
+  Op op[TN][4];
+  float4 bias[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int co = 32 * j + 8 * q;
+      bias[j][q] = p.bias ? *reinterpret_cast<const float4*>(p.bias + ncol + co) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (EPI == GPT2_EPI_RESIDUAL) op[j][q] = *reinterpret_cast<const float4*>(p.R + rb + co);
+      else op[j][q] = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(p.U) + rb + co);
+    }
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int co = 32 * j + 8 * q;
+      const float4 b = bias[j][q];
+      const float v0 = fmaf(p.alpha, acc[j][4 * q + 0], b.x), v1 = fmaf(p.alpha, acc[j][4 * q + 1], b.y);
+      const float v2 = fmaf(p.alpha, acc[j][4 * q + 2], b.z), v3 = fmaf(p.alpha, acc[j][4 * q + 3], b.w);
+      if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+        const float4 r = op[j][q];
+        *reinterpret_cast<float4*>(static_cast<float*>(p.C) + rb + co) =
+            make_float4(r.x + v0, r.y + v1, r.z + v2, r.w + v3);
+      } else {
+        const bf16x4 u = op[j][q];
+        float f0 = bf2f(u[0]), f1 = bf2f(u[1]), f2 = bf2f(u[2]), f3 = bf2f(u[3]);
+        if constexpr (EPI == GPT2_EPI_DGELU) {
+          f0 = gelu_tanh_grad(f0); f1 = gelu_tanh_grad(f1); f2 = gelu_tanh_grad(f2); f3 = gelu_tanh_grad(f3);
+        }
+        const bf16x2 o0 = f2bf2(v0 * f0, v1 * f1), o1 = f2bf2(v2 * f2, v3 * f3);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.C) + rb + co) = bf16x4{o0[0], o0[1], o1[0], o1[1]};
+      }
+    }
+}
+
 template <int EPI, bool OUT_BF16, int TM, int TN, bool CHECK>
 __device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN]) {
 #pragma unroll
@@ -232,6 +277,10 @@ __device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol
     const int m = mrow + 32 * i;
     if (CHECK && m >= p.M) continue;
     const int64_t rb = (int64_t)m * p.ldc + ncol;
+    if constexpr (!CHECK) {
+      epi_row_gathered<EPI, TN>(p, rb, ncol, i, acc[i]);
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -260,16 +309,25 @@ __device__ __forceinline__ void epi_tile_mul_pre(const GemmP& p, int mrow, int n
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t rb = (int64_t)(mrow + 32 * i) * p.ldc + ncol;
+    if (i >= TMP) {  // not prefetched: gather the row group's factors, then store
+      epi_row_gathered<GPT2_EPI_MUL, TN>(p, rb, ncol, i, acc[i]);
+      continue;
+    }
     bf16* crow = static_cast<bf16*>(p.C) + rb;
-    const bf16* urow = static_cast<const bf16*>(p.U) + rb;
+    float4 bias[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bias[j][q] = p.bias ? *reinterpret_cast<const float4*>(p.bias + ncol + 32 * j + 8 * q)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int co = 32 * j + 8 * q;
-        float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p.bias) b = *reinterpret_cast<const float4*>(p.bias + ncol + co);
-        const bf16x4 u = i < TMP ? upre[i < TMP ? i : 0][j][q] : *reinterpret_cast<const bf16x4*>(urow + co);
+        const float4 b = bias[j][q];
+        const bf16x4 u = upre[i < TMP ? i : 0][j][q];
         const f32x16& a = acc[i][j];
         const bf16x2 o0 = f2bf2(fmaf(p.alpha, a[4 * q], b.x) * bf2f(u[0]), fmaf(p.alpha, a[4 * q + 1], b.y) * bf2f(u[1]));
         const bf16x2 o1 =
@@ -383,21 +441,30 @@ __device__ __forceinline__ void epi_tile_swiglu_bwd(const GemmP& p, int mrow, in
     if (CHECK && m >= p.M) continue;
     const bf16* urow = static_cast<const bf16*>(p.U) + (int64_t)m * p.ld2;
     bf16* crow = static_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+    // gate and up of the row group first (all loads in flight), then the stores
+    bf16x4 g[TN][4], u[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int f = ncol + 32 * j + 8 * q;
         if (CHECK && f >= p.N) continue;
-        const bf16x4 g = *reinterpret_cast<const bf16x4*>(urow + f);
-        const bf16x4 u = *reinterpret_cast<const bf16x4*>(urow + F + f);
+        g[j][q] = *reinterpret_cast<const bf16x4*>(urow + f);
+        u[j][q] = *reinterpret_cast<const bf16x4*>(urow + F + f);
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = ncol + 32 * j + 8 * q;
+        if (CHECK && f >= p.N) continue;
         float dg[4], du[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v = p.alpha * acc[i][j][4 * q + e];
-          const float gf = bf2f(g[e]), sg = sigmoid_fast(gf);
+          const float gf = bf2f(g[j][q][e]), sg = sigmoid_fast(gf);
           du[e] = v * gf * sg;
-          dg[e] = v * bf2f(u[e]) * sg * fmaf(gf, 1.f - sg, 1.f);
+          dg[e] = v * bf2f(u[j][q][e]) * sg * fmaf(gf, 1.f - sg, 1.f);
         }
         const bf16x2 g01 = f2bf2(dg[0], dg[1]), g23 = f2bf2(dg[2], dg[3]);
         const bf16x2 u01 = f2bf2(du[0], du[1]), u23 = f2bf2(du[2], du[3]);

@@ -93,21 +93,12 @@ static GemmP make_params(const gpt2_gemm_args& a) {
   return p;
 }
 
-// Launch one instantiation of the multi-stage bf16 kernel, raising its
-// dynamic-LDS limit once.
+// Launch one instantiation of the bf16 kernel (its LDS stages are static).
 template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool A_K, bool B_K, int EPI, bool OB, bool AT, bool SW = false>
 static hipError_t launch_v2(const Launch& L, const GemmP& p) {
   auto kern = gemm2_kernel<BM, BN, BK, WGM, WGN, ST, A_K, B_K, EPI, OB, AT, SW>;
-  constexpr size_t lds = gemm2_lds_bytes<BM, BN, BK, ST>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   dim3 grid(p.tiles_m * p.tiles_n * p.splits), block(64 * WGM * WGN);
-  kern<<<grid, block, lds, L.stream>>>(p);
+  kern<<<grid, block, 0, L.stream>>>(p);
   return hipGetLastError();
 }
 

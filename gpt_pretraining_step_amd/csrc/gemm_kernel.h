@@ -485,7 +485,11 @@ constexpr int EPI_CE_STATS = 16;
 
 template <int BM, int BN, int WGN, int TM, int TN, bool EDGE>
 __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int tn, int wm0, int wn0, int wave,
-                                             int lr, int lg, const f32x16 (&acc)[TM][TN], float* red, char* stage) {
+                                             int lr, int lg, const f32x16 (&acc)[TM][TN], float* red, char* st0,
+                                             char* st1) {
+  // the output tile is staged in the two operand stages: rows below BM / 2
+  // in the first, the others in the second
+  auto srow = [&](int row) { return row < BM / 2 ? st0 + row * (BN * 2) : st1 + (row - BM / 2) * (BN * 2); };
   constexpr float L2E = 1.4426950408889634f;
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   const int wn = wave % WGN;
@@ -540,8 +544,8 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
         const int col = wn0 + 32 * j + 8 * q + 4 * lg;  // within the tile
         const bf16x2 lo = f2bf2(acc[i][j][4 * q] - mx, acc[i][j][4 * q + 1] - mx);
         const bf16x2 hi = f2bf2(acc[i][j][4 * q + 2] - mx, acc[i][j][4 * q + 3] - mx);
-        const int addr = row * (BN * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8;
-        *reinterpret_cast<bf16x4*>(stage + addr) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
+        const int addr = (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8;
+        *reinterpret_cast<bf16x4*>(srow(row) + addr) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
       }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -553,7 +557,7 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
     const int row = idx / CPR, c = idx % CPR;
     const int m = m0 + row, n = n0 + 8 * c;
     if (m >= p.M || (EDGE && n >= p.N)) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4));
+    const uint4 v = *reinterpret_cast<const uint4*>(srow(row) + ((c ^ (row & (CPR - 1))) << 4));
     bf16* d = C + (int64_t)m * p.ldc + n;
     if (!EDGE || n + 8 <= p.N) {
       *reinterpret_cast<uint4*>(d) = v;
@@ -599,8 +603,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // elements per stage
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
-  static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  static_assert(STAGES == 2, "two LDS stages");
+  // The two stages are two distinct LDS objects and the K loop is unrolled
+  // by two, so every copy and every read names its stage statically.  The
+  // compiler then sees that a copy into one stage cannot alias reads of the
+  // other and adds no wait for it; with one object (or a stage picked at run
+  // time) it must assume the transposing reads alias every copy in flight
+  // and drains the next step's copy (s_waitcnt vmcnt(0)) before computing
+  // the current step.
+  __shared__ __attribute__((aligned(16))) bf16 lds0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 lds1[STAGE];
 
   int tm, tn, split;
   tile_of_block(p, tm, tn, split);
@@ -641,49 +653,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   dma_a.init(p.lda, m0, p.M);
   if constexpr (MAP_B) dma_b.init_swiglu(p.ldb, n0, p.N);
   else dma_b.init(p.ldb, n0, p.N);
-  auto issue = [&](int stage, int kstep) {
-    bf16* as = smem + stage * STAGE;
+  auto issue = [&](bf16* as, int kstep) {
     bf16* bs = as + BM * BK;
     const int k0 = kbeg + kstep * BK;
+    // (copies through inline asm: the compiler adds no waits for them; the
+    // top of each K step waits and meets the other waves)
     if (MAP_B || k0 + BK <= kend) {  // SWIGLU: K % BK == 0, checked by the host
       dma_a.issue(as, Ag, p.lda, m0, k0);
       dma_b.issue(bs, Bg, p.ldb, b_row0, k0);
     } else {
-      if constexpr (A_K) dma_rows<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
-      else dma_kr<BM, BK, NW>(as, Ag, p.lda, m0, p.M, k0, kend);
-      if constexpr (B_K) dma_rows<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
-      else dma_kr<BN, BK, NW>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+      if constexpr (A_K) dma_rows<BM, BK, NW, true>(as, Ag, p.lda, m0, p.M, k0, kend);
+      else dma_kr<BM, BK, NW, true>(as, Ag, p.lda, m0, p.M, k0, kend);
+      if constexpr (B_K) dma_rows<BN, BK, NW, true>(bs, Bg, p.ldb, n0, p.N, k0, kend);
+      else dma_kr<BN, BK, NW, true>(bs, Bg, p.ldb, n0, p.N, k0, kend);
     }
   };
-  constexpr int DMA_PER_STEP = (BM + BN) * BK / 512 / NW;  // DMA instructions per wave per K step
   const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
   // MUL epilogue (swapped layout) of an interior tile: the factors this lane
   // multiplies by are loaded during the first K step (64 registers), so
   // their latency hides behind the main loop
   constexpr bool PRE_U = SWAP && EPI == GPT2_EPI_MUL;
-  constexpr int TMP = (TM + 1) / 2;  // accumulator rows whose factors are prefetched (register budget)
+  constexpr int TMP = 1;  // accumulator rows whose factors are prefetched (register budget)
   bf16x4 upre[PRE_U ? TMP : 1][PRE_U ? TN : 1][PRE_U ? 4 : 1];
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // Wait for this wave's DMA of step kt (later steps stay in flight) and
-    // its LDS writes, then meet the other waves.  A plain __syncthreads()
-    // would also drain the later steps' DMA (its release fence waits for
-    // every outstanding load).  The asm statements are compiler memory
-    // barriers, so no LDS access moves across them.
-    if (kt + STAGES - 2 < nk) {
-      if constexpr (STAGES == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else if constexpr (STAGES == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STEP) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_STEP) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // One K step: wait for this wave's copy of step kt, meet the other waves
+  // (so every wave's copy has landed), start the copy of step kt + 1 into
+  // the other stage, then multiply.  The asm is also a compiler memory
+  // barrier: no LDS access moves across it.
+  auto kstep = [&](const bf16* as, bf16* next, int kt) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (PRE_U) {
-      // issued before the next step's DMA, so the next wait covers them
+      // issued before the next step's copy, so the next wait covers them
       if (kt == 0 && interior) {
         const bf16* U = static_cast<const bf16*>(p.U) + (int64_t)(m0 + wm0 + lr) * p.ldc + n0 + wn0 + 4 * lg;
 #pragma unroll
@@ -695,9 +695,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
               upre[i][j][q] = *reinterpret_cast<const bf16x4*>(U + (int64_t)(32 * i) * p.ldc + 32 * j + 8 * q);
       }
     }
-    const int nxt = kt + STAGES - 1;
-    if (nxt < nk) issue(nxt % STAGES, nxt);
-    const bf16* as = smem + (kt % STAGES) * STAGE;
+    if (kt + 1 < nk) issue(next, kt + 1);
     const bf16* bs = as + BM * BK;
     // Fragments of the next 16-wide K slice are read from LDS while the
     // current slice's MFMAs issue.  Without SWAP a lane's accumulator holds
@@ -761,7 +759,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
         for (int k = 0; k < BK; ++k) rsum += bf2f(as[k * BM + 8 * kr_chunk<BM>(k, t >> 3) + (t & 7)]);
       }
     }
+  };
+
+  if (nk > 0) issue(lds0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(lds0, lds1, kt);
+    kstep(lds1, lds0, kt + 1);
   }
+  if (kt < nk) kstep(lds0, lds1, kt);
   if (do_rowsum && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
     unsafeAtomicAdd(p.row_sum + m0 + threadIdx.x, p.alpha * rsum);
 
@@ -769,15 +775,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
     static_assert(SWAP && WN == 64, "statistics epilogue: swapped layout, 64 columns per wave");
     // every wave is done with the operand stages: reuse them for the
     // cross-wave reduction
-    static_assert(BM * BN * 2 <= STAGES * STAGE * 2, "the output tile fits in the operand stages");
+    static_assert(BM / 2 * BN * 2 <= STAGE * 2, "half the output tile fits in one operand stage");
     __shared__ float red[2 * WGN * BM];
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (n0 + BN <= p.N)
       epi_ce_stats<BM, BN, WGN, TM, TN, false>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
-                                               reinterpret_cast<char*>(smem));
+                                               reinterpret_cast<char*>(lds0), reinterpret_cast<char*>(lds1));
     else
       epi_ce_stats<BM, BN, WGN, TM, TN, true>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
-                                              reinterpret_cast<char*>(smem));
+                                              reinterpret_cast<char*>(lds0), reinterpret_cast<char*>(lds1));
   } else if constexpr (EPI == GPT2_EPI_ROPE || EPI == GPT2_EPI_SWIGLU) {
     static_assert(SWAP && WN == 64, "paired epilogues: swapped layout, 64 columns per wave");
     if (interior) epi_tile_pair<EPI, TM, false>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
@@ -813,10 +819,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   }
 }
 
-template <int BM, int BN, int BK, int STAGES>
-constexpr size_t gemm2_lds_bytes() {
-  return (size_t)STAGES * (BM + BN) * BK * sizeof(bf16);
-}
+
 
 
 

@@ -23,6 +23,32 @@ namespace g2 {
 
 __device__ __attribute__((aligned(16))) static const uint4 g2_zero16[4] = {};
 
+// ---- copies issued through inline asm.  The compiler's wait insertion does
+// not see them, so it neither drains them before LDS reads it cannot prove
+// disjoint (it does so, conservatively, before every transposing read that
+// follows a copy it knows of) nor waits for them anywhere else: the caller
+// orders them with s_waitcnt vmcnt and a barrier before any wave reads what
+// they fill.  Each statement sets M0, the LDS byte address of lane 0's 16
+// bytes (lane l writes at M0 + 16 l).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ uint32_t uniform32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// source = uniform base + per-lane 32-bit byte offset
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = (uint64_t)uniform32((uint32_t)b) | ((uint64_t)uniform32((uint32_t)(b >> 32)) << 32);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(uniform32(lds))
+               : "m0");
+}
+// source = per-lane 64-bit address
+__device__ __forceinline__ void dma16_ptr(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(uniform32(lds)) : "m0");
+}
+#pragma clang diagnostic pop
+
 template <int BK>
 __device__ __forceinline__ int swz_chunk(int row, int c) {
   if constexpr (BK == 64) return c ^ (row & 7);
@@ -30,7 +56,7 @@ __device__ __forceinline__ int swz_chunk(int row, int c) {
 }
 
 // K-major tile [ROWS][BK] (source rows row0.., K columns k0..) -> LDS, by DMA.
-template <int ROWS, int BK, int NWAVES>
+template <int ROWS, int BK, int NWAVES, bool ASM = false>
 __device__ __forceinline__ void dma_rows(bf16* lds, const bf16* __restrict__ src, int64_t ld, int row0, int nrows,
                                          int k0, int K) {
   constexpr int CPR = BK / 8;              // 16-byte chunks per row
@@ -47,7 +73,8 @@ __device__ __forceinline__ void dma_rows(bf16* lds, const bf16* __restrict__ src
     const int c = swz_chunk<BK>(r, pc);
     const int gr = row0 + r, gk = k0 + 8 * c;
     const bf16* g = (gr < nrows && gk < K) ? src + (int64_t)gr * ld + gk : reinterpret_cast<const bf16*>(g2_zero16);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), lds + ins * RPI * BK, 16, 0, 0);
+    if constexpr (ASM) dma16_ptr(g, lds_addr(lds + ins * RPI * BK));
+    else __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), lds + ins * RPI * BK, 16, 0, 0);
   }
 }
 
@@ -83,7 +110,7 @@ __device__ __forceinline__ int kr_chunk(int k, int c) {
 // instruction i fills LDS chunks 64 i .. 64 i + 63 of the tile (chunk g is
 // row g / (R/8), position g % (R/8)); the lane whose destination is position
 // p of row k fetches the logical chunk that the swizzle puts there.
-template <int R, int BK, int NWAVES>
+template <int R, int BK, int NWAVES, bool ASM = false>
 __device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, int64_t ld, int col0, int ncols,
                                        int k0, int K) {
   constexpr int CPR = R / 8;             // 16-byte chunks per row
@@ -99,7 +126,8 @@ __device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, 
     const int c = kr_chunk<R>(k, g % CPR);
     const int gk = k0 + k, gc = col0 + 8 * c;
     const bf16* gp = (gk < K && gc < ncols) ? src + (int64_t)gk * ld + gc : reinterpret_cast<const bf16*>(g2_zero16);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp), lds + ins * 512, 16, 0, 0);
+    if constexpr (ASM) dma16_ptr(gp, lds_addr(lds + ins * 512));
+    else __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp), lds + ins * 512, 16, 0, 0);
   }
 }
 
@@ -152,8 +180,7 @@ struct RowsDma {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)row0 * ld + k0);
 #pragma unroll
     for (int i = 0; i < IPW; ++i)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]), lds + (ins0 + i) * RPI * BK, 16,
-                                       0, 0);
+      dma16_off(base, off[i], lds_addr(lds + (ins0 + i) * RPI * BK));
   }
 };
 
@@ -180,8 +207,7 @@ struct KrDma {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * ld + col0);
 #pragma unroll
     for (int i = 0; i < IPW; ++i)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]), lds + (ins0 + i) * 512, 16, 0,
-                                       0);
+      dma16_off(base, off[i], lds_addr(lds + (ins0 + i) * 512));
   }
 };
 

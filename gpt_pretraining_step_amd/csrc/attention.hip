@@ -127,7 +127,10 @@ __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv, const fl
 //
 // Tiles of 64 rows x 64 head dims (128-byte rows) are copied from HBM into
 // LDS by DMA, double-buffered: the next tile's copy is in flight while the
-// current one is multiplied, one barrier per tile.  Rows are stored with
+// current one is multiplied, one barrier per tile.  The copies are issued
+// through inline asm (tile_io.h): the compiler would otherwise drain them
+// before every transposing read; the explicit wait at the top of each tile
+// orders them.  Rows are stored with
 // their 16-byte chunks swizzled (tile_io.h).  Operands read along a row
 // (K, V, Q, dO rows) use 16-byte LDS reads; operands read along a column
 // (V^T, K^T, Q^T, dO^T) use the transposing LDS read, so no tile is ever
@@ -215,8 +218,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
   const int kv_end = min(T, qb * BQ + BQ);
   const int ntiles = (kv_end + 63) / 64;
   auto issue = [&](int st, int tile) {
-    dma_rows<64, 64, NW>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
-    dma_rows<64, 64, NW>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
   };
   // ST-stage ring: tiles jt+1 .. jt+ST-2 stay in flight while tile jt is
   // used; tile jt+ST-1 goes into the buffer of tile jt-1 once every wave has
@@ -224,6 +227,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
 #pragma unroll
   for (int t = 0; t < ST - 1; ++t)
     if (t < ntiles) issue(t, t);
+  drain_vector_loads();
   for (int jt = 0; jt < ntiles; ++jt) {
     if (jt + ST - 2 < ntiles) {
       if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -365,8 +369,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
   const int kv_end = min(T, qb * BQ + BQ);
   const int ntiles = (kv_end + 63) / 64;
   auto issue = [&](int st, int tile) {
-    dma_rows<64, 64, NW>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
-    dma_rows<64, 64, NW>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
   };
   // ST-stage ring: tiles jt+1 .. jt+ST-2 stay in flight while tile jt is
   // used; tile jt+ST-1 goes into the buffer of tile jt-1 once every wave has
@@ -374,6 +378,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
 #pragma unroll
   for (int t = 0; t < ST - 1; ++t)
     if (t < ntiles) issue(t, t);
+  drain_vector_loads();
   for (int jt = 0; jt < ntiles; ++jt) {
     if (jt + ST - 2 < ntiles) {
       if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
                                                                      float scale, float sl2) {
   constexpr int BK = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse * log2 e, D]
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse, D]
   const int kblk = blockIdx.y;  // smallest keys (most queries) first, over all heads
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
@@ -465,28 +470,23 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
   f32x16 dvT[2] = {zero16(), zero16()}, dkT[2] = {zero16(), zero16()};
   const int qstart = kblk * BK;
   const int ntiles = (T - qstart + 63) / 64;
-  // Q and dO tiles by DMA; the tile's 64 lse and D values through registers
-  // of wave 0, written to LDS after the current tile's compute.
-  float lse_r = 0.f, d_r = 0.f;
+  // Q and dO tiles, and the tile's 64 lse and D values, by DMA (lse and D
+  // from wave 0; rows past T read zeros, and their scores are masked)
   const bool w0 = __builtin_amdgcn_readfirstlane(wave) == 0;
   auto issue = [&](int st, int tile) {
     const int q0t = qstart + tile * 64;
-    dma_rows<64, 64, NW>(sm[st][0], Qg, C3, q0t, T, 0, HD);
-    dma_rows<64, 64, NW>(sm[st][1], dOg, C, q0t, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][0], Qg, C3, q0t, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][1], dOg, C, q0t, T, 0, HD);
     if (w0) {
       const int q = q0t + lane;
-      lse_r = (q < T) ? lseg[q] * kLOG2E : 0.f;
-      d_r = (q < T) ? Dg[q] : 0.f;
-    }
-  };
-  auto commit = [&](int st) {
-    if (w0) {
-      rowst[st][0][lane] = lse_r;
-      rowst[st][1][lane] = d_r;
+      dma4_ptr(q < T ? static_cast<const void*>(lseg + q) : static_cast<const void*>(g2_zero16),
+               lds_addr(&rowst[st][0][0]));
+      dma4_ptr(q < T ? static_cast<const void*>(Dg + q) : static_cast<const void*>(g2_zero16),
+               lds_addr(&rowst[st][1][0]));
     }
   };
   issue(0, 0);
-  commit(0);
+  drain_vector_loads();
   for (int jt = 0; jt < ntiles; ++jt) {
     tile_barrier();
     const bool more = jt + 1 < ntiles;
@@ -528,7 +528,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int ql = 32 * c + 8 * a + 4 * lg;
-        const float4 L4 = *reinterpret_cast<const float4*>(Ls + ql);
+        float4 L4 = *reinterpret_cast<const float4*>(Ls + ql);  // natural log: to base 2
+        L4.x *= kLOG2E; L4.y *= kLOG2E; L4.z *= kLOG2E; L4.w *= kLOG2E;
         const float4 D4 = *reinterpret_cast<const float4*>(Ds + ql);
         const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
         const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
@@ -551,7 +552,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
         }
       }
     }
-    if (more) commit((jt + 1) & 1);
   }
   if (kvld) {
     bf16* ok = dqkv + ((int64_t)b * T + kj) * C3 + C + h * HD;

@@ -47,7 +47,18 @@ __device__ __forceinline__ void dma16_off(const void* base, uint32_t voff, uint3
 __device__ __forceinline__ void dma16_ptr(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(uniform32(lds)) : "m0");
 }
+// 4 bytes per lane (lane l writes at M0 + 4 l)
+__device__ __forceinline__ void dma4_ptr(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(uniform32(lds)) : "m0");
+}
 #pragma clang diagnostic pop
+
+// A wait on every vector-memory load that the compiler can see (through the
+// builtin, so that it knows them complete afterwards).  Kernels whose main
+// loop copies with the asm forms above call it before the loop: otherwise the
+// compiler's wait for a load issued before the loop lands at its first use
+// inside the loop and drains the in-flight copies on every iteration.
+__device__ __forceinline__ void drain_vector_loads() { __builtin_amdgcn_s_waitcnt(0x0070); }  // vmcnt(0) lgkmcnt(0)
 
 template <int BK>
 __device__ __forceinline__ int swz_chunk(int row, int c) {

@@ -300,40 +300,57 @@ __device__ __forceinline__ void epi_tile_swap(const GemmP& p, int mrow, int ncol
   }
 }
 
-// MUL epilogue of an interior tile, swapped layout, with the factors of the
-// first TMP accumulator rows already in registers (upre[i][j][q] = U at row
-// mrow + 32 i, columns ncol + 32 j + 8 q .. +3); the others are loaded here.
+// MUL epilogue of an interior tile, swapped layout.  The factors of row
+// group 0 arrive in registers from the first K step (upre); the loop then
+// loads row group i + 1's factors before storing row group i, so one row
+// group of loads is always in flight behind the stores.
 template <int TM, int TN, int TMP>
 __device__ __forceinline__ void epi_tile_mul_pre(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN],
                                                  const bf16x4 (&upre)[TMP][TN][4]) {
+  static_assert(TMP == 1, "row group 0 prefetched");
+  float4 bias[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      bias[j][q] = p.bias ? *reinterpret_cast<const float4*>(p.bias + ncol + 32 * j + 8 * q)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  bf16x4 cur[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cur[j][q] = upre[0][j][q];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t rb = (int64_t)(mrow + 32 * i) * p.ldc + ncol;
-    if (i >= TMP) {  // not prefetched: gather the row group's factors, then store
-      epi_row_gathered<GPT2_EPI_MUL, TN>(p, rb, ncol, i, acc[i]);
-      continue;
+    bf16x4 nxt[TN][4];
+    if (i + 1 < TM) {
+      const bf16* un = static_cast<const bf16*>(p.U) + rb + 32 * p.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) nxt[j][q] = *reinterpret_cast<const bf16x4*>(un + 32 * j + 8 * q);
     }
     bf16* crow = static_cast<bf16*>(p.C) + rb;
-    float4 bias[TN][4];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        bias[j][q] = p.bias ? *reinterpret_cast<const float4*>(p.bias + ncol + 32 * j + 8 * q)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int co = 32 * j + 8 * q;
         const float4 b = bias[j][q];
-        const bf16x4 u = upre[i < TMP ? i : 0][j][q];
+        const bf16x4 u = cur[j][q];
         const f32x16& a = acc[i][j];
         const bf16x2 o0 = f2bf2(fmaf(p.alpha, a[4 * q], b.x) * bf2f(u[0]), fmaf(p.alpha, a[4 * q + 1], b.y) * bf2f(u[1]));
         const bf16x2 o1 =
             f2bf2(fmaf(p.alpha, a[4 * q + 2], b.z) * bf2f(u[2]), fmaf(p.alpha, a[4 * q + 3], b.w) * bf2f(u[3]));
         *reinterpret_cast<bf16x4*>(crow + co) = bf16x4{o0[0], o0[1], o1[0], o1[1]};
       }
+    if (i + 1 < TM) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[j][q] = nxt[j][q];
+    }
   }
 }
 
@@ -432,45 +449,71 @@ __device__ __forceinline__ void epi_tile_pair(const GemmP& p, int mrow, int gcol
 // and up u = U[m][F + f] (row pitch ld2), C[m][f] = d(act) u silu'(g) and
 // C[m][F + f] = d(act) silu(g), silu'(g) = s (1 + g (1 - s)), s = sigmoid(g).
 // Swapped layout, any tile width; N % 4 == 0.
+template <int TN>
+__device__ __forceinline__ void swiglu_bwd_store(const GemmP& p, bf16* crow, int ncol, int F, const bf16x4 (&g)[TN][4],
+                                                 const bf16x4 (&u)[TN][4], const f32x16 (&acc)[TN], bool check) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = ncol + 32 * j + 8 * q;
+      if (check && f >= p.N) continue;
+      float dg[4], du[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = p.alpha * acc[j][4 * q + e];
+        const float gf = bf2f(g[j][q][e]), sg = sigmoid_fast(gf);
+        du[e] = v * gf * sg;
+        dg[e] = v * bf2f(u[j][q][e]) * sg * fmaf(gf, 1.f - sg, 1.f);
+      }
+      const bf16x2 g01 = f2bf2(dg[0], dg[1]), g23 = f2bf2(dg[2], dg[3]);
+      const bf16x2 u01 = f2bf2(du[0], du[1]), u23 = f2bf2(du[2], du[3]);
+      *reinterpret_cast<bf16x4*>(crow + f) = bf16x4{g01[0], g01[1], g23[0], g23[1]};
+      *reinterpret_cast<bf16x4*>(crow + F + f) = bf16x4{u01[0], u01[1], u23[0], u23[1]};
+    }
+}
+
+template <int TN>
+__device__ __forceinline__ void swiglu_bwd_load(const GemmP& p, const bf16* urow, int ncol, int F, bf16x4 (&g)[TN][4],
+                                                bf16x4 (&u)[TN][4], bool check) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = ncol + 32 * j + 8 * q;
+      if (check && f >= p.N) continue;
+      g[j][q] = *reinterpret_cast<const bf16x4*>(urow + f);
+      u[j][q] = *reinterpret_cast<const bf16x4*>(urow + F + f);
+    }
+}
+
+// Rows are visited in order; the gate and up values of row group i + 1 are
+// loaded before row group i is stored (interior tiles), or just before it
+// (edge tiles, whose row groups may be absent).
 template <int TM, int TN, bool CHECK>
 __device__ __forceinline__ void epi_tile_swiglu_bwd(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN]) {
   const int F = p.N;
+  const bf16* U = static_cast<const bf16*>(p.U);
+  bf16* C = static_cast<bf16*>(p.C);
+  if constexpr (CHECK) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = mrow + 32 * i;
-    if (CHECK && m >= p.M) continue;
-    const bf16* urow = static_cast<const bf16*>(p.U) + (int64_t)m * p.ld2;
-    bf16* crow = static_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
-    // gate and up of the row group first (all loads in flight), then the stores
-    bf16x4 g[TN][4], u[TN][4];
+    for (int i = 0; i < TM; ++i) {
+      const int m = mrow + 32 * i;
+      if (m >= p.M) continue;
+      bf16x4 g[TN][4], u[TN][4];
+      swiglu_bwd_load<TN>(p, U + (int64_t)m * p.ld2, ncol, F, g, u, true);
+      swiglu_bwd_store<TN>(p, C + (int64_t)m * p.ldc, ncol, F, g, u, acc[i], true);
+    }
+  } else {
+    bf16x4 g[2][TN][4], u[2][TN][4];
+    swiglu_bwd_load<TN>(p, U + (int64_t)mrow * p.ld2, ncol, F, g[0], u[0], false);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = ncol + 32 * j + 8 * q;
-        if (CHECK && f >= p.N) continue;
-        g[j][q] = *reinterpret_cast<const bf16x4*>(urow + f);
-        u[j][q] = *reinterpret_cast<const bf16x4*>(urow + F + f);
-      }
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = ncol + 32 * j + 8 * q;
-        if (CHECK && f >= p.N) continue;
-        float dg[4], du[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = p.alpha * acc[i][j][4 * q + e];
-          const float gf = bf2f(g[j][q][e]), sg = sigmoid_fast(gf);
-          du[e] = v * gf * sg;
-          dg[e] = v * bf2f(u[j][q][e]) * sg * fmaf(gf, 1.f - sg, 1.f);
-        }
-        const bf16x2 g01 = f2bf2(dg[0], dg[1]), g23 = f2bf2(dg[2], dg[3]);
-        const bf16x2 u01 = f2bf2(du[0], du[1]), u23 = f2bf2(du[2], du[3]);
-        *reinterpret_cast<bf16x4*>(crow + f) = bf16x4{g01[0], g01[1], g23[0], g23[1]};
-        *reinterpret_cast<bf16x4*>(crow + F + f) = bf16x4{u01[0], u01[1], u23[0], u23[1]};
-      }
+    for (int i = 0; i < TM; ++i) {
+      const int m = mrow + 32 * i;
+      if (i + 1 < TM)
+        swiglu_bwd_load<TN>(p, U + (int64_t)(m + 32) * p.ld2, ncol, F, g[(i + 1) & 1], u[(i + 1) & 1], false);
+      swiglu_bwd_store<TN>(p, C + (int64_t)m * p.ldc, ncol, F, g[i & 1], u[i & 1], acc[i], false);
+    }
   }
 }
 

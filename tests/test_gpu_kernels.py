@@ -72,6 +72,32 @@ def test_gemm_bf16_integer_exact_large_tiles(g):
         assert np.array_equal(host(C), ref), (ak, bk)
 
 
+@pytest.mark.parametrize("K", [128, 384, 200])
+def test_gemm_bf16_many_tiles_exact(g, K):
+    """More output tiles than compute units (several rounds of blocks), ragged
+    M and N so that edge tiles sit between interior ones, even and odd K step
+    counts: the float32 store and the residual epilogue stay exact on integer
+    operands, in all four operand layouts."""
+    import torch
+    M, N = 4104, 4136
+    announce(f"gemm bf16 many tiles M={M} N={N} K={K}")
+    rng = np.random.default_rng(K)
+    A = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, size=(N, K)).astype(np.float32)
+    R = rng.integers(-50, 51, size=(M, N)).astype(np.float32)
+    ref = (A.astype(np.int64) @ B.astype(np.int64).T).astype(np.float32)
+    dR = dev(R)
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    for ak, bk in LAYOUTS:
+        dA, dB = dev(_stored(A, ak), torch.bfloat16), dev(_stored(B, bk), torch.bfloat16)
+        C.fill_(7.0)
+        g.op_gemm(dA, dB, C, M, N, K, a_kmajor=ak, b_kmajor=bk)
+        assert np.array_equal(host(C), ref), ("store", ak, bk)
+        C.fill_(7.0)
+        g.op_gemm(dA, dB, C, M, N, K, a_kmajor=ak, b_kmajor=bk, epilogue=g.EPI_RESIDUAL, R=dR)
+        assert np.array_equal(host(C), ref + R), ("residual", ak, bk)
+
+
 @pytest.mark.parametrize("ak,bk", LAYOUTS)
 def test_gemm_bf16_accumulate_split_k_exact(g, ak, bk):
     """Few output tiles and a long K take the split-K path (atomic adds of

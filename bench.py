@@ -57,14 +57,16 @@ def flops_per_token(n_params: int, L=12, H=12, hd=64, T_=1024) -> int:
     return 6 * n_params + 12 * L * H * hd * T_
 
 
-def gemm_site_flops(rows=B * T, F=3072, FC=None):
+def gemm_site_flops(rows=B * T, F=3072, FC=None, L=12):
     """Algorithmic FLOPs of one launch at each GEMM site of the micro-step
     (rows = B*T, C = 768, MLP width F, V = 50304; the lm_head products take
     all rows in one launch).  FC is the fc product's output width: F for
-    GPT-2, 2F (gate and up) for the rotary variant."""
+    GPT-2, 2F (gate and up) for the rotary variant.  gemm.dw is the grouped
+    launch of all L blocks' four weight-gradient products."""
     M, C, V = rows, 768, 50304
     FC = F if FC is None else FC
     return {
+        "gemm.dw": L * 2 * M * C * (3 * C + C + FC + F),
         "gemm.qkv": 2 * M * 3 * C * C,
         "gemm.attn_proj": 2 * M * C * C,
         "gemm.fc": 2 * M * FC * C,

@@ -21,9 +21,9 @@ from dataclasses import dataclass
 from . import _ffi
 from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noqa: F401
                    EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_ACCUMULATE, EPI_GELU_GRAD, EPI_MUL,
-                   EPI_ROPE, EPI_SWIGLU, EPI_SWIGLU_BWD, ARCH_GPT2, ARCH_ROTARY)
+                   EPI_ROPE, EPI_SWIGLU, EPI_SWIGLU_BWD, ARCH_GPT2, ARCH_ROTARY, GPT2_ERR_ARG)
 
-__all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm",
+__all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm", "op_gemm_grouped",
            "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
            "op_rope_table", "op_rope_bwd", "op_rmsnorm_fwd", "op_rmsnorm_bwd", "query_sizes", "param_table",
            "GPT2_ROTARY_124M"]
@@ -254,6 +254,33 @@ def op_gemm(A, B, C, M, N, K, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, 
     a.rope, a.rope_period, a.rope_cols = _ptr(rope), rope_period, rope_cols
     a.ld2 = ld2 if ld2 is not None else {EPI_SWIGLU: N, EPI_SWIGLU_BWD: 2 * N}.get(epilogue, 0)
     check(lib().gpt2_op_gemm(_stream_ptr(stream), ct.byref(a)), "gpt2_op_gemm")
+
+
+def op_gemm_grouped(products, stream=None):
+    """Weight-gradient products in one launch: each item (A, B, C, M, N, K,
+    row_sum, alpha) computes C[M, N] += alpha * A^T B over K (A bf16 stored
+    [K][M], B bf16 stored [K][N], C float32 [M][N]) and, when row_sum is a
+    tensor, row_sum[m] += alpha * sum_k A[k][m]."""
+    import torch
+    n = len(products)
+    arr = (_ffi.GemmArgs * n)()
+    rs = (ct.c_void_p * n)()
+    for i, (A, B, C, M, N, K, row_sum, alpha) in enumerate(products):
+        a = arr[i]
+        a.M, a.N, a.K, a.dtype = M, N, K, PRECISION_BF16
+        a.a_kmajor, a.b_kmajor = 0, 0
+        a.lda, a.ldb, a.ldc = M, N, N
+        a.A, a.B, a.C = A.data_ptr(), B.data_ptr(), C.data_ptr()
+        a.alpha = alpha
+        a.epilogue = EPI_ACCUMULATE
+        a.out_bf16 = 0
+        rs[i] = row_sum.data_ptr() if row_sum is not None else None
+    nbytes = lib().gpt2_gemm_grouped_workspace_bytes(arr, n)
+    if nbytes == 0:
+        raise GPT2Error(GPT2_ERR_ARG, "gpt2_gemm_grouped_workspace_bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    check(lib().gpt2_op_gemm_grouped(_stream_ptr(stream), arr, n, rs, ws.data_ptr()), "gpt2_op_gemm_grouped")
+    return ws
 
 
 def op_rope_table(T, base=10000.0, stream=None):

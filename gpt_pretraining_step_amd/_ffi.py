@@ -99,6 +99,9 @@ SIGNATURES = {
     "gpt2_lmhead_ce": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int,
                                   ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p]),
     "gpt2_op_gemm": (ct.c_int, [ct.c_void_p, ct.POINTER(GemmArgs)]),
+    "gpt2_gemm_grouped_workspace_bytes": (ct.c_size_t, [ct.POINTER(GemmArgs), ct.c_int]),
+    "gpt2_op_gemm_grouped": (ct.c_int, [ct.c_void_p, ct.POINTER(GemmArgs), ct.c_int, ct.POINTER(ct.c_void_p),
+                                        ct.c_void_p]),
     "gpt2_op_colsum": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int64, ct.c_void_p]),
     "gpt2_op_layernorm_fwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
                                          ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int]),

@@ -96,6 +96,15 @@ void prof_end(const Launch& L);
 // row_sum (optional): row_sum[m] += alpha * sum_k A(m, k) -- the bias gradient of
 // a weight-gradient product (bf16 only).
 hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum = nullptr);
+// Grouped weight-gradient products (bf16, both operands K-slow, ACCUMULATE
+// into float32, optional bias row sums): n products in one launch, one
+// 256x256 output tile per block and no K split, so no atomics on C.  The
+// group table lives in device memory (gemm_grouped_table_bytes); its image
+// is built on the host by gemm_grouped_table and copied there by the caller.
+int gemm_grouped_units(const gpt2_gemm_args* a, int n);
+size_t gemm_grouped_table_bytes(int n, int units);
+void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, int units, void* host);
+hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units);
 hipError_t launch_colsum(const Launch& L, const void* y, int y_bf16, int M, int N, int64_t ld, float* db);
 
 hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y,

@@ -14,6 +14,7 @@
 #include "gemm_kernel.h"
 
 #include <algorithm>
+#include <cstring>
 
 namespace g2 {
 
@@ -269,6 +270,60 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
   if (ak && !bk) return dispatch_bf16<true, false>(L, p, a.epilogue, ob);
   if (!ak && bk) return dispatch_bf16<false, true>(L, p, a.epilogue, ob);
   return dispatch_bf16<false, false>(L, p, a.epilogue, ob);
+}
+
+// ------------------------------------------------------- grouped products
+
+namespace {
+constexpr int kGroupTile = 256;
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+int group_units(const gpt2_gemm_args& a) {
+  return ((a.M + kGroupTile - 1) / kGroupTile) * ((a.N + kGroupTile - 1) / kGroupTile);
+}
+}  // namespace
+
+int gemm_grouped_units(const gpt2_gemm_args* a, int n) {
+  int64_t u = 0;
+  for (int i = 0; i < n; ++i) u += group_units(a[i]);
+  return u < (1 << 30) ? (int)u : -1;
+}
+
+size_t gemm_grouped_table_bytes(int n, int units) {
+  return align256(n * sizeof(GemmP)) + align256(n * sizeof(int)) + align256((size_t)units * sizeof(int));
+}
+
+// Host image of the table: parameters of every product, its first unit, and
+// the product of every unit (no pointers into itself: it can be copied
+// anywhere).
+void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, int units, void* host) {
+  char* h = static_cast<char*>(host);
+  memset(h, 0, gemm_grouped_table_bytes(n, units));
+  GemmP* ps = reinterpret_cast<GemmP*>(h);
+  int* first = reinterpret_cast<int*>(h + align256(n * sizeof(GemmP)));
+  int* group_of = reinterpret_cast<int*>(h + align256(n * sizeof(GemmP)) + align256(n * sizeof(int)));
+  int u = 0;
+  for (int i = 0; i < n; ++i) {
+    GemmP p = make_params(a[i]);
+    p.row_sum = row_sums ? row_sums[i] : nullptr;
+    p.tiles_m = (a[i].M + kGroupTile - 1) / kGroupTile;
+    p.tiles_n = (a[i].N + kGroupTile - 1) / kGroupTile;
+    ps[i] = p;
+    first[i] = u;
+    for (int k = 0; k < p.tiles_m * p.tiles_n; ++k) group_of[u++] = i;
+  }
+}
+
+hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units) {
+  const char* d = static_cast<const char*>(d_table);
+  GemmGroups t;
+  t.p = reinterpret_cast<const GemmP*>(d);
+  t.first = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)));
+  t.group_of = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)) + align256(n * sizeof(int)));
+  prof_begin(L);
+  gemm2_grouped_kernel<kGroupTile, kGroupTile, 64, 2, 4, 2, false, false, GPT2_EPI_ACCUMULATE, false, false, false>
+      <<<units, 512, 0, L.stream>>>(t);
+  prof_end(L);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ column sums

@@ -612,12 +612,15 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
 }
 
 // Tile -> block mapping.  Blocks are handed to the 8 XCDs round-robin; the
-// remap makes consecutive logical tiles run on one XCD (sharing its L2), and
-// the grouped order walks GROUP_M row tiles per column panel.
-__device__ __forceinline__ void tile_of_block(const GemmP& p, int& tm, int& tn, int& split) {
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+// remap makes consecutive logical units (tiles, or tiles of a group) run on
+// one XCD (sharing its L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  return (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+}
+
+// Unit -> (row tile, column tile, K split) of one product: the grouped order
+// walks GROUP_M row tiles per column panel.
+__device__ __forceinline__ void tile_of_unit(const GemmP& p, int bid, int& tm, int& tn, int& split) {
   const int per_split = p.tiles_m * p.tiles_n;
   split = bid / per_split;
   int t = bid - split * per_split;
@@ -637,9 +640,11 @@ union GV8 {
   uint32_t w[4];
 };
 
+// One block's unit of a product: its output tile (and K split), main loop
+// and epilogue.
 template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
           bool ATOMIC, bool SWAP>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
+__device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
   constexpr int NW = WGM * WGN;
   constexpr int NT = 64 * NW;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   __shared__ __attribute__((aligned(16))) bf16 lds1[STAGE];
 
   int tm, tn, split;
-  tile_of_block(p, tm, tn, split);
+  tile_of_unit(p, unit, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
@@ -862,8 +867,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   }
 }
 
+template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
+          bool ATOMIC, bool SWAP>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
+  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, xcd_remap(blockIdx.x, gridDim.x));
+}
 
+// Several independent products in one launch.  Unit u (after the XCD remap)
+// belongs to product group_of[u] and is that product's unit u - first[g].
+struct GemmGroups {
+  const GemmP* __restrict__ p;
+  const int* __restrict__ first;
+  const int* __restrict__ group_of;
+};
 
-
+template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
+          bool ATOMIC, bool SWAP>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_grouped_kernel(GemmGroups t) {
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = t.group_of[u];
+  const GemmP p = t.p[g];
+  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, u - t.first[g]);
+}
 
 }  // namespace g2

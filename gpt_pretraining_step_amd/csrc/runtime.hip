@@ -250,9 +250,16 @@ struct Layout {
   std::vector<size_t> Rin, Rmid, A1, mean1, rstd1, QKV, Y, LSE, A2, mean2, rstd2, U, G;
   size_t Z = 0, meanf = 0, rstdf = 0, act_bytes = 0;
   // scratch
-  size_t dR = 0, dRb = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
+  size_t dR = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
   size_t ce_stats = 0, rope = 0;
   size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, scratch_bytes = 0;
+  // bf16: the first operands of the weight-gradient products, kept per layer
+  // until the products run together at the end of the backward: dRbS[2l+1]
+  // the residual gradient entering layer l's MLP branch, dRbS[2l] its
+  // attention branch; dUL[l], dQKVL[l] the gradients of the fc and qkv
+  // outputs; dw_table the group table of that launch
+  std::vector<size_t> dRbS, dUL, dQKVL;
+  size_t dw_table = 0, dw_table_bytes = 0;
 };
 
 struct Bump {
@@ -304,13 +311,31 @@ Layout build_layout(const gpt2_config& c) {
   y.norm = s.take(256);
   y.parts = s.take(kNormParts * 4);
   y.dR = s.take(rows * C * 4);
-  y.dRb = s.take(rows * C * y.es);
   y.dA = s.take(rows * C * 4);
-  y.dQKV = s.take(rows * 3 * C * y.es);
   y.dY = s.take(rows * C * y.es);
-  y.dU = s.take(rows * FU * y.es);
+  if (c.precision != GPT2_PRECISION_BF16) {  // bf16 mode keeps these per layer (below)
+    y.dQKV = s.take(rows * 3 * C * y.es);
+    y.dU = s.take(rows * FU * y.es);
+  }
   y.attnD = s.take(rows * H * 4);
   if (c.arch == GPT2_ARCH_ROTARY) y.rope = s.take((size_t)c.block_size * 32 * sizeof(float2));
+  if (c.precision == GPT2_PRECISION_BF16) {
+    for (int l = 0; l < 2 * L; ++l) y.dRbS.push_back(s.take(rows * C * 2));
+    for (int l = 0; l < L; ++l) {
+      y.dUL.push_back(s.take(rows * FU * 2));
+      y.dQKVL.push_back(s.take(rows * 3 * C * 2));
+    }
+    std::vector<gpt2_gemm_args> dw(4 * (size_t)L);
+    for (int l = 0; l < L; ++l) {
+      const int mn[4][2] = {{(int)C, (int)F}, {(int)FU, (int)C}, {(int)C, (int)C}, {3 * (int)C, (int)C}};
+      for (int k = 0; k < 4; ++k) {
+        dw[4 * l + k].M = mn[k][0];
+        dw[4 * l + k].N = mn[k][1];
+      }
+    }
+    y.dw_table_bytes = gemm_grouped_table_bytes(4 * L, gemm_grouped_units(dw.data(), 4 * L));
+    y.dw_table = s.take(y.dw_table_bytes);
+  }
   if (c.precision == GPT2_PRECISION_BF16) {
     // fused lm_head + cross-entropy over all rows at once: bf16 logits (then
     // dlogits, in place) and per-tile softmax statistics
@@ -336,6 +361,7 @@ struct gpt2_ctx {
   hipStream_t stream;
   int64_t t = 0;
   Prof prof;
+  std::vector<char> dw_image;  // the group table last copied to the device
 
   bool bf() const { return cfg.precision == GPT2_PRECISION_BF16; }
   Launch at(const char* site) { return Launch{stream, &prof, site}; }
@@ -413,6 +439,45 @@ static hipError_t linear_dw(gpt2_ctx* c, const char* site, const void* dy, int M
   hipError_t e = launch_gemm(c->at(site), a);
   if (e != hipSuccess || bi < 0) return e;
   return launch_colsum(c->at("colsum"), dy_f32, 0, M, N, N, c->Gr(bi));
+}
+
+// Weight-gradient products of the bf16 backward, queued per layer and run
+// as one grouped launch once every layer's input gradients exist: with all
+// layers' output tiles in one grid there are enough tiles to fill the chip
+// without splitting K, so no partial sums are added atomically.
+struct DwQueue {
+  std::vector<gpt2_gemm_args> a;
+  std::vector<float*> row_sum;
+};
+
+static void queue_dw(gpt2_ctx* c, DwQueue& q, const void* dy, int M, int N, const void* x, int K, int wi, int bi) {
+  gpt2_gemm_args a = gemm_base(GPT2_PRECISION_BF16);
+  a.M = N; a.N = K; a.K = M;
+  a.a_kmajor = 0; a.b_kmajor = 0;
+  a.lda = N; a.ldb = K; a.ldc = K;
+  a.A = dy; a.B = x; a.C = c->Gr(wi);
+  a.epilogue = GPT2_EPI_ACCUMULATE;
+  q.a.push_back(a);
+  q.row_sum.push_back(bi >= 0 ? c->Gr(bi) : nullptr);
+}
+
+static hipError_t run_dw(gpt2_ctx* c, DwQueue& q) {
+  const int n = (int)q.a.size();
+  const int units = gemm_grouped_units(q.a.data(), n);
+  const size_t bytes = gemm_grouped_table_bytes(n, units);
+  if (units < 1 || bytes > c->lay.dw_table_bytes) return hipErrorInvalidValue;
+  std::vector<char> image(bytes);
+  gemm_grouped_table(q.a.data(), q.row_sum.data(), n, units, image.data());
+  void* d_table = c->scr(c->lay.dw_table);
+  if (image != c->dw_image) {
+    // only when the token count changes: no earlier launch may still read
+    // the table
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(d_table, image.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+    c->dw_image.swap(image);
+  }
+  return launch_gemm_grouped(c->at("gemm.dw"), d_table, n, units);
 }
 
 // Tied lm_head + cross-entropy, bf16, all rows at once: the statistics
@@ -537,42 +602,56 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
 
   // ---- backward through the blocks
   float* dR = c->scr<float>(y.dR);
-  bf16* dRb = bf ? c->scr<bf16>(y.dRb) : nullptr;
-  const void* dRop = bf ? static_cast<const void*>(dRb) : static_cast<const void*>(dR);
+  // bf16 copies of the residual gradient, one slot per (layer, branch) (the
+  // weight-gradient products read them after the loop); float32 mode reads
+  // dR itself
+  auto dRb_slot = [&](int s) -> bf16* { return bf && s >= 0 ? c->scr<bf16>(y.dRbS[s]) : nullptr; };
   // gradient of an LN output: bf16 in BF16 mode (the products' output type,
   // as under autocast), float32 otherwise; dZ (float32) lives here first and
   // the final LN backward consumes it before the buffer is reused
   void* dA = c->scr(y.dA);
+  DwQueue q;
+  // dW += dy^T x (+ bias row sums): queued in bf16 mode, run now in float32
+  auto dw = [&](const char* site, const void* dy, int N, const void* x, int K, int wi, int bi,
+                const float* dy_f32) -> hipError_t {
+    if (bf) {
+      queue_dw(c, q, dy, M, N, x, K, wi, bi);
+      return hipSuccess;
+    }
+    return linear_dw(c, site, dy, M, N, x, K, wi, bi, dy_f32);
+  };
   HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
   HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dZ, 0, rlast, c->act<float>(y.meanf), c->act<float>(y.rstdf),
-                                 c->P(c->tab.lnf_w), dR, dRb, c->Gr(c->tab.lnf_w), c->Gr(c->tab.lnf_b), M, C));
-  void* dU = c->scr(y.dU);
+                                 c->P(c->tab.lnf_w), dR, dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w),
+                                 c->Gr(c->tab.lnf_b), M, C));
   void* dY = c->scr(y.dY);
-  void* dQKV = c->scr(y.dQKV);
   for (int l = g.n_layer - 1; l >= 0; --l) {
+    const void* dRm = bf ? static_cast<const void*>(dRb_slot(2 * l + 1)) : static_cast<const void*>(dR);
+    const void* dRa = bf ? static_cast<const void*>(dRb_slot(2 * l)) : static_cast<const void*>(dR);
+    void* dU = c->scr(bf ? y.dUL[l] : y.dU);
+    void* dQKV = c->scr(bf ? y.dQKVL[l] : y.dQKV);
     // MLP branch: R_{l+1} = Rmid + G Wmp^T + b
-    HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRop, M, C, c->act(y.G[l]), F, c->L(l, MLP_W), c->L(l, MLP_B), dR));
+    HIP_TRY(dw("gemm.mlp_proj_dw", dRm, C, c->act(y.G[l]), F, c->L(l, MLP_W), c->L(l, MLP_B), dR));
     // dU = (dR W_mp) * gelu'(u), gelu'(u) kept by the forward
-    HIP_TRY(linear_dx(c, "gemm.mlp_proj_dx", dRop, M, C, c->L(l, MLP_W), F, GPT2_EPI_MUL, true, dU,
-                      c->act(y.U[l])));
-    HIP_TRY(linear_dw(c, "gemm.fc_dw", dU, M, F, c->act(y.A2[l]), C, c->L(l, FC_W), c->L(l, FC_B),
-                      static_cast<const float*>(dU)));
+    HIP_TRY(linear_dx(c, "gemm.mlp_proj_dx", dRm, M, C, c->L(l, MLP_W), F, GPT2_EPI_MUL, true, dU, c->act(y.U[l])));
+    HIP_TRY(dw("gemm.fc_dw", dU, F, c->act(y.A2[l]), C, c->L(l, FC_W), c->L(l, FC_B), static_cast<const float*>(dU)));
     HIP_TRY(linear_dx(c, "gemm.fc_dx", dU, M, F, c->L(l, FC_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, bf, c->act<float>(y.Rmid[l]), c->act<float>(y.mean2[l]),
-                                   c->act<float>(y.rstd2[l]), c->P(c->L(l, LN2_W)), dR, dRb, c->Gr(c->L(l, LN2_W)),
-                                   c->Gr(c->L(l, LN2_B)), M, C));
+                                   c->act<float>(y.rstd2[l]), c->P(c->L(l, LN2_W)), dR, dRb_slot(2 * l),
+                                   c->Gr(c->L(l, LN2_W)), c->Gr(c->L(l, LN2_B)), M, C));
     // attention branch: Rmid = R_l + Y Wo^T + b
-    HIP_TRY(linear_dw(c, "gemm.attn_proj_dw", dRop, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
-    HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRop, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
+    HIP_TRY(dw("gemm.attn_proj_dw", dRa, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
+    HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
                                  c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
-    HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
-                      static_cast<const float*>(dQKV)));
+    HIP_TRY(dw("gemm.qkv_dw", dQKV, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
+               static_cast<const float*>(dQKV)));
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, bf, c->act<float>(y.Rin[l]), c->act<float>(y.mean1[l]),
-                                   c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb, c->Gr(c->L(l, LN1_W)),
-                                   c->Gr(c->L(l, LN1_B)), M, C));
+                                   c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1),
+                                   c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)), M, C));
   }
+  if (bf) HIP_TRY(run_dw(c, q));
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V));
   return GPT2_OK;
 }
@@ -638,41 +717,48 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
 
   // ---- backward
   float* dR = c->scr<float>(y.dR);
-  bf16* dRb = c->scr<bf16>(y.dRb);
+  // bf16 copies of the residual gradient, one slot per (layer, branch), and
+  // per-layer fc / qkv output gradients: the weight-gradient products read
+  // them in one grouped launch after the loop
+  auto dRb_slot = [&](int s) -> bf16* { return s >= 0 ? c->scr<bf16>(y.dRbS[s]) : nullptr; };
   void* dA = c->scr(y.dA);  // dZ (float32) first, then bf16 norm-output gradients
-  void* dGU = c->scr(y.dU);
   void* dY = c->scr(y.dY);
-  bf16* dQKV = c->scr<bf16>(y.dQKV);
+  DwQueue q;
   HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
-  HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dZ, 0, rlast, c->act<float>(y.rstdf), c->P(c->tab.lnf_w), dR, dRb,
-                             c->Gr(c->tab.lnf_w), M, C));
+  HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dZ, 0, rlast, c->act<float>(y.rstdf), c->P(c->tab.lnf_w), dR,
+                             dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w), M, C));
   for (int l = g.n_layer - 1; l >= 0; --l) {
+    bf16* dRm = dRb_slot(2 * l + 1);
+    bf16* dRa = dRb_slot(2 * l);
+    void* dGU = c->scr(y.dUL[l]);
+    bf16* dQKV = c->scr<bf16>(y.dQKVL[l]);
     // feed-forward: R_{l+1} = Rmid + act Wd^T
-    HIP_TRY(linear_dw(c, "gemm.mlp_proj_dw", dRb, M, C, c->act(y.G[l]), F, c->L(l, MLP_W), -1, nullptr));
+    queue_dw(c, q, dRm, M, C, c->act(y.G[l]), F, c->L(l, MLP_W), -1);
     {  // d(act) = dR Wd; dgate, dup through the SwiGLU gate
       gpt2_gemm_args a = gemm_base(dt);
       a.M = M; a.N = F; a.K = C;
       a.a_kmajor = 1; a.b_kmajor = 0;
       a.lda = C; a.ldb = F; a.ldc = 2 * F; a.ld2 = 2 * F;
-      a.A = dRb; a.B = c->W(c->L(l, MLP_W)); a.C = dGU; a.U = c->act(y.U[l]);
+      a.A = dRm; a.B = c->W(c->L(l, MLP_W)); a.C = dGU; a.U = c->act(y.U[l]);
       a.epilogue = GPT2_EPI_SWIGLU_BWD; a.out_bf16 = 1;
       HIP_TRY(launch_gemm(c->at("gemm.mlp_proj_dx"), a));
     }
-    HIP_TRY(linear_dw(c, "gemm.fc_dw", dGU, M, 2 * F, c->act(y.A2[l]), C, c->L(l, FC_W), -1, nullptr));
+    queue_dw(c, q, dGU, M, 2 * F, c->act(y.A2[l]), C, c->L(l, FC_W), -1);
     HIP_TRY(linear_dx(c, "gemm.fc_dx", dGU, M, 2 * F, c->L(l, FC_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rmid[l]), c->act<float>(y.rstd2[l]),
-                               c->P(c->L(l, LN2_W)), dR, dRb, c->Gr(c->L(l, LN2_W)), M, C));
+                               c->P(c->L(l, LN2_W)), dR, dRa, c->Gr(c->L(l, LN2_W)), M, C));
     // attention: Rmid = R_l + Y Wo^T
-    HIP_TRY(linear_dw(c, "gemm.attn_proj_dw", dRb, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1, nullptr));
-    HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRb, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
+    queue_dw(c, q, dRa, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1);
+    HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
                                  c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
     HIP_TRY(launch_rope_bwd(c->at("rope.bwd"), dQKV, M, 3 * C, 2 * C, T, rope));
-    HIP_TRY(linear_dw(c, "gemm.qkv_dw", dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), -1, nullptr));
+    queue_dw(c, q, dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), -1);
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rin[l]), c->act<float>(y.rstd1[l]),
-                               c->P(c->L(l, LN1_W)), dR, dRb, c->Gr(c->L(l, LN1_W)), M, C));
+                               c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C));
   }
+  HIP_TRY(run_dw(c, q));
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V));
   return GPT2_OK;
 }
@@ -965,6 +1051,38 @@ static bool gemm_args_ok(const gpt2_gemm_args* a) {
 int gpt2_op_gemm(void* stream, const gpt2_gemm_args* a) {
   if (!gemm_args_ok(a)) return GPT2_ERR_ARG;
   HIP_TRY(launch_gemm(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, *a));
+  return GPT2_OK;
+}
+
+static bool grouped_args_ok(const gpt2_gemm_args* a, int n) {
+  if (!a || n < 1) return false;
+  for (int i = 0; i < n; ++i) {
+    if (!gemm_args_ok(a + i)) return false;
+    if (a[i].dtype != GPT2_PRECISION_BF16 || a[i].a_kmajor || a[i].b_kmajor ||
+        a[i].epilogue != GPT2_EPI_ACCUMULATE)
+      return false;
+  }
+  return gemm_grouped_units(a, n) > 0;
+}
+
+size_t gpt2_gemm_grouped_workspace_bytes(const gpt2_gemm_args* args, int n) {
+  if (!grouped_args_ok(args, n)) return 0;
+  return gemm_grouped_table_bytes(n, gemm_grouped_units(args, n));
+}
+
+int gpt2_op_gemm_grouped(void* stream, const gpt2_gemm_args* args, int n, float* const* d_row_sums,
+                         void* d_workspace) {
+  if (!grouped_args_ok(args, n) || !d_workspace || ((uintptr_t)d_workspace & 15)) return GPT2_ERR_ARG;
+  if (d_row_sums)
+    for (int i = 0; i < n; ++i)
+      if ((uintptr_t)d_row_sums[i] & 3) return GPT2_ERR_ARG;
+  const int units = gemm_grouped_units(args, n);
+  std::vector<char> host(gemm_grouped_table_bytes(n, units));
+  gemm_grouped_table(args, d_row_sums, n, units, host.data());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipMemcpyAsync(d_workspace, host.data(), host.size(), hipMemcpyHostToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(launch_gemm_grouped(Launch{s, nullptr, ""}, d_workspace, n, units));
   return GPT2_OK;
 }
 

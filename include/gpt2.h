@@ -327,6 +327,24 @@ typedef struct {
 } gpt2_gemm_args;
 int gpt2_op_gemm(void* stream, const gpt2_gemm_args* args);
 
+/* Grouped weight-gradient products: the n products args[0..n) (each a
+ * Linear's weight gradient dW += dY^T X summed over tokens, the backward of
+ * "How I trained my own GPT-2 124M on FineWeb-Edu" section 2.3's Linear
+ * layers) in ONE launch.  Every product must be bf16 with both operands
+ * K-slow (a_kmajor = b_kmajor = 0), epilogue GPT2_EPI_ACCUMULATE, no bias,
+ * and satisfy gpt2_op_gemm's rules; d_row_sums (a host array of n device
+ * pointers, or NULL; entries may be NULL) receive row_sum_i[m] +=
+ * alpha_i * sum_k A_i(m, k) (the bias gradient).  Each output tile of each
+ * product is computed whole by one block (no K split, no atomics on C), so
+ * the n outputs must not overlap.  d_workspace: device memory of
+ * gpt2_gemm_grouped_workspace_bytes(args, n) bytes (16-byte aligned) that
+ * receives the group table; the call copies it there synchronously (it
+ * blocks until the copy is done), then launches on the stream.
+ * GPT2_ERR_ARG for an invalid product or n < 1. */
+size_t gpt2_gemm_grouped_workspace_bytes(const gpt2_gemm_args* args, int n);
+int gpt2_op_gemm_grouped(void* stream, const gpt2_gemm_args* args, int n, float* const* d_row_sums,
+                         void* d_workspace);
+
 /* Column sums: db[n] += sum_m Y[m][n], Y [M][ld] in bf16 (y_bf16=1) or float32. */
 int gpt2_op_colsum(void* stream, const void* d_y, int y_bf16, int M, int N, int64_t ld, float* d_db);
 

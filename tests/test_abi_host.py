@@ -155,3 +155,32 @@ def test_null_arguments_are_rejected():
     assert L.gpt2_create(ct.byref(c), ct.byref(b), None, ct.byref(h)) == _ffi.GPT2_ERR_UNBOUND
     d = _ffi.ParamDesc()
     assert L.gpt2_param_info(ct.byref(c), 10_000, ct.byref(d)) == _ffi.GPT2_ERR_ARG
+
+
+def test_grouped_products_validate_on_the_host():
+    """The grouped weight-gradient call accepts only bf16 products with both
+    operands K-slow that accumulate into float32, and says so before any
+    device work (fake, aligned pointers: nothing is dereferenced)."""
+    L = _lib()
+    from gpt_pretraining_step_amd import _ffi
+    arr = (_ffi.GemmArgs * 2)()
+    for i, (M, N) in enumerate([(768, 3072), (264, 136)]):
+        a = arr[i]
+        a.M, a.N, a.K, a.dtype = M, N, 1024, _ffi.PRECISION_BF16
+        a.lda, a.ldb, a.ldc = M, N, N
+        a.A, a.B, a.C = 0x10000, 0x20000, 0x30000
+        a.alpha, a.epilogue = 1.0, _ffi.EPI_ACCUMULATE
+    # 3 x 12 + 2 x 1 tiles of 256 x 256: the table holds both products' parameters and the unit map
+    nbytes = L.gpt2_gemm_grouped_workspace_bytes(arr, 2)
+    assert nbytes >= 38 * 4
+    assert L.gpt2_gemm_grouped_workspace_bytes(arr, 0) == 0
+    assert L.gpt2_op_gemm_grouped(None, arr, 0, None, ct.c_void_p(0x40000)) == _ffi.GPT2_ERR_ARG
+    assert L.gpt2_op_gemm_grouped(None, arr, 2, None, None) == _ffi.GPT2_ERR_ARG
+    for field, bad in [("a_kmajor", 1), ("b_kmajor", 1), ("epilogue", _ffi.EPI_STORE), ("dtype", _ffi.PRECISION_FP32),
+                       ("out_bf16", 1), ("lda", 100)]:
+        old = getattr(arr[1], field)
+        setattr(arr[1], field, bad)
+        assert L.gpt2_gemm_grouped_workspace_bytes(arr, 2) == 0, field
+        assert L.gpt2_op_gemm_grouped(None, arr, 2, None, ct.c_void_p(0x40000)) == _ffi.GPT2_ERR_ARG, field
+        setattr(arr[1], field, old)
+    assert L.gpt2_gemm_grouped_workspace_bytes(arr, 2) == nbytes

@@ -98,6 +98,34 @@ def test_gemm_bf16_many_tiles_exact(g, K):
         assert np.array_equal(host(C), ref + R), ("residual", ak, bk)
 
 
+def test_gemm_grouped_exact(g):
+    """Weight-gradient products of different shapes in one launch (K-slow
+    operands, ragged edge tiles, one tiny product): on integer operands
+    C += alpha A^T B and the bias row sums stay exact, and every product
+    lands in its own output."""
+    import torch
+    shapes = [(768, 3072, 1024, True, 1.0), (3072, 768, 1024, True, 0.5), (264, 136, 520, False, 1.0),
+              (8, 16, 64, True, 2.0), (2304, 776, 1032, True, 1.0)]
+    announce(f"gemm grouped {len(shapes)} products")
+    rng = np.random.default_rng(5)
+    items, refs = [], []
+    for M, N, K, with_rs, alpha in shapes:
+        A = rng.integers(-4, 5, size=(K, M)).astype(np.float32)  # stored [K][M]
+        B = rng.integers(-4, 5, size=(K, N)).astype(np.float32)
+        C0 = rng.integers(-100, 101, size=(M, N)).astype(np.float32)
+        r0 = rng.integers(-100, 101, size=M).astype(np.float32)
+        refC = C0 + alpha * (A.astype(np.int64).T @ B.astype(np.int64)).astype(np.float64)
+        refR = r0 + alpha * A.astype(np.int64).sum(axis=0) if with_rs else None
+        C, R = dev(C0), (dev(r0) if with_rs else None)
+        items.append((dev(A, torch.bfloat16), dev(B, torch.bfloat16), C, M, N, K, R, alpha))
+        refs.append((C, refC, R, refR))
+    g.op_gemm_grouped(items)
+    for i, (C, refC, R, refR) in enumerate(refs):
+        assert np.array_equal(host(C), refC.astype(np.float32)), i
+        if R is not None:
+            assert np.array_equal(host(R), refR.astype(np.float32)), i
+
+
 @pytest.mark.parametrize("ak,bk", LAYOUTS)
 def test_gemm_bf16_accumulate_split_k_exact(g, ak, bk):
     """Few output tiles and a long K take the split-K path (atomic adds of

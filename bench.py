@@ -62,11 +62,12 @@ def gemm_site_flops(rows=B * T, F=3072, FC=None, L=12):
     (rows = B*T, C = 768, MLP width F, V = 50304; the lm_head products take
     all rows in one launch).  FC is the fc product's output width: F for
     GPT-2, 2F (gate and up) for the rotary variant.  gemm.dw is the grouped
-    launch of all L blocks' four weight-gradient products."""
+    launch of every weight-gradient product: the tied embedding's (lm_head)
+    and the L blocks' four each."""
     M, C, V = rows, 768, 50304
     FC = F if FC is None else FC
     return {
-        "gemm.dw": L * 2 * M * C * (3 * C + C + FC + F),
+        "gemm.dw": 2 * M * V * C + L * 2 * M * C * (3 * C + C + FC + F),
         "gemm.qkv": 2 * M * 3 * C * C,
         "gemm.attn_proj": 2 * M * C * C,
         "gemm.fc": 2 * M * FC * C,

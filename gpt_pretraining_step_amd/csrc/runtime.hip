@@ -325,15 +325,18 @@ Layout build_layout(const gpt2_config& c) {
       y.dUL.push_back(s.take(rows * FU * 2));
       y.dQKVL.push_back(s.take(rows * 3 * C * 2));
     }
-    std::vector<gpt2_gemm_args> dw(4 * (size_t)L);
+    // the products of that launch: dwte (lm_head), then four per layer
+    std::vector<gpt2_gemm_args> dw(4 * (size_t)L + 1);
+    dw[0].M = (int)V;
+    dw[0].N = (int)C;
     for (int l = 0; l < L; ++l) {
       const int mn[4][2] = {{(int)C, (int)F}, {(int)FU, (int)C}, {(int)C, (int)C}, {3 * (int)C, (int)C}};
       for (int k = 0; k < 4; ++k) {
-        dw[4 * l + k].M = mn[k][0];
-        dw[4 * l + k].N = mn[k][1];
+        dw[4 * l + k + 1].M = mn[k][0];
+        dw[4 * l + k + 1].N = mn[k][1];
       }
     }
-    y.dw_table_bytes = gemm_grouped_table_bytes(4 * L, gemm_grouped_units(dw.data(), 4 * L));
+    y.dw_table_bytes = gemm_grouped_table_bytes((int)dw.size(), gemm_grouped_units(dw.data(), (int)dw.size()));
     y.dw_table = s.take(y.dw_table_bytes);
   }
   if (c.precision == GPT2_PRECISION_BF16) {
@@ -485,7 +488,7 @@ static hipError_t run_dw(gpt2_ctx* c, DwQueue& q) {
 // turns them into the row losses and dlogits in place, then dZ += dlogits
 // wte and dwte += dlogits^T Z.  dZ must hold zeros (float32 [M, C]).
 static hipError_t lmhead_ce_bf16(gpt2_ctx* c, const int32_t* tgt, int M, const int* count, float scale,
-                                 float* rowloss, float* dZ) {
+                                 float* rowloss, float* dZ, DwQueue& q) {
   const Layout& y = c->lay;
   const int C = c->cfg.n_embd, V = c->cfg.vocab_size, dt = c->cfg.precision;
   bf16* dlog = c->scr<bf16>(y.dlogits);
@@ -506,15 +509,9 @@ static hipError_t lmhead_ce_bf16(gpt2_ctx* c, const int32_t* tgt, int M, const i
     e = launch_gemm(c->at("gemm.lm_head_dx"), a);
     if (e != hipSuccess) return e;
   }
-  {  // dwte += dlogits^T Z
-    gpt2_gemm_args a = gemm_base(dt);
-    a.M = V; a.N = C; a.K = M;
-    a.a_kmajor = 0; a.b_kmajor = 0;
-    a.lda = V; a.ldb = C; a.ldc = C;
-    a.A = dlog; a.B = Zb; a.C = c->Gr(c->tab.wte);
-    a.epilogue = GPT2_EPI_ACCUMULATE;
-    e = launch_gemm(c->at("gemm.lm_head_dw"), a);
-  }
+  // dwte += dlogits^T Z: queued with the blocks' weight gradients (dlogits
+  // and Z stay untouched until they run)
+  queue_dw(c, q, dlog, M, V, Zb, C, c->tab.wte, -1);
   return e;
 }
 
@@ -562,7 +559,8 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   float* dZ = c->scr<float>(y.dA);
   HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
   const size_t es = y.es;
-  if (bf) HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ));
+  DwQueue q;  // bf16: weight-gradient products, run together after the backward
+  if (bf) HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ, q));
   for (int r0 = 0; !bf && r0 < M; r0 += y.chunk) {
     const int rows = std::min(y.chunk, M - r0);
     const char* z_c = c->act<char>(y.Z) + (size_t)r0 * C * es;
@@ -610,7 +608,6 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   // as under autocast), float32 otherwise; dZ (float32) lives here first and
   // the final LN backward consumes it before the buffer is reused
   void* dA = c->scr(y.dA);
-  DwQueue q;
   // dW += dy^T x (+ bias row sums): queued in bf16 mode, run now in float32
   auto dw = [&](const char* site, const void* dy, int N, const void* x, int K, int wi, int bi,
                 const float* dy_f32) -> hipError_t {
@@ -712,7 +709,8 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
 
   float* dZ = c->scr<float>(y.dA);
   HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
-  HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ));
+  DwQueue q;  // weight-gradient products, run together after the backward
+  HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ, q));
   HIP_TRY(launch_ce_finish_n(c->at("ce.finish"), rowloss, M, count, loss, flag));
 
   // ---- backward
@@ -723,7 +721,6 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
   auto dRb_slot = [&](int s) -> bf16* { return s >= 0 ? c->scr<bf16>(y.dRbS[s]) : nullptr; };
   void* dA = c->scr(y.dA);  // dZ (float32) first, then bf16 norm-output gradients
   void* dY = c->scr(y.dY);
-  DwQueue q;
   HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
   HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dZ, 0, rlast, c->act<float>(y.rstdf), c->P(c->tab.lnf_w), dR,
                              dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w), M, C));

@@ -104,10 +104,11 @@ static hipError_t launch_v2(const Launch& L, const GemmP& p) {
 }
 
 // bf16 products: 256 x BN block tiles (BN = 256: 8 waves of 128x64; BN =
-// 192: 8 waves of 64x96), K step 64, two LDS stages fed by DMA.  Residual
-// and dGELU epilogues use the accumulator layout with 4 consecutive columns
-// per lane (vector loads of R / U); the others keep 32 consecutive columns
-// per row per instruction (coalesced scalar stores and atomics).
+// 192: 8 waves of 64x96), K step 64, two LDS stages fed by DMA.  Most
+// epilogues keep 32 consecutive columns of a row per instruction (coalesced
+// scalar loads, stores and atomics: the fewest row segments per
+// instruction); the residual of a long-K product (K >= 2048) measured faster
+// with 4 consecutive columns per lane (16-byte loads of R and stores).
 template <int BN, int WGM, int WGN, bool A_K, bool B_K>
 static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
   constexpr int BM = 256, BK = 64, ST = 2;
@@ -122,19 +123,20 @@ static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
              : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_STORE, false, false>(L, p);
       break;
     case GPT2_EPI_RESIDUAL:
-      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_RESIDUAL, false, false, true>(L, p);
+      e = p.K >= 2048 ? launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_RESIDUAL, false, false, true>(L, p)
+                      : launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_RESIDUAL, false, false, false>(L, p);
       break;
     case GPT2_EPI_GELU:
       e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_GELU, true, false>(L, p);
       break;
     case GPT2_EPI_DGELU:
-      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_DGELU, true, false, true>(L, p);
+      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_DGELU, true, false, false>(L, p);
       break;
     case GPT2_EPI_GELU_GRAD:
       e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_GELU_GRAD, true, false>(L, p);
       break;
     case GPT2_EPI_MUL:
-      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_MUL, true, false, true>(L, p);
+      e = launch_v2<BM, BN, BK, WGM, WGN, ST, A_K, B_K, GPT2_EPI_MUL, true, false, false>(L, p);
       break;
     case GPT2_EPI_ROPE:
     case GPT2_EPI_SWIGLU:

@@ -196,6 +196,63 @@ __device__ __forceinline__ void epi_tile(const GemmP& p, int mrow, int ncol, con
     }
 }
 
+// Unswapped layout, interior tile, epilogues that read an operand of C's
+// shape (RESIDUAL: R float32; MUL, DGELU: U in the output dtype).  A lane
+// holds column ncol + 32 j of rows mrow + 32 i + 8 (r / 4) + r % 4, so the 32
+// lanes of a row read and write 128 (float32) or 64 (bf16) contiguous bytes.
+// The operands of row group i + 1 are loaded before row group i is stored:
+// the compiler must assume that C may alias them, so a load issued after a
+// store would wait out the full memory latency.
+template <int EPI, bool OUT_BF16, int TM, int TN>
+__device__ __forceinline__ void epi_tile_gathered(const GemmP& p, int mrow, int ncol, const f32x16 (&acc)[TM][TN]) {
+  static_assert(EPI == GPT2_EPI_RESIDUAL || EPI == GPT2_EPI_MUL || EPI == GPT2_EPI_DGELU, "operand epilogues");
+  using Op = std::conditional_t<EPI == GPT2_EPI_RESIDUAL || !OUT_BF16, float, bf16>;
+  const Op* src = EPI == GPT2_EPI_RESIDUAL ? reinterpret_cast<const Op*>(p.R) : static_cast<const Op*>(p.U);
+  float bj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bj[j] = p.bias ? p.bias[ncol + 32 * j] : 0.f;
+  const int64_t ldc = p.ldc;
+  const int64_t base = (int64_t)mrow * ldc + ncol;
+  auto idx = [&](int i, int j, int r) { return base + (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * ldc + 32 * j; };
+  Op op[2][TN][16];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) op[0][j][r] = src[idx(0, j, r)];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i + 1 < TM) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) op[(i + 1) & 1][j][r] = src[idx(i + 1, j, r)];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float v0 = fmaf(p.alpha, acc[i][j][r], bj[j]), v1 = fmaf(p.alpha, acc[i][j][r + 1], bj[j]);
+        const float u0 = to_f(op[i & 1][j][r]), u1 = to_f(op[i & 1][j][r + 1]);
+        const int64_t i0 = idx(i, j, r), i1 = idx(i, j, r + 1);
+        if constexpr (EPI == GPT2_EPI_RESIDUAL) {
+          static_cast<float*>(p.C)[i0] = u0 + v0;
+          static_cast<float*>(p.C)[i1] = u1 + v1;
+        } else {
+          const float o0 = EPI == GPT2_EPI_MUL ? v0 * u0 : v0 * gelu_tanh_grad(u0);
+          const float o1 = EPI == GPT2_EPI_MUL ? v1 * u1 : v1 * gelu_tanh_grad(u1);
+          if constexpr (OUT_BF16) {
+            const bf16x2 o = f2bf2(o0, o1);
+            static_cast<bf16*>(p.C)[i0] = o[0];
+            static_cast<bf16*>(p.C)[i1] = o[1];
+          } else {
+            static_cast<float*>(p.C)[i0] = o0;
+            static_cast<float*>(p.C)[i1] = o1;
+          }
+        }
+      }
+  }
+}
+
 // Stores 4 consecutive outputs C[idx .. idx+3] whose values v already carry
 // alpha and the bias (idx % 4 == 0); the epilogues of the swapped layout
 // (bf16 output for dGELU and the product).
@@ -848,7 +905,10 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
       if (interior) epi_tile_swap<EPI, OUT_BF16, TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
       else epi_tile_swap<EPI, OUT_BF16, TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
     } else if (interior) {
-      epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+      if constexpr (!ATOMIC && (EPI == GPT2_EPI_RESIDUAL || EPI == GPT2_EPI_MUL || EPI == GPT2_EPI_DGELU))
+        epi_tile_gathered<EPI, OUT_BF16, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+      else
+        epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
     } else {
       // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
 #pragma unroll

@@ -142,14 +142,15 @@ static hipError_t dispatch_tile(const Launch& L, GemmP p, int epi, bool ob) {
     case GPT2_EPI_SWIGLU:
       // paired columns in one lane: 64 columns per wave (256-wide tiles), forward layout
       if constexpr (BN == 256 && A_K && B_K) {
+        // (RoPE measured alike in both layouts; SwiGLU faster unswapped)
         e = epi == GPT2_EPI_ROPE ? launch_v2<BM, BN, BK, WGM, WGN, ST, true, true, GPT2_EPI_ROPE, true, false, true>(L, p)
-                                 : launch_v2<BM, BN, BK, WGM, WGN, ST, true, true, GPT2_EPI_SWIGLU, true, false, true>(L, p);
+                                 : launch_v2<BM, BN, BK, WGM, WGN, ST, true, true, GPT2_EPI_SWIGLU, true, false, false>(L, p);
       } else {
         e = hipErrorInvalidValue;
       }
       break;
     case GPT2_EPI_SWIGLU_BWD:
-      if constexpr (A_K && !B_K) e = launch_v2<BM, BN, BK, WGM, WGN, ST, true, false, GPT2_EPI_SWIGLU_BWD, true, false, true>(L, p);
+      if constexpr (A_K && !B_K) e = launch_v2<BM, BN, BK, WGM, WGN, ST, true, false, GPT2_EPI_SWIGLU_BWD, true, false, false>(L, p);
       else e = hipErrorInvalidValue;
       break;
     default:

@@ -502,6 +502,74 @@ __device__ __forceinline__ void epi_tile_pair(const GemmP& p, int mrow, int gcol
   }
 }
 
+// ROPE and SWIGLU in the unswapped layout (64 columns per wave): this lane
+// holds columns gcol + d (j = 0) and gcol + 32 + d (j = 1), d = lane % 32, of
+// rows mrow + 32 i + 8 (r / 4) + r % 4, so the pair a rotation or the gate
+// combines is again in one lane, and the 32 lanes of a row write 64-byte runs.
+template <int EPI, int TM, bool CHECK>
+__device__ __forceinline__ void epi_tile_pair_rows(const GemmP& p, int mrow, int gcol, int d,
+                                                   const f32x16 (&acc)[TM][2]) {
+  if (CHECK && gcol >= p.N) return;  // N % 64 == 0: a group is wholly in or out
+  const bool rot = EPI == GPT2_EPI_ROPE && gcol < p.rope_cols;
+  const int F = p.N >> 1;
+  float b0 = 0.f, b1 = 0.f;
+  if (EPI == GPT2_EPI_ROPE && p.bias) {
+    b0 = p.bias[gcol + d];
+    b1 = p.bias[gcol + 32 + d];
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int m[2] = {mrow + 32 * i + 8 * (r >> 2) + (r & 3), mrow + 32 * i + 8 * (r >> 2) + (r & 3) + 1};
+      float o0[2], o1[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float v0 = fmaf(p.alpha, acc[i][0][r + t], b0), v1 = fmaf(p.alpha, acc[i][1][r + t], b1);
+        if constexpr (EPI == GPT2_EPI_ROPE) {
+          if (rot) {
+            const float2 cs = p.rope[(int64_t)(m[t] % p.rope_period) * 32 + d];
+            o0[t] = v0 * cs.x - v1 * cs.y;
+            o1[t] = v1 * cs.x + v0 * cs.y;
+          } else {
+            o0[t] = v0;
+            o1[t] = v1;
+          }
+        } else {
+          o0[t] = v0;  // gate
+          o1[t] = v1;  // up
+        }
+      }
+      const bf16x2 a = f2bf2(o0[0], o0[1]), c = f2bf2(o1[0], o1[1]);
+      if constexpr (EPI == GPT2_EPI_ROPE) {
+        bf16* C = static_cast<bf16*>(p.C);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (CHECK && m[t] >= p.M) continue;
+          C[(int64_t)m[t] * p.ldc + gcol + d] = a[t];
+          C[(int64_t)m[t] * p.ldc + gcol + 32 + d] = c[t];
+        }
+      } else {
+        const int f = (gcol >> 1) + d;
+        float act[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float gf = bf2f(a[t]);
+          act[t] = gf * sigmoid_fast(gf) * bf2f(c[t]);
+        }
+        const bf16x2 ab = f2bf2(act[0], act[1]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (CHECK && m[t] >= p.M) continue;
+          static_cast<bf16*>(p.C)[(int64_t)m[t] * p.ldc + f] = ab[t];
+          bf16* c2 = static_cast<bf16*>(p.C2) + (int64_t)m[t] * p.ld2 + f;
+          c2[0] = a[t];
+          c2[F] = c[t];
+        }
+      }
+    }
+}
+
 // SWIGLU_BWD: the product is d(act) [M, F] (F = N); with gate g = U[m][f]
 // and up u = U[m][F + f] (row pitch ld2), C[m][f] = d(act) u silu'(g) and
 // C[m][F + f] = d(act) silu(g), silu'(g) = s (1 + g (1 - s)), s = sigmoid(g).
@@ -571,6 +639,64 @@ __device__ __forceinline__ void epi_tile_swiglu_bwd(const GemmP& p, int mrow, in
         swiglu_bwd_load<TN>(p, U + (int64_t)(m + 32) * p.ld2, ncol, F, g[(i + 1) & 1], u[(i + 1) & 1], false);
       swiglu_bwd_store<TN>(p, C + (int64_t)m * p.ldc, ncol, F, g[i & 1], u[i & 1], acc[i], false);
     }
+  }
+}
+
+// SWIGLU_BWD in the unswapped layout: this lane holds column f = ncol + 32 j
+// of rows mrow + 32 i + 8 (r / 4) + r % 4, so the 32 lanes of a row read gate
+// and up and write dgate and dup in 64-byte runs.  The row group is taken in
+// halves of 8 registers; gate and up of the next half are loaded before the
+// current half is stored (loads after a store would each wait out the full
+// latency: the compiler must assume C may alias U).
+template <int TM, int TN, bool CHECK>
+__device__ __forceinline__ void epi_tile_swiglu_bwd_rows(const GemmP& p, int mrow, int ncol,
+                                                         const f32x16 (&acc)[TM][TN]) {
+  const int F = p.N;
+  const bf16* U = static_cast<const bf16*>(p.U);
+  bf16* Cp = static_cast<bf16*>(p.C);
+  constexpr int NCH = 2 * TM;  // halves of row groups
+  auto row_of = [&](int ch, int e) { return mrow + 32 * (ch >> 1) + 8 * ((8 * (ch & 1) + e) >> 2) + (e & 3); };
+  bf16 g[2][TN][8], u[2][TN][8];
+  auto load = [&](int ch, int b) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = row_of(ch, e), f = ncol + 32 * j;
+        if (CHECK && (m >= p.M || f >= F)) continue;
+        const bf16* ur = U + (int64_t)m * p.ld2 + f;
+        g[b][j][e] = ur[0];
+        u[b][j][e] = ur[F];
+      }
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    if (ch + 1 < NCH) load(ch + 1, (ch + 1) & 1);
+    const int b = ch & 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int m0 = row_of(ch, e), m1 = row_of(ch, e + 1), f = ncol + 32 * j;
+        float dg[2], du[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float v = p.alpha * acc[ch >> 1][j][8 * (ch & 1) + e + t];
+          const float gf = bf2f(g[b][j][e + t]), sg = sigmoid_fast(gf);
+          du[t] = v * gf * sg;
+          dg[t] = v * bf2f(u[b][j][e + t]) * sg * fmaf(gf, 1.f - sg, 1.f);
+        }
+        const bf16x2 dgb = f2bf2(dg[0], dg[1]), dub = f2bf2(du[0], du[1]);
+        if (!CHECK || (m0 < p.M && f < F)) {
+          Cp[(int64_t)m0 * p.ldc + f] = dgb[0];
+          Cp[(int64_t)m0 * p.ldc + F + f] = dub[0];
+        }
+        if (!CHECK || (m1 < p.M && f < F)) {
+          Cp[(int64_t)m1 * p.ldc + f] = dgb[1];
+          Cp[(int64_t)m1 * p.ldc + F + f] = dub[1];
+        }
+      }
   }
 }
 
@@ -753,7 +879,7 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
   // SWIGLU reads B's rows interleaved (64-column group g: gate rows g/2 ..
   // g/2+31, then the up rows F + g/2 ..), from absolute row offsets
   constexpr bool MAP_B = EPI == GPT2_EPI_SWIGLU;
-  static_assert(!MAP_B || (B_K && SWAP && WN == 64), "SwiGLU: K-major B, swapped layout, 64 columns per wave");
+  static_assert(!MAP_B || (B_K && WN == 64), "SwiGLU: K-major B, 64 columns per wave");
   const int b_row0 = MAP_B ? 0 : n0;
   dma_a.init(p.lda, m0, p.M);
   if constexpr (MAP_B) dma_b.init_swiglu(p.ldb, n0, p.N);
@@ -890,13 +1016,22 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
       epi_ce_stats<BM, BN, WGN, TM, TN, true>(p, m0, n0, tn, wm0, wn0, wave, lr, lg, acc, red,
                                               reinterpret_cast<char*>(lds0), reinterpret_cast<char*>(lds1));
   } else if constexpr (EPI == GPT2_EPI_ROPE || EPI == GPT2_EPI_SWIGLU) {
-    static_assert(SWAP && WN == 64, "paired epilogues: swapped layout, 64 columns per wave");
-    if (interior) epi_tile_pair<EPI, TM, false>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
-    else epi_tile_pair<EPI, TM, true>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
+    static_assert(WN == 64, "paired epilogues: 64 columns per wave");
+    if constexpr (SWAP) {
+      if (interior) epi_tile_pair<EPI, TM, false>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
+      else epi_tile_pair<EPI, TM, true>(p, m0 + wm0 + lr, n0 + wn0, lg, acc);
+    } else {
+      if (interior) epi_tile_pair_rows<EPI, TM, false>(p, m0 + wm0 + 4 * lg, n0 + wn0, lr, acc);
+      else epi_tile_pair_rows<EPI, TM, true>(p, m0 + wm0 + 4 * lg, n0 + wn0, lr, acc);
+    }
   } else if constexpr (EPI == GPT2_EPI_SWIGLU_BWD) {
-    static_assert(SWAP, "SwiGLU backward: swapped layout");
-    if (interior) epi_tile_swiglu_bwd<TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
-    else epi_tile_swiglu_bwd<TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    if constexpr (SWAP) {
+      if (interior) epi_tile_swiglu_bwd<TM, TN, false>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+      else epi_tile_swiglu_bwd<TM, TN, true>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc);
+    } else {
+      if (interior) epi_tile_swiglu_bwd_rows<TM, TN, false>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+      else epi_tile_swiglu_bwd_rows<TM, TN, true>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+    }
   } else {
     if constexpr (PRE_U) {
       if (interior) epi_tile_mul_pre<TM, TN, TMP>(p, m0 + wm0 + lr, n0 + wn0 + 4 * lg, acc, upre);

@@ -276,52 +276,91 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
 }
 
 // ------------------------------------------------------- grouped products
+//
+// One block per 256x256 output tile, whole K, so the launch runs in rounds of
+// kUnits equal blocks.  A partial last round would leave CUs idle for a whole
+// tile's time: the products at the end of the list that cover the tiles past
+// the last full round are split in K into two halves (each adds its partial
+// sums atomically) when the halves fit in half a round, which then ends the
+// launch half a round earlier.  Units are placed in block order: the whole
+// tiles XCD-aware (each XCD a contiguous run of them, sharing panels in its
+// L2), then the halves, which the round-robin hands to every XCD alike.
 
 namespace {
 constexpr int kGroupTile = 256;
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
-int group_units(const gpt2_gemm_args& a) {
+int group_tiles(const gpt2_gemm_args& a) {
   return ((a.M + kGroupTile - 1) / kGroupTile) * ((a.N + kGroupTile - 1) / kGroupTile);
+}
+// K splits of each product (1 or 2); returns the unit count or -1
+int64_t group_plan(const gpt2_gemm_args* a, int n, std::vector<int>& splits) {
+  splits.assign(n, 1);
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) tiles += group_tiles(a[i]);
+  const int64_t tail = tiles % kUnits;
+  if (tiles > kUnits && tail > 0 && 2 * tail <= kUnits) {
+    int64_t covered = 0;
+    for (int i = n - 1; i >= 0 && covered < tail; --i) {
+      // halves must keep at least 16 K steps
+      if (a[i].K < 2 * 16 * 64) break;
+      splits[i] = 2;
+      covered += group_tiles(a[i]);
+    }
+    if (covered < tail || 2 * covered > kUnits + tail) splits.assign(n, 1);  // no gain
+  }
+  int64_t units = 0;
+  for (int i = 0; i < n; ++i) units += (int64_t)group_tiles(a[i]) * splits[i];
+  return units;
 }
 }  // namespace
 
 int gemm_grouped_units(const gpt2_gemm_args* a, int n) {
-  int64_t u = 0;
-  for (int i = 0; i < n; ++i) u += group_units(a[i]);
-  return u < (1 << 30) ? (int)u : -1;
+  std::vector<int> splits;
+  const int64_t u = group_plan(a, n, splits);
+  int64_t largest = 0;
+  for (int i = 0; i < n; ++i) largest = std::max<int64_t>(largest, (int64_t)group_tiles(a[i]) * splits[i]);
+  return u < (1 << 30) && largest <= 0xffff && n <= 0x7fff ? (int)u : -1;
 }
 
 size_t gemm_grouped_table_bytes(int n, int units) {
-  return align256(n * sizeof(GemmP)) + align256(n * sizeof(int)) + align256((size_t)units * sizeof(int));
+  return align256(n * sizeof(GemmP)) + align256((size_t)units * sizeof(int));
 }
 
-// Host image of the table: parameters of every product, its first unit, and
-// the product of every unit (no pointers into itself: it can be copied
-// anywhere).
+// Host image of the table: parameters of every product, then the (product,
+// unit) of every block (no pointers into itself: it can be copied anywhere).
 void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, int units, void* host) {
   char* h = static_cast<char*>(host);
   memset(h, 0, gemm_grouped_table_bytes(n, units));
   GemmP* ps = reinterpret_cast<GemmP*>(h);
-  int* first = reinterpret_cast<int*>(h + align256(n * sizeof(GemmP)));
-  int* group_of = reinterpret_cast<int*>(h + align256(n * sizeof(GemmP)) + align256(n * sizeof(int)));
-  int u = 0;
+  int* unit_map = reinterpret_cast<int*>(h + align256(n * sizeof(GemmP)));
+  std::vector<int> splits;
+  group_plan(a, n, splits);
+  std::vector<int> whole, halves;  // (product << 16) | unit, in product order
   for (int i = 0; i < n; ++i) {
     GemmP p = make_params(a[i]);
     p.row_sum = row_sums ? row_sums[i] : nullptr;
     p.tiles_m = (a[i].M + kGroupTile - 1) / kGroupTile;
     p.tiles_n = (a[i].N + kGroupTile - 1) / kGroupTile;
+    if (splits[i] > 1) {
+      p.k_per_split = (a[i].K + splits[i] * 64 - 1) / (splits[i] * 64) * 64;
+      p.splits = (a[i].K + p.k_per_split - 1) / p.k_per_split;
+    }
     ps[i] = p;
-    first[i] = u;
-    for (int k = 0; k < p.tiles_m * p.tiles_n; ++k) group_of[u++] = i;
+    const int nu = p.tiles_m * p.tiles_n * p.splits;
+    for (int k = 0; k < nu; ++k) (p.splits > 1 ? halves : whole).push_back((i << 16) | k);
   }
+  // whole tiles: block b of the first 8 * floor(W / 8) takes the unit that
+  // gives XCD b % 8 a contiguous run
+  const int W = (int)whole.size(), W8 = W / 8 * 8;
+  for (int b = 0; b < W; ++b) unit_map[b] = whole[b < W8 ? xcd_remap_host(b, W8) : b];
+  for (size_t k = 0; k < halves.size(); ++k) unit_map[W + k] = halves[k];
 }
 
 hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units) {
   const char* d = static_cast<const char*>(d_table);
   GemmGroups t;
   t.p = reinterpret_cast<const GemmP*>(d);
-  t.first = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)));
-  t.group_of = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)) + align256(n * sizeof(int)));
+  t.unit_map = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)));
   prof_begin(L);
   gemm2_grouped_kernel<kGroupTile, kGroupTile, 64, 2, 4, 2, false, false, GPT2_EPI_ACCUMULATE, false, false, false>
       <<<units, 512, 0, L.stream>>>(t);

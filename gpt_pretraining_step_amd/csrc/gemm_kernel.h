@@ -38,6 +38,7 @@ struct GemmP {
   int64_t ld2;  // SWIGLU: row pitch of C2; SWIGLU_BWD: row pitch of U
   float alpha;
   int tiles_m, tiles_n, splits, k_per_split;
+  int group_m;  // row tiles walked per column panel (0: 8)
 };
 
 template <int EPI, bool OUT_BF16, bool ATOMIC>
@@ -797,9 +798,10 @@ __device__ __forceinline__ void epi_ce_stats(const GemmP& p, int m0, int n0, int
 // Tile -> block mapping.  Blocks are handed to the 8 XCDs round-robin; the
 // remap makes consecutive logical units (tiles, or tiles of a group) run on
 // one XCD (sharing its L2).
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
 }
+inline int xcd_remap_host(int bid, int nb) { return xcd_remap(bid, nb); }
 
 // Unit -> (row tile, column tile, K split) of one product: the grouped order
 // walks GROUP_M row tiles per column panel.
@@ -807,7 +809,7 @@ __device__ __forceinline__ void tile_of_unit(const GemmP& p, int bid, int& tm, i
   const int per_split = p.tiles_m * p.tiles_n;
   split = bid / per_split;
   int t = bid - split * per_split;
-  const int GROUP_M = 8;
+  const int GROUP_M = p.group_m > 0 ? p.group_m : 8;
   const int in_group = GROUP_M * p.tiles_n;
   const int group = t / in_group;
   const int first_m = group * GROUP_M;
@@ -1043,7 +1045,10 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
       if constexpr (!ATOMIC && (EPI == GPT2_EPI_RESIDUAL || EPI == GPT2_EPI_MUL || EPI == GPT2_EPI_DGELU))
         epi_tile_gathered<EPI, OUT_BF16, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
       else
-        epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+        if (EPI == GPT2_EPI_ACCUMULATE && !ATOMIC && p.splits > 1)  // a grouped launch's split products
+          epi_tile<EPI, OUT_BF16, true, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
+        else
+          epi_tile<EPI, OUT_BF16, ATOMIC, TM, TN>(p, m0 + wm0 + 4 * lg, n0 + wn0 + lr, acc);
     } else {
       // accumulator (i, j), register r: row 8*(r/4) + 4*lg + r%4, column lr
 #pragma unroll
@@ -1055,7 +1060,9 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-            if (m < p.M) epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
+            if (m >= p.M) continue;
+            if (EPI == GPT2_EPI_ACCUMULATE && !ATOMIC && p.splits > 1) epi_store<EPI, OUT_BF16, true>(p, m, n, acc[i][j][r]);
+            else epi_store<EPI, OUT_BF16, ATOMIC>(p, m, n, acc[i][j][r]);
           }
         }
     }
@@ -1068,21 +1075,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
   gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, xcd_remap(blockIdx.x, gridDim.x));
 }
 
-// Several independent products in one launch.  Unit u (after the XCD remap)
-// belongs to product group_of[u] and is that product's unit u - first[g].
+// Several independent products in one launch.  Block b runs unit
+// unit_map[b] & 0xffff of product unit_map[b] >> 16 (the host orders the
+// units: blocks go to the XCDs round-robin in index order).  A product with
+// splits > 1 adds its partial sums atomically (ACCUMULATE).
 struct GemmGroups {
   const GemmP* __restrict__ p;
-  const int* __restrict__ first;
-  const int* __restrict__ group_of;
+  const int* __restrict__ unit_map;
 };
 
 template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
           bool ATOMIC, bool SWAP>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_grouped_kernel(GemmGroups t) {
-  const int u = xcd_remap(blockIdx.x, gridDim.x);
-  const int g = t.group_of[u];
-  const GemmP p = t.p[g];
-  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, u - t.first[g]);
+  const int e = t.unit_map[blockIdx.x];
+  const GemmP p = t.p[e >> 16];
+  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, e & 0xffff);
 }
 
 }  // namespace g2

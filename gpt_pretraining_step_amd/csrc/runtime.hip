@@ -336,6 +336,9 @@ Layout build_layout(const gpt2_config& c) {
         dw[4 * l + k + 1].N = mn[k][1];
       }
     }
+    // sized at the largest token count (K): splitting, hence the unit count,
+    // only grows with K
+    for (auto& a : dw) a.K = (int)rows;
     y.dw_table_bytes = gemm_grouped_table_bytes((int)dw.size(), gemm_grouped_units(dw.data(), (int)dw.size()));
     y.dw_table = s.take(y.dw_table_bytes);
   }

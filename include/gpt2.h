@@ -334,9 +334,11 @@ int gpt2_op_gemm(void* stream, const gpt2_gemm_args* args);
  * K-slow (a_kmajor = b_kmajor = 0), epilogue GPT2_EPI_ACCUMULATE, no bias,
  * and satisfy gpt2_op_gemm's rules; d_row_sums (a host array of n device
  * pointers, or NULL; entries may be NULL) receive row_sum_i[m] +=
- * alpha_i * sum_k A_i(m, k) (the bias gradient).  Each output tile of each
- * product is computed whole by one block (no K split, no atomics on C), so
- * the n outputs must not overlap.  d_workspace: device memory of
+ * alpha_i * sum_k A_i(m, k) (the bias gradient).  One block per 256x256
+ * output tile; when the tiles leave a partial last round of blocks, the
+ * products at the end of the list are split in K into two halves that add
+ * their partial sums atomically, every other tile is computed whole and
+ * added once.  The n outputs must not overlap.  d_workspace: device memory of
  * gpt2_gemm_grouped_workspace_bytes(args, n) bytes (16-byte aligned) that
  * receives the group table; the call copies it there synchronously (it
  * blocks until the copy is done), then launches on the stream.

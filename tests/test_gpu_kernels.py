@@ -126,6 +126,33 @@ def test_gemm_grouped_exact(g):
             assert np.array_equal(host(R), refR.astype(np.float32)), i
 
 
+def test_gemm_grouped_split_tail_exact(g):
+    """276 output tiles: one full round of 256 blocks and a 20-tile tail, so
+    the last product runs split in K (two halves adding atomically): every
+    output and row sum stays exact on integer operands."""
+    import torch
+    shapes = [(2048, 2048)] * 4 + [(1024, 1280)]
+    K = 2048
+    announce(f"gemm grouped split tail {len(shapes)} products K={K}")
+    rng = np.random.default_rng(6)
+    items, refs = [], []
+    for idx, (M, N) in enumerate(shapes):
+        A = rng.integers(-3, 4, size=(K, M)).astype(np.float32)
+        B = rng.integers(-3, 4, size=(K, N)).astype(np.float32)
+        C0 = rng.integers(-100, 101, size=(M, N)).astype(np.float32)
+        r0 = rng.integers(-100, 101, size=M).astype(np.float32)
+        # float64 products of integers below 2^53: exact (and BLAS-fast)
+        refC = C0 + A.astype(np.float64).T @ B.astype(np.float64)
+        refR = r0 + A.astype(np.float64).sum(axis=0)
+        C, R = dev(C0), dev(r0)
+        items.append((dev(A, torch.bfloat16), dev(B, torch.bfloat16), C, M, N, K, R, 1.0))
+        refs.append((C, refC, R, refR))
+    g.op_gemm_grouped(items)
+    for i, (C, refC, R, refR) in enumerate(refs):
+        assert np.array_equal(host(C), refC.astype(np.float32)), i
+        assert np.array_equal(host(R), refR.astype(np.float32)), i
+
+
 @pytest.mark.parametrize("ak,bk", LAYOUTS)
 def test_gemm_bf16_accumulate_split_k_exact(g, ak, bk):
     """Few output tiles and a long K take the split-K path (atomic adds of

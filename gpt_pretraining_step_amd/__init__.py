@@ -156,6 +156,21 @@ class GPT2:
                                  out.data_ptr(), _ptr(token_loss)), "gpt2_fwd_bwd")
         return out
 
+    def graph_capture(self, tokens, targets, loss_scale: float = 1.0, loss_out=None):
+        """Capture one micro-step over these token / target buffers into a HIP
+        graph (see gpt2_graph_capture); replay it with graph_launch()."""
+        import torch
+        assert tokens.dtype == torch.int32 and targets.dtype == torch.int32
+        assert tokens.is_contiguous() and targets.is_contiguous() and tokens.shape == targets.shape
+        B, T = tokens.shape
+        out = self.loss if loss_out is None else loss_out
+        check(lib().gpt2_graph_capture(self._h, tokens.data_ptr(), targets.data_ptr(), B, T, float(loss_scale),
+                                       out.data_ptr()), "gpt2_graph_capture")
+        return out
+
+    def graph_launch(self):
+        check(lib().gpt2_graph_launch(self._h), "gpt2_graph_launch")
+
     def clip_adamw_step(self, lr: float, beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-8,
                         weight_decay: float = 0.1, max_norm: float = 1.0, norm_out=None):
         hp = _ffi.AdamW(lr, beta1, beta2, eps, weight_decay, max_norm)
@@ -359,3 +374,4 @@ def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None):
     check(lib().gpt2_op_attention_bwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
                                       dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr()),
           "gpt2_op_attention_bwd")
+from . import train  # noqa: E402,F401  (the training loop)

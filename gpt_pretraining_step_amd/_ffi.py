@@ -90,7 +90,11 @@ SIGNATURES = {
     "gpt2_zero_grad": (ct.c_int, [ct.c_void_p]),
     "gpt2_fwd_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_float, ct.c_void_p,
                                 ct.c_void_p]),
+    "gpt2_graph_capture": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_float,
+                                      ct.c_void_p]),
+    "gpt2_graph_launch": (ct.c_int, [ct.c_void_p]),
     "gpt2_clip_adamw_step": (ct.c_int, [ct.c_void_p, ct.POINTER(AdamW), ct.c_void_p]),
+    "gpt2_lr_at": (ct.c_double, [ct.c_int64, ct.c_double, ct.c_double, ct.c_int64, ct.c_int64]),
     "gpt2_get_step": (ct.c_int, [ct.c_void_p, ct.POINTER(ct.c_int64)]),
     "gpt2_set_step": (ct.c_int, [ct.c_void_p, ct.c_int64]),
     "gpt2_get_status": (ct.c_int, [ct.c_void_p]),

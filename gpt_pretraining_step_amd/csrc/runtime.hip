@@ -368,6 +368,8 @@ struct gpt2_ctx {
   int64_t t = 0;
   Prof prof;
   std::vector<char> dw_image;  // the group table last copied to the device
+  hipStream_t cap = nullptr;    // capture stream of gpt2_graph_capture
+  hipGraphExec_t graph = nullptr;
 
   bool bf() const { return cfg.precision == GPT2_PRECISION_BF16; }
   Launch at(const char* site) { return Launch{stream, &prof, site}; }
@@ -477,7 +479,12 @@ static hipError_t run_dw(gpt2_ctx* c, DwQueue& q) {
   void* d_table = c->scr(c->lay.dw_table);
   if (image != c->dw_image) {
     // only when the token count changes: no earlier launch may still read
-    // the table
+    // the table.  Not while the stream is being captured into a graph (a
+    // graph replays the table it was captured with): the capturing call
+    // fails instead
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(c->stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return hipErrorStreamCaptureUnsupported;
     hipError_t e = hipDeviceSynchronize();
     if (e == hipSuccess) e = hipMemcpy(d_table, image.data(), bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) return e;
@@ -767,6 +774,14 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
 
 extern "C" {
 
+double gpt2_lr_at(int64_t step, double max_lr, double min_lr, int64_t warmup, int64_t max_steps) {
+  if (warmup < 1 || max_steps <= warmup || step < 0) return NAN;
+  if (step < warmup) return max_lr * (double)(step + 1) / (double)warmup;
+  if (step > max_steps) return min_lr;
+  const double r = (double)(step - warmup) / (double)(max_steps - warmup);
+  return min_lr + (max_lr - min_lr) * 0.5 * (1.0 + cos(M_PI * r));
+}
+
 int gpt2_query_sizes(const gpt2_config* cfg, gpt2_sizes* out) {
   if (!cfg || !out) return GPT2_ERR_ARG;
   if (!check_config(cfg)) return GPT2_ERR_SHAPE;
@@ -826,6 +841,8 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_buffers* bufs, void* stream, 
 int gpt2_destroy(gpt2_ctx* c) {
   if (!c) return GPT2_ERR_ARG;
   (void)hipStreamSynchronize(c->stream);
+  if (c->graph) (void)hipGraphExecDestroy(c->graph);
+  if (c->cap) (void)hipStreamDestroy(c->cap);
   delete c;
   return GPT2_OK;
 }
@@ -882,6 +899,43 @@ int gpt2_fwd_bwd(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
   if (c->cfg.arch == GPT2_ARCH_ROTARY)
     return fwd_bwd_rotary(c, d_tokens, d_targets, B, T, loss_scale, d_loss, d_token_loss);
   return fwd_bwd_impl(c, d_tokens, d_targets, B, T, loss_scale, d_loss, d_token_loss);
+}
+
+int gpt2_graph_capture(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets, int B, int T,
+                       float loss_scale, float* d_loss) {
+  if (!c || !d_tokens || !d_targets || !d_loss) return GPT2_ERR_ARG;
+  if (B < 1 || B > c->cfg.max_batch || T < 1 || T > c->cfg.block_size) return GPT2_ERR_SHAPE;
+  if (!isfinite(loss_scale) || c->prof.on) return GPT2_ERR_ARG;
+  if (!c->cap) HIP_TRY(hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking));
+  // the capture stream starts after everything issued so far
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  const hipStream_t user = c->stream;
+  c->stream = c->cap;
+  hipGraph_t g = nullptr;
+  int rc = GPT2_ERR_HIP;
+  if (hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+    rc = gpt2_fwd_bwd(c, d_tokens, d_targets, B, T, loss_scale, d_loss, nullptr);
+    if (hipStreamEndCapture(c->cap, &g) != hipSuccess) rc = GPT2_ERR_HIP;
+  }
+  c->stream = user;
+  if (rc != GPT2_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return GPT2_ERR_HIP;
+  if (c->graph) (void)hipGraphExecDestroy(c->graph);
+  c->graph = exec;
+  return GPT2_OK;
+}
+
+int gpt2_graph_launch(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (!c->graph) return GPT2_ERR_UNBOUND;
+  HIP_TRY(hipGraphLaunch(c->graph, c->stream));
+  return GPT2_OK;
 }
 
 int gpt2_clip_adamw_step(gpt2_ctx* c, const gpt2_adamw* hp, float* d_grad_norm) {

@@ -194,6 +194,37 @@ int gpt2_zero_grad(gpt2_ctx* ctx);
 int gpt2_fwd_bwd(gpt2_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targets, int B, int T,
                  float loss_scale, float* d_loss, float* d_token_loss);
 
+/* Learning rate of optimizer step `step` (counted from 0) under the warmed-up
+ * cosine schedule that "Reproduce GPT-2 124M 复盘" trains with (its
+ * hyper-parameter listing: max_lr 1.5e-3, min_lr 0.1 max_lr, warmup 300,
+ * max_steps 19,073; the page names the shape, not the formula):
+ *   step < warmup:            max_lr (step + 1) / warmup
+ *   warmup <= step <= max_steps: min_lr + (max_lr - min_lr) (1 + cos(pi r)) / 2,
+ *                              r = (step - warmup) / (max_steps - warmup)
+ *   step > max_steps:         min_lr
+ * Host function (no device work).  NaN when warmup < 1, max_steps <= warmup
+ * or step < 0. */
+double gpt2_lr_at(int64_t step, double max_lr, double min_lr, int64_t warmup, int64_t max_steps);
+
+/* HIP graph of one micro-step (the whole gpt2_fwd_bwd launch sequence),
+ * for callers that replay it instead of issuing ~200 launches per
+ * micro-step.  gpt2_graph_capture captures gpt2_fwd_bwd(ctx, d_tokens,
+ * d_targets, B, T, loss_scale, d_loss, NULL) on an internal stream (after a
+ * synchronisation of the context's stream) and keeps the instantiated graph
+ * in the context, replacing any earlier one; nothing runs during capture.
+ * gpt2_graph_launch replays it on the context's stream: each replay reads
+ * whatever the token and target buffers hold at that time and adds its
+ * gradients like gpt2_fwd_bwd.  Capture needs the profiler off and one
+ * earlier gpt2_fwd_bwd at the same B and T (the weight-gradient table is set
+ * up then); otherwise GPT2_ERR_ARG or GPT2_ERR_HIP.  gpt2_graph_launch
+ * without a captured graph: GPT2_ERR_UNBOUND.  ("Build an LLM From Scratch:
+ * Making Training Fast on One GPU", the compile modes: graphs of the step,
+ * which there fail with gradient accumulation unless the gradients are
+ * zeroed in place, as gpt2_zero_grad does.) */
+int gpt2_graph_capture(gpt2_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targets, int B, int T,
+                       float loss_scale, float* d_loss);
+int gpt2_graph_launch(gpt2_ctx* ctx);
+
 /* Global-norm clipping then AdamW on every parameter, one fused pass
  * ("Reproduce GPT-2 124M 复盘": clip_grad_norm_(params, 1.0) and fused AdamW;
  * "How I trained my own GPT-2 124M on FineWeb-Edu" section 6: betas, eps, and

@@ -47,3 +47,4 @@ from .optim import global_grad_norm, clip_coef, adamw_update, clip_adamw_step  #
 from .init import philox4x32_10, normal_from_philox, init_params  # noqa: F401
 from .flops import flops_per_token, mfu  # noqa: F401
 from . import modern  # noqa: F401
+from .schedule import lr_at, train  # noqa: F401

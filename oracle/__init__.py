@@ -36,6 +36,8 @@ from .model import (  # noqa: F401
     gelu_tanh_grad,
     layernorm_fwd,
     layernorm_bwd,
+    packed_mask,
+    packed_rows,
     attention_fwd,
     attention_bwd,
     cross_entropy_fwd_bwd,

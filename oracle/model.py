@@ -137,15 +137,43 @@ def layernorm_bwd(dy, cache, w):
 # attention
 # ----------------------------------------------------------------------------
 
-def attention_fwd(q, k, v):
+def packed_mask(row, eot):
+    """Document mask of one packed row ([zero2front] "Document boundaries,
+    packing and masking": attention made block-diagonal over the documents
+    of a window, position ids restarted at each document).
+
+    A document begins at its EOT token (the pipeline puts one before every
+    document); tokens before the row's first EOT are the tail of a document
+    cut by the window and begin at position 0.  start[t] is the last EOT
+    position at or before t (0 if none); query t may attend to key s iff
+    start[t] <= s <= t; pos[t] = t - start[t].
+    Returns (mask [T, T] bool, pos [T] int)."""
+    T = row.shape[0]
+    start = np.zeros(T, dtype=np.int64)
+    cur = 0
+    for t in range(T):
+        if row[t] == eot:
+            cur = t
+        start[t] = cur
+    keys = np.arange(T)
+    mask = (keys[None, :] <= keys[:, None]) & (keys[None, :] >= start[:, None])
+    return mask, keys - start
+
+
+def attention_fwd(q, k, v, mask=None):
     """Causal softmax attention for one (batch, head): q, k, v are [T, hd].
 
     S = q k^T / sqrt(hd), S[t, s] = -inf for s > t, P = softmax over s,
-    o = P v ([train-124M] §2.12 and §5).  Returns o and P."""
+    o = P v ([train-124M] §2.12 and §5).  ``mask`` ([T, T] bool, True where
+    query t may see key s) replaces the causal mask, e.g. by packed_mask's
+    document mask.  Returns o and P."""
     T, hd = q.shape
     s = (q @ k.T) / np.sqrt(hd)
-    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
-    s = np.where(mask, -np.inf, s)
+    if mask is None:
+        hidden = np.triu(np.ones((T, T), dtype=bool), k=1)
+    else:
+        hidden = ~mask
+    s = np.where(hidden, -np.inf, s)
     smax = s.max(axis=-1, keepdims=True)
     e = np.exp(s - smax)
     p = e / e.sum(axis=-1, keepdims=True)
@@ -229,11 +257,27 @@ def _merge_heads(x):
     return x.transpose(0, 2, 1, 3).reshape(B, T, H * hd)
 
 
-def forward(cfg: Config, params, idx, targets, scale=1.0, chunk=1024, want_logits=False, n_valid=None):
+def packed_rows(idx, eot):
+    """packed_mask of every row: (masks [B, T, T], pos [B, T]), or (None,
+    positions 0..T-1 in every row) when eot is None."""
+    B, T = idx.shape
+    if eot is None:
+        return None, np.broadcast_to(np.arange(T), (B, T))
+    masks = np.empty((B, T, T), dtype=bool)
+    pos = np.empty((B, T), dtype=np.int64)
+    for b in range(B):
+        masks[b], pos[b] = packed_mask(idx[b], eot)
+    return masks, pos
+
+
+def forward(cfg: Config, params, idx, targets, scale=1.0, chunk=1024, want_logits=False, n_valid=None, eot=None):
     """Forward pass with every activation the backward needs.
 
     idx, targets: int [B, T].  Position ids are 0..T-1 in every row
-    ([train-124M] §2.10).  Returns (loss, row_loss [B*T], cache)."""
+    ([train-124M] §2.10).  With ``eot`` set, every row is a packed window
+    under the document mask of packed_mask, positions restarted at each
+    document ([zero2front] "Document boundaries, packing and masking").
+    Returns (loss, row_loss [B*T], cache)."""
     B, T = idx.shape
     H, L = cfg.n_head, cfg.n_layer
     wte = params["transformer.wte.weight"]
@@ -245,8 +289,9 @@ def forward(cfg: Config, params, idx, targets, scale=1.0, chunk=1024, want_logit
         raise ValueError("T exceeds block_size")
 
     # token + position embedding ([train-124M] §2.2, §2.10)
-    h = wte[idx] + wpe[np.arange(T)][None, :, :]
-    cache = {"idx": idx, "targets": targets, "layers": []}
+    masks, pos = packed_rows(idx, eot)
+    h = wte[idx] + wpe[pos]
+    cache = {"idx": idx, "targets": targets, "layers": [], "pos": None if eot is None else pos}
     for layer in range(L):
         p = f"transformer.h.{layer}."
         lc = {"h_in": h}
@@ -260,7 +305,7 @@ def forward(cfg: Config, params, idx, targets, scale=1.0, chunk=1024, want_logit
         ps = np.empty((B, H, T, T), dtype=dt)
         for b in range(B):
             for j in range(H):
-                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j], vh[b, j])
+                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j], vh[b, j], None if masks is None else masks[b])
         y = _merge_heads(oh)
         lc.update(qh=qh, kh=kh, vh=vh, p=ps, y=y)
         h = h + (y @ params[p + "attn.c_proj.weight"].T + params[p + "attn.c_proj.bias"])
@@ -358,21 +403,26 @@ def backward(cfg: Config, params, cache):
         dh = dh + dx
 
     # embeddings: wte receives the scattered rows on top of its lm_head part
-    # (the tied weight, [train-124M] §4); wpe sums over the batch.
+    # (the tied weight, [train-124M] §4); wpe sums over the batch, or, with
+    # restarted positions, over every token at each position.
     idx = cache["idx"]
     T = idx.shape[1]
     np.add.at(grads["transformer.wte.weight"], idx.reshape(-1), dh.reshape(-1, dh.shape[-1]))
-    grads["transformer.wpe.weight"][:T] += dh.sum(axis=0)
+    if cache["pos"] is None:
+        grads["transformer.wpe.weight"][:T] += dh.sum(axis=0)
+    else:
+        np.add.at(grads["transformer.wpe.weight"], cache["pos"].reshape(-1), dh.reshape(-1, dh.shape[-1]))
     return grads
 
 
-def fwd_bwd(cfg: Config, params, idx, targets, scale=1.0, grads=None, chunk=1024, n_valid=None):
+def fwd_bwd(cfg: Config, params, idx, targets, scale=1.0, grads=None, chunk=1024, n_valid=None, eot=None):
     """One micro-step: loss of the micro-batch (unscaled mean over its valid
     targets) and the gradient of scale * loss added into ``grads``
-    ([train-124M] §8.1: loss / grad_accum_steps, then backward).
+    ([train-124M] §8.1: loss / grad_accum_steps, then backward).  ``eot``
+    selects the packed document mask (forward()).
 
     Returns (loss, row_loss, grads)."""
-    loss, row_loss, cache = forward(cfg, params, idx, targets, scale=scale, chunk=chunk, n_valid=n_valid)
+    loss, row_loss, cache = forward(cfg, params, idx, targets, scale=scale, chunk=chunk, n_valid=n_valid, eot=eot)
     g = backward(cfg, params, cache)
     if cache["n_valid"] == 0:
         g = {k: np.zeros_like(v) for k, v in g.items()}

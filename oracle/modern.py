@@ -43,7 +43,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .model import _merge_heads, _split_heads, attention_bwd, attention_fwd, cross_entropy_fwd_bwd
+from .model import _merge_heads, _split_heads, attention_bwd, attention_fwd, cross_entropy_fwd_bwd, packed_rows
 
 RMS_EPS = float(np.finfo(np.float32).eps)
 ROPE_BASE = 10000.0
@@ -166,9 +166,13 @@ def silu_grad(g):
 # model
 # ----------------------------------------------------------------------------
 
-def forward(cfg: ModernConfig, params, idx, targets, scale=1.0, chunk=1024, n_valid=None):
+def forward(cfg: ModernConfig, params, idx, targets, scale=1.0, chunk=1024, n_valid=None, eot=None, restart=True):
     """Forward pass with every activation the backward needs; idx, targets
-    int [B, T].  Returns (loss, row_loss [B*T], cache)."""
+    int [B, T].  With ``eot`` set, every row is a packed window under the
+    document mask ([zero2front] "Document boundaries, packing and masking");
+    ``restart`` rotates q and k by the restarted positions (else by 0..T-1,
+    which the page says gives the same scores once the mask keeps documents
+    apart).  Returns (loss, row_loss [B*T], cache)."""
     B, T = idx.shape
     H, L, C, F = cfg.n_head, cfg.n_layer, cfg.n_embd, cfg.mlp_hidden
     hd = cfg.head_dim
@@ -179,6 +183,9 @@ def forward(cfg: ModernConfig, params, idx, targets, scale=1.0, chunk=1024, n_va
     if T > cfg.block_size:
         raise ValueError("T exceeds block_size")
     cos, sin = rope_tables(T, hd, cfg.rope_base, dtype=dt)
+    masks, pos = packed_rows(idx, eot)
+    if eot is not None and restart:
+        cos, sin = cos[pos][:, None], sin[pos][:, None]  # [B, 1, T, hd]: per row, shared by the heads
 
     h = wte[idx]
     cache = {"idx": idx, "targets": targets, "layers": [], "cos": cos, "sin": sin}
@@ -196,7 +203,7 @@ def forward(cfg: ModernConfig, params, idx, targets, scale=1.0, chunk=1024, n_va
         ps = np.empty((B, H, T, T), dtype=dt)
         for b in range(B):
             for j in range(H):
-                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j], vh[b, j])
+                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j], vh[b, j], None if masks is None else masks[b])
         y = _merge_heads(oh)
         lc.update(qh=qh, kh=kh, vh=vh, p=ps, y=y)
         h = h + y @ params[p + "attn.c_proj.weight"].T
@@ -285,11 +292,13 @@ def backward(cfg: ModernConfig, params, cache):
     return grads
 
 
-def fwd_bwd(cfg: ModernConfig, params, idx, targets, scale=1.0, grads=None, chunk=1024, n_valid=None):
+def fwd_bwd(cfg: ModernConfig, params, idx, targets, scale=1.0, grads=None, chunk=1024, n_valid=None, eot=None,
+            restart=True):
     """One micro-step: the unscaled mean loss of the micro-batch and the
-    gradient of scale * loss added into ``grads``.  Returns (loss, row_loss,
-    grads)."""
-    loss, row_loss, cache = forward(cfg, params, idx, targets, scale=scale, chunk=chunk, n_valid=n_valid)
+    gradient of scale * loss added into ``grads``; ``eot`` and ``restart`` as
+    in forward().  Returns (loss, row_loss, grads)."""
+    loss, row_loss, cache = forward(cfg, params, idx, targets, scale=scale, chunk=chunk, n_valid=n_valid, eot=eot,
+                                    restart=restart)
     g = backward(cfg, params, cache)
     if cache["n_valid"] == 0:
         g = {k: np.zeros_like(v) for k, v in g.items()}

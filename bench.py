@@ -156,6 +156,9 @@ def main(argv=None):
     ap.add_argument("--traffic-probe", metavar="SITE", help="one marked micro-step for an HBM counter run")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2",
                     help="gpt2 (the headline step, default) or rotary (the modern variant)")
+    ap.add_argument("--doc-mask", type=float, default=None, metavar="MEAN_DOC",
+                    help="packed windows under the document mask, documents of this mean length in tokens "
+                         "(default: the plain causal step over documents of mean length 1000)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)",
@@ -176,7 +179,10 @@ def main(argv=None):
     model = g.GPT2(g.GPT2_124M if args.workload == "gpt2" else g.GPT2_ROTARY_124M)
     model.init_params(seed=42)
     n_params = model.sizes.n_params
-    stream = synthetic.token_stream(ga * B * T + 1, seed=1337)
+    mean_doc = args.doc_mask if args.doc_mask else 1000.0
+    stream = synthetic.token_stream(ga * B * T + 1, seed=1337, mean_doc=mean_doc)
+    if args.doc_mask:
+        model.set_doc_mask(synthetic.EOT_ID)
     xs, ys = [], []
     for k in range(ga):
         x, y = synthetic.micro_batch(stream, k, B, T)
@@ -256,7 +262,9 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (Zipf token stream, EOT-prefixed documents; random N(0,0.02) init)",
-        "config": {"workload": f"{wl['name']}: {ga} x micro-batch B={B} T={T} + clip 1.0 + AdamW lr {wl['lr']:g}",
+        "config": {"workload": f"{wl['name']}: {ga} x micro-batch B={B} T={T} + clip 1.0 + AdamW lr {wl['lr']:g}"
+                               + (f"; packed windows under the document mask, mean document {mean_doc:g} tokens"
+                                  if args.doc_mask else ""),
                    "global_batch_tokens": ga * B * T, "micro_batch": B, "seq_len": T, "grad_accum": ga,
                    "vocab": 50304, "parallelism": "none (1 GPU)"},
         "mfu": round(tps * fpt / PEAK_BF16, 4),

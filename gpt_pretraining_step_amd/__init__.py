@@ -24,7 +24,7 @@ from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noq
                    EPI_ROPE, EPI_SWIGLU, EPI_SWIGLU_BWD, ARCH_GPT2, ARCH_ROTARY, GPT2_ERR_ARG)
 
 __all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm", "op_gemm_grouped",
-           "op_attention_fwd", "op_attention_bwd", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
+           "op_attention_fwd", "op_attention_bwd", "op_segment_starts", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
            "op_rope_table", "op_rope_bwd", "op_rmsnorm_fwd", "op_rmsnorm_bwd", "query_sizes", "param_table",
            "GPT2_ROTARY_124M"]
 
@@ -140,6 +140,11 @@ class GPT2:
 
     def sync_shadow(self):
         check(lib().gpt2_sync_shadow(self._h), "gpt2_sync_shadow")
+
+    def set_doc_mask(self, eot):
+        """Packed windows under the document mask of ``eot`` (None: plain
+        causal rows)."""
+        check(lib().gpt2_set_doc_mask(self._h, -1 if eot is None else int(eot)), "gpt2_set_doc_mask")
 
     def zero_grad(self):
         check(lib().gpt2_zero_grad(self._h), "gpt2_zero_grad")
@@ -359,19 +364,41 @@ def op_layernorm_bwd(dy, x, mean, rstd, w, dx, dw, db, dx_bf16=None, stream=None
           "gpt2_op_layernorm_bwd")
 
 
-def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None):
+def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None, seg=None):
+    """seg: optional int32 device tensor [B, T] of document starts
+    (op_segment_starts) for packed windows."""
     import torch
     dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
+    _check_seg(seg, B, T)
     check(lib().gpt2_op_attention_fwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
-                                      lse.data_ptr()), "gpt2_op_attention_fwd")
+                                      lse.data_ptr(), _ptr(seg)), "gpt2_op_attention_fwd")
 
 
-def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None):
+def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None):
     import torch
     dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
+    _check_seg(seg, B, T)
     nbytes = lib().gpt2_attention_bwd_scratch_bytes(B, T, H)
     scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qkv.device)
     check(lib().gpt2_op_attention_bwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
-                                      dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr()),
+                                      dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr(), _ptr(seg)),
           "gpt2_op_attention_bwd")
+
+
+def _check_seg(seg, B, T):
+    import torch
+    if seg is not None:
+        assert seg.dtype == torch.int32 and seg.is_contiguous() and seg.numel() == B * T
+
+
+def op_segment_starts(tokens, eot: int, stream=None):
+    """Document starts of packed rows: int32 [B, T], entry t = the last
+    position <= t holding ``eot`` (0 if none)."""
+    import torch
+    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.dim() == 2
+    B, T = tokens.shape
+    seg = torch.empty_like(tokens)
+    check(lib().gpt2_op_segment_starts(_stream_ptr(stream), tokens.data_ptr(), B, T, int(eot), seg.data_ptr()),
+          "gpt2_op_segment_starts")
+    return seg
 from . import train  # noqa: E402,F401  (the training loop)

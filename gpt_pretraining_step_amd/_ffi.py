@@ -85,6 +85,7 @@ SIGNATURES = {
     "gpt2_create": (ct.c_int, [ct.POINTER(Config), ct.POINTER(Buffers), ct.c_void_p, ct.POINTER(ct.c_void_p)]),
     "gpt2_destroy": (ct.c_int, [ct.c_void_p]),
     "gpt2_set_stream": (ct.c_int, [ct.c_void_p, ct.c_void_p]),
+    "gpt2_set_doc_mask": (ct.c_int, [ct.c_void_p, ct.c_int]),
     "gpt2_init_params": (ct.c_int, [ct.c_void_p, ct.c_uint64]),
     "gpt2_sync_shadow": (ct.c_int, [ct.c_void_p]),
     "gpt2_zero_grad": (ct.c_int, [ct.c_void_p]),
@@ -111,10 +112,12 @@ SIGNATURES = {
                                          ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int]),
     "gpt2_op_layernorm_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int] + [ct.c_void_p] * 8 + [ct.c_int, ct.c_int]),
     "gpt2_op_attention_fwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
-                                         ct.c_void_p, ct.c_void_p]),
+                                         ct.c_void_p, ct.c_void_p, ct.c_void_p]),
     "gpt2_attention_bwd_scratch_bytes": (ct.c_size_t, [ct.c_int, ct.c_int, ct.c_int]),
     "gpt2_op_attention_bwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
-                                         ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p]),
+                                         ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                         ct.c_void_p]),
+    "gpt2_op_segment_starts": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "gpt2_profile_enable": (ct.c_int, [ct.c_void_p, ct.c_int]),
     "gpt2_profile_only": (ct.c_int, [ct.c_void_p, ct.c_char_p]),
     "gpt2_profile_mark": (ct.c_int, [ct.c_void_p, ct.c_int]),

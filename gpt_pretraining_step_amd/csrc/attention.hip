@@ -19,6 +19,14 @@
 // P recomputed from the saved row log-sum-exp, dV = P^T dO,
 // dS = P o (dO V^T - D), dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd).
 //
+// Packed windows ("GPT" chapter of Zero to Frontier, "Document boundaries,
+// packing and masking"): with a document mask, query t of a row sees only
+// the keys s with start[t] <= s <= t, start[t] being the first position of
+// t's document (seg, [B, T] int32, non-decreasing along a row with
+// start[t] <= t).  Whole key tiles before the block's first document start
+// are skipped; the remaining ones are masked per element where they reach
+// below some query's start.  seg == nullptr is the plain causal mask.
+//
 // float32 (FP32 precision mode, small heads): one thread per query (or key),
 // plain loops.
 #include "tile_io.h"
@@ -31,7 +39,7 @@ constexpr float kLN2 = 0.6931471805599453f;
 // ========================================================= float32 kernels
 
 __global__ void attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __restrict__ y, float* __restrict__ lse,
-                                    int B, int T, int H, int hd, float scale) {
+                                    const int32_t* __restrict__ seg, int B, int T, int H, int hd, float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * H * T) return;
   const int t = i % T, bh = i / T, h = bh % H, b = bh / H;
@@ -40,7 +48,7 @@ __global__ void attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __rest
   float acc[64];
   for (int d = 0; d < hd; ++d) acc[d] = 0.f;
   float m = -INFINITY, l = 0.f;
-  for (int s = 0; s <= t; ++s) {
+  for (int s = seg ? max(seg[(int64_t)b * T + t], 0) : 0; s <= t; ++s) {
     const float* k = qkv + ((int64_t)b * T + s) * C3 + C + h * hd;
     const float* v = k + C;
     float sc = 0.f;
@@ -59,8 +67,8 @@ __global__ void attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __rest
 
 __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const float* __restrict__ y,
                                        const float* __restrict__ dy, const float* __restrict__ lse,
-                                       float* __restrict__ dqkv, float* __restrict__ Dbuf, int B, int T, int H, int hd,
-                                       float scale) {
+                                       float* __restrict__ dqkv, float* __restrict__ Dbuf,
+                                       const int32_t* __restrict__ seg, int B, int T, int H, int hd, float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * H * T) return;
   const int t = i % T, bh = i / T, h = bh % H, b = bh / H;
@@ -74,7 +82,7 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const floa
   float acc[64];
   for (int d = 0; d < hd; ++d) acc[d] = 0.f;
   const float L = lse[i];
-  for (int s = 0; s <= t; ++s) {
+  for (int s = seg ? max(seg[(int64_t)b * T + t], 0) : 0; s <= t; ++s) {
     const float* k = qkv + ((int64_t)b * T + s) * C3 + C + h * hd;
     const float* v = k + C;
     float sc = 0.f, dp = 0.f;
@@ -92,7 +100,8 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const floa
 
 __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv, const float* __restrict__ dy,
                                          const float* __restrict__ lse, const float* __restrict__ Dbuf,
-                                         float* __restrict__ dqkv, int B, int T, int H, int hd, float scale) {
+                                         float* __restrict__ dqkv, const int32_t* __restrict__ seg, int B, int T,
+                                         int H, int hd, float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * H * T) return;
   const int s = i % T, bh = i / T, h = bh % H, b = bh / H;
@@ -102,6 +111,7 @@ __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv, const fl
   float dk[64], dv[64];
   for (int d = 0; d < hd; ++d) dk[d] = dv[d] = 0.f;
   for (int t = s; t < T; ++t) {
+    if (seg && seg[(int64_t)b * T + t] > s) break;  // t's document starts after key s, as do all later ones
     const float* q = qkv + ((int64_t)b * T + t) * C3 + h * hd;
     const float* dO = dy + ((int64_t)b * T + t) * C + h * hd;
     float sc = 0.f, dp = 0.f;
@@ -189,9 +199,11 @@ __device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt vmcnt(0
 // Forward.  Block = NW waves x 32 queries; loop over 64-key tiles.  Each lane
 // owns one query (S^T = K Q^T, O^T = V^T P^T), so the online-softmax state is
 // per lane, shared with the partner lane 32 away.
-template <int NW, int ST>
+template <int NW, int ST, bool DOC>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
-                                                                float* __restrict__ lse, int T, int H, float sl2) {
+                                                                float* __restrict__ lse,
+                                                                const int32_t* __restrict__ seg, int T, int H,
+                                                                float sl2) {
   constexpr int BQ = 32 * NW;
   constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
   __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][64 * HD];  // [stage][K, V]
@@ -217,18 +229,28 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
   float m = -1e30f, l = 0.f;
   const int kv_end = min(T, qb * BQ + BQ);
   const int ntiles = (kv_end + 63) / 64;
+  // document mask: the key tiles before the block's first query's document
+  // start are skipped (that query has the smallest start of the block);
+  // seg_lo is this lane's query's start, seg_hi the wave's largest
+  int jt0 = 0, seg_lo = 0, seg_hi = 0;
+  if constexpr (DOC) {
+    const int32_t* sr = seg + (int64_t)b * T;
+    jt0 = min(max(sr[qb * BQ] / 64, 0), ntiles - 1);
+    seg_lo = sr[min(qi, T - 1)];
+    seg_hi = sr[min(q0 + 31, T - 1)];
+  }
   auto issue = [&](int st, int tile) {
     dma_rows<64, 64, NW, true>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
     dma_rows<64, 64, NW, true>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
   };
   // ST-stage ring: tiles jt+1 .. jt+ST-2 stay in flight while tile jt is
   // used; tile jt+ST-1 goes into the buffer of tile jt-1 once every wave has
-  // passed this iteration's barrier.
+  // passed this iteration's barrier.  Tile jt lives in stage (jt - jt0) % ST.
 #pragma unroll
   for (int t = 0; t < ST - 1; ++t)
-    if (t < ntiles) issue(t, t);
+    if (jt0 + t < ntiles) issue(t, jt0 + t);
   drain_vector_loads();
-  for (int jt = 0; jt < ntiles; ++jt) {
+  for (int jt = jt0; jt < ntiles; ++jt) {
     if (jt + ST - 2 < ntiles) {
       if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else if constexpr (ST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_TILE) : "memory");
@@ -237,13 +259,15 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (jt + ST - 1 < ntiles) issue((jt + ST - 1) % ST, jt + ST - 1);
+    const int stg = (jt - jt0) % ST;
+    if (jt + ST - 1 < ntiles) issue((stg + ST - 1) % ST, jt + ST - 1);
     const int kb = jt * 64;
-    // a tile wholly after this wave's queries is computed anyway (every
-    // score masked, no contribution): a skip would make the compiler copy
-    // the accumulators around the branch on every tile
-    const bf16* Ks = sm[jt % ST][0];
-    const bf16* Vs = sm[jt % ST][1];
+    // a tile wholly after (or, in a packed window, wholly before) this
+    // wave's queries is computed anyway (every score masked, no
+    // contribution): a skip would make the compiler copy the accumulators
+    // around the branch on every tile
+    const bf16* Ks = sm[stg][0];
+    const bf16* Vs = sm[stg][1];
     f32x16 sT[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -252,16 +276,21 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
       for (int kk = 0; kk < 4; ++kk) sT[c] = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT[c]);
     }
     // keys after the query (and past T) only occur in the diagonal and
-    // ragged tiles; the branch is uniform over the wave (the empty asm keeps
-    // the compiler from turning it into selects on every tile).  Element r
-    // of block c is key kb + 32 c + 4 lg + (8 (r / 4) + r % 4).
-    if ((kb + 63 > q0) || (kb + 63 >= T)) {
+    // ragged tiles, keys before its document start only in tiles below the
+    // wave's largest start; the branch is uniform over the wave (the empty
+    // asm keeps the compiler from turning it into selects on every tile).
+    // Element r of block c is key kb + 32 c + 4 lg + (8 (r / 4) + r % 4).
+    if ((kb + 63 > q0) || (kb + 63 >= T) || (DOC && kb < seg_hi)) {
       asm volatile("");
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int lim = min(qi, T - 1) - kb - 32 * c - 4 * lg;
+        const int lo = seg_lo - kb - 32 * c - 4 * lg;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[c][r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : sT[c][r];
+        for (int r = 0; r < 16; ++r) {
+          const int o = 8 * (r >> 2) + (r & 3);
+          sT[c][r] = (o > lim || (DOC && o < lo)) ? -INFINITY : sT[c][r];
+        }
       }
     }
     float mx = -INFINITY;
@@ -320,13 +349,14 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
 }
 
 // Backward, pass 1: D = rowsum(dO o O) and dQ.  Same tiling as the forward.
-template <int NW, int ST>
+template <int NW, int ST, bool DOC>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
                                                                    bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
-                                                                   int T, int H, float scale, float sl2) {
+                                                                   const int32_t* __restrict__ seg, int T, int H,
+                                                                   float scale, float sl2) {
   constexpr int BQ = 32 * NW;
   constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
   __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][64 * HD];  // [stage][K, V]
@@ -368,18 +398,26 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
   f32x16 dqT[2] = {zero16(), zero16()};
   const int kv_end = min(T, qb * BQ + BQ);
   const int ntiles = (kv_end + 63) / 64;
+  // document mask: as in the forward
+  int jt0 = 0, seg_lo = 0, seg_hi = 0;
+  if constexpr (DOC) {
+    const int32_t* sr = seg + (int64_t)b * T;
+    jt0 = min(max(sr[qb * BQ] / 64, 0), ntiles - 1);
+    seg_lo = sr[min(qi, T - 1)];
+    seg_hi = sr[min(q0 + 31, T - 1)];
+  }
   auto issue = [&](int st, int tile) {
     dma_rows<64, 64, NW, true>(sm[st][0], Kg, C3, tile * 64, T, 0, HD);
     dma_rows<64, 64, NW, true>(sm[st][1], Vg, C3, tile * 64, T, 0, HD);
   };
   // ST-stage ring: tiles jt+1 .. jt+ST-2 stay in flight while tile jt is
   // used; tile jt+ST-1 goes into the buffer of tile jt-1 once every wave has
-  // passed this iteration's barrier.
+  // passed this iteration's barrier.  Tile jt lives in stage (jt - jt0) % ST.
 #pragma unroll
   for (int t = 0; t < ST - 1; ++t)
-    if (t < ntiles) issue(t, t);
+    if (jt0 + t < ntiles) issue(t, jt0 + t);
   drain_vector_loads();
-  for (int jt = 0; jt < ntiles; ++jt) {
+  for (int jt = jt0; jt < ntiles; ++jt) {
     if (jt + ST - 2 < ntiles) {
       if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else if constexpr (ST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_TILE) : "memory");
@@ -388,14 +426,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (jt + ST - 1 < ntiles) issue((jt + ST - 1) % ST, jt + ST - 1);
+    const int stg = (jt - jt0) % ST;
+    if (jt + ST - 1 < ntiles) issue((stg + ST - 1) % ST, jt + ST - 1);
     const int kb = jt * 64;
-    // a tile wholly after this wave's queries is computed anyway (every
-    // score masked, no contribution): a skip would make the compiler copy
-    // the accumulators around the branch on every tile
-    const bf16* Ks = sm[jt % ST][0];
-    const bf16* Vs = sm[jt % ST][1];
-    const bool edge = (kb + 63 > q0) || (kb + 63 >= T);  // uniform over the wave
+    // a tile wholly after (or wholly before) this wave's queries is
+    // computed anyway (every score masked, no contribution): a skip would
+    // make the compiler copy the accumulators around the branch on every tile
+    const bf16* Ks = sm[stg][0];
+    const bf16* Vs = sm[stg][1];
+    const bool edge = (kb + 63 > q0) || (kb + 63 >= T) || (DOC && kb < seg_hi);  // uniform over the wave
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       f32x16 sT = zero16(), dpT = zero16();
@@ -407,8 +446,12 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
       if (edge) {
         asm volatile("");
         const int lim = min(qi, T - 1) - kb - 32 * c - 4 * lg;
+        const int lo = seg_lo - kb - 32 * c - 4 * lg;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : sT[r];
+        for (int r = 0; r < 16; ++r) {
+          const int o = 8 * (r >> 2) + (r & 3);
+          sT[r] = (o > lim || (DOC && o < lo)) ? -INFINITY : sT[r];
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[r] = __builtin_amdgcn_exp2f(fmaf(sT[r], sl2, -lse2)) * (dpT[r] - D);
@@ -435,17 +478,20 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
 }
 
 // Backward, pass 2: dK and dV.  Block = NW waves x 32 keys; loop over 64-query
-// tiles from the block's diagonal to T.  Each lane owns one key (S = Q K^T).
-template <int NW>
+// tiles from the block's diagonal to T (in a packed window: to the end of the
+// document of the block's last key).  Each lane owns one key (S = Q K^T).
+template <int NW, bool DOC>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf16* __restrict__ qkv,
                                                                      const bf16* __restrict__ dy,
                                                                      const float* __restrict__ lse,
                                                                      const float* __restrict__ Dbuf,
-                                                                     bf16* __restrict__ dqkv, int T, int H,
+                                                                     bf16* __restrict__ dqkv,
+                                                                     const int32_t* __restrict__ seg, int T, int H,
                                                                      float scale, float sl2) {
   constexpr int BK = 32 * NW;
+  constexpr int NR = DOC ? 3 : 2;
   __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float rowst[2][2][64];   // [stage][lse, D]
+  __shared__ __attribute__((aligned(16))) float rowst[2][NR][64];  // [stage][lse, D, document start (int)]
   const int kblk = blockIdx.y;  // smallest keys (most queries) first, over all heads
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int C = H * HD, C3 = 3 * C;
@@ -469,7 +515,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
   }
   f32x16 dvT[2] = {zero16(), zero16()}, dkT[2] = {zero16(), zero16()};
   const int qstart = kblk * BK;
-  const int ntiles = (T - qstart + 63) / 64;
+  int qend = T;
+  const int32_t* sr = DOC ? seg + (int64_t)b * T : nullptr;
+  if constexpr (DOC) {
+    // the queries that see a key of this block are those before the first
+    // document start past the block's last key (starts never decrease)
+    const int kmax = min(qstart + BK - 1, T - 1);
+    int lo = qstart, hi = T;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sr[mid] > kmax) hi = mid;
+      else lo = mid + 1;
+    }
+    qend = max(lo, qstart + 1);
+  }
+  const int ntiles = (qend - qstart + 63) / 64;
   // Q and dO tiles, and the tile's 64 lse and D values, by DMA (lse and D
   // from wave 0; rows past T read zeros, and their scores are masked)
   const bool w0 = __builtin_amdgcn_readfirstlane(wave) == 0;
@@ -483,6 +543,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
                lds_addr(&rowst[st][0][0]));
       dma4_ptr(q < T ? static_cast<const void*>(Dg + q) : static_cast<const void*>(g2_zero16),
                lds_addr(&rowst[st][1][0]));
+      if constexpr (DOC)
+        dma4_ptr(q < T ? static_cast<const void*>(sr + q) : static_cast<const void*>(g2_zero16),
+                 lds_addr(&rowst[st][NR - 1][0]));
     }
   };
   issue(0, 0);
@@ -499,7 +562,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     const bf16* dOs = sm[jt & 1][1];
     const float* Ls = rowst[jt & 1][0];
     const float* Ds = rowst[jt & 1][1];
-    const bool edge = (qs < k0 + 31) || (qs + 63 >= T);
+    const int* Ss = reinterpret_cast<const int*>(rowst[jt & 1][NR - 1]);
+    // in a packed window: some query of the tile starts its document after
+    // this wave's first key (the tile's last query has the largest start)
+    const bool edge = (qs < k0 + 31) || (qs + 63 >= T) || (DOC && Ss[min(63, T - 1 - qs)] > k0);
     // the two 32-query halves of the tile one after the other (fewer live
     // accumulators and operand fragments)
 #pragma unroll
@@ -523,6 +589,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
         for (int r = 0; r < 16; ++r) {
           const int o = 8 * (r >> 2) + (r & 3);
           sc[r] = (o < lo || o > hi) ? -INFINITY : sc[r];
+        }
+        if constexpr (DOC) {
+          // and queries whose document starts after this lane's key
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int4 S4 = *reinterpret_cast<const int4*>(Ss + 32 * c + 8 * a + 4 * lg);
+            const int Sv[4] = {S4.x, S4.y, S4.z, S4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[4 * a + e] = Sv[e] > kj ? -INFINITY : sc[4 * a + e];
+          }
         }
       }
 #pragma unroll
@@ -575,18 +651,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
 // =============================================================== launchers
 
 hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv, void* y,
-                                float* lse) {
+                                float* lse, const int32_t* seg) {
   const float scale = 1.f / sqrtf((float)hd);
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
     constexpr int NW = 4, ST = 2;
     dim3 grid(B * H, (T + 32 * NW - 1) / (32 * NW));
-    attn_fwd_bf16_kernel<NW, ST><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<bf16*>(y),
-                                                                 lse, T, H, scale * kLOG2E);
+    const bf16* q = static_cast<const bf16*>(qkv);
+    bf16* o = static_cast<bf16*>(y);
+    if (seg) attn_fwd_bf16_kernel<NW, ST, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, lse, seg, T, H, scale * kLOG2E);
+    else attn_fwd_bf16_kernel<NW, ST, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, lse, nullptr, T, H, scale * kLOG2E);
   } else {
     const int n = B * H * T;
     attn_fwd_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(static_cast<const float*>(qkv), static_cast<float*>(y),
-                                                              lse, B, T, H, hd, scale);
+                                                              lse, seg, B, T, H, hd, scale);
   }
   prof_end(L);
   return hipGetLastError();
@@ -595,27 +673,36 @@ hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H,
 size_t attention_bwd_scratch(int B, int T, int H) { return (size_t)B * T * H * sizeof(float); }
 
 hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
-                                const void* y, const void* dy, const float* lse, void* dqkv, void* scratch) {
+                                const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
+                                const int32_t* seg) {
   const float scale = 1.f / sqrtf((float)hd);
   float* Dbuf = static_cast<float*>(scratch);
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
     constexpr int NW = 4;
     dim3 grid(B * H, (T + 32 * NW - 1) / (32 * NW));
-    attn_bwd_dq_bf16_kernel<NW, 2><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(y),
-                                                        static_cast<const bf16*>(dy), lse, static_cast<bf16*>(dqkv),
-                                                        Dbuf, T, H, scale, scale * kLOG2E);
-    attn_bwd_dkdv_bf16_kernel<NW><<<grid, 64 * NW, 0, L.stream>>>(static_cast<const bf16*>(qkv), static_cast<const bf16*>(dy),
-                                                          lse, Dbuf, static_cast<bf16*>(dqkv), T, H, scale,
-                                                          scale * kLOG2E);
+    const bf16* q = static_cast<const bf16*>(qkv);
+    const bf16* o = static_cast<const bf16*>(y);
+    const bf16* dO = static_cast<const bf16*>(dy);
+    bf16* dq = static_cast<bf16*>(dqkv);
+    const float sl2 = scale * kLOG2E;
+    if (seg) {
+      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, seg, T, H, scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, seg, T, H, scale, sl2);
+    } else {
+      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, nullptr, T, H, scale,
+                                                                            sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, nullptr, T, H, scale,
+                                                                           sl2);
+    }
   } else {
     const int n = B * H * T;
     attn_bwd_dq_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(
         static_cast<const float*>(qkv), static_cast<const float*>(y), static_cast<const float*>(dy), lse,
-        static_cast<float*>(dqkv), Dbuf, B, T, H, hd, scale);
+        static_cast<float*>(dqkv), Dbuf, seg, B, T, H, hd, scale);
     attn_bwd_dkdv_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(static_cast<const float*>(qkv),
                                                                    static_cast<const float*>(dy), lse, Dbuf,
-                                                                   static_cast<float*>(dqkv), B, T, H, hd, scale);
+                                                                   static_cast<float*>(dqkv), seg, B, T, H, hd, scale);
   }
   prof_end(L);
   return hipGetLastError();

@@ -123,16 +123,21 @@ hipError_t launch_rmsnorm_fwd(const Launch& L, const float* x, const float* w, b
 hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* rstd,
                               const float* w, float* dx, bf16* dxb, float* dw, int rows, int C);
 
+// seg: [B, T] document starts of packed windows (nullptr: plain causal).
 hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
-                                void* y, float* lse);
+                                void* y, float* lse, const int32_t* seg);
 hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
-                                const void* y, const void* dy, const float* lse, void* dqkv, void* scratch);
+                                const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
+                                const int32_t* seg);
 size_t attention_bwd_scratch(int B, int T, int H);
 
+// seg[b, t] = last position s <= t of row b with tok[b, s] == eot (0 if none).
+hipError_t launch_segment_starts(const Launch& L, const int32_t* tok, int B, int T, int eot, int32_t* seg);
+// seg (nullable): positions restart at each document start, t - seg[b, t].
 hipError_t launch_embed_fwd(const Launch& L, const int32_t* tok, const float* wte, const float* wpe, float* out,
-                            int B, int T, int C, int V, int* flag);
+                            int B, int T, int C, int V, int* flag, const int32_t* seg);
 hipError_t launch_embed_bwd(const Launch& L, const int32_t* tok, const float* dr, float* dwte, float* dwpe, int B,
-                            int T, int C, int V);
+                            int T, int C, int V, const int32_t* seg);
 
 // Cross-entropy helpers for the chunked lm_head.
 hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int* count, int* flag);

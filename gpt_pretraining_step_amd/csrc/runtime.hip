@@ -251,7 +251,7 @@ struct Layout {
   size_t Z = 0, meanf = 0, rstdf = 0, act_bytes = 0;
   // scratch
   size_t dR = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
-  size_t ce_stats = 0, rope = 0;
+  size_t ce_stats = 0, rope = 0, seg = 0;
   size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, scratch_bytes = 0;
   // bf16: the first operands of the weight-gradient products, kept per layer
   // until the products run together at the end of the backward: dRbS[2l+1]
@@ -318,6 +318,7 @@ Layout build_layout(const gpt2_config& c) {
     y.dU = s.take(rows * FU * y.es);
   }
   y.attnD = s.take(rows * H * 4);
+  y.seg = s.take(rows * 4);  // document starts of packed windows
   if (c.arch == GPT2_ARCH_ROTARY) y.rope = s.take((size_t)c.block_size * 32 * sizeof(float2));
   if (c.precision == GPT2_PRECISION_BF16) {
     for (int l = 0; l < 2 * L; ++l) y.dRbS.push_back(s.take(rows * C * 2));
@@ -370,6 +371,7 @@ struct gpt2_ctx {
   std::vector<char> dw_image;  // the group table last copied to the device
   hipStream_t cap = nullptr;    // capture stream of gpt2_graph_capture
   hipGraphExec_t graph = nullptr;
+  int doc_eot = -1;  // >= 0: packed windows under the document mask of this EOT id
 
   bool bf() const { return cfg.precision == GPT2_PRECISION_BF16; }
   Launch at(const char* site) { return Launch{stream, &prof, site}; }
@@ -539,8 +541,13 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   float* rowloss = token_loss ? token_loss : c->scr<float>(y.rowloss);
 
   HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, count, flag));
+  const int32_t* seg = nullptr;
+  if (c->doc_eot >= 0) {
+    seg = c->scr<int32_t>(y.seg);
+    HIP_TRY(launch_segment_starts(c->at("embed.seg"), tok, B, T, c->doc_eot, c->scr<int32_t>(y.seg)));
+  }
   HIP_TRY(launch_embed_fwd(c->at("embed.fwd"), tok, c->P(c->tab.wte), c->P(c->tab.wpe), c->act<float>(y.Rin[0]), B,
-                           T, C, V, flag));
+                           T, C, V, flag, seg));
   // ---- forward
   for (int l = 0; l < g.n_layer; ++l) {
     float* rin = c->act<float>(y.Rin[l]);
@@ -550,7 +557,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     HIP_TRY(linear_fwd(c, "gemm.qkv", c->act(y.A1[l]), M, C, c->L(l, QKV_W), 3 * C, c->L(l, QKV_B), GPT2_EPI_STORE,
                        c->act(y.QKV[l]), nullptr, nullptr));
     HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
-                                 c->act<float>(y.LSE[l])));
+                                 c->act<float>(y.LSE[l]), seg));
     HIP_TRY(linear_fwd(c, "gemm.attn_proj", c->act(y.Y[l]), M, C, c->L(l, PROJ_W), C, c->L(l, PROJ_B),
                        GPT2_EPI_RESIDUAL, rmid, nullptr, rin));
     HIP_TRY(launch_layernorm_fwd(c->at("ln.fwd"), rmid, c->P(c->L(l, LN2_W)), c->P(c->L(l, LN2_B)), c->act(y.A2[l]),
@@ -650,7 +657,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     HIP_TRY(dw("gemm.attn_proj_dw", dRa, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
-                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
+                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg));
     HIP_TRY(dw("gemm.qkv_dw", dQKV, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
                static_cast<const float*>(dQKV)));
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
@@ -659,7 +666,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                                    c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)), M, C));
   }
   if (bf) HIP_TRY(run_dw(c, q));
-  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V));
+  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V, seg));
   return GPT2_OK;
 }
 
@@ -678,8 +685,18 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
 
   HIP_TRY(launch_rope_table(c->at("rope.table"), rope, T, 10000.0));
   HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, count, flag));
+  // packed windows: the mask only.  q and k keep the rotation of position t
+  // (not of t's place in its document): a rotation by t - start of both
+  // differs from one by t by the same angle for every pair of tokens of a
+  // document, and the mask hides every other pair, so the scores are those
+  // of restarted positions
+  const int32_t* seg = nullptr;
+  if (c->doc_eot >= 0) {
+    seg = c->scr<int32_t>(y.seg);
+    HIP_TRY(launch_segment_starts(c->at("embed.seg"), tok, B, T, c->doc_eot, c->scr<int32_t>(y.seg)));
+  }
   HIP_TRY(launch_embed_fwd(c->at("embed.fwd"), tok, c->P(c->tab.wte), nullptr, c->act<float>(y.Rin[0]), B, T, C, V,
-                           flag));
+                           flag, seg));
   for (int l = 0; l < g.n_layer; ++l) {
     float* rin = c->act<float>(y.Rin[l]);
     float* rmid = c->act<float>(y.Rmid[l]);
@@ -696,7 +713,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
       HIP_TRY(launch_gemm(c->at("gemm.qkv"), a));
     }
     HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
-                                 c->act<float>(y.LSE[l])));
+                                 c->act<float>(y.LSE[l]), seg));
     HIP_TRY(linear_fwd(c, "gemm.attn_proj", c->act(y.Y[l]), M, C, c->L(l, PROJ_W), C, -1, GPT2_EPI_RESIDUAL, rmid,
                        nullptr, rin));
     HIP_TRY(launch_rmsnorm_fwd(c->at("norm.fwd"), rmid, c->P(c->L(l, LN2_W)), c->act<bf16>(y.A2[l]),
@@ -758,7 +775,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     queue_dw(c, q, dRa, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1);
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
-                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD)));
+                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg));
     HIP_TRY(launch_rope_bwd(c->at("rope.bwd"), dQKV, M, 3 * C, 2 * C, T, rope));
     queue_dw(c, q, dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), -1);
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
@@ -766,7 +783,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
                                c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C));
   }
   HIP_TRY(run_dw(c, q));
-  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V));
+  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V, seg));
   return GPT2_OK;
 }
 
@@ -850,6 +867,18 @@ int gpt2_destroy(gpt2_ctx* c) {
 int gpt2_set_stream(gpt2_ctx* c, void* stream) {
   if (!c) return GPT2_ERR_ARG;
   c->stream = static_cast<hipStream_t>(stream);
+  return GPT2_OK;
+}
+
+int gpt2_set_doc_mask(gpt2_ctx* c, int eot) {
+  if (!c) return GPT2_ERR_ARG;
+  if (eot < -1 || eot >= c->cfg.vocab_size) return GPT2_ERR_ARG;
+  if (eot != c->doc_eot && c->graph) {  // a captured micro-step keeps the mask it was captured with
+    (void)hipStreamSynchronize(c->stream);
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+  }
+  c->doc_eot = eot;
   return GPT2_OK;
 }
 
@@ -1217,22 +1246,29 @@ static bool attn_shape_ok(int dtype, int B, int T, int H, int hd) {
 }
 
 int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv, void* d_y,
-                          float* d_lse) {
+                          float* d_lse, const int32_t* d_seg) {
   if (!d_qkv || !d_y || !d_lse) return GPT2_ERR_ARG;
   if (!attn_shape_ok(dtype, B, T, H, hd)) return GPT2_ERR_SHAPE;
   HIP_TRY(launch_attention_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, hd, d_qkv, d_y,
-                               d_lse));
+                               d_lse, d_seg));
   return GPT2_OK;
 }
 
 size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H) { return attention_bwd_scratch(B, T, H); }
 
 int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv, const void* d_y,
-                          const void* d_dy, const float* d_lse, void* d_dqkv, void* d_scratch) {
+                          const void* d_dy, const float* d_lse, void* d_dqkv, void* d_scratch, const int32_t* d_seg) {
   if (!d_qkv || !d_y || !d_dy || !d_lse || !d_dqkv || !d_scratch) return GPT2_ERR_ARG;
   if (!attn_shape_ok(dtype, B, T, H, hd)) return GPT2_ERR_SHAPE;
   HIP_TRY(launch_attention_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, hd, d_qkv, d_y,
-                               d_dy, d_lse, d_dqkv, d_scratch));
+                               d_dy, d_lse, d_dqkv, d_scratch, d_seg));
+  return GPT2_OK;
+}
+
+int gpt2_op_segment_starts(void* stream, const int32_t* d_tokens, int B, int T, int eot, int32_t* d_seg) {
+  if (!d_tokens || !d_seg) return GPT2_ERR_ARG;
+  if (B < 1 || T < 1) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_segment_starts(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_tokens, B, T, eot, d_seg));
   return GPT2_OK;
 }
 

@@ -151,6 +151,23 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_buffers* bufs, void* stream, 
 int gpt2_destroy(gpt2_ctx* ctx);
 int gpt2_set_stream(gpt2_ctx* ctx, void* stream);
 
+/* Packed windows under a document mask ("GPT" chapter of Zero to Frontier,
+ * "Document boundaries, packing and masking": documents concatenated with an
+ * end-of-text separator before each, attention block-diagonal over the
+ * documents of a window, position ids restarted at each document).  With
+ * eot in [0, vocab_size), every later gpt2_fwd_bwd treats each row of tokens
+ * as such a window: a document begins at each token equal to eot (the
+ * separator is its first token, at position 0) and the tokens before the
+ * row's first eot form a document of their own.  Query t sees key s iff
+ * start(t) <= s <= t, start(t) the last eot position <= t (0 if none); the
+ * GPT-2 model adds wpe[t - start(t)]; the rotary variant applies only the
+ * mask (with the mask in place, rotating by t or by t - start(t) gives the
+ * same scores, as that section notes).  Targets are untouched (the last
+ * token of a document still predicts the next eot).  eot == -1 restores the
+ * plain causal model.  Changing the setting discards a captured graph
+ * (gpt2_graph_capture).  eot outside [-1, vocab_size): GPT2_ERR_ARG. */
+int gpt2_set_doc_mask(gpt2_ctx* ctx, int eot);
+
 /* Initialise every parameter: Linear weights and both embeddings ~ N(0,
  * 0.02), the two residual projections (attn.c_proj, mlp.c_proj) ~ N(0, 0.02 /
  * sqrt(2 n_layer)), biases 0, LayerNorm weight 1 and bias 0 ("How I trained
@@ -422,15 +439,26 @@ int gpt2_op_rope_bwd(void* stream, void* d_dqkv, int rows, int64_t ld, int cols,
  * FineWeb-Edu" sections 2.12 and 5): qkv [B*T, 3*H*hd] holds q | k | v column
  * thirds, head h at columns h*hd of each third; y [B*T, H*hd] receives the
  * concatenated heads; lse float32 [B, H, T] the row log-sum-exp of the scaled
- * scores (natural log).  dtype selects bf16 or float32 tensors. */
+ * scores (natural log).  dtype selects bf16 or float32 tensors.
+ * d_seg (nullable) int32 [B, T]: document starts of packed windows (as
+ * gpt2_op_segment_starts writes them: 0 <= seg[t] <= t, non-decreasing
+ * along a row); query t then sees only keys seg[t] .. t.  Starts that break
+ * those rules give unspecified values (never an access outside the
+ * tensors). */
 int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv,
-                          void* d_y, float* d_lse);
+                          void* d_y, float* d_lse, const int32_t* d_seg);
 /* Backward: dqkv [B*T, 3*H*hd] is written.  d_scratch needs
- * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes. */
+ * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes; d_seg as in the forward. */
 size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H);
 int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv,
                           const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
-                          void* d_scratch);
+                          void* d_scratch, const int32_t* d_seg);
+
+/* Document starts of packed rows ("GPT" chapter of Zero to Frontier,
+ * "Document boundaries, packing and masking"): d_seg[b*T + t] = the last
+ * position s <= t with d_tokens[b*T + s] == eot, 0 if there is none (int32,
+ * device).  Any eot value is accepted (one that never occurs gives 0s). */
+int gpt2_op_segment_starts(void* stream, const int32_t* d_tokens, int B, int T, int eot, int32_t* d_seg);
 
 /* ---------------------------------------------------------- measurement -- */
 

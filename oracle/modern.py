@@ -61,22 +61,33 @@ class ModernConfig:
     n_embd: int
     mlp_hidden: int
     rope_base: float = ROPE_BASE
+    n_kv_head: int = 0  # key/value heads (grouped-query attention); 0: one per query head
 
     @property
     def head_dim(self) -> int:
         return self.n_embd // self.n_head
 
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_head or self.n_head
+
+    @property
+    def kv_dim(self) -> int:
+        return self.kv_heads * self.head_dim
+
 
 def param_specs(cfg: ModernConfig):
     """Names and shapes, in the order of the module listing (wte, the blocks,
-    ln_f).  Linear weights are [out, in]; lm_head is wte."""
+    ln_f).  Linear weights are [out, in]; lm_head is wte.  c_attn stacks the
+    q rows (C), then the k and the v rows (kv_dim each: fewer than C with
+    grouped-query attention)."""
     V, C, F = cfg.vocab_size, cfg.n_embd, cfg.mlp_hidden
     specs = [("transformer.wte.weight", (V, C))]
     for layer in range(cfg.n_layer):
         p = f"transformer.h.{layer}."
         specs += [
             (p + "ln_1.weight", (C,)),
-            (p + "attn.c_attn.weight", (3 * C, C)),
+            (p + "attn.c_attn.weight", (C + 2 * cfg.kv_dim, C)),
             (p + "attn.c_proj.weight", (C, C)),
             (p + "ln_2.weight", (C,)),
             (p + "mlp.c_fc.weight", (2 * F, C)),
@@ -172,10 +183,17 @@ def forward(cfg: ModernConfig, params, idx, targets, scale=1.0, chunk=1024, n_va
     document mask ([zero2front] "Document boundaries, packing and masking");
     ``restart`` rotates q and k by the restarted positions (else by 0..T-1,
     which the page says gives the same scores once the mask keeps documents
-    apart).  Returns (loss, row_loss [B*T], cache)."""
+    apart).  With grouped-query attention (n_kv_head < n_head) query head j
+    attends with key/value head j // (n_head / n_kv_head), each key/value head
+    serving a run of consecutive query heads ([fast-1gpu] "Step 2: the
+    attention kernel": repeat_interleave of the key and value heads).
+    Returns (loss, row_loss [B*T], cache)."""
     B, T = idx.shape
     H, L, C, F = cfg.n_head, cfg.n_layer, cfg.n_embd, cfg.mlp_hidden
-    hd = cfg.head_dim
+    hd, Hkv, Ckv = cfg.head_dim, cfg.kv_heads, cfg.kv_dim
+    if H % Hkv:
+        raise ValueError("n_head must be a multiple of n_kv_head")
+    grp = H // Hkv
     wte = params["transformer.wte.weight"]
     dt = wte.dtype
     if idx.min() < 0 or idx.max() >= cfg.vocab_size:
@@ -195,15 +213,16 @@ def forward(cfg: ModernConfig, params, idx, targets, scale=1.0, chunk=1024, n_va
         a1, lc["n1"] = rmsnorm_fwd(h, params[p + "ln_1.weight"])
         lc["a1"] = a1
         qkv = a1 @ params[p + "attn.c_attn.weight"].T
-        q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+        q, k, v = qkv[..., :C], qkv[..., C:C + Ckv], qkv[..., C + Ckv:]
         qh = rope_fwd(_split_heads(q, H), cos, sin)
-        kh = rope_fwd(_split_heads(k, H), cos, sin)
-        vh = _split_heads(v, H)
+        kh = rope_fwd(_split_heads(k, Hkv), cos, sin)
+        vh = _split_heads(v, Hkv)
         oh = np.empty_like(qh)
         ps = np.empty((B, H, T, T), dtype=dt)
         for b in range(B):
             for j in range(H):
-                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j], vh[b, j], None if masks is None else masks[b])
+                oh[b, j], ps[b, j] = attention_fwd(qh[b, j], kh[b, j // grp], vh[b, j // grp],
+                                                   None if masks is None else masks[b])
         y = _merge_heads(oh)
         lc.update(qh=qh, kh=kh, vh=vh, p=ps, y=y)
         h = h + y @ params[p + "attn.c_proj.weight"].T
@@ -270,18 +289,24 @@ def backward(cfg: ModernConfig, params, cache):
         dy = dh @ params[p + "attn.c_proj.weight"]
         doh = _split_heads(dy, H)
         dqh = np.empty_like(doh)
-        dkh = np.empty_like(doh)
-        dvh = np.empty_like(doh)
+        dkh = np.zeros_like(lc["kh"])
+        dvh = np.zeros_like(lc["vh"])
         B = doh.shape[0]
+        grp = H // dkh.shape[1]
         for b in range(B):
             for j in range(H):
-                dqh[b, j], dkh[b, j], dvh[b, j] = attention_bwd(
-                    doh[b, j], lc["qh"][b, j], lc["kh"][b, j], lc["vh"][b, j], lc["p"][b, j])
+                # a key/value head shared by a group of query heads gathers
+                # the gradients of all of them
+                dq, dk, dv = attention_bwd(doh[b, j], lc["qh"][b, j], lc["kh"][b, j // grp], lc["vh"][b, j // grp],
+                                           lc["p"][b, j])
+                dqh[b, j] = dq
+                dkh[b, j // grp] += dk
+                dvh[b, j // grp] += dv
         # back through the rotation of q and k
         dqh = rope_bwd(dqh, cos, sin)
         dkh = rope_bwd(dkh, cos, sin)
         dqkv = np.concatenate([_merge_heads(dqh), _merge_heads(dkh), _merge_heads(dvh)], axis=-1)
-        grads[p + "attn.c_attn.weight"] += dqkv.reshape(-1, 3 * C).T @ lc["a1"].reshape(-1, C)
+        grads[p + "attn.c_attn.weight"] += dqkv.reshape(-1, dqkv.shape[-1]).T @ lc["a1"].reshape(-1, C)
         da1 = dqkv @ params[p + "attn.c_attn.weight"]
         dx, dw = rmsnorm_bwd(da1, lc["n1"], params[p + "ln_1.weight"])
         grads[p + "ln_1.weight"] += dw

@@ -40,10 +40,11 @@ class ModelConfig:
     max_batch: int
     precision: int  # PRECISION_FP32 or PRECISION_BF16
     arch: int = ARCH_GPT2  # ARCH_GPT2 or ARCH_ROTARY
+    n_kv_head: int = 0  # key/value heads (grouped-query attention, rotary variant); 0: n_head
 
     def c(self) -> _ffi.Config:
         return _ffi.Config(self.vocab_size, self.block_size, self.n_layer, self.n_head, self.n_embd,
-                           self.mlp_hidden, self.max_batch, self.precision, self.arch)
+                           self.mlp_hidden, self.max_batch, self.precision, self.arch, self.n_kv_head)
 
 
 # The tiny character-level GPT in float32 (vocab 66, 2 layers, 64 wide, 4 heads, MLP 256, T 64, B 4).
@@ -364,23 +365,26 @@ def op_layernorm_bwd(dy, x, mean, rstd, w, dx, dw, db, dx_bf16=None, stream=None
           "gpt2_op_layernorm_bwd")
 
 
-def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None, seg=None):
+def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None, seg=None, n_kv_head=None):
     """seg: optional int32 device tensor [B, T] of document starts
-    (op_segment_starts) for packed windows."""
+    (op_segment_starts) for packed windows; n_kv_head: key/value heads
+    (grouped-query attention; default H)."""
     import torch
     dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
     _check_seg(seg, B, T)
-    check(lib().gpt2_op_attention_fwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
+    Hkv = H if n_kv_head is None else n_kv_head
+    check(lib().gpt2_op_attention_fwd(_stream_ptr(stream), dtype, B, T, H, Hkv, hd, qkv.data_ptr(), y.data_ptr(),
                                       lse.data_ptr(), _ptr(seg)), "gpt2_op_attention_fwd")
 
 
-def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None):
+def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, n_kv_head=None):
     import torch
     dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
     _check_seg(seg, B, T)
+    Hkv = H if n_kv_head is None else n_kv_head
     nbytes = lib().gpt2_attention_bwd_scratch_bytes(B, T, H)
     scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qkv.device)
-    check(lib().gpt2_op_attention_bwd(_stream_ptr(stream), dtype, B, T, H, hd, qkv.data_ptr(), y.data_ptr(),
+    check(lib().gpt2_op_attention_bwd(_stream_ptr(stream), dtype, B, T, H, Hkv, hd, qkv.data_ptr(), y.data_ptr(),
                                       dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr(), _ptr(seg)),
           "gpt2_op_attention_bwd")
 

@@ -41,7 +41,8 @@ ARCH_ROTARY = 1
 
 class Config(ct.Structure):
     _fields_ = [(n, ct.c_int32) for n in (
-        "vocab_size", "block_size", "n_layer", "n_head", "n_embd", "mlp_hidden", "max_batch", "precision", "arch")]
+        "vocab_size", "block_size", "n_layer", "n_head", "n_embd", "mlp_hidden", "max_batch", "precision", "arch",
+        "n_kv_head")]
 
 
 class Sizes(ct.Structure):
@@ -111,12 +112,12 @@ SIGNATURES = {
     "gpt2_op_layernorm_fwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
                                          ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int]),
     "gpt2_op_layernorm_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int] + [ct.c_void_p] * 8 + [ct.c_int, ct.c_int]),
-    "gpt2_op_attention_fwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
-                                         ct.c_void_p, ct.c_void_p, ct.c_void_p]),
+    "gpt2_op_attention_fwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
+                                         ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p]),
     "gpt2_attention_bwd_scratch_bytes": (ct.c_size_t, [ct.c_int, ct.c_int, ct.c_int]),
-    "gpt2_op_attention_bwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
+    "gpt2_op_attention_bwd": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
                                          ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
-                                         ct.c_void_p]),
+                                         ct.c_void_p, ct.c_void_p]),
     "gpt2_op_segment_starts": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "gpt2_profile_enable": (ct.c_int, [ct.c_void_p, ct.c_int]),
     "gpt2_profile_only": (ct.c_int, [ct.c_void_p, ct.c_char_p]),

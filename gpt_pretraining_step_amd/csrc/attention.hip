@@ -27,6 +27,14 @@
 // are skipped; the remaining ones are masked per element where they reach
 // below some query's start.  seg == nullptr is the plain causal mask.
 //
+// Grouped-query attention ("Build an LLM From Scratch: Making Training Fast
+// on One GPU", step 2, the textbook form repeats each key/value head for
+// n_head / n_kv_head consecutive query heads): qkv rows hold H query heads,
+// then Hkv key heads, then Hkv value heads; query head h reads key/value
+// head h / (H / Hkv), and the dK/dV pass runs once per key/value head, its
+// loop covering the query heads of the group one after the other, so the
+// shared head's gradient is summed in registers.
+//
 // float32 (FP32 precision mode, small heads): one thread per query (or key),
 // plain loops.
 #include "tile_io.h"
@@ -39,18 +47,19 @@ constexpr float kLN2 = 0.6931471805599453f;
 // ========================================================= float32 kernels
 
 __global__ void attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __restrict__ y, float* __restrict__ lse,
-                                    const int32_t* __restrict__ seg, int B, int T, int H, int hd, float scale) {
+                                    const int32_t* __restrict__ seg, int B, int T, int H, int Hkv, int hd,
+                                    float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * H * T) return;
   const int t = i % T, bh = i / T, h = bh % H, b = bh / H;
-  const int C = H * hd, C3 = 3 * C;
+  const int C = H * hd, Ckv = Hkv * hd, C3 = C + 2 * Ckv, kvo = C + (h / (H / Hkv)) * hd;
   const float* q = qkv + ((int64_t)b * T + t) * C3 + h * hd;
   float acc[64];
   for (int d = 0; d < hd; ++d) acc[d] = 0.f;
   float m = -INFINITY, l = 0.f;
   for (int s = seg ? max(seg[(int64_t)b * T + t], 0) : 0; s <= t; ++s) {
-    const float* k = qkv + ((int64_t)b * T + s) * C3 + C + h * hd;
-    const float* v = k + C;
+    const float* k = qkv + ((int64_t)b * T + s) * C3 + kvo;
+    const float* v = k + Ckv;
     float sc = 0.f;
     for (int d = 0; d < hd; ++d) sc += q[d] * k[d];
     sc *= scale;
@@ -68,11 +77,12 @@ __global__ void attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __rest
 __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const float* __restrict__ y,
                                        const float* __restrict__ dy, const float* __restrict__ lse,
                                        float* __restrict__ dqkv, float* __restrict__ Dbuf,
-                                       const int32_t* __restrict__ seg, int B, int T, int H, int hd, float scale) {
+                                       const int32_t* __restrict__ seg, int B, int T, int H, int Hkv, int hd,
+                                       float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * H * T) return;
   const int t = i % T, bh = i / T, h = bh % H, b = bh / H;
-  const int C = H * hd, C3 = 3 * C;
+  const int C = H * hd, Ckv = Hkv * hd, C3 = C + 2 * Ckv, kvo = C + (h / (H / Hkv)) * hd;
   const float* q = qkv + ((int64_t)b * T + t) * C3 + h * hd;
   const float* o = y + ((int64_t)b * T + t) * C + h * hd;
   const float* dO = dy + ((int64_t)b * T + t) * C + h * hd;
@@ -83,8 +93,8 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const floa
   for (int d = 0; d < hd; ++d) acc[d] = 0.f;
   const float L = lse[i];
   for (int s = seg ? max(seg[(int64_t)b * T + t], 0) : 0; s <= t; ++s) {
-    const float* k = qkv + ((int64_t)b * T + s) * C3 + C + h * hd;
-    const float* v = k + C;
+    const float* k = qkv + ((int64_t)b * T + s) * C3 + kvo;
+    const float* v = k + Ckv;
     float sc = 0.f, dp = 0.f;
     for (int d = 0; d < hd; ++d) {
       sc += q[d] * k[d];
@@ -101,35 +111,39 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const floa
 __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv, const float* __restrict__ dy,
                                          const float* __restrict__ lse, const float* __restrict__ Dbuf,
                                          float* __restrict__ dqkv, const int32_t* __restrict__ seg, int B, int T,
-                                         int H, int hd, float scale) {
+                                         int H, int Hkv, int hd, float scale) {
+  // one thread per (batch, key/value head, key)
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * H * T) return;
-  const int s = i % T, bh = i / T, h = bh % H, b = bh / H;
-  const int C = H * hd, C3 = 3 * C;
-  const float* k = qkv + ((int64_t)b * T + s) * C3 + C + h * hd;
-  const float* v = k + C;
+  if (i >= B * Hkv * T) return;
+  const int s = i % T, bj = i / T, j = bj % Hkv, b = bj / Hkv, grp = H / Hkv;
+  const int C = H * hd, Ckv = Hkv * hd, C3 = C + 2 * Ckv;
+  const float* k = qkv + ((int64_t)b * T + s) * C3 + C + j * hd;
+  const float* v = k + Ckv;
   float dk[64], dv[64];
   for (int d = 0; d < hd; ++d) dk[d] = dv[d] = 0.f;
-  for (int t = s; t < T; ++t) {
-    if (seg && seg[(int64_t)b * T + t] > s) break;  // t's document starts after key s, as do all later ones
-    const float* q = qkv + ((int64_t)b * T + t) * C3 + h * hd;
-    const float* dO = dy + ((int64_t)b * T + t) * C + h * hd;
-    float sc = 0.f, dp = 0.f;
-    for (int d = 0; d < hd; ++d) {
-      sc += q[d] * k[d];
-      dp += dO[d] * v[d];
-    }
-    const float p = expf(sc * scale - lse[bh * T + t]);
-    const float ds = p * (dp - Dbuf[bh * T + t]);
-    for (int d = 0; d < hd; ++d) {
-      dv[d] += p * dO[d];
-      dk[d] += ds * q[d];
+  for (int h = j * grp; h < (j + 1) * grp; ++h) {
+    const int bh = b * H + h;
+    for (int t = s; t < T; ++t) {
+      if (seg && seg[(int64_t)b * T + t] > s) break;  // t's document starts after key s, as do all later ones
+      const float* q = qkv + ((int64_t)b * T + t) * C3 + h * hd;
+      const float* dO = dy + ((int64_t)b * T + t) * C + h * hd;
+      float sc = 0.f, dp = 0.f;
+      for (int d = 0; d < hd; ++d) {
+        sc += q[d] * k[d];
+        dp += dO[d] * v[d];
+      }
+      const float p = expf(sc * scale - lse[bh * T + t]);
+      const float ds = p * (dp - Dbuf[bh * T + t]);
+      for (int d = 0; d < hd; ++d) {
+        dv[d] += p * dO[d];
+        dk[d] += ds * q[d];
+      }
     }
   }
-  float* o = dqkv + ((int64_t)b * T + s) * C3 + C + h * hd;
+  float* o = dqkv + ((int64_t)b * T + s) * C3 + C + j * hd;
   for (int d = 0; d < hd; ++d) {
     o[d] = dk[d] * scale;
-    o[C + d] = dv[d];
+    o[Ckv + d] = dv[d];
   }
 }
 
@@ -203,7 +217,7 @@ template <int NW, int ST, bool DOC>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
                                                                 float* __restrict__ lse,
                                                                 const int32_t* __restrict__ seg, int T, int H,
-                                                                float sl2) {
+                                                                int Hkv, float sl2) {
   constexpr int BQ = 32 * NW;
   constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
   __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][64 * HD];  // [stage][K, V]
@@ -213,10 +227,10 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
   // causal triangle over the compute units)
   const int qb = nqb - 1 - blockIdx.y;
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const int C = H * HD, C3 = 3 * C;
+  const int C = H * HD, Ckv = Hkv * HD, C3 = C + 2 * Ckv;
   const bf16* Qg = qkv + (int64_t)b * T * C3 + h * HD;
-  const bf16* Kg = Qg + C;
-  const bf16* Vg = Qg + 2 * C;
+  const bf16* Kg = qkv + (int64_t)b * T * C3 + C + (h / (H / Hkv)) * HD;
+  const bf16* Vg = Kg + Ckv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   const int q0 = qb * BQ + wave * 32;
@@ -356,17 +370,17 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
                                                                    const float* __restrict__ lse,
                                                                    bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
                                                                    const int32_t* __restrict__ seg, int T, int H,
-                                                                   float scale, float sl2) {
+                                                                   int Hkv, float scale, float sl2) {
   constexpr int BQ = 32 * NW;
   constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
   __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][64 * HD];  // [stage][K, V]
   const int nqb = (T + BQ - 1) / BQ;
   const int qb = nqb - 1 - blockIdx.y;  // longest work first, over all heads
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const int C = H * HD, C3 = 3 * C;
+  const int C = H * HD, Ckv = Hkv * HD, C3 = C + 2 * Ckv;
   const bf16* Qg = qkv + (int64_t)b * T * C3 + h * HD;
-  const bf16* Kg = Qg + C;
-  const bf16* Vg = Qg + 2 * C;
+  const bf16* Kg = qkv + (int64_t)b * T * C3 + C + (h / (H / Hkv)) * HD;
+  const bf16* Vg = Kg + Ckv;
   const bf16* Og = y + (int64_t)b * T * C + h * HD;
   const bf16* dOg = dy + (int64_t)b * T * C + h * HD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -477,7 +491,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
   }
 }
 
-// Backward, pass 2: dK and dV.  Block = NW waves x 32 keys; loop over 64-query
+// Backward, pass 2: dK and dV.  Block = NW waves x 32 keys of one key/value
+// head; loop over the query heads of its group and, for each, over 64-query
 // tiles from the block's diagonal to T (in a packed window: to the end of the
 // document of the block's last key).  Each lane owns one key (S = Q K^T).
 template <int NW, bool DOC>
@@ -487,20 +502,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
                                                                      const float* __restrict__ Dbuf,
                                                                      bf16* __restrict__ dqkv,
                                                                      const int32_t* __restrict__ seg, int T, int H,
-                                                                     float scale, float sl2) {
+                                                                     int Hkv, float scale, float sl2) {
   constexpr int BK = 32 * NW;
   constexpr int NR = DOC ? 3 : 2;
   __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
   __shared__ __attribute__((aligned(16))) float rowst[2][NR][64];  // [stage][lse, D, document start (int)]
   const int kblk = blockIdx.y;  // smallest keys (most queries) first, over all heads
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const int C = H * HD, C3 = 3 * C;
-  const bf16* Qg = qkv + (int64_t)b * T * C3 + h * HD;
-  const bf16* Kg = Qg + C;
-  const bf16* Vg = Qg + 2 * C;
-  const bf16* dOg = dy + (int64_t)b * T * C + h * HD;
-  const float* lseg = lse + (int64_t)bh * T;
-  const float* Dg = Dbuf + (int64_t)bh * T;
+  const int bj = blockIdx.x, b = bj / Hkv, j = bj % Hkv, grp = H / Hkv;
+  const int C = H * HD, Ckv = Hkv * HD, C3 = C + 2 * Ckv;
+  const bf16* Kg = qkv + (int64_t)b * T * C3 + C + j * HD;
+  const bf16* Vg = Kg + Ckv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   const int k0 = kblk * BK + wave * 32;
@@ -530,13 +541,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     qend = max(lo, qstart + 1);
   }
   const int ntiles = (qend - qstart + 63) / 64;
-  // Q and dO tiles, and the tile's 64 lse and D values, by DMA (lse and D
-  // from wave 0; rows past T read zeros, and their scores are masked)
+  // Q and dO tiles of query head h, and the tile's 64 lse and D values, by
+  // DMA (lse and D from wave 0; rows past T read zeros, and their scores are
+  // masked)
   const bool w0 = __builtin_amdgcn_readfirstlane(wave) == 0;
-  auto issue = [&](int st, int tile) {
+  auto issue = [&](int st, int h, int tile) {
     const int q0t = qstart + tile * 64;
-    dma_rows<64, 64, NW, true>(sm[st][0], Qg, C3, q0t, T, 0, HD);
-    dma_rows<64, 64, NW, true>(sm[st][1], dOg, C, q0t, T, 0, HD);
+    const float* lseg = lse + ((int64_t)b * H + h) * T;
+    const float* Dg = Dbuf + ((int64_t)b * H + h) * T;
+    dma_rows<64, 64, NW, true>(sm[st][0], qkv + (int64_t)b * T * C3 + h * HD, C3, q0t, T, 0, HD);
+    dma_rows<64, 64, NW, true>(sm[st][1], dy + (int64_t)b * T * C + h * HD, C, q0t, T, 0, HD);
     if (w0) {
       const int q = q0t + lane;
       dma4_ptr(q < T ? static_cast<const void*>(lseg + q) : static_cast<const void*>(g2_zero16),
@@ -548,21 +562,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
                  lds_addr(&rowst[st][NR - 1][0]));
     }
   };
-  issue(0, 0);
+  issue(0, j * grp, 0);
   drain_vector_loads();
-  for (int jt = 0; jt < ntiles; ++jt) {
+  // iteration it covers query head j * grp + it / ntiles, tile it % ntiles
+  const int niter = grp * ntiles;
+  int jt = 0, hn = j * grp, jn = 1;  // this tile; head and tile of the next one
+  if (jn == ntiles) { jn = 0; ++hn; }
+  for (int it = 0; it < niter; ++it) {
     tile_barrier();
-    const bool more = jt + 1 < ntiles;
-    if (more) issue((jt + 1) & 1, jt + 1);
+    if (it + 1 < niter) issue((it + 1) & 1, hn, jn);
     const int qs = qstart + jt * 64;
     // a tile wholly before this wave's keys is computed anyway (every score
     // masked, no contribution): a skip would make the compiler copy the
     // accumulators around the branch on every tile
-    const bf16* Qs = sm[jt & 1][0];
-    const bf16* dOs = sm[jt & 1][1];
-    const float* Ls = rowst[jt & 1][0];
-    const float* Ds = rowst[jt & 1][1];
-    const int* Ss = reinterpret_cast<const int*>(rowst[jt & 1][NR - 1]);
+    const bf16* Qs = sm[it & 1][0];
+    const bf16* dOs = sm[it & 1][1];
+    const float* Ls = rowst[it & 1][0];
+    const float* Ds = rowst[it & 1][1];
+    const int* Ss = reinterpret_cast<const int*>(rowst[it & 1][NR - 1]);
     // in a packed window: some query of the tile starts its document after
     // this wave's first key (the tile's last query has the largest start)
     const bool edge = (qs < k0 + 31) || (qs + 63 >= T) || (DOC && Ss[min(63, T - 1 - qs)] > k0);
@@ -628,10 +645,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
         }
       }
     }
+    jt = jn;
+    if (++jn == ntiles) {
+      jn = 0;
+      ++hn;
+    }
   }
   if (kvld) {
-    bf16* ok = dqkv + ((int64_t)b * T + kj) * C3 + C + h * HD;
-    bf16* ov = ok + C;
+    bf16* ok = dqkv + ((int64_t)b * T + kj) * C3 + C + j * HD;
+    bf16* ov = ok + Ckv;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -650,8 +672,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
 
 // =============================================================== launchers
 
-hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv, void* y,
-                                float* lse, const int32_t* seg) {
+hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
+                                void* y, float* lse, const int32_t* seg) {
   const float scale = 1.f / sqrtf((float)hd);
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
@@ -659,12 +681,14 @@ hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H,
     dim3 grid(B * H, (T + 32 * NW - 1) / (32 * NW));
     const bf16* q = static_cast<const bf16*>(qkv);
     bf16* o = static_cast<bf16*>(y);
-    if (seg) attn_fwd_bf16_kernel<NW, ST, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, lse, seg, T, H, scale * kLOG2E);
-    else attn_fwd_bf16_kernel<NW, ST, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, lse, nullptr, T, H, scale * kLOG2E);
+    if (seg)
+      attn_fwd_bf16_kernel<NW, ST, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, lse, seg, T, H, Hkv, scale * kLOG2E);
+    else
+      attn_fwd_bf16_kernel<NW, ST, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, lse, nullptr, T, H, Hkv, scale * kLOG2E);
   } else {
     const int n = B * H * T;
     attn_fwd_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(static_cast<const float*>(qkv), static_cast<float*>(y),
-                                                              lse, seg, B, T, H, hd, scale);
+                                                              lse, seg, B, T, H, Hkv, hd, scale);
   }
   prof_end(L);
   return hipGetLastError();
@@ -672,7 +696,7 @@ hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H,
 
 size_t attention_bwd_scratch(int B, int T, int H) { return (size_t)B * T * H * sizeof(float); }
 
-hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
+hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
                                 const int32_t* seg) {
   const float scale = 1.f / sqrtf((float)hd);
@@ -680,29 +704,34 @@ hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H,
   prof_begin(L);
   if (dtype == GPT2_PRECISION_BF16) {
     constexpr int NW = 4;
-    dim3 grid(B * H, (T + 32 * NW - 1) / (32 * NW));
+    const int nb = (T + 32 * NW - 1) / (32 * NW);
+    dim3 grid(B * H, nb), grid_kv(B * Hkv, nb);
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* o = static_cast<const bf16*>(y);
     const bf16* dO = static_cast<const bf16*>(dy);
     bf16* dq = static_cast<bf16*>(dqkv);
     const float sl2 = scale * kLOG2E;
     if (seg) {
-      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, seg, T, H, scale, sl2);
-      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, seg, T, H, scale, sl2);
+      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, seg, T, H, Hkv,
+                                                                           scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, seg, T, H, Hkv,
+                                                                             scale, sl2);
     } else {
-      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, nullptr, T, H, scale,
-                                                                            sl2);
-      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, nullptr, T, H, scale,
-                                                                           sl2);
+      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, nullptr, T, H, Hkv,
+                                                                            scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, nullptr, T, H,
+                                                                              Hkv, scale, sl2);
     }
   } else {
     const int n = B * H * T;
     attn_bwd_dq_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(
         static_cast<const float*>(qkv), static_cast<const float*>(y), static_cast<const float*>(dy), lse,
-        static_cast<float*>(dqkv), Dbuf, seg, B, T, H, hd, scale);
-    attn_bwd_dkdv_f32_kernel<<<(n + 127) / 128, 128, 0, L.stream>>>(static_cast<const float*>(qkv),
-                                                                   static_cast<const float*>(dy), lse, Dbuf,
-                                                                   static_cast<float*>(dqkv), seg, B, T, H, hd, scale);
+        static_cast<float*>(dqkv), Dbuf, seg, B, T, H, Hkv, hd, scale);
+    const int nkv = B * Hkv * T;
+    attn_bwd_dkdv_f32_kernel<<<(nkv + 127) / 128, 128, 0, L.stream>>>(static_cast<const float*>(qkv),
+                                                                     static_cast<const float*>(dy), lse, Dbuf,
+                                                                     static_cast<float*>(dqkv), seg, B, T, H, Hkv, hd,
+                                                                     scale);
   }
   prof_end(L);
   return hipGetLastError();

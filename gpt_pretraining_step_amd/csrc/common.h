@@ -124,9 +124,10 @@ hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, cons
                               const float* w, float* dx, bf16* dxb, float* dw, int rows, int C);
 
 // seg: [B, T] document starts of packed windows (nullptr: plain causal).
-hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
+// Hkv key/value heads (H % Hkv == 0); qkv rows [H q | Hkv k | Hkv v] heads.
+hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 void* y, float* lse, const int32_t* seg);
-hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int hd, const void* qkv,
+hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
                                 const int32_t* seg);
 size_t attention_bwd_scratch(int B, int T, int H);

@@ -129,8 +129,13 @@ struct Table {
   std::vector<int> layer;  // [n_layer * N_KINDS] -> index into d
 };
 
+// key/value heads of the attention (n_kv_head, 0 meaning n_head)
+int kv_heads(const gpt2_config& c) { return c.n_kv_head ? c.n_kv_head : c.n_head; }
+
 bool check_config(const gpt2_config* c) {
   if (!c) return false;
+  if (c->n_kv_head < 0 || c->n_head < 1 || c->n_head % kv_heads(*c)) return false;
+  if (c->arch == GPT2_ARCH_GPT2 && kv_heads(*c) != c->n_head) return false;
   if (c->vocab_size < 1 || c->block_size < 1 || c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1 ||
       c->mlp_hidden < 1 || c->max_batch < 1)
     return false;
@@ -156,6 +161,7 @@ bool check_config(const gpt2_config* c) {
 
 Table build_table(const gpt2_config& c) {
   const int V = c.vocab_size, T = c.block_size, C = c.n_embd, F = c.mlp_hidden, L = c.n_layer;
+  const int NQKV = C + 2 * kv_heads(c) * (C / c.n_head);  // q, k and v columns
   std::vector<Desc> hf;
   auto add = [&](const std::string& n, int nd, int s0, int s1) {
     Desc x;
@@ -174,7 +180,7 @@ Table build_table(const gpt2_config& c) {
     for (int l = 0; l < L; ++l) {
       const std::string p = "transformer.h." + std::to_string(l) + ".";
       add(p + "ln_1.weight", 1, C, 1);
-      add(p + "attn.c_attn.weight", 2, 3 * C, C);
+      add(p + "attn.c_attn.weight", 2, NQKV, C);
       add(p + "attn.c_proj.weight", 2, C, C);
       add(p + "ln_2.weight", 1, C, 1);
       add(p + "mlp.c_fc.weight", 2, 2 * F, C);
@@ -187,8 +193,8 @@ Table build_table(const gpt2_config& c) {
     const std::string p = "transformer.h." + std::to_string(l) + ".";
     add(p + "ln_1.weight", 1, C, 1);
     add(p + "ln_1.bias", 1, C, 1);
-    add(p + "attn.c_attn.weight", 2, 3 * C, C);
-    add(p + "attn.c_attn.bias", 1, 3 * C, 1);
+    add(p + "attn.c_attn.weight", 2, NQKV, C);
+    add(p + "attn.c_attn.bias", 1, NQKV, 1);
     add(p + "attn.c_proj.weight", 2, C, C);
     add(p + "attn.c_proj.bias", 1, C, 1);
     add(p + "ln_2.weight", 1, C, 1);
@@ -276,6 +282,7 @@ Layout build_layout(const gpt2_config& c) {
   Layout y;
   const size_t rows = (size_t)c.max_batch * c.block_size;
   const size_t C = c.n_embd, F = c.mlp_hidden, H = c.n_head, V = c.vocab_size;
+  const size_t NQKV = C + 2 * (size_t)kv_heads(c) * (C / H);  // q, k and v columns
   const int L = c.n_layer;
   // U / dU: gelu'(u) [rows, F] for GPT-2; [gate | up] [rows, 2F] for the
   // rotary variant (G then holds silu(gate) up)
@@ -290,7 +297,7 @@ Layout build_layout(const gpt2_config& c) {
     y.A1.push_back(a.take(rows * C * y.es));
     y.mean1.push_back(a.take(rows * 4));
     y.rstd1.push_back(a.take(rows * 4));
-    y.QKV.push_back(a.take(rows * 3 * C * y.es));
+    y.QKV.push_back(a.take(rows * NQKV * y.es));
     y.Y.push_back(a.take(rows * C * y.es));
     y.LSE.push_back(a.take(rows * H * 4));
     y.A2.push_back(a.take(rows * C * y.es));
@@ -314,7 +321,7 @@ Layout build_layout(const gpt2_config& c) {
   y.dA = s.take(rows * C * 4);
   y.dY = s.take(rows * C * y.es);
   if (c.precision != GPT2_PRECISION_BF16) {  // bf16 mode keeps these per layer (below)
-    y.dQKV = s.take(rows * 3 * C * y.es);
+    y.dQKV = s.take(rows * NQKV * y.es);
     y.dU = s.take(rows * FU * y.es);
   }
   y.attnD = s.take(rows * H * 4);
@@ -324,14 +331,14 @@ Layout build_layout(const gpt2_config& c) {
     for (int l = 0; l < 2 * L; ++l) y.dRbS.push_back(s.take(rows * C * 2));
     for (int l = 0; l < L; ++l) {
       y.dUL.push_back(s.take(rows * FU * 2));
-      y.dQKVL.push_back(s.take(rows * 3 * C * 2));
+      y.dQKVL.push_back(s.take(rows * NQKV * 2));
     }
     // the products of that launch: dwte (lm_head), then four per layer
     std::vector<gpt2_gemm_args> dw(4 * (size_t)L + 1);
     dw[0].M = (int)V;
     dw[0].N = (int)C;
     for (int l = 0; l < L; ++l) {
-      const int mn[4][2] = {{(int)C, (int)F}, {(int)FU, (int)C}, {(int)C, (int)C}, {3 * (int)C, (int)C}};
+      const int mn[4][2] = {{(int)C, (int)F}, {(int)FU, (int)C}, {(int)C, (int)C}, {(int)NQKV, (int)C}};
       for (int k = 0; k < 4; ++k) {
         dw[4 * l + k + 1].M = mn[k][0];
         dw[4 * l + k + 1].N = mn[k][1];
@@ -556,7 +563,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                                  bf, c->act<float>(y.mean1[l]), c->act<float>(y.rstd1[l]), M, C));
     HIP_TRY(linear_fwd(c, "gemm.qkv", c->act(y.A1[l]), M, C, c->L(l, QKV_W), 3 * C, c->L(l, QKV_B), GPT2_EPI_STORE,
                        c->act(y.QKV[l]), nullptr, nullptr));
-    HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
+    HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
                                  c->act<float>(y.LSE[l]), seg));
     HIP_TRY(linear_fwd(c, "gemm.attn_proj", c->act(y.Y[l]), M, C, c->L(l, PROJ_W), C, c->L(l, PROJ_B),
                        GPT2_EPI_RESIDUAL, rmid, nullptr, rin));
@@ -656,7 +663,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     // attention branch: Rmid = R_l + Y Wo^T + b
     HIP_TRY(dw("gemm.attn_proj_dw", dRa, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
-    HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
+    HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
                                  c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg));
     HIP_TRY(dw("gemm.qkv_dw", dQKV, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
                static_cast<const float*>(dQKV)));
@@ -677,6 +684,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
   const gpt2_config& g = c->cfg;
   const Layout& y = c->lay;
   const int M = B * T, C = g.n_embd, F = g.mlp_hidden, V = g.vocab_size, H = g.n_head, hd = C / H;
+  const int Hkv = kv_heads(g), Ckv = Hkv * hd, NQKV = C + 2 * Ckv;  // grouped-query attention when Hkv < H
   const int dt = g.precision;
   int* flag = c->flag();
   int* count = c->scr<int>(y.count);
@@ -704,15 +712,15 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
                                c->act<float>(y.rstd1[l]), M, C));
     {  // qkv = a1 Wqkv^T, q and k rotated in the epilogue
       gpt2_gemm_args a = gemm_base(dt);
-      a.M = M; a.N = 3 * C; a.K = C;
+      a.M = M; a.N = NQKV; a.K = C;
       a.a_kmajor = 1; a.b_kmajor = 1;
-      a.lda = C; a.ldb = C; a.ldc = 3 * C;
+      a.lda = C; a.ldb = C; a.ldc = NQKV;
       a.A = c->act(y.A1[l]); a.B = c->W(c->L(l, QKV_W)); a.C = c->act(y.QKV[l]);
       a.epilogue = GPT2_EPI_ROPE; a.out_bf16 = 1;
-      a.rope = rope; a.rope_period = T; a.rope_cols = 2 * C;
+      a.rope = rope; a.rope_period = T; a.rope_cols = C + Ckv;
       HIP_TRY(launch_gemm(c->at("gemm.qkv"), a));
     }
-    HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
+    HIP_TRY(launch_attention_fwd(c->at("attn.fwd"), dt, B, T, H, Hkv, hd, c->act(y.QKV[l]), c->act(y.Y[l]),
                                  c->act<float>(y.LSE[l]), seg));
     HIP_TRY(linear_fwd(c, "gemm.attn_proj", c->act(y.Y[l]), M, C, c->L(l, PROJ_W), C, -1, GPT2_EPI_RESIDUAL, rmid,
                        nullptr, rin));
@@ -774,11 +782,11 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     // attention: Rmid = R_l + Y Wo^T
     queue_dw(c, q, dRa, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1);
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
-    HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
+    HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, Hkv, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
                                  c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg));
-    HIP_TRY(launch_rope_bwd(c->at("rope.bwd"), dQKV, M, 3 * C, 2 * C, T, rope));
-    queue_dw(c, q, dQKV, M, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), -1);
-    HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
+    HIP_TRY(launch_rope_bwd(c->at("rope.bwd"), dQKV, M, NQKV, C + Ckv, T, rope));
+    queue_dw(c, q, dQKV, M, NQKV, c->act(y.A1[l]), C, c->L(l, QKV_W), -1);
+    HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, NQKV, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rin[l]), c->act<float>(y.rstd1[l]),
                                c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C));
   }
@@ -1238,30 +1246,31 @@ int gpt2_op_rope_bwd(void* stream, void* d_dqkv, int rows, int64_t ld, int cols,
   return GPT2_OK;
 }
 
-static bool attn_shape_ok(int dtype, int B, int T, int H, int hd) {
-  if (B < 1 || T < 1 || H < 1) return false;
+static bool attn_shape_ok(int dtype, int B, int T, int H, int Hkv, int hd) {
+  if (B < 1 || T < 1 || H < 1 || Hkv < 1 || H % Hkv) return false;
   if (dtype == GPT2_PRECISION_BF16) return hd == 64;
   if (dtype == GPT2_PRECISION_FP32) return hd >= 1 && hd <= 64;
   return false;
 }
 
-int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv, void* d_y,
-                          float* d_lse, const int32_t* d_seg) {
+int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
+                          void* d_y, float* d_lse, const int32_t* d_seg) {
   if (!d_qkv || !d_y || !d_lse) return GPT2_ERR_ARG;
-  if (!attn_shape_ok(dtype, B, T, H, hd)) return GPT2_ERR_SHAPE;
-  HIP_TRY(launch_attention_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, hd, d_qkv, d_y,
-                               d_lse, d_seg));
+  if (!attn_shape_ok(dtype, B, T, H, Hkv, hd)) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_attention_fwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, Hkv, hd, d_qkv,
+                               d_y, d_lse, d_seg));
   return GPT2_OK;
 }
 
 size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H) { return attention_bwd_scratch(B, T, H); }
 
-int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv, const void* d_y,
-                          const void* d_dy, const float* d_lse, void* d_dqkv, void* d_scratch, const int32_t* d_seg) {
+int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
+                          const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv, void* d_scratch,
+                          const int32_t* d_seg) {
   if (!d_qkv || !d_y || !d_dy || !d_lse || !d_dqkv || !d_scratch) return GPT2_ERR_ARG;
-  if (!attn_shape_ok(dtype, B, T, H, hd)) return GPT2_ERR_SHAPE;
-  HIP_TRY(launch_attention_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, hd, d_qkv, d_y,
-                               d_dy, d_lse, d_dqkv, d_scratch, d_seg));
+  if (!attn_shape_ok(dtype, B, T, H, Hkv, hd)) return GPT2_ERR_SHAPE;
+  HIP_TRY(launch_attention_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, Hkv, hd, d_qkv,
+                               d_y, d_dy, d_lse, d_dqkv, d_scratch, d_seg));
   return GPT2_OK;
 }
 

@@ -80,7 +80,14 @@ enum { GPT2_ARCH_GPT2 = 0, GPT2_ARCH_ROTARY = 1 };
  *                     ln_1.weight, attn.c_attn.weight [3C, C],
  *                     attn.c_proj.weight, ln_2.weight, mlp.c_fc.weight
  *                     [2F, C] (rows 0..F-1 W_gate, F..2F-1 W_up),
- *                     mlp.c_proj.weight [C, F], then ln_f.weight. */
+ *                     mlp.c_proj.weight [C, F], then ln_f.weight.
+ * n_kv_head (0 means n_head) selects grouped-query attention ("Making
+ * Training Fast on One GPU", step 2, whose model shares each key/value head
+ * among n_head / n_kv_head consecutive query heads): the rotary variant
+ * accepts any divisor of n_head, c_attn.weight then being
+ * [C + 2 n_kv_head head_dim, C] (q rows, then the k rows and the v rows of
+ * the n_kv_head shared heads); the GPT-2 model requires n_kv_head == n_head
+ * (or 0). */
 typedef struct {
   int32_t vocab_size;
   int32_t block_size;
@@ -91,6 +98,7 @@ typedef struct {
   int32_t max_batch;
   int32_t precision;
   int32_t arch;
+  int32_t n_kv_head;  /* key/value heads; 0 = n_head (see below) */
 } gpt2_config;
 
 /* Byte sizes of the caller-owned buffers. */
@@ -436,8 +444,11 @@ int gpt2_op_rope_table(void* stream, int T, double base, float* d_table);
 int gpt2_op_rope_bwd(void* stream, void* d_dqkv, int rows, int64_t ld, int cols, int T, const float* d_table);
 
 /* Causal multi-head attention ("How I trained my own GPT-2 124M on
- * FineWeb-Edu" sections 2.12 and 5): qkv [B*T, 3*H*hd] holds q | k | v column
- * thirds, head h at columns h*hd of each third; y [B*T, H*hd] receives the
+ * FineWeb-Edu" sections 2.12 and 5): qkv [B*T, (H + 2 Hkv) hd] holds the H
+ * query heads, then the Hkv key heads, then the Hkv value heads (hd columns
+ * each); query head h attends with key/value head h / (H / Hkv) (grouped-
+ * query attention, "Making Training Fast on One GPU" step 2; Hkv == H is
+ * plain multi-head attention, H % Hkv must be 0); y [B*T, H*hd] receives the
  * concatenated heads; lse float32 [B, H, T] the row log-sum-exp of the scaled
  * scores (natural log).  dtype selects bf16 or float32 tensors.
  * d_seg (nullable) int32 [B, T]: document starts of packed windows (as
@@ -445,12 +456,13 @@ int gpt2_op_rope_bwd(void* stream, void* d_dqkv, int rows, int64_t ld, int cols,
  * along a row); query t then sees only keys seg[t] .. t.  Starts that break
  * those rules give unspecified values (never an access outside the
  * tensors). */
-int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv,
+int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
                           void* d_y, float* d_lse, const int32_t* d_seg);
-/* Backward: dqkv [B*T, 3*H*hd] is written.  d_scratch needs
+/* Backward: dqkv [B*T, (H + 2 Hkv) hd] is written (a shared key/value
+ * head receives the sum over its query heads).  d_scratch needs
  * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes; d_seg as in the forward. */
 size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H);
-int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int hd, const void* d_qkv,
+int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
                           const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
                           void* d_scratch, const int32_t* d_seg);
 

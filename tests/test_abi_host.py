@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header_sizes():
     from gpt_pretraining_step_amd import _ffi
-    assert ct.sizeof(_ffi.Config) == 9 * 4
+    assert ct.sizeof(_ffi.Config) == 10 * 4
     assert ct.sizeof(_ffi.AdamW) == 6 * 4
     assert ct.sizeof(_ffi.Buffers) == 7 * 8
     assert ct.sizeof(_ffi.ParamDesc) == 64 + 8 + 4 + 8 + 4
@@ -58,8 +58,11 @@ def test_rotary_param_table_matches_oracle_specs():
     import gpt_pretraining_step_amd as g
     from oracle import modern as MM
     for cfg in (g.GPT2_ROTARY_124M,
-                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY)):
-        oc = MM.ModernConfig(cfg.vocab_size, cfg.block_size, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.mlp_hidden)
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY),
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY, n_kv_head=2),
+                g.ModelConfig(50304, 1024, 12, 12, 768, 2048, 8, g.PRECISION_BF16, g.ARCH_ROTARY, n_kv_head=4)):
+        oc = MM.ModernConfig(cfg.vocab_size, cfg.block_size, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.mlp_hidden,
+                             n_kv_head=cfg.n_kv_head)
         table = g.param_table(cfg)
         assert {n: tuple(s) for n, _, s, _ in table} == dict(MM.param_specs(oc))
         decayed = [d for _, _, _, d in table]
@@ -70,7 +73,10 @@ def test_rotary_param_table_matches_oracle_specs():
     for bad in (g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_FP32, g.ARCH_ROTARY),  # bf16 only
                 g.ModelConfig(1024, 256, 2, 2, 128, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY),   # C % 256
                 g.ModelConfig(1024, 256, 2, 4, 256, 150, 3, g.PRECISION_BF16, g.ARCH_ROTARY),   # F % 32
-                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, 7)):
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, 7),
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY, n_kv_head=3),  # 4 % 3
+                g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY, n_kv_head=-1),
+                g.ModelConfig(1024, 256, 2, 4, 256, 1024, 3, g.PRECISION_BF16, n_kv_head=2)):  # GPT-2: MHA only
         with pytest.raises(g.GPT2Error):
             g.query_sizes(bad)
 

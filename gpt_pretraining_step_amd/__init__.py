@@ -377,7 +377,9 @@ def op_attention_fwd(qkv, y, lse, B, T, H, hd, stream=None, seg=None, n_kv_head=
                                       lse.data_ptr(), _ptr(seg)), "gpt2_op_attention_fwd")
 
 
-def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, n_kv_head=None):
+def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, n_kv_head=None, rope=None):
+    """rope: optional [T][32] (cos, sin) table (op_rope_table): dq and dk are
+    rotated back before they are written."""
     import torch
     dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
     _check_seg(seg, B, T)
@@ -385,7 +387,8 @@ def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, 
     nbytes = lib().gpt2_attention_bwd_scratch_bytes(B, T, H)
     scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qkv.device)
     check(lib().gpt2_op_attention_bwd(_stream_ptr(stream), dtype, B, T, H, Hkv, hd, qkv.data_ptr(), y.data_ptr(),
-                                      dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr(), _ptr(seg)),
+                                      dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr(), _ptr(seg),
+                                      _ptr(rope)),
           "gpt2_op_attention_bwd")
 
 

@@ -35,6 +35,12 @@
 // loop covering the query heads of the group one after the other, so the
 // shared head's gradient is summed in registers.
 //
+// Rotary variant ("Reproduce GPT-2 124M": q and k rotated after c_attn):
+// given the (cos, sin) table of the positions, the bf16 backward applies the
+// transpose of the rotation to dQ and dK in registers before their one bf16
+// rounding (dims i and i + 32 of a head sit in the same lane), so no
+// separate pass over dQKV is needed.
+//
 // float32 (FP32 precision mode, small heads): one thread per query (or key),
 // plain loops.
 #include "tile_io.h"
@@ -206,6 +212,43 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
+// Write a head's 64 gradient values held as the transposed accumulators g[0]
+// (dims 0..31) and g[1] (dims 32..63): register 4a + e of g[dt] is dim
+// 32 dt + 8a + 4 lg + e.  With a rotary table (rope != nullptr: row `pos`
+// of [T][32] (cos, sin) pairs) the pair (i, i + 32) is first rotated back:
+// z_i' = z_i c + z_{i+32} s, z_{i+32}' = z_{i+32} c - z_i s.
+__device__ __forceinline__ void store_head_grad(bf16* out, const f32x16 (&g)[2], float scale,
+                                                const float2* __restrict__ rope, int pos, int lg) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = g[0][4 * a + e] * scale;
+      hi[e] = g[1][4 * a + e] * scale;
+    }
+    if (rope) {
+      const float4* cs = reinterpret_cast<const float4*>(rope + (int64_t)pos * 32 + 8 * a + 4 * lg);
+      const float4 c01 = cs[0], c23 = cs[1];
+      const float cv[4] = {c01.x, c01.z, c23.x, c23.z}, sv[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float z1 = lo[e], z2 = hi[e];
+        lo[e] = z1 * cv[e] + z2 * sv[e];
+        hi[e] = z2 * cv[e] - z1 * sv[e];
+      }
+    }
+    bf16x4 l4, h4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      l4[e] = f2bf(lo[e]);
+      h4[e] = f2bf(hi[e]);
+    }
+    *reinterpret_cast<bf16x4*>(out + 8 * a + 4 * lg) = l4;
+    *reinterpret_cast<bf16x4*>(out + 32 + 8 * a + 4 * lg) = h4;
+  }
+}
+
 // Wait for this wave's outstanding DMA and LDS writes, then meet the other
 // waves (no fence: later tiles' copies are not in flight at this point).
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -369,7 +412,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
                                                                    bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
-                                                                   const int32_t* __restrict__ seg, int T, int H,
+                                                                   const int32_t* __restrict__ seg,
+                                                                   const float2* __restrict__ rope, int T, int H,
                                                                    int Hkv, float scale, float sl2) {
   constexpr int BQ = 32 * NW;
   constexpr int DMA_TILE = 2 * 64 * HD / 512 / NW;  // DMA instructions per wave per K/V tile
@@ -477,18 +521,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
       }
     }
   }
-  if (qv) {
-    bf16* o = dqkv + ((int64_t)b * T + qi) * C3 + h * HD;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        bf16x4 o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = f2bf(dqT[dt][4 * a + e] * scale);
-        *reinterpret_cast<bf16x4*>(o + 32 * dt + 8 * a + 4 * lg) = o4;
-      }
-  }
+  if (qv) store_head_grad(dqkv + ((int64_t)b * T + qi) * C3 + h * HD, dqT, scale, rope, qi, lg);
 }
 
 // Backward, pass 2: dK and dV.  Block = NW waves x 32 keys of one key/value
@@ -501,7 +534,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
                                                                      const float* __restrict__ lse,
                                                                      const float* __restrict__ Dbuf,
                                                                      bf16* __restrict__ dqkv,
-                                                                     const int32_t* __restrict__ seg, int T, int H,
+                                                                     const int32_t* __restrict__ seg,
+                                                                     const float2* __restrict__ rope, int T, int H,
                                                                      int Hkv, float scale, float sl2) {
   constexpr int BK = 32 * NW;
   constexpr int NR = DOC ? 3 : 2;
@@ -653,20 +687,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
   }
   if (kvld) {
     bf16* ok = dqkv + ((int64_t)b * T + kj) * C3 + C + j * HD;
-    bf16* ov = ok + Ckv;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = f2bf(dkT[dt][4 * a + e] * scale);
-          v4[e] = f2bf(dvT[dt][4 * a + e]);
-        }
-        *reinterpret_cast<bf16x4*>(ok + 32 * dt + 8 * a + 4 * lg) = k4;
-        *reinterpret_cast<bf16x4*>(ov + 32 * dt + 8 * a + 4 * lg) = v4;
-      }
+    store_head_grad(ok, dkT, scale, rope, kj, lg);
+    store_head_grad(ok + Ckv, dvT, 1.f, nullptr, kj, lg);
   }
 }
 
@@ -698,7 +720,7 @@ size_t attention_bwd_scratch(int B, int T, int H) { return (size_t)B * T * H * s
 
 hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
-                                const int32_t* seg) {
+                                const int32_t* seg, const float2* rope) {
   const float scale = 1.f / sqrtf((float)hd);
   float* Dbuf = static_cast<float*>(scratch);
   prof_begin(L);
@@ -712,15 +734,15 @@ hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H,
     bf16* dq = static_cast<bf16*>(dqkv);
     const float sl2 = scale * kLOG2E;
     if (seg) {
-      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, seg, T, H, Hkv,
-                                                                           scale, sl2);
-      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, seg, T, H, Hkv,
-                                                                             scale, sl2);
+      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, seg, rope, T, H,
+                                                                           Hkv, scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, seg, rope, T, H,
+                                                                             Hkv, scale, sl2);
     } else {
-      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, nullptr, T, H, Hkv,
-                                                                            scale, sl2);
-      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, nullptr, T, H,
-                                                                              Hkv, scale, sl2);
+      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, nullptr, rope, T,
+                                                                            H, Hkv, scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, nullptr, rope, T,
+                                                                              H, Hkv, scale, sl2);
     }
   } else {
     const int n = B * H * T;

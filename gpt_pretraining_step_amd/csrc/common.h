@@ -127,9 +127,11 @@ hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, cons
 // Hkv key/value heads (H % Hkv == 0); qkv rows [H q | Hkv k | Hkv v] heads.
 hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 void* y, float* lse, const int32_t* seg);
+// rope (nullable, bf16 only): [T][32] (cos, sin) table; dq and dk are
+// rotated back with it before they are written.
 hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
-                                const int32_t* seg);
+                                const int32_t* seg, const float2* rope);
 size_t attention_bwd_scratch(int B, int T, int H);
 
 // seg[b, t] = last position s <= t of row b with tok[b, s] == eot (0 if none).

@@ -664,7 +664,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     HIP_TRY(dw("gemm.attn_proj_dw", dRa, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, H, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
-                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg));
+                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg, nullptr));
     HIP_TRY(dw("gemm.qkv_dw", dQKV, 3 * C, c->act(y.A1[l]), C, c->L(l, QKV_W), c->L(l, QKV_B),
                static_cast<const float*>(dQKV)));
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
@@ -783,8 +783,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     queue_dw(c, q, dRa, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1);
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
     HIP_TRY(launch_attention_bwd(c->at("attn.bwd"), dt, B, T, H, Hkv, hd, c->act(y.QKV[l]), c->act(y.Y[l]), dY,
-                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg));
-    HIP_TRY(launch_rope_bwd(c->at("rope.bwd"), dQKV, M, NQKV, C + Ckv, T, rope));
+                                 c->act<float>(y.LSE[l]), dQKV, c->scr(y.attnD), seg, rope));
     queue_dw(c, q, dQKV, M, NQKV, c->act(y.A1[l]), C, c->L(l, QKV_W), -1);
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, NQKV, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rin[l]), c->act<float>(y.rstd1[l]),
@@ -1266,11 +1265,12 @@ size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H) { return attention_
 
 int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
                           const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv, void* d_scratch,
-                          const int32_t* d_seg) {
+                          const int32_t* d_seg, const float* d_rope) {
   if (!d_qkv || !d_y || !d_dy || !d_lse || !d_dqkv || !d_scratch) return GPT2_ERR_ARG;
   if (!attn_shape_ok(dtype, B, T, H, Hkv, hd)) return GPT2_ERR_SHAPE;
+  if (d_rope && (dtype != GPT2_PRECISION_BF16 || ((uintptr_t)d_rope & 15))) return GPT2_ERR_ARG;
   HIP_TRY(launch_attention_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, Hkv, hd, d_qkv,
-                               d_y, d_dy, d_lse, d_dqkv, d_scratch, d_seg));
+                               d_y, d_dy, d_lse, d_dqkv, d_scratch, d_seg, reinterpret_cast<const float2*>(d_rope)));
   return GPT2_OK;
 }
 

@@ -460,11 +460,16 @@ int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int Hkv,
                           void* d_y, float* d_lse, const int32_t* d_seg);
 /* Backward: dqkv [B*T, (H + 2 Hkv) hd] is written (a shared key/value
  * head receives the sum over its query heads).  d_scratch needs
- * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes; d_seg as in the forward. */
+ * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes; d_seg as in the forward.
+ * d_rope (nullable; bf16 only, 16-byte aligned): a [T][32] (cos, sin) table
+ * as gpt2_op_rope_table writes it; dq and dk are then rotated back with the
+ * transpose of the rotary embedding at their row's position before they
+ * are written (what gpt2_op_rope_bwd does in a separate pass, here with one
+ * bf16 rounding instead of two). */
 size_t gpt2_attention_bwd_scratch_bytes(int B, int T, int H);
 int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
                           const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
-                          void* d_scratch, const int32_t* d_seg);
+                          void* d_scratch, const int32_t* d_seg, const float* d_rope);
 
 /* Document starts of packed rows ("GPT" chapter of Zero to Frontier,
  * "Document boundaries, packing and masking"): d_seg[b*T + t] = the last

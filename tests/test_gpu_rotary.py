@@ -64,6 +64,62 @@ def test_rope_bwd_vs_oracle(g, rows, T, C):
     assert np.array_equal(out[:, 2 * C:], d[:, 2 * C:])
 
 
+@pytest.mark.parametrize("B,T,H,Hkv", [(2, 300, 4, 4), (1, 1024, 6, 2)])
+def test_attention_bwd_fused_rope(g, B, T, H, Hkv):
+    """gpt2_op_attention_bwd with the rotary table rotates dq and dk back in
+    registers: against the oracle (attention backward, then the transpose of
+    the rotation, in float64) and against the two-pass path (backward, then
+    gpt2_op_rope_bwd); dv is untouched."""
+    import torch
+    from oracle import model as OM
+    hd = 64
+    announce(f"attention bwd + fused rope B={B} T={T} H={H} Hkv={Hkv}")
+    rng = np.random.default_rng(T + H)
+    C, Ckv = H * hd, Hkv * hd
+    W = C + 2 * Ckv
+    qkv = bf16_round(rng.standard_normal((B * T, W)).astype(np.float32))
+    dy = bf16_round(rng.standard_normal((B * T, C)).astype(np.float32))
+    dq_ = dev(qkv, torch.bfloat16)
+    y = torch.zeros((B * T, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    g.op_attention_fwd(dq_, y, lse, B, T, H, hd, n_kv_head=Hkv)
+    tab = g.op_rope_table(T)
+    fused = torch.zeros((B * T, W), dtype=torch.bfloat16, device="cuda")
+    g.op_attention_bwd(dq_, y, dev(dy, torch.bfloat16), lse, fused, B, T, H, hd, n_kv_head=Hkv, rope=tab)
+    two = torch.zeros((B * T, W), dtype=torch.bfloat16, device="cuda")
+    g.op_attention_bwd(dq_, y, dev(dy, torch.bfloat16), lse, two, B, T, H, hd, n_kv_head=Hkv)
+    # the separate pass rotates the first `C + Ckv` columns (q and k heads)
+    assert g.lib().gpt2_op_rope_bwd(None, two.data_ptr(), B * T, W, C + Ckv, T, tab.data_ptr()) == 0
+    f, t2 = host(fused), host(two)
+    assert np.array_equal(f[:, C + Ckv:], t2[:, C + Ckv:])  # dv: no rotation, same kernel
+    np.testing.assert_allclose(f[:, :C + Ckv], t2[:, :C + Ckv], rtol=2e-2, atol=2e-2)
+    # oracle: per-head attention backward on the shared heads, then the
+    # transpose of the rotation at each row's position
+    cos, sin = MM.rope_tables(T, 64)
+    x = qkv.reshape(B, T, W).astype(np.float64)
+    ref = np.zeros((B, T, W))
+    grp = H // Hkv
+    yh = host(y).reshape(B, T, C).astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            j = h // grp
+            q, k = x[b, :, h * hd:(h + 1) * hd], x[b, :, C + j * hd:C + (j + 1) * hd]
+            v = x[b, :, C + Ckv + j * hd:C + Ckv + (j + 1) * hd]
+            _, p = OM.attention_fwd(q, k, v)
+            dq, dk, dv = OM.attention_bwd(dy.reshape(B, T, C)[b, :, h * hd:(h + 1) * hd].astype(np.float64), q, k, v, p)
+            ref[b, :, h * hd:(h + 1) * hd] = MM.rope_bwd(dq, cos, sin)
+            ref[b, :, C + j * hd:C + (j + 1) * hd] += MM.rope_bwd(dk, cos, sin)
+            ref[b, :, C + Ckv + j * hd:C + Ckv + (j + 1) * hd] += dv
+    ref = ref.reshape(B * T, W)
+    for name, sl in (("dq", slice(0, C)), ("dk", slice(C, C + Ckv))):
+        assert cosine(f[:, sl], ref[:, sl]) > 0.999, name
+        assert np.abs(f[:, sl] - ref[:, sl]).max() <= 3e-2 * max(1.0, np.abs(ref[:, sl]).max()), name
+    # a misaligned or float32 table is refused
+    with pytest.raises(g.GPT2Error):
+        g.op_attention_bwd(dq_, y, dev(dy, torch.bfloat16), lse, fused, B, T, H, hd, n_kv_head=Hkv,
+                           rope=tab.view(-1)[2:])
+
+
 @pytest.mark.parametrize("rows,C,dyb", [(1, 256, False), (1000, 768, True), (129, 1024, False), (70, 512, True)])
 def test_rmsnorm_vs_oracle(g, rows, C, dyb):
     import torch

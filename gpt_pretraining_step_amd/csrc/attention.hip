@@ -307,7 +307,9 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
   for (int t = 0; t < ST - 1; ++t)
     if (jt0 + t < ntiles) issue(t, jt0 + t);
   drain_vector_loads();
-  for (int jt = jt0; jt < ntiles; ++jt) {
+  // wait for tile jt, meet the other waves, start the copy of tile jt+ST-1;
+  // returns the stage of tile jt
+  auto sync = [&](int jt) {
     if (jt + ST - 2 < ntiles) {
       if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else if constexpr (ST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_TILE) : "memory");
@@ -318,11 +320,22 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int stg = (jt - jt0) % ST;
     if (jt + ST - 1 < ntiles) issue((stg + ST - 1) % ST, jt + ST - 1);
+    return stg;
+  };
+  // The tiles this wave can see are jw0 .. jw1 (wave-uniform): the ones
+  // after its last query, and in a packed window the ones before its first
+  // query's document start, hold only masked keys.  The wave takes part in
+  // the copies and barriers of every tile of the block but computes only
+  // its own range (three loops, so that no branch sits in the computing one).
+  const int qw = __builtin_amdgcn_readfirstlane(q0);
+  const int jw1 = min(ntiles - 1, min(qw + 31, T - 1) / 64);
+  int jw0 = jt0;
+  if constexpr (DOC) jw0 = min(max(jt0, __builtin_amdgcn_readfirstlane(seg[(int64_t)b * T + min(qw, T - 1)]) / 64), jw1);
+  int jt = jt0;
+  for (; jt < jw0; ++jt) sync(jt);
+  for (; jt <= jw1; ++jt) {
+    const int stg = sync(jt);
     const int kb = jt * 64;
-    // a tile wholly after (or, in a packed window, wholly before) this
-    // wave's queries is computed anyway (every score masked, no
-    // contribution): a skip would make the compiler copy the accumulators
-    // around the branch on every tile
     const bf16* Ks = sm[stg][0];
     const bf16* Vs = sm[stg][1];
     f32x16 sT[2];
@@ -388,6 +401,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
         for (int dt = 0; dt < 2; ++dt) oT[dt] = MFMA(colfrag(Vs, 32 * c + 16 * s, 32 * dt, lg), pb, oT[dt]);
       }
   }
+  for (; jt < ntiles; ++jt) sync(jt);
   l += __shfl_xor(l, 32);
   if (qi < T) {
     const float inv = 1.f / l;
@@ -475,7 +489,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
   for (int t = 0; t < ST - 1; ++t)
     if (jt0 + t < ntiles) issue(t, jt0 + t);
   drain_vector_loads();
-  for (int jt = jt0; jt < ntiles; ++jt) {
+  // wait for tile jt, meet the other waves, start the copy of tile jt+ST-1;
+  // returns the stage of tile jt
+  auto sync = [&](int jt) {
     if (jt + ST - 2 < ntiles) {
       if constexpr (ST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else if constexpr (ST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_TILE) : "memory");
@@ -486,10 +502,22 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int stg = (jt - jt0) % ST;
     if (jt + ST - 1 < ntiles) issue((stg + ST - 1) % ST, jt + ST - 1);
+    return stg;
+  };
+  // The tiles this wave can see are jw0 .. jw1 (wave-uniform): the ones
+  // after its last query, and in a packed window the ones before its first
+  // query's document start, hold only masked keys.  The wave takes part in
+  // the copies and barriers of every tile of the block but computes only
+  // its own range (three loops, so that no branch sits in the computing one).
+  const int qw = __builtin_amdgcn_readfirstlane(q0);
+  const int jw1 = min(ntiles - 1, min(qw + 31, T - 1) / 64);
+  int jw0 = jt0;
+  if constexpr (DOC) jw0 = min(max(jt0, __builtin_amdgcn_readfirstlane(seg[(int64_t)b * T + min(qw, T - 1)]) / 64), jw1);
+  int jt = jt0;
+  for (; jt < jw0; ++jt) sync(jt);
+  for (; jt <= jw1; ++jt) {
+    const int stg = sync(jt);
     const int kb = jt * 64;
-    // a tile wholly after (or wholly before) this wave's queries is
-    // computed anyway (every score masked, no contribution): a skip would
-    // make the compiler copy the accumulators around the branch on every tile
     const bf16* Ks = sm[stg][0];
     const bf16* Vs = sm[stg][1];
     const bool edge = (kb + 63 > q0) || (kb + 63 >= T) || (DOC && kb < seg_hi);  // uniform over the wave
@@ -521,6 +549,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
       }
     }
   }
+  for (; jt < ntiles; ++jt) sync(jt);
   if (qv) store_head_grad(dqkv + ((int64_t)b * T + qi) * C3 + h * HD, dqT, scale, rope, qi, lg);
 }
 

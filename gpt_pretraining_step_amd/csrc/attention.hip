@@ -627,17 +627,32 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
   };
   issue(0, j * grp, 0);
   drain_vector_loads();
-  // iteration it covers query head j * grp + it / ntiles, tile it % ntiles
+  // Iteration it covers query head j * grp + it / ntiles, tile it % ntiles.
+  // sync: wait for this iteration's tile, meet the other waves, start the
+  // copy of the next iteration's tile (head hg, tile jt now).
   const int niter = grp * ntiles;
-  int jt = 0, hn = j * grp, jn = 1;  // this tile; head and tile of the next one
-  if (jn == ntiles) { jn = 0; ++hn; }
-  for (int it = 0; it < niter; ++it) {
+  auto sync = [&](int it, int hg, int jt) {
     tile_barrier();
-    if (it + 1 < niter) issue((it + 1) & 1, hn, jn);
+    if (it + 1 < niter) {
+      if (jt + 1 < ntiles) issue((it + 1) & 1, j * grp + hg, jt + 1);
+      else issue((it + 1) & 1, j * grp + hg + 1, 0);
+    }
+  };
+  // The query tiles this wave can see start at jw0 (wave-uniform): tiles
+  // that end before its first key are all masked.  The wave joins the
+  // copies and barriers of every tile but computes from jw0 on (two loops
+  // per head, no branch in the computing one).  (In a packed window a
+  // per-wave end, found by a second search over the starts, cost more than
+  // the tiles it saved.)
+  const int kw = __builtin_amdgcn_readfirstlane(k0);
+  const int jw0 = min(max((kw - qstart) / 64, 0), ntiles - 1);
+  int it = 0;
+  for (int hg = 0; hg < grp; ++hg) {
+  int jt = 0;
+  for (; jt < jw0; ++jt, ++it) sync(it, hg, jt);
+  for (; jt < ntiles; ++jt, ++it) {
+    sync(it, hg, jt);
     const int qs = qstart + jt * 64;
-    // a tile wholly before this wave's keys is computed anyway (every score
-    // masked, no contribution): a skip would make the compiler copy the
-    // accumulators around the branch on every tile
     const bf16* Qs = sm[it & 1][0];
     const bf16* dOs = sm[it & 1][1];
     const float* Ls = rowst[it & 1][0];
@@ -708,11 +723,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
         }
       }
     }
-    jt = jn;
-    if (++jn == ntiles) {
-      jn = 0;
-      ++hn;
-    }
+  }
   }
   if (kvld) {
     bf16* ok = dqkv + ((int64_t)b * T + kj) * C3 + C + j * HD;

@@ -4,8 +4,15 @@
 //    one wave instruction fills 1 KB of consecutive LDS bytes (lane l at byte
 //    16 l from the wave's base).
 //  * Swizzle: a tile row of BK bf16 elements is stored without padding, its
-//    16-byte chunk c at position c ^ swz(row).  The 32 rows touched by one
-//    MFMA operand fetch then fall on distinct banks.
+//    16-byte chunk c at position c ^ swz(row).  The LDS has 64 banks of 4
+//    bytes (256 bytes per pass); a 16-byte read serves 16 lanes per pass
+//    and an 8-byte (transposing) read 32.  For 128-byte rows two rows share
+//    a pass's 256 bytes, so swz(row) must take 8 distinct values on the
+//    even and on the odd rows of any 16 consecutive rows (the 16 lanes of a
+//    row-fragment read), and rows r and r + 2 of a 4-row transposing read
+//    must differ in bit 2: swz(row) = ((row >> 1) & 1) << 2 | (row >> 2) & 3.
+//    (row & 7, the 32-bank choice, leaves every such read 2-way
+//    conflicted.)
 //  * Transposed operand reads: ds_read_b64_tr_b16 (gfx950).  Within each
 //    group of 16 lanes, source lane j supplies the 8 bytes at its address and
 //    result lane i receives element i%4 of the vectors of source lanes i/4,
@@ -62,7 +69,7 @@ __device__ __forceinline__ void drain_vector_loads() { __builtin_amdgcn_s_waitcn
 
 template <int BK>
 __device__ __forceinline__ int swz_chunk(int row, int c) {
-  if constexpr (BK == 64) return c ^ (row & 7);
+  if constexpr (BK == 64) return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
   else return c ^ ((row >> 1) & 3);  // BK == 32: 4 chunks per 64-byte row
 }
 
@@ -98,7 +105,7 @@ __device__ __forceinline__ bf16x4 tr_read4(const bf16* tile, int r0, int c0) {
   const int j = threadIdx.x & 15;
   const int row = r0 + (j >> 2);
   const int col = c0 + 4 * (j & 3);
-  const int byte = row * 128 + ((((col >> 3) ^ (row & 7))) << 4) + ((col & 7) << 1);
+  const int byte = row * 128 + (swz_chunk<64>(row, col >> 3) << 4) + ((col & 7) << 1);
   auto base = (__attribute__((address_space(3))) char*)(tile);
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + byte));
   return __builtin_bit_cast(bf16x4, v);
@@ -106,14 +113,17 @@ __device__ __forceinline__ bf16x4 tr_read4(const bf16* tile, int r0, int c0) {
 
 // ---- tiles stored with K as the row index: [BK rows][R columns], R bf16 per
 // row (the output rows of a product whose operand is K-slow in memory).
-// 16-byte chunk c of row k sits at c ^ ((k & 3) << 1), so the 4 rows of one
-// transposing read fall on distinct banks.  The XOR flips only bits 1 and 2
-// of c, so it stays inside the row whenever R / 8 is a multiple of 8 (R = 64,
-// 128, 192, 256).
+// One transposing read (32 lanes per pass) covers 4 rows x 4 chunks.  With
+// rows of 512 bytes (R = 256; R = 128 likewise) every row starts on bank 0,
+// so chunk c of row k sits at c ^ ((k & 3) << 2): the 4 rows use 4 disjoint
+// 4-chunk groups.  With R = 192 or 64 the row stride alone staggers the
+// rows over the banks and c ^ ((k & 3) << 1) is conflict-free.  The XOR
+// stays inside the row (R / 8 a multiple of 16, resp. 8).
 template <int R>
 __device__ __forceinline__ int kr_chunk(int k, int c) {
   static_assert(R % 64 == 0, "rows of whole 8-chunk groups");
-  return c ^ ((k & 3) << 1);
+  if constexpr (R % 128 == 0) return c ^ ((k & 3) << 2);
+  else return c ^ ((k & 3) << 1);
 }
 
 // [BK][R] tile (source rows k0.. of a [K][ld] matrix, columns col0..col0+R)

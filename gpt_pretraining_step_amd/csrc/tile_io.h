@@ -69,8 +69,8 @@ __device__ __forceinline__ void drain_vector_loads() { __builtin_amdgcn_s_waitcn
 
 template <int BK>
 __device__ __forceinline__ int swz_chunk(int row, int c) {
-  if constexpr (BK == 64) return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-  else return c ^ ((row >> 1) & 3);  // BK == 32: 4 chunks per 64-byte row
+  static_assert(BK == 64, "128-byte tile rows");
+  return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 // K-major tile [ROWS][BK] (source rows row0.., K columns k0..) -> LDS, by DMA.

@@ -24,8 +24,14 @@
 // the keys s with start[t] <= s <= t, start[t] being the first position of
 // t's document (seg, [B, T] int32, non-decreasing along a row with
 // start[t] <= t).  Whole key tiles before the block's first document start
-// are skipped; the remaining ones are masked per element where they reach
-// below some query's start.  seg == nullptr is the plain causal mask.
+// are not copied at all, each wave computes only from its own first
+// document start, and the remaining tiles are masked per element where they
+// reach below some query's start.  seg == nullptr is the plain causal mask.
+//
+// Within a block every wave takes part in the copies and barriers of all
+// tiles but runs the products only on the tiles it can see (the causal
+// diagonal leaves the last forward tile of the first two waves, and the
+// first dK/dV tile of the last two, wholly masked).
 //
 // Grouped-query attention ("Build an LLM From Scratch: Making Training Fast
 // on One GPU", step 2, the textbook form repeats each key/value head for

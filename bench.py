@@ -286,7 +286,7 @@ def main(argv=None):
             "frac": round(fl[gsite] / gavg / PEAK_BF16, 4),
             # HBM bytes per launch from the two counter runs recorded under
             # profiles/ (null when none matches this kernel's current sources)
-            "traffic": load_traffic(os.path.join(ROOT, "profiles"), gsite),
+            "traffic": load_traffic(os.path.join(ROOT, "profiles"), gsite, args.workload),
             "avg_launch_us": round(gavg * 1e6, 2), "flops_per_launch": fl[gsite],
             "launches_timed": gcnt,
         }

@@ -126,7 +126,7 @@ def traffic_record(fetch_dir: str, write_dir: str, site: str, copy_bytes: int, c
     tb = f_kib * 1024 * scale_f + w_kib * 1024 * scale_w
     rec = {"site": site, "kernel": kf, "bytes_per_launch": round(tb), "fetch_kib": round(f_kib, 1),
            "write_kib": round(w_kib, 1), "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4),
-           "launches": len(fetch), "sources_sha256_16": site_sources_hash(site)}
+           "launches": len(fetch), "sources_sha256_16": site_sources_hash(site), "workload": "gpt2"}
     lines = [f"# HBM traffic per launch: {site}", "",
              f"Kernel: `{kf}`", "",
              "Commands (from the repository root, on one MI355X):", "",
@@ -140,9 +140,11 @@ def traffic_record(fetch_dir: str, write_dir: str, site: str, copy_bytes: int, c
     return "\n".join(lines)
 
 
-def load_traffic(profiles_dir: str, site: str):
-    """Bytes per launch recorded for `site`, or None when there is no record or
-    the site's kernel sources have changed since it was taken."""
+def load_traffic(profiles_dir: str, site: str, workload: str = "gpt2"):
+    """Bytes per launch recorded for `site` of `workload` (the traffic probe
+    runs the GPT-2 micro-step; records without a workload are that one), or
+    None when there is no record or the site's kernel sources have changed
+    since it was taken."""
     for path in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
         with open(path) as fh:
             for line in fh:
@@ -152,7 +154,8 @@ def load_traffic(profiles_dir: str, site: str):
                     rec = json.loads(line[len("traffic: "):])
                 except json.JSONDecodeError:
                     continue
-                if rec.get("site") == site and rec.get("sources_sha256_16") == site_sources_hash(site):
+                if (rec.get("site") == site and rec.get("workload", "gpt2") == workload
+                        and rec.get("sources_sha256_16") == site_sources_hash(site)):
                     return int(rec["bytes_per_launch"])
     return None
 

@@ -1,7 +1,8 @@
 """Host logic of the measurement helpers (gpt_pretraining_step_amd.profiling):
 attribution of counter rows to the dispatch after each marker, the traffic
 record's scaling by the calibration copy, and the per-site, per-workload,
-per-source-hash lookup that bench.py uses.  CPU only: synthetic CSV rows."""
+per-source-hash lookup that bench.py uses, bench.py's refusal of more than one
+GPU and its FLOP accounting.  CPU only: synthetic CSV rows."""
 
 import csv
 import json
@@ -66,3 +67,30 @@ def test_traffic_record_scales_and_is_found_only_for_its_site_workload_and_sourc
     stale = text.replace(rec["sources_sha256_16"], "0" * 16)
     (prof / "x_hbm_traffic.md").write_text(stale)
     assert P.load_traffic(str(prof), site) is None                  # sources changed since
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0 and r.stdout == ""
+    assert "one GPU" in r.stderr
+
+
+def test_bench_flop_accounting():
+    """The FLOPs per token of the MFU line and the grouped weight-gradient
+    launch's FLOPs, against sums written out from the shapes."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    # 6N + 12 L H Q T with the padded-vocabulary parameter count
+    assert bench.flops_per_token(124_475_904) == 6 * 124_475_904 + 12 * 12 * 12 * 64 * 1024 == 860_101_632
+    M, C, V, F = 16 * 1024, 768, 50304, 3072
+    fl = bench.gemm_site_flops(M, F)
+    per_layer = 2 * M * C * (3 * C) + 2 * M * C * C + 2 * M * C * F + 2 * M * F * C
+    assert fl["gemm.dw"] == 2 * M * V * C + 12 * per_layer == 4_049_080_418_304
+    assert fl["gemm.qkv"] == 2 * M * 3 * C * C

@@ -98,7 +98,7 @@ typedef struct {
   int32_t max_batch;
   int32_t precision;
   int32_t arch;
-  int32_t n_kv_head;  /* key/value heads; 0 = n_head (see below) */
+  int32_t n_kv_head;  /* key/value heads; 0 = n_head (see above) */
 } gpt2_config;
 
 /* Byte sizes of the caller-owned buffers. */

@@ -114,18 +114,21 @@ def cpu_baseline(rows: int = 8, workload: str = "gpt2"):
 COPY_BYTES = 256 << 20
 
 
-def traffic_probe(site: str) -> int:
-    """One micro-step with the library's marker kernel launched before every
-    launch of `site`, then the marker and a plain device copy of COPY_BYTES
-    (read and written once) that calibrates the HBM byte counters.  Run under
-    `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc WRITE_SIZE`."""
+def traffic_probe(site: str, workload: str = "gpt2") -> int:
+    """One micro-step of `workload` with the library's marker kernel launched
+    before every launch of `site`, then the marker and a plain device copy of
+    COPY_BYTES (read and written once) that calibrates the HBM byte counters.
+    Run under `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc
+    WRITE_SIZE`."""
     import torch
     import gpt_pretraining_step_amd as g
     import synthetic
-    model = g.GPT2(g.GPT2_124M)
+    wl = WORKLOADS[workload]
+    Bw, Gw = wl["B"], wl["G"]
+    model = g.GPT2(g.GPT2_124M if workload == "gpt2" else g.GPT2_ROTARY_124M)
     model.init_params(seed=42)
-    stream = synthetic.token_stream(B * T + 1, seed=1337)
-    x, y = synthetic.micro_batch(stream, 0, B, T)
+    stream = synthetic.token_stream(Bw * T + 1, seed=1337)
+    x, y = synthetic.micro_batch(stream, 0, Bw, T)
     x, y = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -134,14 +137,15 @@ def traffic_probe(site: str) -> int:
     model.profile(True)
     model.profile_only(site)
     model.profile_mark(True)
-    model.fwd_bwd(x, y, loss_scale=1.0 / G)
+    model.fwd_bwd(x, y, loss_scale=1.0 / Gw)
     g.op_marker()
     dst.copy_(src)
     torch.cuda.synchronize()
     st = model.status()
     n = model.profile_entries().get(site, (0, 0.0))[0]
     model.close()
-    print(f"[bench] traffic probe: site {site}, {n} marked launches, status {st}", file=sys.stderr, flush=True)
+    print(f"[bench] traffic probe: {workload} site {site}, {n} marked launches, status {st}", file=sys.stderr,
+          flush=True)
     return 0 if st == 0 and n > 0 else 1
 
 
@@ -165,7 +169,7 @@ def main(argv=None):
               file=sys.stderr)
         return 2
     if args.traffic_probe:
-        return traffic_probe(args.traffic_probe)
+        return traffic_probe(args.traffic_probe, args.workload)
 
     import numpy as np
     import torch

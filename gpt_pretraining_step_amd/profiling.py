@@ -114,7 +114,8 @@ def attribute(rows, counter: str):
     return names.pop(), [per[d][1] for d in site_ids], per[copy_id][1]
 
 
-def traffic_record(fetch_dir: str, write_dir: str, site: str, copy_bytes: int, cmd_f: str, cmd_w: str) -> str:
+def traffic_record(fetch_dir: str, write_dir: str, site: str, copy_bytes: int, cmd_f: str, cmd_w: str,
+                   workload: str = "gpt2") -> str:
     kf, fetch, copy_f = attribute(_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
     kw, write, copy_w = attribute(_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
     if kf != kw:
@@ -126,8 +127,8 @@ def traffic_record(fetch_dir: str, write_dir: str, site: str, copy_bytes: int, c
     tb = f_kib * 1024 * scale_f + w_kib * 1024 * scale_w
     rec = {"site": site, "kernel": kf, "bytes_per_launch": round(tb), "fetch_kib": round(f_kib, 1),
            "write_kib": round(w_kib, 1), "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4),
-           "launches": len(fetch), "sources_sha256_16": site_sources_hash(site), "workload": "gpt2"}
-    lines = [f"# HBM traffic per launch: {site}", "",
+           "launches": len(fetch), "sources_sha256_16": site_sources_hash(site), "workload": workload}
+    lines = [f"# HBM traffic per launch: {site}" + ("" if workload == "gpt2" else f" ({workload} workload)"), "",
              f"Kernel: `{kf}`", "",
              "Commands (from the repository root, on one MI355X):", "",
              "    " + cmd_f, "    " + cmd_w, "",
@@ -141,10 +142,9 @@ def traffic_record(fetch_dir: str, write_dir: str, site: str, copy_bytes: int, c
 
 
 def load_traffic(profiles_dir: str, site: str, workload: str = "gpt2"):
-    """Bytes per launch recorded for `site` of `workload` (the traffic probe
-    runs the GPT-2 micro-step; records without a workload are that one), or
-    None when there is no record or the site's kernel sources have changed
-    since it was taken."""
+    """Bytes per launch recorded for `site` of `workload` (records without a
+    workload are the GPT-2 micro-step's), or None when there is no record or
+    the site's kernel sources have changed since it was taken."""
     for path in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
         with open(path) as fh:
             for line in fh:
@@ -174,12 +174,13 @@ def main(argv=None) -> int:
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    t.add_argument("--workload", default="gpt2")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.command, a.title))
     else:
         sys.stdout.write(traffic_record(a.fetch_dir, a.write_dir, a.site, a.copy_bytes, a.command_fetch,
-                                        a.command_write))
+                                        a.command_write, a.workload))
     return 0
 
 

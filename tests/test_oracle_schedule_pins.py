@@ -75,3 +75,63 @@ def test_oracle_loop_on_a_tiny_model_lowers_the_loss():
     assert hist[0][0] == pytest.approx(math.log(32), abs=0.1)
     assert hist[-1][0] < 0.5 * hist[0][0]
     assert [h[2] for h in hist[:5]] == pytest.approx([3e-3 * (s + 1) / 5 for s in range(5)])
+
+
+def _tiny_problem(seed):
+    cfg = OM.Config(vocab_size=24, block_size=8, n_layer=2, n_head=2, n_embd=16, mlp_hidden=32)
+    params = OM.init_params(cfg, seed=seed, dtype=np.float64)
+    rng = np.random.default_rng(seed)
+    tok = rng.integers(0, 24, size=(4, 8)).astype(np.int64)
+    tgt = rng.integers(0, 24, size=(4, 8)).astype(np.int64)
+    return cfg, params, tok, tgt
+
+
+def test_oracle_loop_micro_batches_equal_their_union():
+    """One optimizer step over G = 2 micro-batches with loss / G is the step
+    over their union when both hold the same number of targets ([grad-accum]
+    "Gradient accumulation averages across micro-steps"; [train-124M] 8.1):
+    same parameters, same reported loss and pre-clip norm.  A loop that
+    forgot the 1 / G scale would double the gradient (and the norm)."""
+    cfg, p0, tok, tgt = _tiny_problem(11)
+    pa = {k: v.copy() for k, v in p0.items()}
+    pb = {k: v.copy() for k, v in p0.items()}
+    halves = [(tok[:2], tgt[:2]), (tok[2:], tgt[2:])]
+    ha = OM.train(cfg, pa, lambda s: halves, 1, OM.fwd_bwd, 1e-2, 1e-3, 1, 10, max_norm=1e9)
+    hb = OM.train(cfg, pb, lambda s: [(tok, tgt)], 1, OM.fwd_bwd, 1e-2, 1e-3, 1, 10, max_norm=1e9)
+    assert ha[0][0] == pytest.approx(hb[0][0], rel=1e-12)
+    assert ha[0][1] == pytest.approx(hb[0][1], rel=1e-10)
+    for k in p0:
+        np.testing.assert_allclose(pa[k], pb[k], rtol=0, atol=1e-12, err_msg=k)
+    # the norm is the one of the union's mean-loss gradient, computed directly
+    _, _, g = OM.fwd_bwd(cfg, {k: v.copy() for k, v in p0.items()}, tok, tgt)
+    assert ha[0][1] == pytest.approx(OM.global_grad_norm(g), rel=1e-10)
+    # with the clip active the two runs still agree
+    pc = {k: v.copy() for k, v in p0.items()}
+    pd = {k: v.copy() for k, v in p0.items()}
+    OM.train(cfg, pc, lambda s: halves, 1, OM.fwd_bwd, 1e-2, 1e-3, 1, 10, max_norm=1e-3)
+    OM.train(cfg, pd, lambda s: [(tok, tgt)], 1, OM.fwd_bwd, 1e-2, 1e-3, 1, 10, max_norm=1e-3)
+    for k in p0:
+        np.testing.assert_allclose(pc[k], pd[k], rtol=0, atol=1e-12, err_msg=k)
+
+
+def test_oracle_loop_two_steps_compose_from_single_steps():
+    """Each optimizer step starts from zero gradients ([train-124M] 8.1,
+    optimizer.zero_grad() at the top of the step).  With betas 0 (AdamW then
+    keeps no history: m = g, v = g^2, bias corrections 1) and a constant
+    rate, a two-step run must equal two one-step runs applied in turn; a loop
+    that did not zero the gradients would feed step 1's gradient into step 2."""
+    cfg, p0, tok, tgt = _tiny_problem(12)
+    b0 = [(tok[:2], tgt[:2]), (tok[2:], tgt[2:])]
+    b1 = [(tok[[1, 3]], tgt[[0, 2]]), (tok[[0, 2]], tgt[[1, 3]])]
+    hp = dict(beta1=0.0, beta2=0.0, max_norm=0.5)
+    pa = {k: v.copy() for k, v in p0.items()}
+    ha = OM.train(cfg, pa, lambda s: b0 if s == 0 else b1, 2, OM.fwd_bwd, 5e-3, 5e-3, 1, 10, **hp)
+    pb = {k: v.copy() for k, v in p0.items()}
+    h0 = OM.train(cfg, pb, lambda s: b0, 1, OM.fwd_bwd, 5e-3, 5e-3, 1, 10, **hp)
+    h1 = OM.train(cfg, pb, lambda s: b1, 1, OM.fwd_bwd, 5e-3, 5e-3, 1, 10, **hp)
+    assert [ha[0][0], ha[1][0]] == pytest.approx([h0[0][0], h1[0][0]], rel=1e-12)
+    assert [ha[0][1], ha[1][1]] == pytest.approx([h0[0][1], h1[0][1]], rel=1e-10)
+    for k in p0:
+        np.testing.assert_allclose(pa[k], pb[k], rtol=0, atol=1e-12, err_msg=k)
+    # and the second step really moved the weights (the pin is not vacuous)
+    assert max(float(np.abs(pa[k] - p0[k]).max()) for k in p0) > 1e-3

@@ -44,6 +44,7 @@ from .model import (  # noqa: F401
     forward,
     fwd_bwd,
     lmhead_ce,
+    lmhead_ce_sampled,
 )
 from .optim import global_grad_norm, clip_coef, adamw_update, clip_adamw_step  # noqa: F401
 from .init import philox4x32_10, normal_from_philox, init_params  # noqa: F401

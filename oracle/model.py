@@ -198,13 +198,17 @@ def attention_bwd(do, q, k, v, p):
 # loss
 # ----------------------------------------------------------------------------
 
-def cross_entropy_fwd_bwd(logits, targets, n_valid, scale):
+def cross_entropy_fwd_bwd(logits, targets, n_valid, scale, ignore_index=-1):
     """Cross-entropy rows ([train-124M] §4): softmax, pick the target, -log.
 
     Returns per-row losses (0 for ignored rows) and dlogits of
-    scale * (sum of valid row losses) / n_valid.  Rows with target -1 are
-    ignored."""
-    valid = targets >= 0
+    scale * (sum of valid row losses) / n_valid.  Rows whose target equals
+    ``ignore_index`` are ignored (the documented ``ignore_index`` of the
+    library cross-entropy the pages call; -1 for the isolated lm_head
+    workload); every other target must lie in [0, V)."""
+    valid = targets != ignore_index
+    if np.any(valid & ((targets < 0) | (targets >= logits.shape[-1]))):
+        raise ValueError("target outside [0, V) that is not ignore_index")
     m = logits.max(axis=-1, keepdims=True)
     e = np.exp(logits - m)
     se = e.sum(axis=-1, keepdims=True)
@@ -219,28 +223,55 @@ def cross_entropy_fwd_bwd(logits, targets, n_valid, scale):
     return row_loss, dlogits
 
 
-def lmhead_ce(hidden, weight, targets, chunk=1024):
+def lmhead_ce(hidden, weight, targets, chunk=1024, ignore_index=-1):
     """Tied lm_head + mean cross-entropy, forward and backward, for the
     isolated lm_head workload: logits = hidden @ weight^T (no bias), loss =
-    mean over valid targets, dHidden and dWeight of that mean.
+    mean over valid targets (those not equal to ``ignore_index``), dHidden
+    and dWeight of that mean.
 
     Rows are processed in chunks so the dense logits never exceed
     chunk x V; the arithmetic is the dense definition.
     Returns (loss, row_loss, dhidden, dweight)."""
     M = hidden.shape[0]
-    n_valid = int((targets >= 0).sum())
+    n_valid = int((targets != ignore_index).sum())
     dhidden = np.zeros_like(hidden)
     dweight = np.zeros_like(weight)
     row_loss = np.zeros(M, dtype=hidden.dtype)
     for r0 in range(0, M, chunk):
         r1 = min(M, r0 + chunk)
         logits = hidden[r0:r1] @ weight.T
-        rl, dl = cross_entropy_fwd_bwd(logits, targets[r0:r1], n_valid, 1.0)
+        rl, dl = cross_entropy_fwd_bwd(logits, targets[r0:r1], n_valid, 1.0, ignore_index)
         row_loss[r0:r1] = rl
         dhidden[r0:r1] = dl @ weight
         dweight += dl.T @ hidden[r0:r1]
     loss = row_loss.astype(np.float64).sum() / n_valid if n_valid > 0 else float("nan")
     return loss, row_loss, dhidden, dweight
+
+
+def lmhead_ce_sampled(hidden, weight, targets, rows, cols, chunk=1024, ignore_index=-1):
+    """lmhead_ce restricted to what a large case can afford: the loss and
+    per-row losses over all M rows, the rows ``rows`` of dHidden and the rows
+    ``cols`` of dWeight (vocabulary entries).  Same arithmetic as lmhead_ce,
+    chunk by chunk; only the requested slices of the two gradients are
+    formed.  Returns (loss, row_loss, dhidden[rows], dweight[cols])."""
+    M = hidden.shape[0]
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    n_valid = int((targets != ignore_index).sum())
+    row_loss = np.zeros(M, dtype=hidden.dtype)
+    dh = np.zeros((len(rows), hidden.shape[1]), dtype=hidden.dtype)
+    dw = np.zeros((len(cols), weight.shape[1]), dtype=weight.dtype)
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        logits = hidden[r0:r1] @ weight.T
+        rl, dl = cross_entropy_fwd_bwd(logits, targets[r0:r1], n_valid, 1.0, ignore_index)
+        row_loss[r0:r1] = rl
+        here = np.nonzero((rows >= r0) & (rows < r1))[0]
+        if len(here):
+            dh[here] = dl[rows[here] - r0] @ weight
+        dw += dl[:, cols].T @ hidden[r0:r1]
+    loss = row_loss.astype(np.float64).sum() / n_valid if n_valid > 0 else float("nan")
+    return loss, row_loss, dh, dw
 
 
 # ----------------------------------------------------------------------------

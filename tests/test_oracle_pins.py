@@ -301,6 +301,71 @@ def test_ce_brute_force_and_invariants():
     assert np.all(dh[3] == 0)
 
 
+def test_ce_ignore_index_brute_force_and_library():
+    """ignore_index names the ignored target value, as in the library
+    cross-entropy the pages call; a value inside [0, V) ignores that class's
+    rows.  Brute force by per-element loops over the rows that count, and
+    torch's CPU cross_entropy(ignore_index=...) with autograd (float64)."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(5)
+    Mr, C, V = 11, 4, 7
+    h = rng.standard_normal((Mr, C))
+    W = rng.standard_normal((V, C))
+    tg = rng.integers(0, V, size=Mr)
+    tg[tg == 4] = 5
+    tg[[1, 6, 9]] = 4
+    for ig in (4, -100):
+        t2 = tg.copy()
+        if ig < 0:
+            t2[[1, 6, 9]] = ig
+        loss, rl, dh, dw = M.lmhead_ce(h, W, t2, chunk=4, ignore_index=ig)
+        keep = [i for i in range(Mr) if t2[i] != ig]
+        nv = len(keep)
+        assert nv == Mr - 3
+        bl, bdh, bdw = 0.0, np.zeros_like(h), np.zeros_like(W)
+        for i in keep:
+            z = [sum(h[i, c] * W[v, c] for c in range(C)) for v in range(V)]
+            mz = max(z)
+            se = sum(math.exp(zz - mz) for zz in z)
+            bl += (mz + math.log(se) - z[t2[i]]) / nv
+            for v in range(V):
+                d = (math.exp(z[v] - mz) / se - (1.0 if v == t2[i] else 0.0)) / nv
+                bdh[i] += d * W[v]
+                bdw[v] += d * h[i]
+        assert loss == pytest.approx(bl, rel=1e-12)
+        np.testing.assert_allclose(dh, bdh, rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(dw, bdw, rtol=1e-10, atol=1e-14)
+        ht = torch.tensor(h, requires_grad=True)
+        Wt = torch.tensor(W, requires_grad=True)
+        lt = F.cross_entropy(ht @ Wt.T, torch.tensor(t2), ignore_index=ig)
+        lt.backward()
+        assert float(lt) == pytest.approx(loss, rel=1e-12)
+        np.testing.assert_allclose(ht.grad.numpy(), dh, rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(Wt.grad.numpy(), dw, rtol=1e-10, atol=1e-14)
+    with pytest.raises(ValueError):  # a negative target other than ignore_index is not a class
+        M.lmhead_ce(h, W, np.where(tg == 4, -1, tg), ignore_index=-100)
+
+
+def test_ce_sampled_slices_equal_dense():
+    """lmhead_ce_sampled gives the dense lmhead_ce's loss and per-row losses
+    and exactly its rows / vocabulary entries of dHidden and dWeight."""
+    rng = np.random.default_rng(6)
+    Mr, C, V = 23, 6, 13
+    h = rng.standard_normal((Mr, C))
+    W = rng.standard_normal((V, C))
+    tg = rng.integers(0, V, size=Mr)
+    tg[[0, 5, 22]] = -1
+    loss, rl, dh, dw = M.lmhead_ce(h, W, tg)
+    rows, cols = np.array([0, 4, 5, 17, 22]), np.array([12, 0, 3, 3])
+    for chunk in (1, 5, 1024):
+        l2, rl2, dhs, dws = M.lmhead_ce_sampled(h, W, tg, rows, cols, chunk=chunk)
+        assert l2 == pytest.approx(loss, rel=1e-13)
+        np.testing.assert_allclose(rl2, rl, rtol=1e-13, atol=0)
+        np.testing.assert_allclose(dhs, dh[rows], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(dws, dw[cols], rtol=1e-12, atol=1e-15)
+
+
 def test_ce_all_ignored_gives_nan_and_no_grad():
     h = np.ones((3, 4))
     W = np.ones((5, 4))

@@ -1,6 +1,7 @@
 """Throughput of the GPT-2 124M training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--no-cpu-baseline]
+    python bench.py --workload lmhead         (the isolated lm_head + loss)
     python bench.py --traffic-probe SITE     (under rocprofv3 --pmc, see below)
 
 One step is the pages' full optimizer step: zero_grad, 32 micro-steps of
@@ -12,14 +13,21 @@ full steps with a device synchronisation on both sides, the loss read back
 once per step).  Inputs are a synthetic Zipf token stream resident in HBM
 before timing starts; weights are the library's own N(0, 0.02) init.
 
-Prints one JSON line with tokens/s, MFU, the roofline of the dominant kernel
-(its launches timed with HIP events on the library's stream during the timed
-steps; the per-site breakdown comes from the first warm-up step), and the CPU
-oracle timed on a bounded sample on this host.  The roofline's `traffic`
+Prints one JSON line with tokens/s, MFU (against the bf16 peak and against
+the best bf16 product this library measures on the box), the GPU clock
+sampled during the timed steps, the roofline of the dominant kernel (its
+launches timed with HIP events on the library's stream during the timed
+steps; the per-site breakdown comes from the first warm-up step), and the
+CPU oracle timed on a bounded sample on this host.  The roofline's `traffic`
 (HBM bytes per launch of the dominant kernel) is read from a record under
 profiles/ written by `python -m gpt_pretraining_step_amd.profiling traffic`
 from two counter runs of `--traffic-probe`, and is null when no record
 matches the kernel's current sources.
+
+`--workload lmhead` times the isolated tied lm_head + cross-entropy forward
+and backward (hidden [65,536 x 768], vocabulary 50,304, 10% of targets
+ignored): the median of the timed calls, in TFLOP/s of its 3 x 2 M C V
+algorithmic FLOPs.
 """
 
 from __future__ import annotations
@@ -57,33 +65,130 @@ def flops_per_token(n_params: int, L=12, H=12, hd=64, T_=1024) -> int:
     return 6 * n_params + 12 * L * H * hd * T_
 
 
+CE_CHUNK = 8192  # rows per lm_head chunk of the library (bf16)
+
+
 def gemm_site_flops(rows=B * T, F=3072, FC=None, L=12):
     """Algorithmic FLOPs of one launch at each GEMM site of the micro-step
-    (rows = B*T, C = 768, MLP width F, V = 50304; the lm_head products take
-    all rows in one launch).  FC is the fc product's output width: F for
-    GPT-2, 2F (gate and up) for the rotary variant.  gemm.dw is the grouped
-    launch of every weight-gradient product: the tied embedding's (lm_head)
-    and the L blocks' four each."""
+    (rows = B*T, C = 768, MLP width F, V = 50304).  FC is the fc product's
+    output width: F for GPT-2, 2F (gate and up) for the rotary variant.
+    gemm.dw is the grouped launch of the L blocks' four weight-gradient
+    products.  The lm_head runs per chunk of CE_CHUNK rows: gemm.lm_head is
+    one chunk's logits product, gemm.lm_head_bwd one chunk's dZ and dW
+    products together."""
     M, C, V = rows, 768, 50304
     FC = F if FC is None else FC
+    chunk = min(M, CE_CHUNK)
     return {
-        "gemm.dw": 2 * M * V * C + L * 2 * M * C * (3 * C + C + FC + F),
+        "gemm.dw": L * 2 * M * C * (3 * C + C + FC + F),
         "gemm.qkv": 2 * M * 3 * C * C,
         "gemm.attn_proj": 2 * M * C * C,
         "gemm.fc": 2 * M * FC * C,
         "gemm.mlp_proj": 2 * M * C * F,
-        "gemm.lm_head": 2 * M * V * C,
-        "gemm.lm_head_dx": 2 * M * V * C,
-        "gemm.lm_head_dw": 2 * M * V * C,
-        "gemm.mlp_proj_dw": 2 * M * C * F,
+        "gemm.lm_head": 2 * chunk * V * C,
+        "gemm.lm_head_bwd": 2 * 2 * chunk * V * C,
         "gemm.mlp_proj_dx": 2 * M * C * F,
-        "gemm.fc_dw": 2 * M * FC * C,
         "gemm.fc_dx": 2 * M * FC * C,
-        "gemm.attn_proj_dw": 2 * M * C * C,
         "gemm.attn_proj_dx": 2 * M * C * C,
-        "gemm.qkv_dw": 2 * M * 3 * C * C,
         "gemm.qkv_dx": 2 * M * 3 * C * C,
     }
+
+
+class ClockSampler:
+    """The GPU's graphics clock, sampled with amd-smi from a host thread
+    while the timed steps run ("Making Training Fast on One GPU", clock
+    drift as noise: the clock is logged beside each timing)."""
+
+    def __init__(self, period: float = 1.0):
+        import threading
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def read_mhz():
+        import subprocess
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                               timeout=10)
+            data = json.loads(r.stdout)
+        except Exception:
+            return None
+        vals = []
+
+        def walk(x, key=""):
+            if isinstance(x, dict):
+                for k, v in x.items():
+                    if key.startswith("gfx") and k == "clk":
+                        val = v.get("value") if isinstance(v, dict) else v
+                        if isinstance(val, (int, float)):
+                            vals.append(float(val))
+                    else:
+                        walk(v, k if isinstance(k, str) else "")
+            elif isinstance(x, list):
+                for v in x:
+                    walk(v, key)
+        walk(data)
+        return sum(vals) / len(vals) if vals else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self.read_mhz()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=15)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"gfx_mhz_median": round(v[len(v) // 2], 1), "gfx_mhz_min": round(v[0], 1),
+                "gfx_mhz_max": round(v[-1], 1), "samples": len(v), "source": "amd-smi metric -c (mean over XCDs)"}
+
+
+def measured_peak_tflops(reps: int = 20):
+    """Measured bf16 product rates on the box, the yardstick "Making
+    Training Fast on One GPU" reports MFU against beside the spec sheet's
+    peak: an 8192^3 bf16 product through torch.mm (the vendor BLAS, run here
+    only as a measuring stick, never in the training path) and the same
+    product through this library's gpt2_op_gemm; median of `reps` launches
+    each, timed with HIP events."""
+    import torch
+    import gpt_pretraining_step_amd as g
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    st = torch.cuda.current_stream()
+
+    def rate(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        ts.sort()
+        return 2 * n ** 3 / ts[len(ts) // 2] / 1e12
+
+    out = {"vendor_blas_8192": round(rate(lambda: torch.mm(a, b, out=c)), 1),
+           "library_8192": round(rate(lambda: g.op_gemm(a, b, c, n, n, n)), 1)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(rows: int = 8, workload: str = "gpt2"):
@@ -158,8 +263,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no HIP events at all (no roofline, no breakdown)")
     ap.add_argument("--traffic-probe", metavar="SITE", help="one marked micro-step for an HBM counter run")
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2",
-                    help="gpt2 (the headline step, default) or rotary (the modern variant)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["lmhead"], default="gpt2",
+                    help="gpt2 (the headline step, default), rotary (the modern variant) or lmhead (the isolated "
+                         "tied lm_head + cross-entropy)")
     ap.add_argument("--doc-mask", type=float, default=None, metavar="MEAN_DOC",
                     help="packed windows under the document mask, documents of this mean length in tokens "
                          "(default: the plain causal step over documents of mean length 1000)")
@@ -170,6 +276,8 @@ def main(argv=None):
         return 2
     if args.traffic_probe:
         return traffic_probe(args.traffic_probe, args.workload)
+    if args.workload == "lmhead":
+        return bench_lmhead(args)
 
     import numpy as np
     import torch
@@ -232,17 +340,18 @@ def main(argv=None):
         model.profile_only(gsite)
         model.profile_reset()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     step_times, log = [], []
-    for i in range(args.steps):
-        s0 = time.perf_counter()
-        loss, norm = step()
-        step_times.append(time.perf_counter() - s0)
-        log.append((loss, norm))
-        print(f"[bench] step {i}: loss {loss:.4f} grad-norm {norm:.4f} {step_times[-1] * 1e3:.1f} ms",
-              file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            s0 = time.perf_counter()
+            loss, norm = step()
+            step_times.append(time.perf_counter() - s0)
+            log.append((loss, norm))
+            print(f"[bench] step {i}: loss {loss:.4f} grad-norm {norm:.4f} {step_times[-1] * 1e3:.1f} ms",
+                  file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     st = model.status()
     if st != 0:
         raise RuntimeError(f"device status {st} after timed steps")
@@ -275,6 +384,7 @@ def main(argv=None):
         "flops_per_token": fpt,
         "loss_last_step": round(log[-1][0], 5),
         "grad_norm_last_step": round(log[-1][1], 5),
+        "clock": clock.summary(),
     }
 
     # dominant kernel: the GEMM launch site with the largest summed time in the
@@ -300,10 +410,89 @@ def main(argv=None):
             k: round(v[1], 3) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][1])}
         result["time_breakdown_note"] = "first warm-up step, every launch bracketed with HIP events"
         result["top_site"] = {"site": site, "share": round(ms / total_ms, 4)}
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+    if not args.no_profile:
+        pk = measured_peak_tflops()
+        peak = max(pk.values())
+        result["mfu_vs_measured_peak"] = {"mfu": round(tps * fpt / (peak * 1e12), 4), "peak_tflops": peak,
+                                          "products": pk, "note": "8192^3 bf16 products on this box"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(workload=args.workload)
-    model.close()
+    print(json.dumps(result))
+    return 0
+
+
+def bench_lmhead(args):
+    """The isolated tied lm_head + cross-entropy, forward and backward, at
+    hidden [65,536 x 768] bf16, vocabulary 50,304, Zipf targets with 10% set
+    to ignore_index -1: W untimed calls, then K calls each bracketed by HIP
+    events on the stream they run on; the median call."""
+    import torch
+    import gpt_pretraining_step_amd as g
+    import synthetic
+    M, C, V = 65536, 768, 50304
+    h, w, t = synthetic.lmhead_inputs(M=M, C=C, V=V, ignore_frac=0.1, seed=1337)
+    H = torch.from_numpy(h).to(torch.bfloat16).cuda()
+    W = torch.from_numpy(w).to(torch.bfloat16).cuda()
+    Tg = torch.from_numpy(t).cuda()
+    dw = torch.zeros((V, C), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(g.lib().gpt2_lmhead_ce_scratch_bytes(M, C, V), dtype=torch.uint8, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    dh = torch.empty_like(H)
+    st = torch.cuda.current_stream()
+
+    def call():
+        g.lmhead_ce(H, W, Tg, dw, stream=st, scratch=scratch, loss=loss, dhidden=dh)
+
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(st)
+            call()
+            b.record(st)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ts = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+    med = ts[len(ts) // 2]
+    flops = 3 * 2 * M * C * V
+    tf = flops / med / 1e12
+    print(f"[bench] lmhead: median {med * 1e3:.3f} ms over {steps} calls, loss {float(loss.item()):.5f}",
+          file=sys.stderr, flush=True)
+    result = {
+        "metric": "isolated tied lm_head + cross-entropy fwd+bwd, hidden 65536x768, V=50304, 1 MI355X",
+        "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(med * 1e3, 3), "ms_mean_wall": round(1e3 * elapsed / steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (hidden N(0,1), weight N(0,0.02^2), Zipf targets, 10% ignored)",
+        "config": {"workload": "lmhead_ce: hidden [65536, 768] bf16, weight [50304, 768] bf16, ignore_index -1, "
+                               "rows in chunks of 8192", "rows": M, "n_embd": C, "vocab": V,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "gpt2_lmhead_ce (all launches of one call)", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": round(flops / med / PEAK_BF16, 4), "traffic": None,
+                     "avg_launch_us": round(med * 1e6, 2), "flops_per_launch": flops},
+        "loss": round(float(loss.item()), 5),
+        "clock": clock.summary(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 8192
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        c0 = time.perf_counter()
+        oracle.lmhead_ce(h[:rows], w, t[:rows])
+        dt = time.perf_counter() - c0
+        result["cpu_baseline"] = {"value": round(3 * 2 * rows * C * V / dt / 1e12, 4), "unit": "TFLOP/s",
+                                  "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                  "sample": f"the oracle's lm_head + loss (float32 NumPy) on the first {rows} rows; "
+                                            f"{dt:.1f} s"}
     print(json.dumps(result))
     return 0
 

@@ -238,19 +238,23 @@ class GPT2:
 
 # ------------------------------------------------------------------ single ops
 
-def lmhead_ce(hidden, weight, targets, dweight, stream=None, flag=None):
+def lmhead_ce(hidden, weight, targets, dweight, stream=None, flag=None, ignore_index=-1, scratch=None, loss=None,
+              dhidden=None):
     """Isolated tied lm_head + mean cross-entropy (bf16 hidden [M, C], bf16
-    weight [V, C], int32 targets [M]); dweight (float32 [V, C]) is added to.
-    Returns (loss [1] float32, dhidden bf16 [M, C])."""
+    weight [V, C], int32 targets [M]; targets equal to ignore_index are
+    ignored); dweight (float32 [V, C]) is added to.  scratch, loss and
+    dhidden may be passed in (reused across calls).  Returns (loss [1]
+    float32, dhidden bf16 [M, C])."""
     import torch
     M, C = hidden.shape
     V = weight.shape[0]
-    nbytes = lib().gpt2_lmhead_ce_scratch_bytes(M, C, V)
-    scratch = torch.empty(nbytes, dtype=torch.uint8, device=hidden.device)
-    loss = torch.empty(1, dtype=torch.float32, device=hidden.device)
-    dh = torch.empty_like(hidden)
+    if scratch is None:
+        scratch = torch.empty(lib().gpt2_lmhead_ce_scratch_bytes(M, C, V), dtype=torch.uint8, device=hidden.device)
+    loss = torch.empty(1, dtype=torch.float32, device=hidden.device) if loss is None else loss
+    dh = torch.empty_like(hidden) if dhidden is None else dhidden
     check(lib().gpt2_lmhead_ce(_stream_ptr(stream), hidden.data_ptr(), weight.data_ptr(), targets.data_ptr(), M, C, V,
-                               loss.data_ptr(), dh.data_ptr(), dweight.data_ptr(), scratch.data_ptr(), _ptr(flag)),
+                               int(ignore_index), loss.data_ptr(), dh.data_ptr(), dweight.data_ptr(),
+                               scratch.data_ptr(), _ptr(flag)),
           "gpt2_lmhead_ce")
     return loss, dh
 

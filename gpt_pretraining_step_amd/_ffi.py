@@ -103,7 +103,7 @@ SIGNATURES = {
     "gpt2_strerror": (ct.c_char_p, [ct.c_int]),
     "gpt2_lmhead_ce_scratch_bytes": (ct.c_size_t, [ct.c_int, ct.c_int, ct.c_int]),
     "gpt2_lmhead_ce": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int,
-                                  ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p]),
+                                  ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p]),
     "gpt2_op_gemm": (ct.c_int, [ct.c_void_p, ct.POINTER(GemmArgs)]),
     "gpt2_gemm_grouped_workspace_bytes": (ct.c_size_t, [ct.POINTER(GemmArgs), ct.c_int]),
     "gpt2_op_gemm_grouped": (ct.c_int, [ct.c_void_p, ct.POINTER(GemmArgs), ct.c_int, ct.POINTER(ct.c_void_p),

@@ -1,9 +1,11 @@
 // Cross-entropy over the tied lm_head's logits, one row chunk at a time
 // ("How I trained my own GPT-2 124M on FineWeb-Edu" section 4: softmax, pick
-// the target's probability, -log, mean over positions).  Rows whose target is
-// -1 are ignored and the mean divides by the valid count ("Multi-GPU
-// calculation of gradients for accelerated training", "Cross-entropy averages
-// within one micro-batch").  The softmax runs over every padded column.
+// the target's probability, -log, mean over positions).  Rows whose target
+// equals ignore_index (the library cross-entropy's argument; the training
+// step passes -1) are ignored and the mean divides by the valid count
+// ("Multi-GPU calculation of gradients for accelerated training",
+// "Cross-entropy averages within one micro-batch").  The softmax runs over
+// every padded column.
 #include "common.h"
 
 namespace g2 {
@@ -13,18 +15,19 @@ constexpr float LN2 = 0.6931471805599453f;
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ bool target_valid(int t, int V) { return t >= 0 && t < V; }
+__device__ __forceinline__ bool target_valid(int t, int V, int ig) { return t != ig && t >= 0 && t < V; }
 
-// count[0] = number of targets in [0, V); ids outside [0, V) other than -1
-// raise GPT2_ERR_BAD_ID (and are then treated as ignored).  One block.
-__global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __restrict__ tgt, int n, int V,
+// count[0] = number of targets in [0, V) other than ignore_index; ids outside
+// [0, V) other than ignore_index raise GPT2_ERR_BAD_ID (and are then treated
+// as ignored).  One block.
+__global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __restrict__ tgt, int n, int V, int ig,
                                                              int* __restrict__ count, int* flag) {
   __shared__ int red[1024];
   int c = 0, bad = 0;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int t = tgt[i];
-    c += target_valid(t, V);
-    bad |= (t != -1 && !target_valid(t, V));
+    c += target_valid(t, V, ig);
+    bad |= (t != ig && (t < 0 || t >= V));
   }
   red[threadIdx.x] = c;
   __syncthreads();
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __re
 template <typename LT, typename DT, bool VEC>
 __global__ __launch_bounds__(256) void ce_rows_kernel(const LT* __restrict__ logits, int64_t ld_l, DT* __restrict__ dl,
                                                       int64_t ld_d, const int32_t* __restrict__ tgt, int V,
-                                                      const int* __restrict__ count, float scale,
+                                                      int ig, const int* __restrict__ count, float scale,
                                                       float* __restrict__ row_loss) {
   const int r = blockIdx.x;
   const LT* z = logits + (int64_t)r * ld_l;
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const LT* __restrict__ log
   }
   const float lse2 = sm[0] + log2f(ss[0]);  // log2-domain log-sum-exp
   const int t = tgt[r];
-  const bool valid = target_valid(t, V);
+  const bool valid = target_valid(t, V, ig);
   const int n = count[0];
   if (threadIdx.x == 0) row_loss[r] = valid ? (lse2 * LN2 - to_f<LT>(z[t])) : 0.f;
   const float coef = (valid && n > 0) ? scale / (float)n : 0.f;
@@ -150,8 +153,8 @@ __global__ __launch_bounds__(1024) void ce_finish_kernel(const float* __restrict
 __global__ __launch_bounds__(256) void ce_apply_kernel(bf16* __restrict__ y, const float2* __restrict__ stats,
                                                        int tiles, const bf16* __restrict__ hidden,
                                                        const bf16* __restrict__ wte, const int32_t* __restrict__ tgt,
-                                                       int V, int C, const int* __restrict__ count, float scale,
-                                                       float* __restrict__ row_loss) {
+                                                       int V, int C, int ig, const int* __restrict__ count,
+                                                       float scale, float* __restrict__ row_loss) {
   extern __shared__ float shift[];  // [tiles]: mx_t - lse, then scratch
   __shared__ float red[256 / 64];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(256) void ce_apply_kernel(bf16* __restrict__ y, con
   const float lse = mx + log2f(sm) * LN2;
   for (int t = tid; t < tiles; t += 256) shift[t] = (st[t].x - lse) * LOG2E;
   const int t = tgt[r];
-  const bool valid = target_valid(t, V);
+  const bool valid = target_valid(t, V, ig);
   float zt = 0.f;
   if (valid) {
     const bf16* h = hidden + (int64_t)r * C;
@@ -229,19 +232,20 @@ __global__ __launch_bounds__(256) void ce_apply_kernel(bf16* __restrict__ y, con
 }
 
 hipError_t launch_ce_apply(const Launch& L, bf16* y, const float2* stats, const bf16* hidden, const bf16* wte,
-                           const int32_t* tgt, int rows, int V, int C, const int* count, float scale,
-                           float* row_loss) {
+                           const int32_t* tgt, int rows, int V, int C, int ignore_index, const int* count,
+                           float scale, float* row_loss) {
   const int tiles = ce_stat_tiles(V);
   prof_begin(L);
-  ce_apply_kernel<<<rows, 256, tiles * sizeof(float), L.stream>>>(y, stats, tiles, hidden, wte, tgt, V, C, count,
-                                                                   scale, row_loss);
+  ce_apply_kernel<<<rows, 256, tiles * sizeof(float), L.stream>>>(y, stats, tiles, hidden, wte, tgt, V, C,
+                                                                   ignore_index, count, scale, row_loss);
   prof_end(L);
   return hipGetLastError();
 }
 
-hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int* count, int* flag) {
+hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int ignore_index, int* count,
+                                int* flag) {
   prof_begin(L);
-  count_targets_kernel<<<1, 1024, 0, L.stream>>>(tgt, n, V, count, flag);
+  count_targets_kernel<<<1, 1024, 0, L.stream>>>(tgt, n, V, ignore_index, count, flag);
   prof_end(L);
   return hipGetLastError();
 }
@@ -253,11 +257,11 @@ hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, 
   prof_begin(L);
   const bool vec = sizeof(LT) == 4 && V % 4 == 0 && ld_logits % 4 == 0 && ld_d % 4 == 0;
   if (vec)
-    ce_rows_kernel<LT, DT, true><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, count, scale,
-                                                             row_loss);
+    ce_rows_kernel<LT, DT, true><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, -1, count,
+                                                             scale, row_loss);
   else
-    ce_rows_kernel<LT, DT, false><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, count, scale,
-                                                              row_loss);
+    ce_rows_kernel<LT, DT, false><<<rows, 256, 0, L.stream>>>(logits, ld_logits, dlogits, ld_d, tgt, V, -1, count,
+                                                              scale, row_loss);
   prof_end(L);
   return hipGetLastError();
 }

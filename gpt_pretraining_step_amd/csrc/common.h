@@ -104,7 +104,14 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum 
 int gemm_grouped_units(const gpt2_gemm_args* a, int n);
 size_t gemm_grouped_table_bytes(int n, int units);
 void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, int units, void* host);
-hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units);
+// K_all > 0: every product reduces over K_all (the table's own K values and
+// splits are kept otherwise).
+hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units, int K_all = 0);
+// Two bf16 ACCUMULATE products in one launch: a0 with A K-major and B
+// K-slow, a1 with both K-slow (the lm_head's dZ and dW products of one row
+// chunk); each may be split in K (atomic adds), as a plan of the launch's
+// span decides.
+hipError_t launch_gemm_pair(const Launch& L, const gpt2_gemm_args& a0, const gpt2_gemm_args& a1);
 hipError_t launch_colsum(const Launch& L, const void* y, int y_bf16, int M, int N, int64_t ld, float* db);
 
 hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y,
@@ -143,7 +150,10 @@ hipError_t launch_embed_bwd(const Launch& L, const int32_t* tok, const float* dr
                             int T, int C, int V, const int32_t* seg);
 
 // Cross-entropy helpers for the chunked lm_head.
-hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int* count, int* flag);
+// count = number of targets in [0, V) other than ignore_index (the fp32 row
+// pass ignores -1).
+hipError_t launch_count_targets(const Launch& L, const int32_t* tgt, int n, int V, int ignore_index, int* count,
+                                int* flag);
 template <typename LT, typename DT>
 hipError_t launch_ce_rows(const Launch& L, const LT* logits, int64_t ld_logits, DT* dlogits, int64_t ld_d,
                           const int32_t* tgt, int rows, int V, const int* count, float scale, float* loss_sum,
@@ -159,14 +169,17 @@ inline int ce_stat_tiles(int V) { return (V + kCeTile - 1) / kCeTile; }
 hipError_t launch_gemm_ce_stats(const Launch& L, const bf16* hidden, const bf16* wte, bf16* y, float2* stats, int M,
                                 int V, int C);
 hipError_t launch_ce_apply(const Launch& L, bf16* y, const float2* stats, const bf16* hidden, const bf16* wte,
-                           const int32_t* tgt, int rows, int V, int C, const int* count, float scale,
-                           float* row_loss);
+                           const int32_t* tgt, int rows, int V, int C, int ignore_index, const int* count,
+                           float scale, float* row_loss);
 
 // Optimizer.
 hipError_t launch_sumsq_partials(const Launch& L, const float* g, size_t n, float* partials, int nparts);
-hipError_t launch_adamw(const Launch& L, float* p, const float* g, float* m, float* v, bf16* shadow, size_t n,
-                        size_t decay_end, const float* partials, int nparts, float lr, float b1, float b2,
-                        float eps, float wd, float max_norm, float bc1, float bc2, float* norm_out, int* flag);
+// The norm of the partials and, when it is finite, ++step[0] and the update
+// scalars sc[4] (one block, on Lprep), then the update pass (on L).
+hipError_t launch_adamw(const Launch& L, const Launch& Lprep, float* p, const float* g, float* m, float* v,
+                        bf16* shadow, size_t n, size_t decay_end, const float* partials, int nparts, float lr,
+                        float b1, float b2, float eps, float wd, float max_norm, int64_t* step, float* sc,
+                        float* norm_out, int* flag);
 hipError_t launch_fill_f32(const Launch& L, float* p, size_t n, float value);
 hipError_t launch_fill_i32(const Launch& L, int* p, size_t n, int value);
 hipError_t launch_to_bf16(const Launch& L, const float* src, bf16* dst, size_t n);

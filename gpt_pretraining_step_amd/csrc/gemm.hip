@@ -15,6 +15,8 @@
 
 #include <algorithm>
 #include <cstring>
+#include <functional>
+#include <vector>
 
 namespace g2 {
 
@@ -356,14 +358,85 @@ void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, 
   for (size_t k = 0; k < halves.size(); ++k) unit_map[W + k] = halves[k];
 }
 
-hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units) {
+hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units, int K_all) {
   const char* d = static_cast<const char*>(d_table);
   GemmGroups t;
   t.p = reinterpret_cast<const GemmP*>(d);
   t.unit_map = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)));
   prof_begin(L);
   gemm2_grouped_kernel<kGroupTile, kGroupTile, 64, 2, 4, 2, false, false, GPT2_EPI_ACCUMULATE, false, false, false>
-      <<<units, 512, 0, L.stream>>>(t);
+      <<<units, 512, 0, L.stream>>>(t, K_all);
+  prof_end(L);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ product pairs
+//
+// Two accumulating products of the lm_head backward for one row chunk, in
+// one launch: dZ += dlogits W (A K-major, B K-slow; few output tiles, K = V)
+// and dW += dlogits^T Z (both K-slow; many tiles, K = the chunk's rows).  The
+// split counts come from a list-scheduling estimate of the launch: units
+// are handed in block order to the earliest-free of the 256 CUs, a unit
+// costing its K steps plus an epilogue (twice as long when it adds
+// atomically), and the plan with the shortest estimated span wins.
+
+namespace {
+constexpr int kPairTile = 256;
+struct PairPlan {
+  int s0 = 1, s1 = 1;
+  double span = 0.0;
+};
+double pair_span(int64_t u0, double c0, int64_t u1, double c1) {
+  // in-order list scheduling over kUnits CUs: each unit starts on the CU
+  // that frees up first
+  std::vector<double> load(kUnits, 0.0);  // a min-heap of CU finish times
+  std::make_heap(load.begin(), load.end(), std::greater<double>());
+  for (int64_t i = 0; i < u0 + u1; ++i) {
+    std::pop_heap(load.begin(), load.end(), std::greater<double>());
+    load.back() += i < u0 ? c0 : c1;
+    std::push_heap(load.begin(), load.end(), std::greater<double>());
+  }
+  return *std::max_element(load.begin(), load.end());
+}
+PairPlan plan_pair(const gpt2_gemm_args& a0, const gpt2_gemm_args& a1) {
+  const int64_t t0 = (int64_t)((a0.M + kPairTile - 1) / kPairTile) * ((a0.N + kPairTile - 1) / kPairTile);
+  const int64_t t1 = (int64_t)((a1.M + kPairTile - 1) / kPairTile) * ((a1.N + kPairTile - 1) / kPairTile);
+  const int k0 = (a0.K + 63) / 64, k1 = (a1.K + 63) / 64;
+  constexpr double EPI = 4.0;  // epilogue of a 256x256 float32 read-modify-write, in K steps
+  PairPlan best;
+  best.span = 1e300;
+  for (int s0 = 1; s0 <= 64 && (s0 == 1 || k0 / s0 >= 8); ++s0)
+    for (int s1 = 1; s1 <= 4 && (s1 == 1 || k1 / s1 >= 8); ++s1) {
+      const double c0 = (k0 + s0 - 1) / s0 + (s0 > 1 ? 2 * EPI : EPI);
+      const double c1 = (k1 + s1 - 1) / s1 + (s1 > 1 ? 2 * EPI : EPI);
+      const double span = pair_span(t0 * s0, c0, t1 * s1, c1);
+      if (span < 0.99 * best.span) {
+        best.s0 = s0;
+        best.s1 = s1;
+        best.span = span;
+      }
+    }
+  return best;
+}
+GemmP pair_params(const gpt2_gemm_args& a, int splits) {
+  GemmP p = make_params(a);
+  p.tiles_m = (a.M + kPairTile - 1) / kPairTile;
+  p.tiles_n = (a.N + kPairTile - 1) / kPairTile;
+  p.k_per_split = (a.K + splits * 64 - 1) / (splits * 64) * 64;
+  p.splits = (a.K + p.k_per_split - 1) / p.k_per_split;
+  return p;
+}
+}  // namespace
+
+hipError_t launch_gemm_pair(const Launch& L, const gpt2_gemm_args& a0, const gpt2_gemm_args& a1) {
+  if (!a0.a_kmajor || a0.b_kmajor || a1.a_kmajor || a1.b_kmajor) return hipErrorInvalidValue;
+  const PairPlan pl = plan_pair(a0, a1);
+  const GemmP p0 = pair_params(a0, pl.s0), p1 = pair_params(a1, pl.s1);
+  const int units0 = p0.tiles_m * p0.tiles_n * p0.splits;
+  const int units1 = p1.tiles_m * p1.tiles_n * p1.splits;
+  prof_begin(L);
+  gemm2_pair_kernel<kPairTile, kPairTile, 64, 2, 4, true, false, false, false>
+      <<<units0 + units1, 512, 0, L.stream>>>(p0, p1, units0);
   prof_end(L);
   return hipGetLastError();
 }

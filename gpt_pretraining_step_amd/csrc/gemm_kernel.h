@@ -827,9 +827,22 @@ union GV8 {
 
 // One block's unit of a product: its output tile (and K split), main loop
 // and epilogue.
+// The two LDS stages of a block: (BM + BN) * BK bf16 elements each.  They are
+// two distinct LDS objects, declared by the kernel and passed down (a kernel
+// that runs units of several operand layouts shares them among those), and
+// the K loop is unrolled by two, so every copy and every read names its stage
+// statically.  The compiler then sees that a copy into one stage cannot
+// alias reads of the other and adds no wait for it; with one object (or a
+// stage picked at run time) it must assume the transposing reads alias every
+// copy in flight and drains the next step's copy (s_waitcnt vmcnt(0)) before
+// computing the current step.
+#define G2_STAGES(BM, BN, BK)                                      \
+  __shared__ __attribute__((aligned(16))) bf16 lds0[((BM) + (BN)) * (BK)]; \
+  __shared__ __attribute__((aligned(16))) bf16 lds1[((BM) + (BN)) * (BK)]
+
 template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
           bool ATOMIC, bool SWAP>
-__device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
+__device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit, bf16* lds0, bf16* lds1) {
   constexpr int NW = WGM * WGN;
   constexpr int NT = 64 * NW;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -837,15 +850,6 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
   constexpr int STAGE = (BM + BN) * BK;  // elements per stage
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(STAGES == 2, "two LDS stages");
-  // The two stages are two distinct LDS objects and the K loop is unrolled
-  // by two, so every copy and every read names its stage statically.  The
-  // compiler then sees that a copy into one stage cannot alias reads of the
-  // other and adds no wait for it; with one object (or a stage picked at run
-  // time) it must assume the transposing reads alias every copy in flight
-  // and drains the next step's copy (s_waitcnt vmcnt(0)) before computing
-  // the current step.
-  __shared__ __attribute__((aligned(16))) bf16 lds0[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 lds1[STAGE];
 
   int tm, tn, split;
   tile_of_unit(p, unit, tm, tn, split);
@@ -1072,13 +1076,18 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit) {
 template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
           bool ATOMIC, bool SWAP>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
-  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, xcd_remap(blockIdx.x, gridDim.x));
+  G2_STAGES(BM, BN, BK);
+  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, xcd_remap(blockIdx.x, gridDim.x),
+                                                                               lds0, lds1);
 }
 
 // Several independent products in one launch.  Block b runs unit
 // unit_map[b] & 0xffff of product unit_map[b] >> 16 (the host orders the
 // units: blocks go to the XCDs round-robin in index order).  A product with
-// splits > 1 adds its partial sums atomically (ACCUMULATE).
+// splits > 1 adds its partial sums atomically (ACCUMULATE).  K_all > 0
+// replaces every product's K (all products of one launch reduce over the
+// same tokens), so one table serves every token count: a product split in
+// two takes halves of ceil(K_all / 128) * 64.
 struct GemmGroups {
   const GemmP* __restrict__ p;
   const int* __restrict__ unit_map;
@@ -1086,10 +1095,36 @@ struct GemmGroups {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool A_K, bool B_K, int EPI, bool OUT_BF16,
           bool ATOMIC, bool SWAP>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_grouped_kernel(GemmGroups t) {
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_grouped_kernel(GemmGroups t, int K_all) {
+  G2_STAGES(BM, BN, BK);
   const int e = t.unit_map[blockIdx.x];
-  const GemmP p = t.p[e >> 16];
-  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, e & 0xffff);
+  GemmP p = t.p[e >> 16];
+  if (K_all > 0) {
+    p.K = K_all;
+    p.k_per_split = p.splits > 1 ? (K_all + p.splits * BK - 1) / (p.splits * BK) * BK : K_all;
+  }
+  gemm2_unit<BM, BN, BK, WGM, WGN, STAGES, A_K, B_K, EPI, OUT_BF16, ATOMIC, SWAP>(p, e & 0xffff, lds0, lds1);
+}
+
+// Two accumulating products of different operand layouts in one launch,
+// their parameters passed by value: blocks [0, units0) run product 0 (layout
+// A_K0, B_K0), the others product 1 (A_K1, B_K1).  Within each product the
+// units are spread XCD-aware (when both unit counts are multiples of 8, each
+// XCD takes a contiguous run of each product).  A product with splits > 1
+// adds its partial sums atomically.
+template <int BM, int BN, int BK, int WGM, int WGN, bool A_K0, bool B_K0, bool A_K1, bool B_K1>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_pair_kernel(GemmP p0, GemmP p1, int units0) {
+  G2_STAGES(BM, BN, BK);
+  const int b = blockIdx.x;
+  if (b < units0) {
+    gemm2_unit<BM, BN, BK, WGM, WGN, 2, A_K0, B_K0, GPT2_EPI_ACCUMULATE, false, false, false>(
+        p0, xcd_remap(b, units0), lds0, lds1);
+  } else {
+    const int n1 = (int)gridDim.x - units0;
+    const int u = b - units0;
+    gemm2_unit<BM, BN, BK, WGM, WGN, 2, A_K1, B_K1, GPT2_EPI_ACCUMULATE, false, false, false>(
+        p1, (units0 & 7) == 0 ? xcd_remap(u, n1) : u, lds0, lds1);
+  }
 }
 
 }  // namespace g2

@@ -6,9 +6,12 @@
 // tensors of dim >= 2).  The update is the documented decoupled-decay AdamW
 // with bias correction; the clip coefficient is min(1, max_norm/(norm+1e-6)).
 // Two passes over the gradients: per-block partial sums of squares, then one
-// fused pass in which every block re-reduces the partials in the same fixed
-// order (so every block sees the same norm) and updates p, m, v and the bf16
-// shadow.  HBM traffic: 4 B/param for the norm, 30 B/param for the update.
+// fused pass that updates p, m, v and the bf16 shadow.  Between them one
+// block reduces the partials in a fixed order to the norm and, when it is
+// finite, advances the step counter (kept on the device, so a skipped step
+// leaves it unchanged) and writes the clip coefficient and the two bias
+// corrections for the update pass.  HBM traffic: 4 B/param for the norm, 30
+// B/param for the update.
 //
 // Init ("How I trained my own GPT-2 124M on FineWeb-Edu" section 7): normals
 // from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) through the
@@ -46,12 +49,14 @@ __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v
   p -= (lr / bc1) * m / denom;
 }
 
-__global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
-                                                    float* __restrict__ m, float* __restrict__ v,
-                                                    bf16* __restrict__ shadow, size_t n, size_t decay_end,
-                                                    const float* __restrict__ partials, int nparts, float lr, float b1,
-                                                    float b2, float eps, float wd, float max_norm, float bc1,
-                                                    float bc2, float* norm_out, int* flag) {
+// One block: norm = sqrt(sum of the partials), reduced in a fixed order.
+// Finite: t = ++step[0]; sc = (clip coefficient, 1 - b1^t, sqrt(1 - b2^t),
+// 1).  Not finite: GPT2_ERR_NONFINITE is raised and sc[3] = 0, so the update
+// pass changes nothing and the step counter stays.
+__global__ __launch_bounds__(256) void adamw_prep_kernel(const float* __restrict__ partials, int nparts, float b1,
+                                                         float b2, float max_norm, int64_t* __restrict__ step,
+                                                         float* __restrict__ sc, float* __restrict__ norm_out,
+                                                         int* flag) {
   __shared__ float red[256];
   float s = 0.f;
   for (int i = threadIdx.x; i < nparts; i += 256) s += partials[i];
@@ -61,14 +66,29 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
     if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
     __syncthreads();
   }
+  if (threadIdx.x != 0) return;
   const float norm = sqrtf(red[0]);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (norm_out) norm_out[0] = norm;
-    if (!isfinite(norm)) raise_flag(flag, GPT2_ERR_NONFINITE);
+  norm_out[0] = norm;
+  if (!isfinite(norm)) {
+    raise_flag(flag, GPT2_ERR_NONFINITE);
+    sc[3] = 0.f;
+    return;
   }
-  if (!isfinite(norm)) return;
-  const float coef = fminf(1.f, max_norm / (norm + 1e-6f));
-  const float bc2s = sqrtf(bc2);
+  const int64_t t = step[0] + 1;
+  step[0] = t;
+  sc[0] = fminf(1.f, max_norm / (norm + 1e-6f));
+  sc[1] = (float)(1.0 - pow((double)b1, (double)t));
+  sc[2] = sqrtf((float)(1.0 - pow((double)b2, (double)t)));
+  sc[3] = 1.f;
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    bf16* __restrict__ shadow, size_t n, size_t decay_end,
+                                                    const float* __restrict__ sc, float lr, float b1, float b2,
+                                                    float eps, float wd) {
+  if (sc[3] == 0.f) return;
+  const float coef = sc[0], bc1 = sc[1], bc2s = sc[2];
   const float dec = 1.f - lr * wd;
   const size_t n4 = n / 4;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
@@ -174,12 +194,18 @@ hipError_t launch_sumsq_partials(const Launch& L, const float* g, size_t n, floa
   return hipGetLastError();
 }
 
-hipError_t launch_adamw(const Launch& L, float* p, const float* g, float* m, float* v, bf16* shadow, size_t n,
-                        size_t decay_end, const float* partials, int nparts, float lr, float b1, float b2, float eps,
-                        float wd, float max_norm, float bc1, float bc2, float* norm_out, int* flag) {
+hipError_t launch_adamw(const Launch& L, const Launch& Lprep, float* p, const float* g, float* m, float* v,
+                        bf16* shadow, size_t n, size_t decay_end, const float* partials, int nparts, float lr,
+                        float b1, float b2, float eps, float wd, float max_norm, int64_t* step, float* sc,
+                        float* norm_out, int* flag) {
+  prof_begin(Lprep);
+  adamw_prep_kernel<<<1, 256, 0, Lprep.stream>>>(partials, nparts, b1, b2, max_norm, step, sc, norm_out, flag);
+  prof_end(Lprep);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   prof_begin(L);
-  adamw_kernel<<<grid_for(n / 4, 256, 2048), 256, 0, L.stream>>>(p, g, m, v, shadow, n, decay_end, partials, nparts, lr,
-                                                                  b1, b2, eps, wd, max_norm, bc1, bc2, norm_out, flag);
+  adamw_kernel<<<grid_for(n / 4, 256, 2048), 256, 0, L.stream>>>(p, g, m, v, shadow, n, decay_end, sc, lr, b1, b2, eps,
+                                                                  wd);
   prof_end(L);
   return hipGetLastError();
 }

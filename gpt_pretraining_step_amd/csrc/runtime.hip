@@ -106,7 +106,13 @@ namespace {
 
 constexpr size_t kAlignElems = 64;  // 256 B for float32 tensors
 constexpr int kNormParts = 1024;
-constexpr int kCeChunk = 4096;
+constexpr int kCeChunk = 4096;  // rows per lm_head chunk, float32 mode
+// Rows per lm_head chunk in bf16 mode: the bf16 logit buffer holds one chunk
+// (8192 x 50304 x 2 B = 824 MB for GPT-2), never the whole micro-batch.
+#ifndef GPT2_CE_CHUNK_ROWS
+#define GPT2_CE_CHUNK_ROWS 8192
+#endif
+constexpr int kCeChunkBf16 = GPT2_CE_CHUNK_ROWS;
 
 struct Desc {
   std::string name;
@@ -258,14 +264,16 @@ struct Layout {
   // scratch
   size_t dR = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
   size_t ce_stats = 0, rope = 0, seg = 0;
-  size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, scratch_bytes = 0;
+  size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, step = 0, adam_sc = 0, scratch_bytes = 0;
   // bf16: the first operands of the weight-gradient products, kept per layer
   // until the products run together at the end of the backward: dRbS[2l+1]
   // the residual gradient entering layer l's MLP branch, dRbS[2l] its
   // attention branch; dUL[l], dQKVL[l] the gradients of the fc and qkv
   // outputs; dw_table the group table of that launch
   std::vector<size_t> dRbS, dUL, dQKVL;
-  size_t dw_table = 0, dw_table_bytes = 0;
+  // two copies of that table: [0] without K splits (fewer than 2048
+  // tokens), [1] with the split tail (see run_dw)
+  size_t dw_table[2] = {0, 0}, dw_table_bytes = 0;
 };
 
 struct Bump {
@@ -316,6 +324,8 @@ Layout build_layout(const gpt2_config& c) {
   y.count = s.take(256);
   y.loss = s.take(256);
   y.norm = s.take(256);
+  y.step = s.take(256);     // the optimizer step counter (int64)
+  y.adam_sc = s.take(256);  // clip coefficient and bias corrections of the step
   y.parts = s.take(kNormParts * 4);
   y.dR = s.take(rows * C * 4);
   y.dA = s.take(rows * C * 4);
@@ -333,29 +343,23 @@ Layout build_layout(const gpt2_config& c) {
       y.dUL.push_back(s.take(rows * FU * 2));
       y.dQKVL.push_back(s.take(rows * NQKV * 2));
     }
-    // the products of that launch: dwte (lm_head), then four per layer
-    std::vector<gpt2_gemm_args> dw(4 * (size_t)L + 1);
-    dw[0].M = (int)V;
-    dw[0].N = (int)C;
+    // the products of that launch: four per layer; a table holds at most
+    // two units per output tile (every product split in two)
+    int tiles = 0;
     for (int l = 0; l < L; ++l) {
       const int mn[4][2] = {{(int)C, (int)F}, {(int)FU, (int)C}, {(int)C, (int)C}, {(int)NQKV, (int)C}};
-      for (int k = 0; k < 4; ++k) {
-        dw[4 * l + k + 1].M = mn[k][0];
-        dw[4 * l + k + 1].N = mn[k][1];
-      }
+      for (int k = 0; k < 4; ++k) tiles += ((mn[k][0] + 255) / 256) * ((mn[k][1] + 255) / 256);
     }
-    // sized at the largest token count (K): splitting, hence the unit count,
-    // only grows with K
-    for (auto& a : dw) a.K = (int)rows;
-    y.dw_table_bytes = gemm_grouped_table_bytes((int)dw.size(), gemm_grouped_units(dw.data(), (int)dw.size()));
-    y.dw_table = s.take(y.dw_table_bytes);
+    y.dw_table_bytes = gemm_grouped_table_bytes(4 * L, 2 * tiles);
+    y.dw_table[0] = s.take(y.dw_table_bytes);
+    y.dw_table[1] = s.take(y.dw_table_bytes);
   }
   if (c.precision == GPT2_PRECISION_BF16) {
-    // fused lm_head + cross-entropy over all rows at once: bf16 logits (then
-    // dlogits, in place) and per-tile softmax statistics
-    y.chunk = (int)rows;
-    y.dlogits = s.take(rows * V * 2);
-    y.ce_stats = s.take(rows * (size_t)ce_stat_tiles((int)V) * sizeof(float2));
+    // fused lm_head + cross-entropy, one row chunk at a time: the chunk's
+    // bf16 logits (then dlogits, in place) and per-tile softmax statistics
+    y.chunk = (int)std::min<size_t>(rows, kCeChunkBf16);
+    y.dlogits = s.take((size_t)y.chunk * V * 2);
+    y.ce_stats = s.take((size_t)y.chunk * ce_stat_tiles((int)V) * sizeof(float2));
   } else {
     y.logits = s.take((size_t)y.chunk * V * 4);
     y.dlogits = s.take((size_t)y.chunk * V * y.es);
@@ -373,9 +377,13 @@ struct gpt2_ctx {
   Layout lay;
   gpt2_buffers buf;
   hipStream_t stream;
-  int64_t t = 0;
   Prof prof;
-  std::vector<char> dw_image;  // the group table last copied to the device
+  // the weight-gradient launch's two table images (see run_dw), kept for
+  // the context's life: their device copies are made from them
+  // asynchronously, once
+  std::vector<char> dw_image[2];
+  std::vector<gpt2_gemm_args> dw_sig;  // the products they describe
+  int dw_units[2] = {0, 0};
   hipStream_t cap = nullptr;    // capture stream of gpt2_graph_capture
   hipGraphExec_t graph = nullptr;
   int doc_eot = -1;  // >= 0: packed windows under the document mask of this EOT id
@@ -395,7 +403,16 @@ struct gpt2_ctx {
   template <typename T = void>
   T* scr(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(buf.scratch) + off); }
   int* flag() const { return scr<int>(lay.flag); }
+  int64_t* step() const { return scr<int64_t>(lay.step); }
 };
+
+// step counter <- t (two 32-bit halves, little-endian), on the stream
+static hipError_t set_step_dev(gpt2_ctx* c, int64_t t) {
+  int* w = reinterpret_cast<int*>(c->step());
+  hipError_t e = launch_fill_i32(c->at("fill"), w, 1, (int)(uint32_t)((uint64_t)t & 0xffffffffu));
+  if (e == hipSuccess) e = launch_fill_i32(c->at("fill"), w + 1, 1, (int)(uint32_t)((uint64_t)t >> 32));
+  return e;
+}
 
 // --------------------------------------------------------------- helpers
 
@@ -478,60 +495,93 @@ static void queue_dw(gpt2_ctx* c, DwQueue& q, const void* dy, int M, int N, cons
   q.row_sum.push_back(bi >= 0 ? c->Gr(bi) : nullptr);
 }
 
-static hipError_t run_dw(gpt2_ctx* c, DwQueue& q) {
+// The grouped launch reads its products from a table in device memory.  All
+// products reduce over the micro-step's tokens, and the kernel takes that
+// count (K) as an argument, so the table depends on the token count only
+// through the split plan: without splits below 2048 tokens, with the split
+// tail from 2048 on.  Both tables are built from the first queue and copied
+// once, asynchronously on the stream (their host images live as long as
+// the context); later calls only check that the queue is the same.
+static hipError_t run_dw(gpt2_ctx* c, DwQueue& q, int tokens) {
   const int n = (int)q.a.size();
-  const int units = gemm_grouped_units(q.a.data(), n);
-  const size_t bytes = gemm_grouped_table_bytes(n, units);
-  if (units < 1 || bytes > c->lay.dw_table_bytes) return hipErrorInvalidValue;
-  std::vector<char> image(bytes);
-  gemm_grouped_table(q.a.data(), q.row_sum.data(), n, units, image.data());
-  void* d_table = c->scr(c->lay.dw_table);
-  if (image != c->dw_image) {
-    // only when the token count changes: no earlier launch may still read
-    // the table.  Not while the stream is being captured into a graph (a
-    // graph replays the table it was captured with): the capturing call
-    // fails instead
+  std::vector<gpt2_gemm_args> sig = q.a;
+  for (auto& a : sig) a.K = 0;
+  if (c->dw_sig.empty()) {
+    // not while the stream is being captured into a graph (the copies
+    // would be recorded with it): the capturing call fails instead
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(c->stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
       return hipErrorStreamCaptureUnsupported;
-    hipError_t e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipMemcpy(d_table, image.data(), bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return e;
-    c->dw_image.swap(image);
+    for (int pl = 0; pl < 2; ++pl) {
+      std::vector<gpt2_gemm_args> a = q.a;
+      for (auto& x : a) x.K = pl ? (1 << 20) : 1;  // no split below 2048 tokens; the split tail above
+      const int units = gemm_grouped_units(a.data(), n);
+      const size_t bytes = gemm_grouped_table_bytes(n, units);
+      if (units < 1 || bytes > c->lay.dw_table_bytes) return hipErrorInvalidValue;
+      c->dw_image[pl].assign(bytes, 0);
+      gemm_grouped_table(a.data(), q.row_sum.data(), n, units, c->dw_image[pl].data());
+      c->dw_units[pl] = units;
+      hipError_t e = hipMemcpyAsync(c->scr(c->lay.dw_table[pl]), c->dw_image[pl].data(), bytes,
+                                    hipMemcpyHostToDevice, c->stream);
+      if (e != hipSuccess) return e;
+    }
+    c->dw_sig = sig;
+  } else {
+    // the buffers behind the products never change
+    auto same = [](const gpt2_gemm_args& a, const gpt2_gemm_args& b) {
+      return a.A == b.A && a.B == b.B && a.C == b.C && a.M == b.M && a.N == b.N && a.lda == b.lda &&
+             a.ldb == b.ldb && a.ldc == b.ldc && a.alpha == b.alpha;
+    };
+    if (sig.size() != c->dw_sig.size()) return hipErrorInvalidValue;
+    for (size_t i = 0; i < sig.size(); ++i)
+      if (!same(sig[i], c->dw_sig[i])) return hipErrorInvalidValue;
   }
-  return launch_gemm_grouped(c->at("gemm.dw"), d_table, n, units);
+  const int pl = tokens >= 2048 ? 1 : 0;
+  return launch_gemm_grouped(c->at("gemm.dw"), c->scr(c->lay.dw_table[pl]), n, c->dw_units[pl], tokens);
 }
 
-// Tied lm_head + cross-entropy, bf16, all rows at once: the statistics
-// product (logit offsets + per-tile softmax statistics), the row pass that
-// turns them into the row losses and dlogits in place, then dZ += dlogits
-// wte and dwte += dlogits^T Z.  dZ must hold zeros (float32 [M, C]).
-static hipError_t lmhead_ce_bf16(gpt2_ctx* c, const int32_t* tgt, int M, const int* count, float scale,
-                                 float* rowloss, float* dZ, DwQueue& q) {
-  const Layout& y = c->lay;
-  const int C = c->cfg.n_embd, V = c->cfg.vocab_size, dt = c->cfg.precision;
-  bf16* dlog = c->scr<bf16>(y.dlogits);
-  float2* stats = c->scr<float2>(y.ce_stats);
-  const bf16* Zb = c->act<bf16>(y.Z);
-  const bf16* Wb = static_cast<const bf16*>(c->W(c->tab.wte));
-  hipError_t e = launch_gemm_ce_stats(c->at("gemm.lm_head"), Zb, Wb, dlog, stats, M, V, C);
-  if (e != hipSuccess) return e;
-  e = launch_ce_apply(c->at("ce.rows"), dlog, stats, Zb, Wb, tgt, M, V, C, count, scale, rowloss);
-  if (e != hipSuccess) return e;
-  {  // dZ += dlogits wte
-    gpt2_gemm_args a = gemm_base(dt);
-    a.M = M; a.N = C; a.K = V;
-    a.a_kmajor = 1; a.b_kmajor = 0;
-    a.lda = V; a.ldb = C; a.ldc = C;
-    a.A = dlog; a.B = Wb; a.C = dZ;
-    a.epilogue = GPT2_EPI_ACCUMULATE;
-    e = launch_gemm(c->at("gemm.lm_head_dx"), a);
+// Tied lm_head + cross-entropy, bf16, one chunk of rows at a time, so the
+// logits are never held for the whole batch: per chunk the statistics
+// product (bf16 logit offsets + per-tile softmax statistics), the row pass
+// that turns them into the row losses and the chunk's dlogits in place,
+// then dZ += dlogits wte and dW += dlogits^T Z in one launch, before the
+// chunk buffer is reused.  count holds the number of valid targets of all M
+// rows; dZ (float32 [M, C]) must hold zeros.
+static hipError_t lmhead_ce_chunked(Prof* prof, hipStream_t st, const bf16* Z, const bf16* W, const int32_t* tgt,
+                                    int M, int C, int V, int ig, const int* count, float scale, float* rowloss,
+                                    float* dZ, float* dW, bf16* dlog, float2* stats, int chunk) {
+  for (int r0 = 0; r0 < M; r0 += chunk) {
+    const int rows = std::min(chunk, M - r0);
+    const bf16* Zc = Z + (size_t)r0 * C;
+    hipError_t e = launch_gemm_ce_stats(Launch{st, prof, "gemm.lm_head"}, Zc, W, dlog, stats, rows, V, C);
+    if (e != hipSuccess) return e;
+    e = launch_ce_apply(Launch{st, prof, "ce.rows"}, dlog, stats, Zc, W, tgt + r0, rows, V, C, ig, count, scale,
+                        rowloss + r0);
+    if (e != hipSuccess) return e;
+    gpt2_gemm_args dz = gemm_base(GPT2_PRECISION_BF16);  // dZ_c += dlogits_c wte
+    dz.M = rows; dz.N = C; dz.K = V;
+    dz.a_kmajor = 1; dz.b_kmajor = 0;
+    dz.lda = V; dz.ldb = C; dz.ldc = C;
+    dz.A = dlog; dz.B = W; dz.C = dZ + (size_t)r0 * C;
+    dz.epilogue = GPT2_EPI_ACCUMULATE;
+    gpt2_gemm_args dw = gemm_base(GPT2_PRECISION_BF16);  // dW += dlogits_c^T Z_c
+    dw.M = V; dw.N = C; dw.K = rows;
+    dw.a_kmajor = 0; dw.b_kmajor = 0;
+    dw.lda = V; dw.ldb = C; dw.ldc = C;
+    dw.A = dlog; dw.B = Zc; dw.C = dW;
+    dw.epilogue = GPT2_EPI_ACCUMULATE;
+    e = launch_gemm_pair(Launch{st, prof, "gemm.lm_head_bwd"}, dz, dw);
     if (e != hipSuccess) return e;
   }
-  // dwte += dlogits^T Z: queued with the blocks' weight gradients (dlogits
-  // and Z stay untouched until they run)
-  queue_dw(c, q, dlog, M, V, Zb, C, c->tab.wte, -1);
-  return e;
+  return hipSuccess;
+}
+
+static hipError_t lmhead_ce_bf16(gpt2_ctx* c, const int32_t* tgt, int M, const int* count, float scale,
+                                 float* rowloss, float* dZ) {
+  const Layout& y = c->lay;
+  return lmhead_ce_chunked(&c->prof, c->stream, c->act<bf16>(y.Z), static_cast<const bf16*>(c->W(c->tab.wte)), tgt,
+                           M, c->cfg.n_embd, c->cfg.vocab_size, -1, count, scale, rowloss, dZ, c->Gr(c->tab.wte),
+                           c->scr<bf16>(y.dlogits), c->scr<float2>(y.ce_stats), y.chunk);
 }
 
 // ------------------------------------------------------------- the step
@@ -547,7 +597,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   int* count = c->scr<int>(y.count);
   float* rowloss = token_loss ? token_loss : c->scr<float>(y.rowloss);
 
-  HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, count, flag));
+  HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, -1, count, flag));
   const int32_t* seg = nullptr;
   if (c->doc_eot >= 0) {
     seg = c->scr<int32_t>(y.seg);
@@ -584,7 +634,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
   HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
   const size_t es = y.es;
   DwQueue q;  // bf16: weight-gradient products, run together after the backward
-  if (bf) HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ, q));
+  if (bf) HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ));
   for (int r0 = 0; !bf && r0 < M; r0 += y.chunk) {
     const int rows = std::min(y.chunk, M - r0);
     const char* z_c = c->act<char>(y.Z) + (size_t)r0 * C * es;
@@ -672,7 +722,7 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                                    c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1),
                                    c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)), M, C));
   }
-  if (bf) HIP_TRY(run_dw(c, q));
+  if (bf) HIP_TRY(run_dw(c, q, M));
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V, seg));
   return GPT2_OK;
 }
@@ -692,7 +742,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
   float2* rope = c->scr<float2>(y.rope);
 
   HIP_TRY(launch_rope_table(c->at("rope.table"), rope, T, 10000.0));
-  HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, count, flag));
+  HIP_TRY(launch_count_targets(c->at("ce.count"), tgt, M, V, -1, count, flag));
   // packed windows: the mask only.  q and k keep the rotation of position t
   // (not of t's place in its document): a rotation by t - start of both
   // differs from one by t by the same angle for every pair of tokens of a
@@ -745,7 +795,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
   float* dZ = c->scr<float>(y.dA);
   HIP_TRY(launch_fill_f32(c->at("fill"), dZ, (size_t)M * C, 0.f));
   DwQueue q;  // weight-gradient products, run together after the backward
-  HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ, q));
+  HIP_TRY(lmhead_ce_bf16(c, tgt, M, count, scale, rowloss, dZ));
   HIP_TRY(launch_ce_finish_n(c->at("ce.finish"), rowloss, M, count, loss, flag));
 
   // ---- backward
@@ -789,7 +839,7 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rin[l]), c->act<float>(y.rstd1[l]),
                                c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C));
   }
-  HIP_TRY(run_dw(c, q));
+  HIP_TRY(run_dw(c, q, M));
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V, seg));
   return GPT2_OK;
 }
@@ -853,8 +903,7 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_buffers* bufs, void* stream, 
   c->lay = build_layout(*cfg);
   c->buf = *bufs;
   c->stream = static_cast<hipStream_t>(stream);
-  c->t = 0;
-  if (launch_fill_i32(c->at("fill"), c->flag(), 1, GPT2_OK) != hipSuccess) {
+  if (launch_fill_i32(c->at("fill"), c->flag(), 1, GPT2_OK) != hipSuccess || set_step_dev(c, 0) != hipSuccess) {
     delete c;
     return GPT2_ERR_HIP;
   }
@@ -917,7 +966,7 @@ int gpt2_init_params(gpt2_ctx* c, uint64_t seed) {
   HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.grads), n, 0.f));
   HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.adam_m), n, 0.f));
   HIP_TRY(launch_fill_f32(c->at("fill"), static_cast<float*>(c->buf.adam_v), n, 0.f));
-  c->t = 0;
+  HIP_TRY(set_step_dev(c, 0));
   return gpt2_sync_shadow(c);
 }
 
@@ -979,31 +1028,29 @@ int gpt2_clip_adamw_step(gpt2_ctx* c, const gpt2_adamw* hp, float* d_grad_norm) 
   if (!(hp->lr >= 0.f) || !(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f) ||
       !(hp->eps > 0.f) || !(hp->max_norm > 0.f) || !isfinite(hp->weight_decay))
     return GPT2_ERR_ARG;
-  c->t += 1;
-  const double bc1 = 1.0 - pow((double)hp->beta1, (double)c->t);
-  const double bc2 = 1.0 - pow((double)hp->beta2, (double)c->t);
   const Layout& y = c->lay;
   float* parts = c->scr<float>(y.parts);
   float* norm = d_grad_norm ? d_grad_norm : c->scr<float>(y.norm);
   HIP_TRY(launch_sumsq_partials(c->at("opt.sumsq"), static_cast<const float*>(c->buf.grads), c->tab.n_elems, parts,
                                 kNormParts));
-  HIP_TRY(launch_adamw(c->at("opt.adamw"), static_cast<float*>(c->buf.params), static_cast<const float*>(c->buf.grads),
-                       static_cast<float*>(c->buf.adam_m), static_cast<float*>(c->buf.adam_v),
-                       c->bf() ? static_cast<bf16*>(c->buf.shadow) : nullptr, c->tab.n_elems, c->tab.decay_end, parts,
-                       kNormParts, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_norm, (float)bc1,
-                       (float)bc2, norm, c->flag()));
+  HIP_TRY(launch_adamw(c->at("opt.adamw"), c->at("opt.prep"), static_cast<float*>(c->buf.params),
+                       static_cast<const float*>(c->buf.grads), static_cast<float*>(c->buf.adam_m),
+                       static_cast<float*>(c->buf.adam_v), c->bf() ? static_cast<bf16*>(c->buf.shadow) : nullptr,
+                       c->tab.n_elems, c->tab.decay_end, parts, kNormParts, hp->lr, hp->beta1, hp->beta2, hp->eps,
+                       hp->weight_decay, hp->max_norm, c->step(), c->scr<float>(y.adam_sc), norm, c->flag()));
   return GPT2_OK;
 }
 
 int gpt2_get_step(gpt2_ctx* c, int64_t* t) {
   if (!c || !t) return GPT2_ERR_ARG;
-  *t = c->t;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+  if (hipMemcpy(t, c->step(), sizeof(int64_t), hipMemcpyDeviceToHost) != hipSuccess) return GPT2_ERR_HIP;
   return GPT2_OK;
 }
 
 int gpt2_set_step(gpt2_ctx* c, int64_t t) {
   if (!c || t < 0) return GPT2_ERR_ARG;
-  c->t = t;
+  HIP_TRY(set_step_dev(c, t));
   return GPT2_OK;
 }
 
@@ -1037,51 +1084,49 @@ const char* gpt2_strerror(int s) {
 
 // ---------------------------------------------------- isolated lm_head + CE
 
-size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V) {
-  if (M < 1 || C < 1 || V < 1) return 0;
+// scratch of gpt2_lmhead_ce: count, row losses, one chunk's bf16 logits and
+// tile statistics, dHidden in float32
+static size_t lmhead_scratch(int M, int C, int V, size_t* off) {
+  const int chunk = std::min(M, kCeChunkBf16);
   Bump s;
-  s.take(256);                                            // count
-  s.take((size_t)M * 4);                                  // row losses
-  s.take((size_t)M * V * 2);                              // bf16 logits, then dlogits
-  s.take((size_t)M * ce_stat_tiles(V) * sizeof(float2));  // per-tile softmax statistics
-  s.take((size_t)M * C * 4);                              // dhidden (float32 accumulation)
+  off[0] = s.take(256);                                               // count
+  off[1] = s.take((size_t)M * 4);                                     // row losses
+  off[2] = s.take((size_t)chunk * V * 2);                             // a chunk's logits, then dlogits
+  off[3] = s.take((size_t)chunk * ce_stat_tiles(V) * sizeof(float2));  // its per-tile softmax statistics
+  off[4] = s.take((size_t)M * C * 4);                                 // dhidden (float32 accumulation)
   return (s.off + 255) / 256 * 256;
 }
 
+size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V) {
+  if (M < 1 || C < 1 || V < 1) return 0;
+  size_t off[5];
+  return lmhead_scratch(M, C, V, off);
+}
+
 int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, const int32_t* d_targets, int M, int C,
-                   int V, float* d_loss, void* d_dhidden, float* d_dweight, void* d_scratch, int32_t* d_flag) {
+                   int V, int ignore_index, float* d_loss, void* d_dhidden, float* d_dweight, void* d_scratch,
+                   int32_t* d_flag) {
   if (!d_hidden || !d_weight || !d_targets || !d_loss || !d_dhidden || !d_dweight || !d_scratch) return GPT2_ERR_ARG;
   if (M < 1 || C < 8 || V < 8 || C % 8 || V % 8) return GPT2_ERR_SHAPE;
+  if (((uintptr_t)d_hidden | (uintptr_t)d_weight | (uintptr_t)d_dhidden | (uintptr_t)d_dweight |
+       (uintptr_t)d_scratch) & 15)
+    return GPT2_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Launch L{st, nullptr, ""};
-  Bump s;
+  size_t off[5];
+  lmhead_scratch(M, C, V, off);
   char* base = static_cast<char*>(d_scratch);
-  int* count = reinterpret_cast<int*>(base + s.take(256));
-  float* rowloss = reinterpret_cast<float*>(base + s.take((size_t)M * 4));
-  bf16* dlog = reinterpret_cast<bf16*>(base + s.take((size_t)M * V * 2));
-  float2* stats = reinterpret_cast<float2*>(base + s.take((size_t)M * ce_stat_tiles(V) * sizeof(float2)));
-  float* dh32 = reinterpret_cast<float*>(base + s.take((size_t)M * C * 4));
+  int* count = reinterpret_cast<int*>(base + off[0]);
+  float* rowloss = reinterpret_cast<float*>(base + off[1]);
+  bf16* dlog = reinterpret_cast<bf16*>(base + off[2]);
+  float2* stats = reinterpret_cast<float2*>(base + off[3]);
+  float* dh32 = reinterpret_cast<float*>(base + off[4]);
   int* flag = reinterpret_cast<int*>(d_flag);
-  const bf16* H = static_cast<const bf16*>(d_hidden);
-  const bf16* W = static_cast<const bf16*>(d_weight);
-  HIP_TRY(launch_count_targets(L, d_targets, M, V, count, flag));
+  HIP_TRY(launch_count_targets(L, d_targets, M, V, ignore_index, count, flag));
   HIP_TRY(launch_fill_f32(L, dh32, (size_t)M * C, 0.f));
-  HIP_TRY(launch_gemm_ce_stats(L, H, W, dlog, stats, M, V, C));
-  HIP_TRY(launch_ce_apply(L, dlog, stats, H, W, d_targets, M, V, C, count, 1.f, rowloss));
-  gpt2_gemm_args a = gemm_base(GPT2_PRECISION_BF16);
-  a.M = M; a.N = C; a.K = V;
-  a.a_kmajor = 1; a.b_kmajor = 0;
-  a.lda = V; a.ldb = C; a.ldc = C;
-  a.A = dlog; a.B = W; a.C = dh32;
-  a.epilogue = GPT2_EPI_ACCUMULATE;
-  HIP_TRY(launch_gemm(L, a));
-  a = gemm_base(GPT2_PRECISION_BF16);
-  a.M = V; a.N = C; a.K = M;
-  a.a_kmajor = 0; a.b_kmajor = 0;
-  a.lda = V; a.ldb = C; a.ldc = C;
-  a.A = dlog; a.B = H; a.C = d_dweight;
-  a.epilogue = GPT2_EPI_ACCUMULATE;
-  HIP_TRY(launch_gemm(L, a));
+  HIP_TRY(lmhead_ce_chunked(nullptr, st, static_cast<const bf16*>(d_hidden), static_cast<const bf16*>(d_weight),
+                            d_targets, M, C, V, ignore_index, count, 1.f, rowloss, dh32, d_dweight, dlog, stats,
+                            std::min(M, kCeChunkBf16)));
   HIP_TRY(launch_ce_finish_n(L, rowloss, M, count, d_loss, flag));
   HIP_TRY(launch_to_bf16(L, dh32, static_cast<bf16*>(d_dhidden), (size_t)M * C));
   return GPT2_OK;

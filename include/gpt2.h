@@ -15,8 +15,10 @@
  *    which must stay valid until gpt2_destroy.  Sizes come from
  *    gpt2_query_sizes.  Pointers named d_* are device pointers.
  *  - Streams: `stream` arguments are hipStream_t values passed as void*
- *    (NULL = the default stream).  Every call is asynchronous on its stream;
- *    only gpt2_get_status synchronises.
+ *    (NULL = the default stream).  Every call is asynchronous on its stream,
+ *    except the few whose comments say they synchronise: gpt2_get_status,
+ *    gpt2_get_step, gpt2_graph_capture, gpt2_op_gemm_grouped,
+ *    gpt2_profile_reset and gpt2_destroy.
  *  - Layouts: row-major.  Tokens and targets are int32 [B, T].  Linear
  *    weights are [out, in] (nn.Linear).  The parameter table (order, offsets,
  *    shapes) is given by gpt2_param_info.
@@ -215,7 +217,11 @@ int gpt2_zero_grad(gpt2_ctx* ctx);
  *   d_token_loss: optional device float [B, T], per-position loss (0 where
  *     the target is ignored).
  * The logits are never stored whole: the tied lm_head and the loss run over
- * row chunks. */
+ * chunks of 8192 rows (bf16 mode, as gpt2_lmhead_ce) or 4096 rows (FP32
+ * mode), and each chunk's part of the backward runs before the next chunk.
+ * The first call on a context (any B, T) also copies the weight-gradient
+ * launch's table to the scratch buffer, once, asynchronously on the stream;
+ * the call does not synchronise. */
 int gpt2_fwd_bwd(gpt2_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targets, int B, int T,
                  float loss_scale, float* d_loss, float* d_token_loss);
 
@@ -240,8 +246,8 @@ double gpt2_lr_at(int64_t step, double max_lr, double min_lr, int64_t warmup, in
  * gpt2_graph_launch replays it on the context's stream: each replay reads
  * whatever the token and target buffers hold at that time and adds its
  * gradients like gpt2_fwd_bwd.  Capture needs the profiler off and one
- * earlier gpt2_fwd_bwd at the same B and T (the weight-gradient table is set
- * up then); otherwise GPT2_ERR_ARG or GPT2_ERR_HIP.  gpt2_graph_launch
+ * earlier gpt2_fwd_bwd on the context (any B and T: the weight-gradient
+ * table is set up then); otherwise GPT2_ERR_ARG or GPT2_ERR_HIP.  gpt2_graph_launch
  * without a captured graph: GPT2_ERR_UNBOUND.  ("Build an LLM From Scratch:
  * Making Training Fast on One GPU", the compile modes: graphs of the step,
  * which there fail with gradient accumulation unless the gradients are
@@ -253,17 +259,24 @@ int gpt2_graph_launch(gpt2_ctx* ctx);
 /* Global-norm clipping then AdamW on every parameter, one fused pass
  * ("Reproduce GPT-2 124M 复盘": clip_grad_norm_(params, 1.0) and fused AdamW;
  * "How I trained my own GPT-2 124M on FineWeb-Edu" section 6: betas, eps, and
- * decay only on dim >= 2).  Increments the step counter t, then
- *   norm = ||grads||_2 over every parameter;  coef = min(1, max_norm / (norm + 1e-6))
+ * decay only on dim >= 2):
+ *   norm = ||grads||_2 over every parameter;  if norm is finite:
+ *   t = t + 1;  coef = min(1, max_norm / (norm + 1e-6))
  *   g = coef * grad;  p *= 1 - lr*wd (decayed tensors only)
  *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2
  *   p -= lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
  * and refreshes the bf16 shadow.  grads are left as they were (unclipped).
  * d_grad_norm (optional device float) receives the pre-clip norm.  A
- * non-finite norm leaves params, m and v unchanged and sets
- * GPT2_ERR_NONFINITE in the context flag (t is still incremented). */
+ * non-finite norm leaves params, m, v and the step counter t unchanged (a
+ * skipped step, as an optimizer that skips on overflow leaves its count) and
+ * sets GPT2_ERR_NONFINITE in the context flag.  The decision is taken on the
+ * device: t lives in the scratch buffer. */
 int gpt2_clip_adamw_step(gpt2_ctx* ctx, const gpt2_adamw* hp, float* d_grad_norm);
 
+/* The step counter t (the number of updates applied since gpt2_init_params
+ * or the last gpt2_set_step).  gpt2_get_step synchronises the context's
+ * stream and reads it back; gpt2_set_step writes it asynchronously (t >= 0,
+ * GPT2_ERR_ARG otherwise). */
 int gpt2_get_step(gpt2_ctx* ctx, int64_t* t);
 int gpt2_set_step(gpt2_ctx* ctx, int64_t t);
 
@@ -277,28 +290,41 @@ const char* gpt2_strerror(int status);
 
 /* --------------------------------------------- isolated lm_head + loss -- */
 
-/* Bytes of scratch gpt2_lmhead_ce needs for M rows, width C, vocab V. */
+/* Bytes of scratch gpt2_lmhead_ce needs for M rows, width C, vocab V:
+ * M * (C + 1) * 4 bytes plus one chunk of min(M, 8192) rows of bf16 logits
+ * and their tile statistics (8192 * V * 2 + 8192 * ceil(V / 256) * 8). */
 size_t gpt2_lmhead_ce_scratch_bytes(int M, int C, int V);
 
 /* Tied lm_head and mean cross-entropy, forward and backward, for M rows
  * ("How I trained my own GPT-2 124M on FineWeb-Edu" section 4: logits =
- * hidden @ weight^T without bias, cross-entropy over every column; rows with
- * target -1 ignored, the mean divides by the valid count).
+ * hidden @ weight^T without bias, cross-entropy over every column; the mean
+ * divides by the number of valid targets, "Multi-GPU calculation of
+ * gradients for accelerated training", "Cross-entropy averages within one
+ * micro-batch").
  *   d_hidden: bf16 [M, C]; d_weight: bf16 [V, C]; d_targets: int32 [M].
+ *   ignore_index: rows whose target equals it are ignored (the library
+ *     cross-entropy's argument of that name; the isolated lm_head workload
+ *     uses -1).  Any other target must lie in [0, V).
  *   d_loss: device float, the mean loss (NaN if no target is valid).
  *   d_dhidden: bf16 [M, C], written: d(loss)/d(hidden).
  *   d_dweight: float32 [V, C], d(loss)/d(weight) is ADDED to it.
  *   d_scratch: gpt2_lmhead_ce_scratch_bytes(M, C, V) bytes.
- *   d_flag: optional device int32, receives GPT2_ERR_BAD_ID if a target is
- *     out of range (else left unchanged).
- * C and V must be multiples of 8, M >= 1.  The logits product keeps, per
+ *   d_flag: optional device int32, receives GPT2_ERR_BAD_ID if a target
+ *     other than ignore_index is outside [0, V) (that row is then ignored)
+ *     or GPT2_WARN_NO_TARGETS if no target is valid (else left unchanged).
+ * C and V must be multiples of 8, M >= 1, every pointer but d_targets,
+ * d_loss and d_flag 16-byte aligned (GPT2_ERR_SHAPE / GPT2_ERR_ARG
+ * otherwise).  Device-side only: asynchronous on `stream`.
+ * The rows run in chunks of 8192: per chunk the logits product keeps, per
  * row and 256-column tile, the float32 maximum and sum of exponentials and
- * stores the logits in bf16 as offsets from that tile maximum; one pass per
- * row then forms the log-sum-exp, the loss (target logit recomputed in
- * float32) and the bf16 logit gradient in place, and the two products of the
- * backward read it.  Scratch grows as M * V * 2 bytes. */
+ * stores the chunk's logits in bf16 as offsets from that tile maximum; one
+ * pass per row then forms the log-sum-exp, the loss (target logit
+ * recomputed in float32) and the bf16 logit gradient in place, and one
+ * launch runs both products of the backward on it (dHidden rows of the
+ * chunk, and the chunk's share of dWeight) before the next chunk reuses the
+ * buffer.  The logits of all M rows are never stored. */
 int gpt2_lmhead_ce(void* stream, const void* d_hidden, const void* d_weight, const int32_t* d_targets,
-                   int M, int C, int V, float* d_loss, void* d_dhidden, float* d_dweight,
+                   int M, int C, int V, int ignore_index, float* d_loss, void* d_dhidden, float* d_dweight,
                    void* d_scratch, int32_t* d_flag);
 
 /* ------------------------------------------------------- single kernels -- */

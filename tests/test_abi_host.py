@@ -190,3 +190,44 @@ def test_grouped_products_validate_on_the_host():
         assert L.gpt2_op_gemm_grouped(None, arr, 2, None, ct.c_void_p(0x40000)) == _ffi.GPT2_ERR_ARG, field
         setattr(arr[1], field, old)
     assert L.gpt2_gemm_grouped_workspace_bytes(arr, 2) == nbytes
+
+
+def _declarations():
+    """name -> number of parameters, from the header's prototypes."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(gpt2_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        args = m.group(2).strip()
+        out[m.group(1)] = 0 if args in ("", "void") else args.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_the_header():
+    from gpt_pretraining_step_amd import _ffi
+    decl = _declarations()
+    assert set(decl) == set(_ffi.SIGNATURES)
+    wrong = {n: (k, len(_ffi.SIGNATURES[n][1])) for n, k in decl.items() if k != len(_ffi.SIGNATURES[n][1])}
+    assert not wrong, wrong
+
+
+def test_logits_are_never_sized_for_the_whole_batch():
+    """The lm_head runs in row chunks: neither the training step's scratch
+    nor the isolated lm_head's grows with rows x vocabulary beyond one chunk
+    of 8192 rows."""
+    _lib()
+    import gpt_pretraining_step_amd as g
+    from gpt_pretraining_step_amd import _ffi
+    L = _ffi.lib()
+    V, C = 50304, 768
+    chunk_bytes = 8192 * V * 2 + 8192 * ((V + 255) // 256) * 8
+    for M in (8192, 16384, 65536):
+        got = L.gpt2_lmhead_ce_scratch_bytes(M, C, V)
+        assert got <= M * (C + 1) * 4 + chunk_bytes + 5 * 256, M
+        if M > 8192:
+            assert got < M * V * 2  # less than the whole logit matrix in bf16
+    # the training step at B=16 (16,384 rows): 256 more vocabulary columns
+    # cost one chunk's worth of logits (8192 rows) and statistics, not 16,384
+    sa = g.query_sizes(g.GPT2_124M).scratch_bytes
+    sb = g.query_sizes(g.ModelConfig(50304 + 256, 1024, 12, 12, 768, 3072, 16, g.PRECISION_BF16)).scratch_bytes
+    assert 8192 * 256 * 2 <= sb - sa <= 8192 * 256 * 2 + 8192 * 8 + 1024, sb - sa

@@ -405,11 +405,13 @@ def test_layernorm_vs_oracle(g, rows, C, bf, dyb):
 
 # ------------------------------------------------------------- lm_head + loss
 
-@pytest.mark.parametrize("M,C,V,wscale", [(300, 64, 1000, 1.0), (5000, 128, 2056, 1.0), (1000, 128, 4096, 16.0)])
+@pytest.mark.parametrize("M,C,V,wscale", [(300, 64, 1000, 1.0), (5000, 128, 2056, 1.0), (1000, 128, 4096, 16.0),
+                                           (20000, 64, 1024, 1.0)])
 def test_lmhead_ce_small_vs_oracle(g, M, C, V, wscale):
     """The fused lm_head + loss against the oracle.  wscale = 16 makes logits
     of size ~10 with a peaked softmax: the bf16 logits stored as offsets from
-    their tile maximum must still give accurate probabilities."""
+    their tile maximum must still give accurate probabilities.  M = 20000
+    runs three row chunks (8192, 8192 and a ragged 3616)."""
     import torch
     announce(f"lmhead_ce M={M} C={C} V={V} wscale={wscale}")
     h, w, t = synthetic.lmhead_inputs(M=M, C=C, V=V, seed=M)
@@ -422,6 +424,39 @@ def test_lmhead_ce_small_vs_oracle(g, M, C, V, wscale):
     assert cosine(host(dh), dh_ref) > 0.999
     assert cosine(host(dw), dw_ref) > 0.999
     assert np.all(host(dh)[t < 0] == 0)
+
+
+def test_lmhead_ce_ignore_index(g):
+    """ignore_index other than -1: rows whose target equals it are ignored,
+    -1 is then an out-of-range target (flagged GPT2_ERR_BAD_ID and ignored
+    too), and the result equals the oracle's with that ignore_index."""
+    import torch
+    announce("lmhead_ce ignore_index 7")
+    M, C, V = 3000, 64, 512
+    h, w, t = synthetic.lmhead_inputs(M=M, C=C, V=V, seed=9)
+    t = np.where(t >= 0, t % V, 7).astype(np.int32)  # the ignored rows now hold 7
+    n7 = int((t == 7).sum())
+    assert n7 >= 250
+    loss_ref, _, dh_ref, dw_ref = OM.lmhead_ce(h.astype(np.float64), w.astype(np.float64), t, ignore_index=7)
+    dw = torch.zeros((V, C), dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loss, dh = g.lmhead_ce(dev(h, torch.bfloat16), dev(w, torch.bfloat16), dev(t), dw, flag=flag, ignore_index=7)
+    assert abs(float(host(loss)[0]) - loss_ref) <= 2e-5 * abs(loss_ref)
+    assert cosine(host(dh), dh_ref) > 0.999 and cosine(host(dw), dw_ref) > 0.999
+    assert np.all(host(dh)[t == 7] == 0)
+    assert int(host(flag)[0]) == 0
+    # the same call with ignore_index 7 and a -1 among the targets: -1 is a
+    # bad id now (flagged, its row ignored like the 7s)
+    t2 = t.copy()
+    t2[5] = -1
+    t3 = t.copy()
+    t3[5] = 7
+    loss_ref3, _, dh_ref3, _ = OM.lmhead_ce(h.astype(np.float64), w.astype(np.float64), t3, ignore_index=7)
+    dw.zero_()
+    loss2, dh2 = g.lmhead_ce(dev(h, torch.bfloat16), dev(w, torch.bfloat16), dev(t2), dw, flag=flag, ignore_index=7)
+    assert int(host(flag)[0]) == g._ffi.GPT2_ERR_BAD_ID
+    assert abs(float(host(loss2)[0]) - loss_ref3) <= 2e-5 * abs(loss_ref3)
+    assert np.all(host(dh2)[5] == 0)
 
 
 def test_lmhead_ce_all_ignored(g):

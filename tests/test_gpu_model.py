@@ -312,11 +312,20 @@ def test_error_paths(g):
     loss, _, st = run_gpu(g, m, x, np.full_like(y, -1))
     assert math.isnan(loss) and st == g._ffi.GPT2_WARN_NO_TARGETS
     assert float(host(m.grads).__abs__().max()) == 0.0
-    # non-finite gradient: update skipped, flag raised
+    # non-finite gradient: update skipped (the step counter too), flag raised
     p0 = host(m.params).copy()
+    t0 = m.step
     m.grads[5] = float("inf")
     m.clip_adamw_step(lr=1e-3)
     assert m.status() == g._ffi.GPT2_ERR_NONFINITE
     assert np.array_equal(host(m.params), p0)
+    assert m.step == t0
+    # a finite step afterwards counts from there and uses t0 + 1 in its
+    # bias corrections; set_step moves the counter
+    m.grads[5] = 0.0
+    m.clip_adamw_step(lr=1e-3)
+    assert m.status() == 0 and m.step == t0 + 1
+    m.step = 41
+    assert m.step == 41
     torch.cuda.synchronize()
     m.close()

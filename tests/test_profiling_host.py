@@ -92,5 +92,9 @@ def test_bench_flop_accounting():
     M, C, V, F = 16 * 1024, 768, 50304, 3072
     fl = bench.gemm_site_flops(M, F)
     per_layer = 2 * M * C * (3 * C) + 2 * M * C * C + 2 * M * C * F + 2 * M * F * C
-    assert fl["gemm.dw"] == 2 * M * V * C + 12 * per_layer == 4_049_080_418_304
+    assert fl["gemm.dw"] == 12 * per_layer == 2_783_138_807_808
+    # the lm_head's products run per chunk of 8192 rows: two chunks at B=16
+    assert fl["gemm.lm_head"] == 2 * 8192 * V * C
+    assert fl["gemm.lm_head_bwd"] == 2 * fl["gemm.lm_head"]
+    assert 2 * (fl["gemm.lm_head"] + fl["gemm.lm_head_bwd"]) == 3 * 2 * M * V * C
     assert fl["gemm.qkv"] == 2 * M * 3 * C * C

@@ -99,7 +99,7 @@ class ClockSampler:
     while the timed steps run ("Making Training Fast on One GPU", clock
     drift as noise: the clock is logged beside each timing)."""
 
-    def __init__(self, period: float = 1.0):
+    def __init__(self, period: float = 0.5):
         import threading
         self.period = period
         self.samples = []
@@ -254,6 +254,36 @@ def traffic_probe(site: str, workload: str = "gpt2") -> int:
     return 0 if st == 0 and n > 0 else 1
 
 
+def counter_probe(workload: str = "gpt2") -> int:
+    """One micro-step of `workload` and one clip + AdamW step, then the
+    library's marker kernel and a plain device copy of COPY_BYTES that
+    calibrates the HBM byte counters.  Run under `rocprofv3 --pmc ...` (one
+    counter set per run) and under `--kernel-trace --stats`; the summaries
+    come from `python -m gpt_pretraining_step_amd.profiling counters`."""
+    import torch
+    import gpt_pretraining_step_amd as g
+    import synthetic
+    wl = WORKLOADS[workload]
+    Bw, Gw = wl["B"], wl["G"]
+    model = g.GPT2(g.GPT2_124M if workload == "gpt2" else g.GPT2_ROTARY_124M)
+    model.init_params(seed=42)
+    stream = synthetic.token_stream(Bw * T + 1, seed=1337)
+    x, y = synthetic.micro_batch(stream, 0, Bw, T)
+    x, y = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    model.zero_grad()
+    model.fwd_bwd(x, y, loss_scale=1.0 / Gw)
+    model.clip_adamw_step(lr=wl["lr"])
+    g.op_marker()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    st = model.status()
+    model.close()
+    print(f"[bench] counter probe: {workload} micro-step + optimizer step, status {st}", file=sys.stderr, flush=True)
+    return 0 if st == 0 else 1
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +293,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no HIP events at all (no roofline, no breakdown)")
     ap.add_argument("--traffic-probe", metavar="SITE", help="one marked micro-step for an HBM counter run")
+    ap.add_argument("--counter-probe", action="store_true",
+                    help="one micro-step + optimizer step + calibration copy, for per-kernel counter runs")
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["lmhead"], default="gpt2",
                     help="gpt2 (the headline step, default), rotary (the modern variant) or lmhead (the isolated "
                          "tied lm_head + cross-entropy)")
@@ -276,6 +308,8 @@ def main(argv=None):
         return 2
     if args.traffic_probe:
         return traffic_probe(args.traffic_probe, args.workload)
+    if args.counter_probe:
+        return counter_probe(args.workload)
     if args.workload == "lmhead":
         return bench_lmhead(args)
 
@@ -447,9 +481,13 @@ def bench_lmhead(args):
     def call():
         g.lmhead_ce(H, W, Tg, dw, stream=st, scratch=scratch, loss=loss, dhidden=dh)
 
-    for _ in range(max(1, args.warmup)):
+    # warm-up: at least `warmup` calls and at least 2 s of them, so that the
+    # clocks have left their idle state before the timed calls
+    w0, nw = time.perf_counter(), 0
+    while nw < max(1, args.warmup) or time.perf_counter() - w0 < 2.0:
         call()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        nw += 1
     steps = max(args.steps, 1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     with ClockSampler() as clock:
@@ -469,7 +507,7 @@ def bench_lmhead(args):
     result = {
         "metric": "isolated tied lm_head + cross-entropy fwd+bwd, hidden 65536x768, V=50304, 1 MI355X",
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
-        "ms_per_step": round(med * 1e3, 3), "ms_mean_wall": round(1e3 * elapsed / steps, 3),
+        "ms_per_step": round(med * 1e3, 3), "ms_mean_wall": round(1e3 * elapsed / steps, 3), "warmup_calls": nw,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (hidden N(0,1), weight N(0,0.02^2), Zipf targets, 10% ignored)",
         "config": {"workload": "lmhead_ce: hidden [65536, 768] bf16, weight [50304, 768] bf16, ignore_index -1, "

@@ -5,7 +5,12 @@
         --command-fetch "<cmd>" --command-write "<cmd>"
 
 `stats` turns a `rocprofv3 --kernel-trace --stats` kernel-statistics CSV
-into a Markdown table.  `traffic` reads two per-dispatch counter runs
+into a Markdown table.  `counters` joins a per-dispatch kernel trace and
+any number of per-dispatch counter runs of the same program (`bench.py
+--counter-probe`: one micro-step, one optimizer step, then the marker and a
+calibration copy) dispatch by dispatch, and tabulates per kernel and grid:
+duration, MfmaUtil and VALUBusy, HBM bytes from FETCH_SIZE / WRITE_SIZE
+scaled by the copy's readings, and the resulting GB/s.  `traffic` reads two per-dispatch counter runs
 (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`) of `bench.py --traffic-probe`:
 in those runs the library launches its empty marker kernel before every
 launch of the probed site, and once more before a plain device copy of
@@ -160,6 +165,83 @@ def load_traffic(profiles_dir: str, site: str, workload: str = "gpt2"):
     return None
 
 
+# -------------------------------------------------------------- counters
+
+def _grid(r):
+    for k in ("Grid_Size", "Grid_Size_X", "grid_size"):
+        if k in r and r[k] not in (None, ""):
+            return r[k]
+    return ""
+
+
+def _dispatches(rows, counters=True):
+    """Per-dispatch records in dispatch order: (kernel, grid, {counter: value})
+    for a counter run, (kernel, grid, duration ns) for a kernel trace."""
+    out = {}
+    for r in rows:
+        d = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        if counters:
+            rec = out.setdefault(d, [r["Kernel_Name"], _grid(r), {}])
+            rec[2][r["Counter_Name"]] = rec[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        else:
+            out[d] = [r["Kernel_Name"], _grid(r), float(r["End_Timestamp"]) - float(r["Start_Timestamp"])]
+    return [out[k] for k in sorted(out)]
+
+
+def counters_markdown(trace_dir: str, pmc_dirs, copy_bytes: int, command: str, title: str) -> str:
+    trace = _dispatches(_rows(trace_dir, "kernel_trace.csv"), counters=False)
+    runs = [_dispatches(_rows(d, "counter_collection.csv")) for d in pmc_dirs]
+    for run in runs:
+        if len(run) != len(trace) or any(a[0] != b[0] for a, b in zip(run, trace)):
+            raise ValueError("the runs did not dispatch the same kernels in the same order")
+    n = len(trace)
+    vals = [{} for _ in range(n)]
+    for run in runs:
+        for i, (_, _, c) in enumerate(run):
+            vals[i].update(c)
+    if MARKER not in trace[-2][0]:
+        raise ValueError("the last dispatch must be the calibration copy after the marker")
+    cal = vals[-1]
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if c in cal and cal[c] > 0:
+            scale[c] = copy_bytes / 1024.0 / cal[c]
+    groups = {}
+    for i in range(n - 2):  # all but the marker and the copy
+        k, g, dur = trace[i]
+        if MARKER in k:
+            continue
+        e = groups.setdefault((k, g), {"n": 0, "dur": 0.0, "c": {}})
+        e["n"] += 1
+        e["dur"] += dur
+        for c, v in vals[i].items():
+            e["c"][c] = e["c"].get(c, 0.0) + v
+    cols = [c for c in ("MfmaUtil", "VALUBusy") if any(c in e["c"] for e in groups.values())]
+    have_b = [c for c in ("FETCH_SIZE", "WRITE_SIZE") if c in scale]
+    head = ["kernel", "grid", "calls", "avg us"] + [f"{c} %" for c in cols]
+    if have_b:
+        head += [f"{'read' if c == 'FETCH_SIZE' else 'written'} MB" for c in have_b] + ["HBM GB/s"]
+    out = [f"# {title}", "", "Commands (from the repository root, on one MI355X):", ""]
+    out += ["    " + line for line in command.split("\n")]
+    out += ["", f"Calibration: a device copy of {copy_bytes} bytes read as "
+            + ", ".join(f"{c} {cal.get(c, 0):.1f} KiB (scale {scale[c]:.4f})" for c in have_b) + ".", "",
+            "| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    total = sum(e["dur"] for e in groups.values())
+    for (k, g), e in sorted(groups.items(), key=lambda kv: -kv[1]["dur"]):
+        name = k.replace("|", "\\|")
+        if len(name) > 140:
+            name = name[:137] + "..."
+        avg = e["dur"] / e["n"]
+        row = [f"`{name}`", str(g), str(e["n"]), f"{avg / 1e3:.2f}"]
+        row += [f"{e['c'][c] / e['n']:.1f}" if c in e["c"] else "" for c in cols]
+        if have_b:
+            byts = [e["c"].get(c, 0.0) / e["n"] * 1024 * scale[c] for c in have_b]
+            row += [f"{b / 1e6:.1f}" for b in byts] + [f"{sum(byts) / avg:.0f}"]
+        out.append("| " + " | ".join(row) + " |")
+    out.append(f"| (all) | | | {total / 1e3:.1f} total | |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -175,9 +257,17 @@ def main(argv=None) -> int:
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--workload", default="gpt2")
+    c = sub.add_parser("counters")
+    c.add_argument("trace_dir")
+    c.add_argument("pmc_dirs", nargs="+")
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--command", required=True, help="the commands, newline-separated")
+    c.add_argument("--title", default="Per-kernel counters")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.command, a.title))
+    elif a.cmd == "counters":
+        sys.stdout.write(counters_markdown(a.trace_dir, a.pmc_dirs, a.copy_bytes, a.command, a.title))
     else:
         sys.stdout.write(traffic_record(a.fetch_dir, a.write_dir, a.site, a.copy_bytes, a.command_fetch,
                                         a.command_write, a.workload))

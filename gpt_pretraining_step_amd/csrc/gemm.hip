@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <vector>
 
 namespace g2 {
@@ -398,10 +399,7 @@ double pair_span(int64_t u0, double c0, int64_t u1, double c1) {
   }
   return *std::max_element(load.begin(), load.end());
 }
-PairPlan plan_pair(const gpt2_gemm_args& a0, const gpt2_gemm_args& a1) {
-  const int64_t t0 = (int64_t)((a0.M + kPairTile - 1) / kPairTile) * ((a0.N + kPairTile - 1) / kPairTile);
-  const int64_t t1 = (int64_t)((a1.M + kPairTile - 1) / kPairTile) * ((a1.N + kPairTile - 1) / kPairTile);
-  const int k0 = (a0.K + 63) / 64, k1 = (a1.K + 63) / 64;
+PairPlan plan_pair_uncached(int64_t t0, int k0, int64_t t1, int k1) {
   constexpr double EPI = 4.0;  // epilogue of a 256x256 float32 read-modify-write, in K steps
   PairPlan best;
   best.span = 1e300;
@@ -417,6 +415,30 @@ PairPlan plan_pair(const gpt2_gemm_args& a0, const gpt2_gemm_args& a1) {
       }
     }
   return best;
+}
+// The search above costs milliseconds of host time; a training step asks
+// for the same few shapes every micro-step, so plans are kept.
+PairPlan plan_pair(const gpt2_gemm_args& a0, const gpt2_gemm_args& a1) {
+  const int64_t t0 = (int64_t)((a0.M + kPairTile - 1) / kPairTile) * ((a0.N + kPairTile - 1) / kPairTile);
+  const int64_t t1 = (int64_t)((a1.M + kPairTile - 1) / kPairTile) * ((a1.N + kPairTile - 1) / kPairTile);
+  const int k0 = (a0.K + 63) / 64, k1 = (a1.K + 63) / 64;
+  struct Entry {
+    int64_t t0, t1;
+    int k0, k1;
+    PairPlan plan;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry& e : cache)
+      if (e.t0 == t0 && e.t1 == t1 && e.k0 == k0 && e.k1 == k1) return e.plan;
+  }
+  const PairPlan pl = plan_pair_uncached(t0, k0, t1, k1);
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache.size() >= 256) cache.erase(cache.begin());
+  cache.push_back(Entry{t0, t1, k0, k1, pl});
+  return pl;
 }
 GemmP pair_params(const gpt2_gemm_args& a, int splits) {
   GemmP p = make_params(a);

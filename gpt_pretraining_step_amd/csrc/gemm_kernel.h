@@ -825,6 +825,34 @@ union GV8 {
   uint32_t w[4];
 };
 
+// Instruction order of one K step (sched_group_barrier masks: 0x008 MFMA,
+// 0x100 LDS read): NR reads of the first slice, then for every slice but the
+// last its NM MFMAs with the NR reads of the next slice spread among them,
+// then the last slice's MFMAs.
+template <int NR, int NM, int M>
+__device__ __forceinline__ void sched_pair() {
+  if constexpr (M < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int per = (NR + NM - 1) / NM;
+    constexpr int left = NR - M * per;
+    if constexpr (left > 0) __builtin_amdgcn_sched_group_barrier(0x100, left < per ? left : per, 0);
+    sched_pair<NR, NM, M + 1>();
+  }
+}
+template <int NR, int NM, int S>
+__device__ __forceinline__ void sched_slices() {
+  if constexpr (S > 0) {
+    sched_pair<NR, NM, 0>();
+    sched_slices<NR, NM, S - 1>();
+  }
+}
+template <int NR, int NM, int SLICES>
+__device__ __forceinline__ void sched_kstep() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  sched_slices<NR, NM, SLICES - 1>();
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+}
+
 // One block's unit of a product: its output tile (and K split), main loop
 // and epilogue.
 // The two LDS stages of a block: (BM + BN) * BK bf16 elements each.  They are
@@ -980,6 +1008,10 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit, bf16* lds0,
           acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cb][j], a[cb][i], acc[i][j], 0, 0, 0)
                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
     }
+    // Left to itself the compiler issues each slice's fragment reads just
+    // before that slice's MFMAs and waits for them there; this order keeps
+    // the next slice's reads in flight behind the current slice's MFMAs.
+    sched_kstep<TM * (A_K ? 1 : 2) + TN * (B_K ? 1 : 2), TM * TN, BK / 16>();
     if (do_rowsum && threadIdx.x < BM) {
       // row sums of this block's A tile (K values past kend read as zeros)
       const int t = threadIdx.x;

@@ -24,7 +24,7 @@ from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noq
                    EPI_ROPE, EPI_SWIGLU, EPI_SWIGLU_BWD, ARCH_GPT2, ARCH_ROTARY, GPT2_ERR_ARG)
 
 __all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm", "op_gemm_grouped",
-           "op_attention_fwd", "op_attention_bwd", "op_segment_starts", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
+           "op_attention_fwd", "op_attention_bwd", "op_attention_bwd_noalloc", "op_segment_starts", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
            "op_rope_table", "op_rope_bwd", "op_rmsnorm_fwd", "op_rmsnorm_bwd", "query_sizes", "param_table",
            "GPT2_ROTARY_124M"]
 
@@ -394,6 +394,20 @@ def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, 
                                       dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(), scratch.data_ptr(), _ptr(seg),
                                       _ptr(rope)),
           "gpt2_op_attention_bwd")
+
+
+def op_attention_bwd_noalloc(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, n_kv_head=None, rope=None):
+    """op_attention_bwd without a workspace: the library's static per-GPU
+    array holds D (B * H * T <= 1,048,576); calls overlapping on one GPU
+    race on it."""
+    import torch
+    dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
+    _check_seg(seg, B, T)
+    Hkv = H if n_kv_head is None else n_kv_head
+    check(lib().gpt2_op_attention_bwd_noalloc(_stream_ptr(stream), dtype, B, T, H, Hkv, hd, qkv.data_ptr(),
+                                              y.data_ptr(), dy.data_ptr(), lse.data_ptr(), dqkv.data_ptr(),
+                                              _ptr(seg), _ptr(rope)),
+          "gpt2_op_attention_bwd_noalloc")
 
 
 def _check_seg(seg, B, T):

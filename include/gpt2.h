@@ -497,6 +497,24 @@ int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv,
                           const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
                           void* d_scratch, const int32_t* d_seg, const float* d_rope);
 
+/* The attention backward above without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels, with
+ * D = rowsum(dO o O) kept in a static device array of the library (one per
+ * GPU, gpt2_noalloc_scratch_bytes() = 4 MiB, held until the process ends).
+ * B * H * T must not exceed gpt2_noalloc_scratch_bytes() / 4 = 1,048,576
+ * (GPT2_ERR_SHAPE otherwise; nothing is launched).  Allocates nothing: the
+ * first call on a device looks up that device's copy of the array once.
+ * Every call on one GPU shares the array; calls that overlap in time on one
+ * GPU (two streams or threads) race on it and must be serialised by the
+ * caller.  Arguments, layouts and results as gpt2_op_attention_bwd;
+ * GPT2_ERR_HIP if the array's address cannot be obtained or the launch
+ * fails. */
+size_t gpt2_noalloc_scratch_bytes(void);
+int gpt2_op_attention_bwd_noalloc(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
+                                  const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
+                                  const int32_t* d_seg, const float* d_rope);
+
 /* Document starts of packed rows ("GPT" chapter of Zero to Frontier,
  * "Document boundaries, packing and masking"): d_seg[b*T + t] = the last
  * position s <= t with d_tokens[b*T + s] == eot, 0 if there is none (int32,

@@ -378,7 +378,7 @@ hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int 
 // and dW += dlogits^T Z (both K-slow; many tiles, K = the chunk's rows).  The
 // split counts come from a list-scheduling estimate of the launch: units
 // are handed in block order to the earliest-free of the 256 CUs, a unit
-// costing its K steps plus an epilogue (twice as long when it adds
+// costing its K steps plus an epilogue (much longer when it adds
 // atomically), and the plan with the shortest estimated span wins.
 
 namespace {
@@ -400,13 +400,17 @@ double pair_span(int64_t u0, double c0, int64_t u1, double c1) {
   return *std::max_element(load.begin(), load.end());
 }
 PairPlan plan_pair_uncached(int64_t t0, int k0, int64_t t1, int k1) {
-  constexpr double EPI = 4.0;  // epilogue of a 256x256 float32 read-modify-write, in K steps
+  // epilogue of a 256x256 float32 read-modify-write, in K steps; an atomic
+  // one is charged 8 times as much (measured: with 2 times, the plan split
+  // the lm_head's dZ 7 ways and the launch took 78.4 ms per GPT-2 step; with
+  // 8 times it splits 2 ways, 73.1 ms, on the same box)
+  constexpr double EPI = 4.0, EPI_ATOMIC = 8 * EPI;
   PairPlan best;
   best.span = 1e300;
   for (int s0 = 1; s0 <= 64 && (s0 == 1 || k0 / s0 >= 8); ++s0)
     for (int s1 = 1; s1 <= 4 && (s1 == 1 || k1 / s1 >= 8); ++s1) {
-      const double c0 = (k0 + s0 - 1) / s0 + (s0 > 1 ? 2 * EPI : EPI);
-      const double c1 = (k1 + s1 - 1) / s1 + (s1 > 1 ? 2 * EPI : EPI);
+      const double c0 = (k0 + s0 - 1) / s0 + (s0 > 1 ? EPI_ATOMIC : EPI);
+      const double c1 = (k1 + s1 - 1) / s1 + (s1 > 1 ? EPI_ATOMIC : EPI);
       const double span = pair_span(t0 * s0, c0, t1 * s1, c1);
       if (span < 0.99 * best.span) {
         best.s0 = s0;

@@ -199,15 +199,21 @@ def counters_markdown(trace_dir: str, pmc_dirs, copy_bytes: int, command: str, t
     for run in runs:
         for i, (_, _, c) in enumerate(run):
             vals[i].update(c)
-    if MARKER not in trace[-2][0]:
-        raise ValueError("the last dispatch must be the calibration copy after the marker")
-    cal = vals[-1]
+    marks = [i for i, t in enumerate(trace) if MARKER in t[0]]
+    if not marks:
+        raise ValueError("no marker before the calibration copy")
+    last = marks[-1]
+    # the copy may run as several dispatches: its readings are their sum
+    cal = {}
+    for i in range(last + 1, n):
+        for c, v in vals[i].items():
+            cal[c] = cal.get(c, 0.0) + v
     scale = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         if c in cal and cal[c] > 0:
             scale[c] = copy_bytes / 1024.0 / cal[c]
     groups = {}
-    for i in range(n - 2):  # all but the marker and the copy
+    for i in range(last):  # everything before the marker and the copy
         k, g, dur = trace[i]
         if MARKER in k:
             continue

@@ -398,8 +398,8 @@ def op_attention_bwd(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, 
 
 def op_attention_bwd_noalloc(qkv, y, dy, lse, dqkv, B, T, H, hd, stream=None, seg=None, n_kv_head=None, rope=None):
     """op_attention_bwd without a workspace: the library's static per-GPU
-    array holds D (B * H * T <= 1,048,576); calls overlapping on one GPU
-    race on it."""
+    array holds its two floats per row (B * H * T <= 1,048,576); calls
+    overlapping on one GPU race on it."""
     import torch
     dtype = PRECISION_BF16 if qkv.dtype == torch.bfloat16 else PRECISION_FP32
     _check_seg(seg, B, T)

@@ -218,6 +218,24 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
+// dS = P o (dP - D) without a subtraction per score: -D is split into two
+// bf16 values hi = bf16(-D), lo = bf16(-D - hi) (together exact to about
+// 2^-17 |D|), which ride as two extra contraction slots of the dP product
+// against two ones on the other side.  An MFMA operand's lane holds
+// contraction slots 8 lg .. 8 lg + 7, so lanes with lg = 0 carry the pair in
+// slots 0 and 1 and all other slots are zero.
+__device__ __forceinline__ uint32_t neg_d_pair(float D) {
+  const bf16 hi = f2bf(-D);
+  const bf16 lo = f2bf(-D - bf2f(hi));
+  return (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+}
+__device__ __forceinline__ bf16x8 slot01(uint32_t pair, int lg) {
+  V8 r;
+  r.u = make_uint4(lg ? 0u : pair, 0u, 0u, 0u);
+  return r.v;
+}
+constexpr uint32_t kOnePair = 0x3F803F80u;  // bf16 1.0 in slots 0 and 1
+
 // Write a head's 64 gradient values held as the transposed accumulators g[0]
 // (dims 0..31) and g[1] (dims 32..63): register 4a + e of g[dt] is dim
 // 32 dt + 8a + 4 lg + e.  With a rotary table (rope != nullptr: row `pos`
@@ -426,12 +444,15 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_kernel(const bf16* __re
 }
 
 // Backward, pass 1: D = rowsum(dO o O) and dQ.  Same tiling as the forward.
+// For the dK/dV pass it leaves, per query, -D as a bf16 pair (neg_d_pair) in
+// Dpk and the log-sum-exp in log2 units in L2buf.
 template <int NW, int ST, bool DOC>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
-                                                                   bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
+                                                                   bf16* __restrict__ dqkv, uint32_t* __restrict__ Dpk,
+                                                                   float* __restrict__ L2buf,
                                                                    const int32_t* __restrict__ seg,
                                                                    const float2* __restrict__ rope, int T, int H,
                                                                    int Hkv, float scale, float sl2) {
@@ -470,8 +491,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
     }
   }
   const float D = Dp + __shfl_xor(Dp, 32);
-  if (qv && lg == 0) Dbuf[(int64_t)bh * T + qi] = D;
+  const uint32_t dpair = neg_d_pair(D);
   const float lse2 = qv ? lse[(int64_t)bh * T + qi] * kLOG2E : 0.f;
+  if (qv && lg == 0) {
+    Dpk[(int64_t)bh * T + qi] = dpair;
+    L2buf[(int64_t)bh * T + qi] = lse2;
+  }
+  // the extra contraction step of dP^T = V dO^T: ones on the key side, this
+  // lane's query's -D pair on the query side
+  const bf16x8 ones = slot01(kOnePair, lg), negd = slot01(dpair, lg);
 
   f32x16 dqT[2] = {zero16(), zero16()};
   const int kv_end = min(T, qb * BQ + BQ);
@@ -535,6 +563,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
         sT = MFMA(rowfrag(Ks, 32 * c + lr, kk, lg), qf[kk], sT);
         dpT = MFMA(rowfrag(Vs, 32 * c + lr, kk, lg), dof[kk], dpT);
       }
+      dpT = MFMA(ones, negd, dpT);  // dP - D
       if (edge) {
         asm volatile("");
         const int lim = min(qi, T - 1) - kb - 32 * c - 4 * lg;
@@ -546,7 +575,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sT[r] = __builtin_amdgcn_exp2f(fmaf(sT[r], sl2, -lse2)) * (dpT[r] - D);
+      for (int r = 0; r < 16; ++r) sT[r] = __builtin_amdgcn_exp2f(fmaf(sT[r], sl2, -lse2)) * dpT[r];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bf16x8 db = acc_frag(sT, s);
@@ -566,8 +595,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_kernel(const bf16* _
 template <int NW, bool DOC>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf16* __restrict__ qkv,
                                                                      const bf16* __restrict__ dy,
-                                                                     const float* __restrict__ lse,
-                                                                     const float* __restrict__ Dbuf,
+                                                                     const float* __restrict__ L2buf,
+                                                                     const uint32_t* __restrict__ Dpk,
                                                                      bf16* __restrict__ dqkv,
                                                                      const int32_t* __restrict__ seg,
                                                                      const float2* __restrict__ rope, int T, int H,
@@ -575,7 +604,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
   constexpr int BK = 32 * NW;
   constexpr int NR = DOC ? 3 : 2;
   __shared__ __attribute__((aligned(16))) bf16 sm[2][2][64 * HD];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float rowst[2][NR][64];  // [stage][lse, D, document start (int)]
+  // [stage][log2 lse, -D pair (u32), document start (int)]
+  __shared__ __attribute__((aligned(16))) float rowst[2][NR][64];
   const int kblk = blockIdx.y;  // smallest keys (most queries) first, over all heads
   const int bj = blockIdx.x, b = bj / Hkv, j = bj % Hkv, grp = H / Hkv;
   const int C = H * HD, Ckv = Hkv * HD, C3 = C + 2 * Ckv;
@@ -610,14 +640,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     qend = max(lo, qstart + 1);
   }
   const int ntiles = (qend - qstart + 63) / 64;
-  // Q and dO tiles of query head h, and the tile's 64 lse and D values, by
-  // DMA (lse and D from wave 0; rows past T read zeros, and their scores are
+  // Q and dO tiles of query head h, and the tile's 64 lse and -D values, by
+  // DMA (those two from wave 0; rows past T read zeros, and their scores are
   // masked)
   const bool w0 = __builtin_amdgcn_readfirstlane(wave) == 0;
+  const bf16x8 ones = slot01(kOnePair, lg);  // key side of the -D contraction step
   auto issue = [&](int st, int h, int tile) {
     const int q0t = qstart + tile * 64;
-    const float* lseg = lse + ((int64_t)b * H + h) * T;
-    const float* Dg = Dbuf + ((int64_t)b * H + h) * T;
+    const float* lseg = L2buf + ((int64_t)b * H + h) * T;
+    const uint32_t* Dg = Dpk + ((int64_t)b * H + h) * T;
     dma_rows<64, 64, NW, true>(sm[st][0], qkv + (int64_t)b * T * C3 + h * HD, C3, q0t, T, 0, HD);
     dma_rows<64, 64, NW, true>(sm[st][1], dy + (int64_t)b * T * C + h * HD, C, q0t, T, 0, HD);
     if (w0) {
@@ -662,7 +693,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
     const bf16* Qs = sm[it & 1][0];
     const bf16* dOs = sm[it & 1][1];
     const float* Ls = rowst[it & 1][0];
-    const float* Ds = rowst[it & 1][1];
+    const uint32_t* Ds = reinterpret_cast<const uint32_t*>(rowst[it & 1][1]);
     const int* Ss = reinterpret_cast<const int*>(rowst[it & 1][NR - 1]);
     // in a packed window: some query of the tile starts its document after
     // this wave's first key (the tile's last query has the largest start)
@@ -680,6 +711,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
         sc = MFMA(rowfrag(Qs, 32 * c + lr, kk, lg), kf[kk], sc);
         dp = MFMA(rowfrag(dOs, 32 * c + lr, kk, lg), vf[kk], dp);
       }
+      dp = MFMA(slot01(Ds[32 * c + lr], lg), ones, dp);  // dP - D
       if (edge) {
         // element r is query qs + 32 c + 4 lg + (8 (r / 4) + r % 4): keep
         // lo <= 8 (r / 4) + r % 4 <= hi (query >= key, query < T)
@@ -704,18 +736,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16_kernel(const bf
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int ql = 32 * c + 8 * a + 4 * lg;
-        float4 L4 = *reinterpret_cast<const float4*>(Ls + ql);  // natural log: to base 2
-        L4.x *= kLOG2E; L4.y *= kLOG2E; L4.z *= kLOG2E; L4.w *= kLOG2E;
-        const float4 D4 = *reinterpret_cast<const float4*>(Ds + ql);
+        const float4 L4 = *reinterpret_cast<const float4*>(Ls + 32 * c + 8 * a + 4 * lg);
         const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-        const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -Lv[e]));
           sc[r] = p;
-          dp[r] = p * (dp[r] - Dv[e]);
+          dp[r] = p * dp[r];
         }
       }
 #pragma unroll
@@ -762,7 +790,8 @@ hipError_t launch_attention_fwd(const Launch& L, int dtype, int B, int T, int H,
   return hipGetLastError();
 }
 
-size_t attention_bwd_scratch(int B, int T, int H) { return (size_t)B * T * H * sizeof(float); }
+// bf16: [-D pairs (u32) | lse in log2 units (fp32)], B * H * T each; fp32: D.
+size_t attention_bwd_scratch(int B, int T, int H) { return 2 * (size_t)B * T * H * sizeof(float); }
 
 hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H, int Hkv, int hd, const void* qkv,
                                 const void* y, const void* dy, const float* lse, void* dqkv, void* scratch,
@@ -779,15 +808,17 @@ hipError_t launch_attention_bwd(const Launch& L, int dtype, int B, int T, int H,
     const bf16* dO = static_cast<const bf16*>(dy);
     bf16* dq = static_cast<bf16*>(dqkv);
     const float sl2 = scale * kLOG2E;
+    uint32_t* Dpk = static_cast<uint32_t*>(scratch);
+    float* L2buf = Dbuf + (size_t)B * H * T;
     if (seg) {
-      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, seg, rope, T, H,
-                                                                           Hkv, scale, sl2);
-      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, seg, rope, T, H,
+      attn_bwd_dq_bf16_kernel<NW, 2, true><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dpk, L2buf, seg, rope,
+                                                                           T, H, Hkv, scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, true><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, L2buf, Dpk, dq, seg, rope, T, H,
                                                                              Hkv, scale, sl2);
     } else {
-      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dbuf, nullptr, rope, T,
-                                                                            H, Hkv, scale, sl2);
-      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, lse, Dbuf, dq, nullptr, rope, T,
+      attn_bwd_dq_bf16_kernel<NW, 2, false><<<grid, 64 * NW, 0, L.stream>>>(q, o, dO, lse, dq, Dpk, L2buf, nullptr,
+                                                                            rope, T, H, Hkv, scale, sl2);
+      attn_bwd_dkdv_bf16_kernel<NW, false><<<grid_kv, 64 * NW, 0, L.stream>>>(q, dO, L2buf, Dpk, dq, nullptr, rope, T,
                                                                               H, Hkv, scale, sl2);
     }
   } else {

@@ -1,21 +1,22 @@
 // The attention backward for callers that cannot allocate device memory
 // (code under HIP graph capture, tight serving loops, harnesses that forbid
 // hipMalloc): gpt2_op_attention_bwd_noalloc runs the same kernels as
-// gpt2_op_attention_bwd, with the per-row D = rowsum(dO o O) buffer in a
+// gpt2_op_attention_bwd, with its per-row buffers (D = rowsum(dO o O) and
+// the log-sum-exp in log2 units, the workspace of gpt2_op_attention_bwd) in a
 // static device array of this library instead of a caller-given workspace.
 //
 // The array lives on every GPU the library runs on until the process ends.
 // Host code never uses its name as an address: on each device, the first
 // call (with that device current) asks the runtime for the device address of
 // the array and keeps it for that device.  Every call on one GPU shares that
-// GPU's array; the kernels write every D entry they read, so nothing needs
+// GPU's array; the kernels write every entry they read, so nothing needs
 // clearing between calls, but calls that overlap in time on one GPU (two
 // streams, two threads) race on it.
 #include <mutex>
 
 #include "common.h"
 
-constexpr size_t kNoAllocFloats = size_t(1) << 20;  // 4 MiB: B * H * T <= 1,048,576
+constexpr size_t kNoAllocFloats = size_t(1) << 21;  // 8 MiB: two floats per row, B * H * T <= 1,048,576
 
 static __device__ __align__(256) float scratch[kNoAllocFloats];
 

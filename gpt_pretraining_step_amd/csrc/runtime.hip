@@ -334,7 +334,7 @@ Layout build_layout(const gpt2_config& c) {
     y.dQKV = s.take(rows * NQKV * y.es);
     y.dU = s.take(rows * FU * y.es);
   }
-  y.attnD = s.take(rows * H * 4);
+  y.attnD = s.take(attention_bwd_scratch(1, (int)rows, H));
   y.seg = s.take(rows * 4);  // document starts of packed windows
   if (c.arch == GPT2_ARCH_ROTARY) y.rope = s.take((size_t)c.block_size * 32 * sizeof(float2));
   if (c.precision == GPT2_PRECISION_BF16) {

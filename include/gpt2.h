@@ -486,7 +486,8 @@ int gpt2_op_attention_fwd(void* stream, int dtype, int B, int T, int H, int Hkv,
                           void* d_y, float* d_lse, const int32_t* d_seg);
 /* Backward: dqkv [B*T, (H + 2 Hkv) hd] is written (a shared key/value
  * head receives the sum over its query heads).  d_scratch needs
- * gpt2_attention_bwd_scratch_bytes(B, T, H) bytes; d_seg as in the forward.
+ * gpt2_attention_bwd_scratch_bytes(B, T, H) = 8 B H T bytes (two floats
+ * per row, 4-byte aligned); d_seg as in the forward.
  * d_rope (nullable; bf16 only, 16-byte aligned): a [T][32] (cos, sin) table
  * as gpt2_op_rope_table writes it; dq and dk are then rotated back with the
  * transpose of the rotary embedding at their row's position before they
@@ -500,9 +501,10 @@ int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv,
 /* The attention backward above without a workspace argument, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): the same kernels, with
- * D = rowsum(dO o O) kept in a static device array of the library (one per
- * GPU, gpt2_noalloc_scratch_bytes() = 4 MiB, held until the process ends).
- * B * H * T must not exceed gpt2_noalloc_scratch_bytes() / 4 = 1,048,576
+ * their two floats per row (D = rowsum(dO o O) and the row's log-sum-exp in
+ * log2 units) kept in a static device array of the library (one per GPU,
+ * gpt2_noalloc_scratch_bytes() = 8 MiB, held until the process ends).
+ * B * H * T must not exceed gpt2_noalloc_scratch_bytes() / 8 = 1,048,576
  * (GPT2_ERR_SHAPE otherwise; nothing is launched).  Allocates nothing: the
  * first call on a device looks up that device's copy of the array once.
  * Every call on one GPU shares the array; calls that overlap in time on one

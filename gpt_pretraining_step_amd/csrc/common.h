@@ -146,8 +146,12 @@ hipError_t launch_segment_starts(const Launch& L, const int32_t* tok, int B, int
 // seg (nullable): positions restart at each document start, t - seg[b, t].
 hipError_t launch_embed_fwd(const Launch& L, const int32_t* tok, const float* wte, const float* wpe, float* out,
                             int B, int T, int C, int V, int* flag, const int32_t* seg);
+// Deterministic: every gradient row sums its token's (position's) rows in a
+// fixed order.  part: [B*T, C] float32 scratch; ws: embed_bwd_scratch bytes.
+size_t embed_bwd_scratch(int rows);
+int embed_bwd_max_rows();  // rows (B * T) one backward call can take: 131,072
 hipError_t launch_embed_bwd(const Launch& L, const int32_t* tok, const float* dr, float* dwte, float* dwpe, int B,
-                            int T, int C, int V, const int32_t* seg);
+                            int T, int C, int V, const int32_t* seg, float* part, void* ws);
 
 // Cross-entropy helpers for the chunked lm_head.
 // count = number of targets in [0, V) other than ignore_index (the fp32 row

@@ -156,6 +156,8 @@ bool check_config(const gpt2_config* c) {
     if (hd > 64) return false;
   }
   if ((int64_t)c->max_batch * c->block_size > (1 << 30) / 4) return false;
+  // the embedding backward's sorted scatter keeps every 32-row tile's first key in LDS
+  if ((int64_t)c->max_batch * c->block_size > (int64_t)embed_bwd_max_rows()) return false;
   if (c->arch != GPT2_ARCH_GPT2 && c->arch != GPT2_ARCH_ROTARY) return false;
   if (c->arch == GPT2_ARCH_ROTARY) {
     // bf16 kernels only: vector RMSNorm (C % 256), paired rotary / SwiGLU
@@ -263,7 +265,7 @@ struct Layout {
   size_t Z = 0, meanf = 0, rstdf = 0, act_bytes = 0;
   // scratch
   size_t dR = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
-  size_t ce_stats = 0, rope = 0, seg = 0;
+  size_t ce_stats = 0, rope = 0, seg = 0, embws = 0;
   size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, step = 0, adam_sc = 0, scratch_bytes = 0;
   // bf16: the first operands of the weight-gradient products, kept per layer
   // until the products run together at the end of the backward: dRbS[2l+1]
@@ -336,6 +338,7 @@ Layout build_layout(const gpt2_config& c) {
   }
   y.attnD = s.take(attention_bwd_scratch(1, (int)rows, H));
   y.seg = s.take(rows * 4);  // document starts of packed windows
+  y.embws = s.take(embed_bwd_scratch((int)rows));  // sort of the embedding gradient
   if (c.arch == GPT2_ARCH_ROTARY) y.rope = s.take((size_t)c.block_size * 32 * sizeof(float2));
   if (c.precision == GPT2_PRECISION_BF16) {
     for (int l = 0; l < 2 * L; ++l) y.dRbS.push_back(s.take(rows * C * 2));
@@ -723,7 +726,9 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
                                    c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)), M, C));
   }
   if (bf) HIP_TRY(run_dw(c, q, M));
-  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V, seg));
+  // (dA, free after the last block, holds the scatter's partial sums)
+  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V, seg,
+                           static_cast<float*>(dA), c->scr(y.embws)));
   return GPT2_OK;
 }
 
@@ -840,7 +845,8 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
                                c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C));
   }
   HIP_TRY(run_dw(c, q, M));
-  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V, seg));
+  HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V, seg,
+                           static_cast<float*>(dA), c->scr(y.embws)));
   return GPT2_OK;
 }
 

@@ -66,7 +66,10 @@ enum { GPT2_ARCH_GPT2 = 0, GPT2_ARCH_ROTARY = 1 };
  * Limits: n_embd % n_head == 0; head_dim = n_embd / n_head must be 64 in
  * BF16 mode and at most 64 in FP32 mode; in BF16 mode vocab_size, n_embd and
  * mlp_hidden must be multiples of 8 (the page pads the vocabulary to 50304
- * for the same alignment reason, section 8.3).
+ * for the same alignment reason, section 8.3); max_batch * block_size (the
+ * rows of one micro-step) at most 131,072 (the embedding backward sorts a
+ * micro-step's rows by token so that every gradient row sums its rows in a
+ * fixed order).
  * arch selects the model family:
  *   GPT2_ARCH_GPT2:   the GPT-2 model above (LayerNorm, learned positions,
  *                     GELU MLP of width mlp_hidden, biases).

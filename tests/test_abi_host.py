@@ -76,9 +76,11 @@ def test_rotary_param_table_matches_oracle_specs():
                 g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, 7),
                 g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY, n_kv_head=3),  # 4 % 3
                 g.ModelConfig(1024, 256, 2, 4, 256, 160, 3, g.PRECISION_BF16, g.ARCH_ROTARY, n_kv_head=-1),
-                g.ModelConfig(1024, 256, 2, 4, 256, 1024, 3, g.PRECISION_BF16, n_kv_head=2)):  # GPT-2: MHA only
+                g.ModelConfig(1024, 256, 2, 4, 256, 1024, 3, g.PRECISION_BF16, n_kv_head=2),  # GPT-2: MHA only
+                g.ModelConfig(1024, 1024, 2, 2, 128, 512, 129, g.PRECISION_BF16)):  # > 131,072 rows
         with pytest.raises(g.GPT2Error):
             g.query_sizes(bad)
+    g.query_sizes(g.ModelConfig(1024, 1024, 2, 2, 128, 512, 128, g.PRECISION_BF16))  # 131,072 rows
 
 
 def _cfgs():

@@ -244,6 +244,32 @@ def test_full_accumulation_identity_on_gpu(g, full):
 
 
 @pytest.mark.timeout(600)
+def test_full_embedding_gradients_are_deterministic(g, full):
+    """The embedding gradients of a micro-step are bitwise identical when it
+    is run again: the Zipf stream repeats ids hundreds of times among the
+    16,384 rows, and each wte row sums its token's rows in row order (no
+    atomics); with the document mask the restarted positions scatter into
+    wpe the same way."""
+    cfg, m, stream = full
+    x, y = synthetic.micro_batch(stream, 0, 16, 1024)
+    counts = np.bincount(x.reshape(-1))
+    assert counts.max() >= 100  # ids really repeat
+    for eot in (None, synthetic.EOT_ID):
+        announce(f"gpt2-124m embedding gradient determinism, doc mask {eot}")
+        m.set_doc_mask(eot)
+        runs = []
+        for _ in range(2):
+            m.zero_grad()
+            run_gpu(g, m, x, y)
+            gr = read_named(m, m.grads)
+            runs.append((gr["transformer.wte.weight"].copy(), gr["transformer.wpe.weight"].copy()))
+        assert np.array_equal(runs[0][0], runs[1][0]), eot
+        assert np.array_equal(runs[0][1], runs[1][1]), eot
+    m.set_doc_mask(None)
+    m.zero_grad()
+
+
+@pytest.mark.timeout(600)
 def test_full_optimizer_step_adamw_parity(g, full):
     """Full optimizer step at the benchmarked shape: grads accumulated over
     micro-steps with loss/G, then clip 1.0 + AdamW (lr 6e-4, betas 0.9/0.95,

@@ -1,8 +1,8 @@
 // Matrix products of the training step.
 //
 // bf16: the multi-stage MFMA kernel of gemm_kernel.h on 256x256 tiles.
-// float32 (FP32 precision mode, small models): a plain LDS-tiled SIMT kernel
-// with the same operand layouts and epilogues.
+// float32 (FP32 precision mode, small models): a float32-MFMA kernel on
+// 64x64 tiles with the same operand layouts and epilogues.
 //
 // The epilogues fuse what follows each product in the step: bias, the
 // residual add of the block ("How I trained my own GPT-2 124M on
@@ -21,7 +21,14 @@
 
 namespace g2 {
 
-// ------------------------------------------------------- float32 SIMT GEMM
+// ------------------------------------------------------- float32 MFMA GEMM
+//
+// FP32 precision mode: v_mfma_f32_32x32x2_f32 on 64x64 block tiles (4 waves,
+// each one 32x32 MFMA tile), K step 16 staged through LDS as [k][row] for
+// either operand layout (ragged edges read as zeros), float32 accumulation;
+// the same epilogues as the bf16 kernel, element by element.  The MFMA takes
+// A[row = lane % 32][k = lane / 32] and B[k = lane / 32][col = lane % 32]
+// and leaves D[8 (r / 4) + 4 (lane / 32) + r % 4][lane % 32] in register r.
 
 template <bool A_K, bool B_K, int EPI, bool ATOMIC>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmP p) {
@@ -35,10 +42,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmP p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int lr = lane & 31, lg = lane >> 5;
   const float* A = static_cast<const float*>(p.A);
   const float* B = static_cast<const float*>(p.B);
-  float acc[4][4] = {};
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
     for (int e = threadIdx.x; e < BM * BK; e += 256) {
       int mm, kk;
@@ -58,26 +69,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmP p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
+    for (int kk = 0; kk < BK; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + lg][wm + lr], Bs[kk + lg][wn + lr], acc, 0, 0, 0);
     __syncthreads();
   }
+  const int n = n0 + wn + lr;
+  if (n >= p.N) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + ty + 16 * i, n = n0 + tx + 16 * j;
-      if (m < p.M && n < p.N) epi_store<EPI, false, ATOMIC>(p, m, n, acc[i][j]);
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wm + 8 * (r >> 2) + 4 * lg + (r & 3);
+    if (m < p.M) epi_store<EPI, false, ATOMIC>(p, m, n, acc[r]);
+  }
 }
 
 // ------------------------------------------------------------- dispatching

@@ -54,6 +54,27 @@ def test_gemm_bf16_integer_exact(g, ak, bk, M, N, K):
     assert np.array_equal(host(C), ref)
 
 
+@pytest.mark.parametrize("ak,bk", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_fp32_mfma_integer_exact(g, ak, bk, M, N, K):
+    """The float32 mode's product (float32 MFMA on 64x64 tiles): exact on
+    small integers in every layout, over ragged tiles and K steps, with the
+    residual epilogue on top."""
+    import torch
+    announce(f"gemm fp32 int M={M} N={N} K={K} ak={ak} bk={bk}")
+    rng = np.random.default_rng(M * 5 + N * 11 + K)
+    A = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, size=(N, K)).astype(np.float32)
+    R = rng.integers(-50, 51, size=(M, N)).astype(np.float32)
+    ref = (A.astype(np.int64) @ B.astype(np.int64).T).astype(np.float32)
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    g.op_gemm(dev(_stored(A, ak)), dev(_stored(B, bk)), C, M, N, K, a_kmajor=ak, b_kmajor=bk)
+    assert np.array_equal(host(C), ref)
+    g.op_gemm(dev(_stored(A, ak)), dev(_stored(B, bk)), C, M, N, K, a_kmajor=ak, b_kmajor=bk,
+              epilogue=g.EPI_RESIDUAL, R=dev(R))
+    assert np.array_equal(host(C), ref + R)
+
+
 def test_gemm_bf16_integer_exact_large_tiles(g):
     import torch
     M, N, K = 4096, 8192, 64  # >= 1024 tiles of 256x128: the large-tile kernel

@@ -222,6 +222,9 @@ int gpt2_zero_grad(gpt2_ctx* ctx);
  * The logits are never stored whole: the tied lm_head and the loss run over
  * chunks of 8192 rows (bf16 mode, as gpt2_lmhead_ce) or 4096 rows (FP32
  * mode), and each chunk's part of the backward runs before the next chunk.
+ * The embedding gradients (wte rows of repeated tokens, and wpe rows of
+ * restarted positions under the document mask) are summed in a fixed order,
+ * so they are the same bit for bit when a call is repeated.
  * The first call on a context (any B, T) also copies the weight-gradient
  * launch's table to the scratch buffer, once, asynchronously on the stream;
  * the call does not synchronise. */

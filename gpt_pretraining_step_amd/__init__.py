@@ -24,7 +24,7 @@ from ._ffi import (GPT2Error, check, lib, PRECISION_BF16, PRECISION_FP32,  # noq
                    EPI_ROPE, EPI_SWIGLU, EPI_SWIGLU_BWD, ARCH_GPT2, ARCH_ROTARY, GPT2_ERR_ARG)
 
 __all__ = ["ModelConfig", "GPT2", "TINY_CHAR_FP32", "GPT2_124M", "GPT2Error", "lmhead_ce", "op_gemm", "op_gemm_grouped",
-           "op_attention_fwd", "op_attention_bwd", "op_attention_bwd_noalloc", "op_segment_starts", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
+           "op_attention_fwd", "op_attention_bwd", "op_attention_bwd_noalloc", "op_embedding_bwd", "op_segment_starts", "op_layernorm_fwd", "op_layernorm_bwd", "op_colsum", "op_marker",
            "op_rope_table", "op_rope_bwd", "op_rmsnorm_fwd", "op_rmsnorm_bwd", "query_sizes", "param_table",
            "GPT2_ROTARY_124M"]
 
@@ -414,6 +414,26 @@ def _check_seg(seg, B, T):
     import torch
     if seg is not None:
         assert seg.dtype == torch.int32 and seg.is_contiguous() and seg.numel() == B * T
+
+
+def op_embedding_bwd(tokens, dres, dwte, dwpe=None, seg=None, stream=None):
+    """dwte[tokens[i]] += dres[i] and dwpe[t(i)] += dres[i] (float32, accumulated
+    in place; t(i) restarts at document starts when seg is given), each
+    gradient row summing its rows in increasing i."""
+    import torch
+    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.dim() == 2
+    B, T = tokens.shape
+    V, C = dwte.shape
+    assert dres.dtype == torch.float32 and dres.is_contiguous() and dres.numel() == B * T * C
+    assert dwte.dtype == torch.float32 and dwte.is_contiguous()
+    if dwpe is not None:
+        assert dwpe.dtype == torch.float32 and dwpe.is_contiguous() and dwpe.shape == (T, C)
+    _check_seg(seg, B, T)
+    nbytes = lib().gpt2_embedding_bwd_scratch_bytes(B * T, C)
+    scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dres.device)
+    check(lib().gpt2_op_embedding_bwd(_stream_ptr(stream), tokens.data_ptr(), dres.data_ptr(), dwte.data_ptr(),
+                                      _ptr(dwpe), B, T, C, V, _ptr(seg), scratch.data_ptr()),
+          "gpt2_op_embedding_bwd")
 
 
 def op_segment_starts(tokens, eot: int, stream=None):

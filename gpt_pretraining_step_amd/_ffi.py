@@ -122,6 +122,9 @@ SIGNATURES = {
     "gpt2_op_attention_bwd_noalloc": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
                                                  ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                                  ct.c_void_p, ct.c_void_p, ct.c_void_p]),
+    "gpt2_embedding_bwd_scratch_bytes": (ct.c_size_t, [ct.c_int, ct.c_int]),
+    "gpt2_op_embedding_bwd": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
+                                         ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]),
     "gpt2_op_segment_starts": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "gpt2_profile_enable": (ct.c_int, [ct.c_void_p, ct.c_int]),
     "gpt2_profile_only": (ct.c_int, [ct.c_void_p, ct.c_char_p]),

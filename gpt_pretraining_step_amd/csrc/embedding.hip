@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
 // [N, C], each destination row summing its source rows in increasing i, so
 // the result does not depend on scheduling (float addition is not
 // associative; atomics would make the gradient vary from run to run).
-//  1. a stable LSD radix sort (8-bit digits) of (key, row) pairs: rows come
-//     out grouped by key and, within a key, in increasing row order;
+//  1. a stable sort of (key, row) pairs by key: rows come out grouped by key
+//     and, within a key, in increasing row order (up to 16,384 rows: one
+//     block, in LDS; more: LSD radix passes of 8-bit digits over the grid);
 //  2. the sorted list in tiles of 32 positions: each tile sums every run of
 //     one key that falls inside it, in order; a run that is the key's whole
 //     run is added to dst there, otherwise its sum goes to part[first
@@ -89,261 +90,380 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
 //     adds the partials of its tiles, in tile order, to dst.
 // Every destination row has exactly one writer, in a fixed order.
 constexpr int kScatTile = 32;
+constexpr int kScatMaxTiles = 4096;  // rows one call sorts: at most 131,072
 
-__global__ __launch_bounds__(256) void scat_keys_tok_kernel(const int32_t* __restrict__ tok, int N, int V,
-                                                            int32_t* __restrict__ key, int32_t* __restrict__ val) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= N) return;
-  const int id = tok[i];
-  key[i] = (id < 0 || id >= V) ? 0 : id;  // the forward flagged it and read row 0
-  val[i] = i;
-}
-__global__ __launch_bounds__(256) void scat_keys_pos_kernel(const int32_t* __restrict__ seg, int N, int T,
-                                                            int32_t* __restrict__ key, int32_t* __restrict__ val) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= N) return;
-  key[i] = min(max(i % T - seg[i], 0), T - 1);  // (starts from segment_start_kernel are in range)
-  val[i] = i;
-}
+template <int VW>
+struct FVec;
+template <>
+struct FVec<1> {
+  using T = float;
+  static __device__ __forceinline__ T zero() { return 0.f; }
+  static __device__ __forceinline__ T add(T a, T b) { return a + b; }
+};
+template <>
+struct FVec<2> {
+  using T = float2;
+  static __device__ __forceinline__ T zero() { return make_float2(0.f, 0.f); }
+  static __device__ __forceinline__ T add(T a, T b) { return make_float2(a.x + b.x, a.y + b.y); }
+};
+template <>
+struct FVec<4> {
+  using T = float4;
+  static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ __forceinline__ T add(T a, T b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+};
 
-// Exclusive scan of n ints in place by one block of 1024 threads: chunks of
-// 4096 staged through LDS (coalesced), four consecutive elements per
-// thread, wave scans by shuffles, the 16 wave totals scanned by one wave,
-// a running carry between chunks.
-__global__ __launch_bounds__(1024) void scat_scan_kernel(int* __restrict__ a, int n) {
-  __shared__ int buf[4096];
-  __shared__ int wtot[16];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  int carry = 0;
-  for (int base = 0; base < n; base += 4096) {
-    const int m = min(4096, n - base);
-    for (int i = t; i < m; i += 1024) buf[i] = a[base + i];
-    __syncthreads();
-    int x[4], s = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[u] = 4 * t + u < m ? buf[4 * t + u] : 0;
-      s += x[u];
-    }
-    int inc = s;  // inclusive scan of the thread totals within the wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(inc, d);
-      if (lane >= d) inc += v;
-    }
-    if (lane == 63) wtot[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-      int w = lane < 16 ? wtot[lane] : 0;
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) {
-        const int v = __shfl_up(w, d);
-        if (lane >= d) w += v;
-      }
-      if (lane < 16) wtot[lane] = w;  // inclusive over the waves
-    }
-    __syncthreads();
-    int run = carry + (wave ? wtot[wave - 1] : 0) + inc - s;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (4 * t + u < m) buf[4 * t + u] = run;
-      run += x[u];
-    }
-    carry += wtot[15];
-    __syncthreads();
-    for (int i = t; i < m; i += 1024) a[base + i] = buf[i];
-    __syncthreads();
+// Step 1: LSD radix passes over 8-bit digits of the key, 1,024 elements per
+// block (one per thread), two launches per pass.
+//  count: block b's digit histogram -> hist[d * nb + b] (the first pass
+//         also forms the keys and the row indices, in row order);
+//  place: block b finds, for every digit d, its first position: the count
+//         of smaller digits overall plus the count of d in blocks before b;
+//         each wave ranks its 64 elements among the lanes of equal digit
+//         (ballots on the digit's 8 bits), the waves' counts are prefixed in
+//         wave order, and every element goes to first[d] + (earlier waves'
+//         count of d) + rank.
+// Each pass is stable, so the result is sorted by (key, row).
+constexpr int kRadixBlock = 1024;
+__device__ __forceinline__ int scat_key(const int32_t* __restrict__ ids, int i, int nkeys, int T, bool by_token) {
+  if (by_token) {
+    const int id = ids[i];
+    return (id < 0 || id >= nkeys) ? 0 : id;  // the forward flagged it and read row 0
   }
+  return min(max(i % T - ids[i], 0), T - 1);  // (starts from segment_start_kernel are in range)
 }
 
-// Radix pass, digit (key >> shift) & 255; nb blocks of 256 elements.
-// hist[d * nb + block] = how many of the block's elements have digit d.
-__global__ __launch_bounds__(256) void radix_hist_kernel(const int32_t* __restrict__ key, int N, int shift,
-                                                         int* __restrict__ hist) {
-  __shared__ int h[256];
-  h[threadIdx.x] = 0;
-  __syncthreads();
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < N) atomicAdd(&h[(key[i] >> shift) & 255], 1);
-  __syncthreads();
-  hist[threadIdx.x * gridDim.x + blockIdx.x] = h[threadIdx.x];
+// dwpe[t, :] += sum_b dR[b,t,:], b in increasing order (no atomics): thread
+// e owns VW columns of one position, its B loads in flight 16 at a time.
+template <int VW>
+__device__ __forceinline__ void wpe_sum(const float* __restrict__ dr, float* __restrict__ dwpe, int B, int T, int C,
+                                        int64_t e) {
+  using F = FVec<VW>;
+  using VT = typename F::T;
+  const int64_t i = e * VW;
+  const int64_t TC = (int64_t)T * C;
+  if (i >= TC) return;
+  VT s = *reinterpret_cast<const VT*>(dr + i);
+  for (int b0 = 1; b0 < B; b0 += 16) {
+    VT v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const VT*>(dr + (b0 + u < B ? b0 + u : 0) * TC + i);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (b0 + u < B) s = F::add(s, v[u]);
+  }
+  VT* o = reinterpret_cast<VT*>(dwpe + i);
+  *o = F::add(*o, s);
 }
-// Stable scatter: an element's place among the block's elements of its digit
-// is the count of those before it (lanes below it in its wave, found with
-// ballots on the digit's 8 bits, plus the earlier waves' counts).
-__global__ __launch_bounds__(256) void radix_scatter_kernel(const int32_t* __restrict__ key,
-                                                            const int32_t* __restrict__ val, int N, int shift,
-                                                            const int* __restrict__ off, int32_t* __restrict__ key2,
-                                                            int32_t* __restrict__ val2) {
-  __shared__ int wc[4][256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = threadIdx.x; j < 4 * 256; j += 256) (&wc[0][0])[j] = 0;
+
+// Blocks [0, nb) count; with WVW > 0 the blocks after them sum the position
+// table's gradient (wpe_sum, VW = WVW), independent work that fills the
+// compute units the sort leaves idle.
+template <bool FIRST, int WVW>
+__global__ __launch_bounds__(kRadixBlock) void radix_count_kernel(const int32_t* __restrict__ ids, int N, int nb,
+                                                                  int nkeys, int T, int by_token, int shift,
+                                                                  int32_t* __restrict__ key,
+                                                                  int32_t* __restrict__ val, int* __restrict__ hist,
+                                                                  const float* __restrict__ wsrc,
+                                                                  float* __restrict__ wdst, int B, int C) {
+  if constexpr (WVW > 0) {
+    if ((int)blockIdx.x >= nb) {
+      wpe_sum<WVW>(wsrc, wdst, B, T, C, (int64_t)(blockIdx.x - nb) * kRadixBlock + threadIdx.x);
+      return;
+    }
+  }
+  __shared__ int h[256];
+  if (threadIdx.x < 256) h[threadIdx.x] = 0;
   __syncthreads();
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = blockIdx.x * kRadixBlock + threadIdx.x;
+  if (i < N) {
+    int k;
+    if constexpr (FIRST) {
+      k = scat_key(ids, i, nkeys, T, by_token != 0);
+      key[i] = k;
+      val[i] = i;
+    } else {
+      k = key[i];
+    }
+    atomicAdd(&h[(k >> shift) & 255], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) hist[threadIdx.x * nb + blockIdx.x] = h[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kRadixBlock) void radix_place_kernel(const int32_t* __restrict__ key,
+                                                                  const int32_t* __restrict__ val, int N, int shift,
+                                                                  const int* __restrict__ hist,
+                                                                  int32_t* __restrict__ key2,
+                                                                  int32_t* __restrict__ val2) {
+  __shared__ int first[256];
+  __shared__ int wc[kRadixBlock / 64][256];
+  __shared__ int wsum[4];
+  const int nb = gridDim.x, blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // per digit (threads 0..255): its elements in earlier blocks, and in all
+  int before = 0, total = 0;
+  if (tid < 256) {
+    const int* hd = hist + tid * nb;
+    for (int j0 = 0; j0 < nb; j0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = j0 + u < nb ? hd[j0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        total += c[u];
+        before += j0 + u < blk ? c[u] : 0;
+      }
+    }
+  }
+  int inc = total;  // inclusive scan of the totals within each wave of digits
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d);
+    if (lane >= d) inc += v;
+  }
+  if (tid < 256 && lane == 63) wsum[wave] = inc;
+  for (int d = lane; d < 256; d += 64) wc[wave][d] = 0;
+  // this wave's 64 elements: rank among the lanes of equal digit
+  const int i = blk * kRadixBlock + tid;
   const bool ok = i < N;
   const int k = ok ? key[i] : 0;
-  const int d = (k >> shift) & 255;
+  const int dg = (k >> shift) & 255;
   uint64_t same = __ballot(ok);
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const uint64_t m = __ballot((d >> b) & 1);
-    same &= ((d >> b) & 1) ? m : ~m;
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t m = __ballot((dg >> bit) & 1);
+    same &= ((dg >> bit) & 1) ? m : ~m;
   }
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  const int rank = __popcll(same & below);
-  if (ok && rank == 0) wc[wave][d] = __popcll(same);
+  const int rank = __popcll(same & ((1ull << lane) - 1));
+  __syncthreads();  // wsum and the zeroed wc rows are complete
+  if (ok && rank == 0) wc[wave][dg] = __popcll(same);
+  if (tid < 256) {
+    int off = inc - total + before;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    first[tid] = off;
+  }
   __syncthreads();
-  if (!ok) return;
-  int pos = off[d * gridDim.x + blockIdx.x] + rank;
-  for (int w = 0; w < wave; ++w) pos += wc[w][d];
-  key2[pos] = k;
-  val2[pos] = val[i];
+  if (tid < 256) {  // per digit: the waves' counts -> counts of earlier waves
+    int run = 0;
+    for (int w = 0; w < kRadixBlock / 64; ++w) {
+      const int c = wc[w][tid];
+      wc[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (ok) {
+    const int pos = first[dg] + wc[wave][dg] + rank;
+    key2[pos] = k;
+    val2[pos] = val[i];
+  }
 }
 
-// Step 2 over the sorted (key, row) list.  A thread owns columns c, c + 256,
-// ...; it loads the tile's 32 source values of a column first (independent
-// loads in flight together), then sums the runs in order.
-__global__ __launch_bounds__(256) void scat_tile_kernel(const int32_t* __restrict__ skey,
+// Step 2 over the sorted (key, row) list, one block per tile.  Wave 0 finds
+// the tile's runs with ballots: for each position j, whether a run ends there
+// (end), whether that run is its key's whole run (whole: it neither began
+// before the tile nor continues after it) and the run's first position in
+// the tile (head).  Every thread then owns VW adjacent columns: it loads the
+// tile's 32 source rows and the destination rows of its whole runs (all
+// independent loads in flight together), sums the runs in order, and writes
+// dst (whole runs) or part[p0 + head] (the others).
+template <int VW>
+__global__ __launch_bounds__(512) void scat_tile_kernel(const int32_t* __restrict__ skey,
                                                         const int32_t* __restrict__ srow, int N,
                                                         const float* __restrict__ src, int C,
                                                         float* __restrict__ dst, float* __restrict__ part) {
-  __shared__ int key[kScatTile + 2], row[kScatTile];
+  using F = FVec<VW>;
+  using VT = typename F::T;
+  // per position j, as element offsets (N C and V C stay below 2^31,
+  // checked by the host): the source row; the dst row read for a whole run
+  // ending at j (else the tile's first key's, read and not written); where
+  // a run ending at j goes (kind 1: dst, 2: part, 0: no run ends at j)
+  __shared__ int s_src[kScatTile], s_ld[kScatTile], s_st[kScatTile], s_kind[kScatTile];
   const int p0 = blockIdx.x * kScatTile, n = min(N - p0, kScatTile);
-  if (threadIdx.x < n) {
-    key[threadIdx.x + 1] = skey[p0 + threadIdx.x];
-    row[threadIdx.x] = srow[p0 + threadIdx.x];
-  }
-  if (threadIdx.x == 0) {
-    key[0] = p0 > 0 ? skey[p0 - 1] : -1;      // the key before the tile
-    key[n + 1] = p0 + n < N ? skey[p0 + n] : -1;  // and after it
-  }
-  __syncthreads();
-  // run structure (the same for every column): end[j] = a run ends at j;
-  // whole[j] = and it is its key's whole run, added to dst here; otherwise
-  // its sum goes to part at the run's first position head[j]
-  __shared__ bool end[kScatTile], whole[kScatTile];
-  __shared__ int head[kScatTile];
-  if (threadIdx.x == 0) {
-    int a = 0;
-    for (int j = 0; j < kScatTile; ++j) {
-      end[j] = j < n && (key[j + 2] != key[j + 1] || j + 1 == n);
-      if (end[j]) {
-        const int k = key[j + 1];
-        whole[j] = !(a == 0 && key[0] == k) && !(j + 1 == n && key[n + 1] == k);
-        head[j] = a;
-        a = j + 1;
-      }
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const bool in = l < n;
+    const int k = in ? skey[p0 + l] : -1;
+    const int kprev = p0 > 0 ? skey[p0 - 1] : -1;   // the key before the tile
+    const int knext = p0 + n < N ? skey[p0 + n] : -1;  // and after it
+    const int kl = __shfl(k, l > 0 ? l - 1 : 0), kr = __shfl(k, l + 1 < 64 ? l + 1 : 63);
+    const uint64_t heads = __ballot(in && (l == 0 || kl != k));
+    const int head = 63 - __clzll(heads & ((2ull << l) - 1));
+    const bool end = in && (l == n - 1 || kr != k);
+    const bool whole = end && !(head == 0 && kprev == k) && !(l == n - 1 && knext == k);
+    const int k0 = __shfl(k, 0), r0 = srow[p0];
+    if (l < kScatTile) {
+      s_src[l] = (in ? srow[p0 + l] : r0) * C;
+      s_ld[l] = (whole ? k : k0) * C;
+      s_st[l] = whole ? k * C : (p0 + head) * C;
+      s_kind[l] = whole ? 1 : end ? 2 : 0;
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float v[kScatTile], d[kScatTile];
+  for (int c = VW * threadIdx.x; c < C; c += VW * blockDim.x) {
+    // the tile in two halves of 16 positions (fewer registers, so that two
+    // blocks share a compute unit); the run sum carries across
+    VT acc = F::zero();
 #pragma unroll
-    for (int j = 0; j < kScatTile; ++j) v[j] = j < n ? src[(int64_t)row[j] * C + c] : 0.f;
-    // the dst rows the tile adds to, loaded together
+    for (int h = 0; h < kScatTile; h += kScatTile / 2) {
+      VT v[kScatTile / 2], d[kScatTile / 2];
 #pragma unroll
-    for (int j = 0; j < kScatTile; ++j) d[j] = end[j] && whole[j] ? dst[(int64_t)key[j + 1] * C + c] : 0.f;
-    float acc = 0.f;
+      for (int j = 0; j < kScatTile / 2; ++j) v[j] = *reinterpret_cast<const VT*>(src + (uint32_t)(s_src[h + j] + c));
 #pragma unroll
-    for (int j = 0; j < kScatTile; ++j) {
-      acc += v[j];
-      if (end[j]) {
-        if (whole[j]) dst[(int64_t)key[j + 1] * C + c] = d[j] + acc;
-        else part[(int64_t)(p0 + head[j]) * C + c] = acc;
-        acc = 0.f;
+      for (int j = 0; j < kScatTile / 2; ++j) d[j] = *reinterpret_cast<const VT*>(dst + (uint32_t)(s_ld[h + j] + c));
+#pragma unroll
+      for (int j = 0; j < kScatTile / 2; ++j) {
+        acc = F::add(acc, v[j]);
+        const int kind = s_kind[h + j];
+        if (kind == 1) *reinterpret_cast<VT*>(dst + (uint32_t)(s_st[h + j] + c)) = F::add(d[j], acc);
+        else if (kind == 2) *reinterpret_cast<VT*>(part + (uint32_t)(s_st[h + j] + c)) = acc;
+        if (kind) acc = F::zero();
       }
     }
   }
 }
 // Step 3: block t joins the key whose run starts in tile t and continues
-// past its end (at most one per tile).  The tile's keys and every tile's
-// first key are staged in LDS, so finding the run's extent takes no
-// dependent global loads.
-constexpr int kScatMaxTiles = 4096;  // tile-start keys held in LDS: N <= 131,072
+// past its end (at most one per tile): its partials are the one at the
+// run's first position a and those at the first positions of tiles t+1 ..
+// t+m.  The block's threads form G groups of one thread per VW columns;
+// group g sums the g-th contiguous share of the partials in order, and the
+// G group sums are then added in group order (a fixed order for a given m).
+template <int VW>
 __global__ __launch_bounds__(1024) void scat_join_kernel(const int32_t* __restrict__ skey, int N, int C,
                                                         const float* __restrict__ part, float* __restrict__ dst) {
-  __shared__ int tk[kScatTile], first[kScatMaxTiles];
-  __shared__ int s_a, s_m;
+  using F = FVec<VW>;
+  using VT = typename F::T;
+  __shared__ int s_a, s_k, s_own;
+  __shared__ VT gsum[1024];
   const int t = blockIdx.x, ntiles = (N + kScatTile - 1) / kScatTile;
   const int p0 = t * kScatTile, p1 = min(N, p0 + kScatTile);
   if (p1 >= N) return;  // the last tile's runs end inside it
-  if (threadIdx.x < p1 - p0) tk[threadIdx.x] = skey[p0 + threadIdx.x];
-  for (int i = t + 1 + threadIdx.x; i < ntiles; i += blockDim.x) first[i] = skey[i * kScatTile];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int k = tk[p1 - p0 - 1];
-    int a = p1 - p0 - 1, m = 0;
-    if (first[t + 1] == k) {  // the tile's last run continues past its end
-      while (a > 0 && tk[a - 1] == k) --a;
-      if (!(a == 0 && p0 > 0 && skey[p0 - 1] == k)) {  // and began in this tile
-        m = 1;
-        while (t + 1 + m < ntiles && first[t + 1 + m] == k) ++m;  // tiles t+1 .. t+m hold the rest
-      }
+  if (threadIdx.x < 64) {
+    // the tile's keys and its two neighbours in one round of loads
+    const int l = threadIdx.x;
+    const int kl = p0 + l < p1 ? skey[p0 + l] : -1;
+    const int kafter = skey[p1], kbefore = p0 > 0 ? skey[p0 - 1] : -1;
+    const int k = __shfl(kl, p1 - p0 - 1);  // the tile's last key
+    const uint64_t eq = __ballot(kl == k);  // a suffix of the tile
+    const int a = p0 + __ffsll((long long)eq) - 1;
+    if (l == 0) {
+      s_k = k;
+      s_a = a;
+      // the run continues past the tile and began in it
+      s_own = kafter == k && (a > p0 || kbefore != k);
     }
-    s_a = p0 + a;
-    s_m = m;
   }
   __syncthreads();
-  const int m = s_m, a = s_a;
-  if (m == 0) return;
-  const int k = tk[p1 - p0 - 1];
-  // partials at a, then at the starts of tiles t+1 .. t+m; loaded 8 at a time,
-  // added in that order
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float acc = part[(int64_t)a * C + c];
-    for (int i = 1; i <= m; i += 16) {
-      float v[16];
+  if (!s_own) return;
+  const int a = s_a, k = s_k;
+  // tiles after t whose first key is k: consecutive, since the keys are sorted
+  __shared__ int s_m;
+  if (threadIdx.x == 0) s_m = 0;
+  __syncthreads();
+  int cm = 0;
+  for (int i = t + 1 + (int)threadIdx.x; i < ntiles; i += blockDim.x) cm += skey[i * kScatTile] == k;
+  if (cm) atomicAdd(&s_m, cm);
+  __syncthreads();
+  const int np = s_m + 1;  // partials: at a, then at p0 + 32 i for i = 1 .. m
+  const int cw = (C + VW - 1) / VW;                     // threads per row of columns
+  const int gw = (cw + 63) / 64 * 64;                   // a group: whole waves
+  const int G = gw <= (int)blockDim.x ? (int)blockDim.x / gw : 1;
+  const int g = G > 1 ? (int)threadIdx.x / gw : 0;
+  const int ct = G > 1 ? (int)threadIdx.x % gw : (int)threadIdx.x;
+  const int cstride = G > 1 ? gw : (int)blockDim.x;
+  const int lo = g * np / G, hi = (g + 1) * np / G;
+  auto pos = [&](int i) { return i == 0 ? a : p0 + i * kScatTile; };
+  // (G > 1) group 0 reads the destination row together with its partials
+  VT old = F::zero();
+  if (G > 1 && g == 0 && VW * ct < C) old = *reinterpret_cast<const VT*>(dst + (int64_t)k * C + VW * ct);
+  for (int c = VW * ct; c < C; c += VW * cstride) {
+    VT acc = F::zero();
+    if (g < G && lo < hi) {
+      acc = *reinterpret_cast<const VT*>(part + (int64_t)pos(lo) * C + c);
+      for (int i = lo + 1; i < hi; i += 16) {
+        VT v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = i + u <= m ? part[(int64_t)(p0 + (i + u) * kScatTile) * C + c] : 0.f;
+        for (int u = 0; u < 16; ++u)
+          v[u] = *reinterpret_cast<const VT*>(part + (int64_t)pos(i + u < hi ? i + u : lo) * C + c);
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (i + u <= m) acc += v[u];
+        for (int u = 0; u < 16; ++u)
+          if (i + u < hi) acc = F::add(acc, v[u]);
+      }
     }
-    dst[(int64_t)k * C + c] += acc;
+    if (G == 1) {
+      VT* o = reinterpret_cast<VT*>(dst + (int64_t)k * C + c);
+      *o = F::add(*o, acc);
+    } else {
+      gsum[threadIdx.x] = acc;
+    }
+  }
+  if (G == 1) return;
+  __syncthreads();
+  if (g == 0 && VW * ct < C) {
+    VT tot = gsum[ct];
+    for (int h = 1; h < G; ++h)
+      if (h * np / G < (h + 1) * np / G) tot = F::add(tot, gsum[h * gw + ct]);
+    *reinterpret_cast<VT*>(dst + (int64_t)k * C + VW * ct) = F::add(old, tot);
   }
 }
 
 size_t det_scatter_scratch(int N) {
-  const size_t nb = (size_t)(N + 255) / 256;
+  const size_t nb = (size_t)(N + kRadixBlock - 1) / kRadixBlock;
   return (4 * (size_t)N + 256 * nb) * sizeof(int) + 256;
 }
 
 // keys in [0, nkeys); part: [N, C] float32 scratch; ws: det_scatter_scratch(N) bytes.
+// With wpe != NULL (and B * T == N) the first launch also runs wpe_sum of src
+// into wpe.
 static hipError_t det_scatter_add(const Launch& L, bool by_token, const int32_t* ids, int N, int nkeys, int T,
-                                  const float* src, int C, float* dst, float* part, void* ws) {
+                                  const float* src, int C, float* dst, float* part, void* ws, float* wpe = nullptr,
+                                  int B = 0) {
   if ((N + kScatTile - 1) / kScatTile > kScatMaxTiles) return hipErrorInvalidValue;
-  const int nb = (N + 255) / 256;
+  // the tile pass addresses rows with 32-bit element offsets
+  if ((int64_t)N * C >= ((int64_t)1 << 31) || (int64_t)nkeys * C >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int nb = (N + kRadixBlock - 1) / kRadixBlock;
   int32_t* k0 = static_cast<int32_t*>(ws);
   int32_t* v0 = k0 + N;
   int32_t* k1 = v0 + N;
   int32_t* v1 = k1 + N;
   int* hist = v1 + N;
-  if (by_token) scat_keys_tok_kernel<<<nb, 256, 0, L.stream>>>(ids, N, nkeys, k0, v0);
-  else scat_keys_pos_kernel<<<nb, 256, 0, L.stream>>>(ids, N, T, k0, v0);
-  for (int shift = 0; (nkeys - 1) >> shift; shift += 8) {
-    radix_hist_kernel<<<nb, 256, 0, L.stream>>>(k0, N, shift, hist);
-    scat_scan_kernel<<<1, 1024, 0, L.stream>>>(hist, 256 * nb);
-    radix_scatter_kernel<<<nb, 256, 0, L.stream>>>(k0, v0, N, shift, hist, k1, v1);
-    std::swap(k0, k1);
-    std::swap(v0, v1);
+  const int64_t TC = (int64_t)T * C;
+  const bool wvec = (C % 4) == 0 && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(wpe)) & 15) == 0;
+  const int nw = wpe ? (int)((TC / (wvec ? 4 : 1) + kRadixBlock - 1) / kRadixBlock) : 0;
+  for (int shift = 0; shift == 0 || ((nkeys - 1) >> shift); shift += 8) {
+    const int bt = by_token ? 1 : 0;
+    if (shift == 0 && !wpe)
+      radix_count_kernel<true, 0><<<nb, kRadixBlock, 0, L.stream>>>(ids, N, nb, nkeys, T, bt, shift, k0, v0, hist,
+                                                                    nullptr, nullptr, 0, C);
+    else if (shift == 0 && wvec)
+      radix_count_kernel<true, 4><<<nb + nw, kRadixBlock, 0, L.stream>>>(ids, N, nb, nkeys, T, bt, shift, k0, v0,
+                                                                         hist, src, wpe, B, C);
+    else if (shift == 0)
+      radix_count_kernel<true, 1><<<nb + nw, kRadixBlock, 0, L.stream>>>(ids, N, nb, nkeys, T, bt, shift, k0, v0,
+                                                                         hist, src, wpe, B, C);
+    else
+      radix_count_kernel<false, 0><<<nb, kRadixBlock, 0, L.stream>>>(nullptr, N, nb, nkeys, T, 0, shift, k0, v0, hist,
+                                                                     nullptr, nullptr, 0, C);
+    if (nkeys > 1) {
+      radix_place_kernel<<<nb, kRadixBlock, 0, L.stream>>>(k0, v0, N, shift, hist, k1, v1);
+      std::swap(k0, k1);
+      std::swap(v0, v1);
+    }
   }
-  // the join: one thread per column (up to 1024; more columns loop); the
-  // tiles: 256 threads, so that several blocks share a compute unit
-  const int ntiles = (N + kScatTile - 1) / kScatTile, nt = std::min(1024, std::max(64, (C + 63) / 64 * 64));
-  scat_tile_kernel<<<ntiles, 256, 0, L.stream>>>(k0, v0, N, src, C, dst, part);
-  scat_join_kernel<<<ntiles, nt, 0, L.stream>>>(k0, N, C, part, dst);
+  // tiles: one thread per VW columns; the join: up to 1024 threads in
+  // groups of one row of columns
+  const int ntiles = (N + kScatTile - 1) / kScatTile;
+  const bool vec = (C % 4) == 0 && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) |
+                                     reinterpret_cast<uintptr_t>(part)) & 15) == 0;
+  auto threads = [](int cols) { return std::min(512, std::max(64, (cols + 63) / 64 * 64)); };
+  if (vec) {
+    scat_tile_kernel<2><<<ntiles, threads(C / 2), 0, L.stream>>>(k0, v0, N, src, C, dst, part);
+    scat_join_kernel<4><<<ntiles, 1024, 0, L.stream>>>(k0, N, C, part, dst);
+  } else {
+    scat_tile_kernel<1><<<ntiles, threads(C), 0, L.stream>>>(k0, v0, N, src, C, dst, part);
+    scat_join_kernel<1><<<ntiles, 1024, 0, L.stream>>>(k0, N, C, part, dst);
+  }
   return hipGetLastError();
-}
-
-// dwpe[t, :] += sum_b dR[b,t,:]  (one thread per (t, c); no atomics)
-__global__ __launch_bounds__(256) void embed_bwd_wpe_kernel(const float* __restrict__ dr, float* __restrict__ dwpe,
-                                                            int B, int T, int C) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)T * C) return;
-  const int t = (int)(i / C), c = (int)(i % C);
-  float s = 0.f;
-  for (int b = 0; b < B; ++b) s += dr[((int64_t)b * T + t) * C + c];
-  dwpe[i] += s;
 }
 
 hipError_t launch_segment_starts(const Launch& L, const int32_t* tok, int B, int T, int eot, int32_t* seg) {
@@ -368,16 +488,11 @@ hipError_t launch_embed_bwd(const Launch& L, const int32_t* tok, const float* dr
                             int T, int C, int V, const int32_t* seg, float* part, void* ws) {
   prof_begin(L);
   const int N = B * T;
-  hipError_t e = det_scatter_add(L, true, tok, N, V, T, dr, C, dwte, part, ws);
-  if (e == hipSuccess && dwpe) {
-    if (seg) {  // restarted positions: another scatter
-      e = det_scatter_add(L, false, seg, N, T, T, dr, C, dwpe, part, ws);
-    } else {
-      const int64_t n = (int64_t)T * C;
-      embed_bwd_wpe_kernel<<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(dr, dwpe, B, T, C);
-      e = hipGetLastError();
-    }
-  }
+  // without a document mask the position table's gradient is summed by
+  // extra blocks of the sort's first launch; with one, positions restart,
+  // and a second sorted scatter adds it
+  hipError_t e = det_scatter_add(L, true, tok, N, V, T, dr, C, dwte, part, ws, seg ? nullptr : dwpe, B);
+  if (e == hipSuccess && dwpe && seg) e = det_scatter_add(L, false, seg, N, T, T, dr, C, dwpe, part, ws);
   prof_end(L);
   return e;
 }

@@ -156,8 +156,10 @@ bool check_config(const gpt2_config* c) {
     if (hd > 64) return false;
   }
   if ((int64_t)c->max_batch * c->block_size > (1 << 30) / 4) return false;
-  // the embedding backward's sorted scatter keeps every 32-row tile's first key in LDS
+  // the rows one embedding backward sorts, and the 32-bit element offsets
+  // of its tile pass (rows C and V C)
   if ((int64_t)c->max_batch * c->block_size > (int64_t)embed_bwd_max_rows()) return false;
+  if ((int64_t)c->vocab_size * c->n_embd >= ((int64_t)1 << 31)) return false;
   if (c->arch != GPT2_ARCH_GPT2 && c->arch != GPT2_ARCH_ROTARY) return false;
   if (c->arch == GPT2_ARCH_ROTARY) {
     // bf16 kernels only: vector RMSNorm (C % 256), paired rotary / SwiGLU
@@ -1322,6 +1324,26 @@ int gpt2_op_attention_bwd(void* stream, int dtype, int B, int T, int H, int Hkv,
   if (d_rope && (dtype != GPT2_PRECISION_BF16 || ((uintptr_t)d_rope & 15))) return GPT2_ERR_ARG;
   HIP_TRY(launch_attention_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, dtype, B, T, H, Hkv, hd, d_qkv,
                                d_y, d_dy, d_lse, d_dqkv, d_scratch, d_seg, reinterpret_cast<const float2*>(d_rope)));
+  return GPT2_OK;
+}
+
+size_t gpt2_embedding_bwd_scratch_bytes(int rows, int C) {
+  if (rows < 1 || C < 1) return 0;
+  return ((size_t)rows * C * 4 + 255) / 256 * 256 + embed_bwd_scratch(rows);
+}
+
+int gpt2_op_embedding_bwd(void* stream, const int32_t* d_tokens, const float* d_dres, float* d_dwte, float* d_dwpe,
+                          int B, int T, int C, int V, const int32_t* d_seg, void* d_scratch) {
+  if (!d_tokens || !d_dres || !d_dwte || !d_scratch) return GPT2_ERR_ARG;
+  if (B < 1 || T < 1 || C < 1 || V < 1) return GPT2_ERR_SHAPE;
+  const int64_t rows = (int64_t)B * T;
+  if (rows > embed_bwd_max_rows() || rows * C >= ((int64_t)1 << 31) || (int64_t)V * C >= ((int64_t)1 << 31))
+    return GPT2_ERR_SHAPE;
+  if ((uintptr_t)d_scratch & 255) return GPT2_ERR_ARG;
+  float* part = static_cast<float*>(d_scratch);
+  void* ws = static_cast<char*>(d_scratch) + ((size_t)rows * C * 4 + 255) / 256 * 256;
+  HIP_TRY(launch_embed_bwd(Launch{static_cast<hipStream_t>(stream), nullptr, ""}, d_tokens, d_dres, d_dwte, d_dwpe, B,
+                           T, C, V, d_seg, part, ws));
   return GPT2_OK;
 }
 

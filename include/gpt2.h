@@ -69,7 +69,7 @@ enum { GPT2_ARCH_GPT2 = 0, GPT2_ARCH_ROTARY = 1 };
  * for the same alignment reason, section 8.3); max_batch * block_size (the
  * rows of one micro-step) at most 131,072 (the embedding backward sorts a
  * micro-step's rows by token so that every gradient row sums its rows in a
- * fixed order).
+ * fixed order); vocab_size * n_embd below 2^31.
  * arch selects the model family:
  *   GPT2_ARCH_GPT2:   the GPT-2 model above (LayerNorm, learned positions,
  *                     GELU MLP of width mlp_hidden, biases).
@@ -522,6 +522,22 @@ size_t gpt2_noalloc_scratch_bytes(void);
 int gpt2_op_attention_bwd_noalloc(void* stream, int dtype, int B, int T, int H, int Hkv, int hd, const void* d_qkv,
                                   const void* d_y, const void* d_dy, const float* d_lse, void* d_dqkv,
                                   const int32_t* d_seg, const float* d_rope);
+
+/* Embedding backward ("How I trained my own GPT-2 124M on FineWeb-Edu"
+ * sections 2.2 and 2.10, x = wte[idx] + wpe[t]), the kernels gpt2_fwd_bwd
+ * runs: for every row i = b T + t of d_dres [B*T, C] (float32, the gradient
+ * of x), d_dwte[tokens[i]] += d_dres[i] and, when d_dwpe is not NULL,
+ * d_dwpe[p(i)] += d_dres[i], with p(i) = t, or t - d_seg[i] under a
+ * document mask (d_seg as gpt2_op_segment_starts writes it; nullable).
+ * Both tables are float32 [V, C] and [T, C] and are accumulated into.  Every
+ * gradient row adds its source rows in increasing i, so repeated calls give
+ * the same bits.  Token ids outside [0, V) add to row 0 (the forward flags
+ * them).  d_scratch: gpt2_embedding_bwd_scratch_bytes(B*T, C) bytes,
+ * 256-byte aligned (GPT2_ERR_ARG otherwise).  GPT2_ERR_SHAPE unless
+ * B*T <= 131,072, B*T*C < 2^31 and V*C < 2^31. */
+size_t gpt2_embedding_bwd_scratch_bytes(int rows, int C);
+int gpt2_op_embedding_bwd(void* stream, const int32_t* d_tokens, const float* d_dres, float* d_dwte, float* d_dwpe,
+                          int B, int T, int C, int V, const int32_t* d_seg, void* d_scratch);
 
 /* Document starts of packed rows ("GPT" chapter of Zero to Frontier,
  * "Document boundaries, packing and masking"): d_seg[b*T + t] = the last

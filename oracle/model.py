@@ -301,6 +301,25 @@ def packed_rows(idx, eot):
     return masks, pos
 
 
+def embedding_bwd(idx, dh, V, T, pos=None):
+    """Gradients of x = wte[idx] + wpe[pos] ([train-124M] §2.2, §2.10) for
+    dh = dL/dx [B, T, C]: (dwte [V, C], dwpe [T, C]).  Every table row
+    collects the rows dh of the tokens that read it: wte by token id, wpe by
+    position (0..T-1 in every row, or ``pos`` [B, T] restarted at document
+    starts)."""
+    C = dh.shape[-1]
+    rows = dh.reshape(-1, C)
+    dwte = np.zeros((V, C), dtype=dh.dtype)
+    np.add.at(dwte, idx.reshape(-1), rows)
+    if pos is None:
+        dwpe = np.zeros((T, C), dtype=dh.dtype)
+        dwpe[:idx.shape[1]] = dh.sum(axis=0)
+    else:
+        dwpe = np.zeros((T, C), dtype=dh.dtype)
+        np.add.at(dwpe, pos.reshape(-1), rows)
+    return dwte, dwpe
+
+
 def forward(cfg: Config, params, idx, targets, scale=1.0, chunk=1024, want_logits=False, n_valid=None, eot=None):
     """Forward pass with every activation the backward needs.
 
@@ -436,13 +455,9 @@ def backward(cfg: Config, params, cache):
     # embeddings: wte receives the scattered rows on top of its lm_head part
     # (the tied weight, [train-124M] §4); wpe sums over the batch, or, with
     # restarted positions, over every token at each position.
-    idx = cache["idx"]
-    T = idx.shape[1]
-    np.add.at(grads["transformer.wte.weight"], idx.reshape(-1), dh.reshape(-1, dh.shape[-1]))
-    if cache["pos"] is None:
-        grads["transformer.wpe.weight"][:T] += dh.sum(axis=0)
-    else:
-        np.add.at(grads["transformer.wpe.weight"], cache["pos"].reshape(-1), dh.reshape(-1, dh.shape[-1]))
+    dwte, dwpe = embedding_bwd(cache["idx"], dh, cfg.vocab_size, cfg.block_size, cache["pos"])
+    grads["transformer.wte.weight"] += dwte
+    grads["transformer.wpe.weight"] += dwpe
     return grads
 
 

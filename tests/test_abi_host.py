@@ -233,3 +233,20 @@ def test_logits_are_never_sized_for_the_whole_batch():
     sa = g.query_sizes(g.GPT2_124M).scratch_bytes
     sb = g.query_sizes(g.ModelConfig(50304 + 256, 1024, 12, 12, 768, 3072, 16, g.PRECISION_BF16)).scratch_bytes
     assert 8192 * 256 * 2 <= sb - sa <= 8192 * 256 * 2 + 8192 * 8 + 1024, sb - sa
+
+
+def test_embedding_backward_validates_on_the_host():
+    """gpt2_op_embedding_bwd rejects bad shapes, null pointers and a
+    misaligned workspace before it launches anything."""
+    L = _lib()
+    from gpt_pretraining_step_amd import _ffi
+    p = ct.c_void_p(0x40000)
+    call = lambda B, T, C, V, tok=p, scr=p: L.gpt2_op_embedding_bwd(None, tok, p, p, None, B, T, C, V, None, scr)
+    assert call(0, 4, 4, 4) == _ffi.GPT2_ERR_SHAPE
+    assert call(129, 1024, 4, 4) == _ffi.GPT2_ERR_SHAPE       # more than 131,072 rows
+    assert call(1, 4, 1 << 20, 4096) == _ffi.GPT2_ERR_SHAPE   # V * C >= 2^31
+    assert call(1, 4, 4, 4, tok=None) == _ffi.GPT2_ERR_ARG
+    assert call(1, 4, 4, 4, scr=ct.c_void_p(0x40010)) == _ffi.GPT2_ERR_ARG
+    n = L.gpt2_embedding_bwd_scratch_bytes(16384, 768)
+    assert n >= 16384 * 768 * 4 + 2 * 16384 * 4
+    assert L.gpt2_embedding_bwd_scratch_bytes(0, 768) == 0

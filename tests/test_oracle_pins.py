@@ -378,6 +378,32 @@ def test_ce_all_ignored_gives_nan_and_no_grad():
 # LayerNorm, attention, GELU
 # ----------------------------------------------------------------------------
 
+def test_embedding_bwd_brute_force_and_chain_rule():
+    """Scatter-add of the embedding gradients: brute-force loops over every
+    token (wte by id, wpe by position, restarted positions under a document
+    mask), and the chain rule through x = wte[idx] + wpe[pos]: for any
+    tables, sum(dh * x) = sum(dwte * wte) + sum(dwpe * wpe)."""
+    rng = np.random.default_rng(11)
+    B, T, C, V = 3, 9, 5, 7
+    idx = rng.integers(0, V, size=(B, T))
+    idx[0, 4] = 6  # an EOT id inside a row
+    dh = rng.standard_normal((B, T, C))
+    _, pos = M.packed_rows(idx, 6)
+    for p in (None, pos):
+        dwte, dwpe = M.embedding_bwd(idx, dh, V, T + 2, p)
+        bw, bp = np.zeros((V, C)), np.zeros((T + 2, C))
+        for b in range(B):
+            for t in range(T):
+                bw[idx[b, t]] += dh[b, t]
+                bp[t if p is None else p[b, t]] += dh[b, t]
+        np.testing.assert_allclose(dwte, bw, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dwpe, bp, rtol=0, atol=1e-12)
+        wte, wpe = rng.standard_normal((V, C)), rng.standard_normal((T + 2, C))
+        x = wte[idx] + wpe[np.broadcast_to(np.arange(T), (B, T)) if p is None else p]
+        assert np.sum(dh * x) == pytest.approx(np.sum(dwte * wte) + np.sum(dwpe * wpe), rel=1e-12)
+    assert np.all(pos[0, 4:] == np.arange(T - 4))  # the positions restart at the EOT
+
+
 def test_layernorm_invariants():
     rng = np.random.default_rng(2)
     x = rng.standard_normal((10, 32)) * 3 + 1

@@ -24,10 +24,16 @@ __global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __re
                                                              int* __restrict__ count, int* flag) {
   __shared__ int red[1024];
   int c = 0, bad = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int t = tgt[i];
-    c += target_valid(t, V, ig);
-    bad |= (t != ig && (t < 0 || t >= V));
+  // 16 loads per thread in flight at a time
+  for (int i0 = threadIdx.x; i0 < n; i0 += 16 * blockDim.x) {
+    int tv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) tv[u] = i0 + u * (int)blockDim.x < n ? tgt[i0 + u * blockDim.x] : ig;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      c += target_valid(tv[u], V, ig);
+      bad |= (tv[u] != ig && (tv[u] < 0 || tv[u] >= V));
+    }
   }
   red[threadIdx.x] = c;
   __syncthreads();
@@ -126,7 +132,16 @@ __global__ __launch_bounds__(1024) void ce_finish_kernel(const float* __restrict
                                                          int* flag) {
   __shared__ float red[1024];
   float s = 0.f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) s += row_loss[i];
+  // this thread's rows i, i + blockDim, ... in increasing order, 16 loads in
+  // flight at a time
+  for (int i0 = threadIdx.x; i0 < n; i0 += 16 * blockDim.x) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = i0 + u * (int)blockDim.x < n ? row_loss[i0 + u * blockDim.x] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + u * (int)blockDim.x < n) s += v[u];
+  }
   red[threadIdx.x] = s;
   __syncthreads();
   for (int k = 512; k > 0; k >>= 1) {

@@ -367,8 +367,13 @@ hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int 
   t.p = reinterpret_cast<const GemmP*>(d);
   t.unit_map = reinterpret_cast<const int*>(d + align256(n * sizeof(GemmP)));
   prof_begin(L);
-  gemm2_grouped_kernel<kGroupTile, kGroupTile, 64, 2, 4, 2, false, false, GPT2_EPI_ACCUMULATE, false, false, false>
-      <<<units, 512, 0, L.stream>>>(t, K_all);
+  // 16 waves of 64 x 64 (four per SIMD): the weight gradients' transposing
+  // fragment reads and MFMAs hide better behind four waves than behind the
+  // two of the 8-wave 128 x 64 layout (the grouped launch 83.9 -> 79.6 ms per
+  // GPT-2 step, same box); both operands K-slow keep that within 128
+  // registers, the K-major layouts would spill
+  gemm2_grouped_kernel<kGroupTile, kGroupTile, 64, 4, 4, 2, false, false, GPT2_EPI_ACCUMULATE, false, false, false>
+      <<<units, 1024, 0, L.stream>>>(t, K_all);
   prof_end(L);
   return hipGetLastError();
 }

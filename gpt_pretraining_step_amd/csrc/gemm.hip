@@ -109,7 +109,8 @@ static hipError_t launch_v2(const Launch& L, const GemmP& p) {
 }
 
 // bf16 products: 256 x BN block tiles (BN = 256: 8 waves of 128x64; BN =
-// 192: 8 waves of 64x96), K step 64, two LDS stages fed by DMA.  Most
+// 192: 12 waves of 64x64, three per SIMD, which hide the fragment reads
+// better than 8 waves of 64x96 did), K step 64, two LDS stages fed by DMA.  Most
 // epilogues keep 32 consecutive columns of a row per instruction (coalesced
 // scalar loads, stores and atomics: the fewest row segments per
 // instruction); the residual of a long-K product (K >= 2048) measured faster
@@ -206,7 +207,7 @@ static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
   const int splits = narrow ? s192 : s256;
   p.k_per_split = (p.K + splits * 64 - 1) / (splits * 64) * 64;
   p.splits = (p.K + p.k_per_split - 1) / p.k_per_split;
-  if (narrow) return dispatch_tile<192, 4, 2, A_K, B_K>(L, p, epi, ob);
+  if (narrow) return dispatch_tile<192, 4, 3, A_K, B_K>(L, p, epi, ob);
   return dispatch_tile<256, 2, 4, A_K, B_K>(L, p, epi, ob);
 }
 

@@ -80,13 +80,17 @@ __device__ __forceinline__ void dma_rows(bf16* lds, const bf16* __restrict__ src
   constexpr int CPR = BK / 8;              // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;            // rows per wave instruction
   constexpr int INSTR = ROWS / RPI;        // instructions per tile
-  static_assert(INSTR % NWAVES == 0, "tile rows must split evenly over the waves");
-  constexpr int IPW = INSTR / NWAVES;
+  static_assert(ROWS % RPI == 0, "whole instructions");
+  // an even split gives each wave a contiguous run of instructions; an
+  // uneven one deals them out in turn (some waves issue one fewer)
+  constexpr bool EVEN = INSTR % NWAVES == 0;
+  constexpr int IPW = (INSTR + NWAVES - 1) / NWAVES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rl = lane / CPR, pc = lane % CPR;
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int ins = wave * IPW + i;
+    const int ins = EVEN ? wave * IPW + i : wave + i * NWAVES;
+    if (!EVEN && ins >= INSTR) break;
     const int r = ins * RPI + rl;
     const int c = swz_chunk<BK>(r, pc);
     const int gr = row0 + r, gk = k0 + 8 * c;
@@ -136,12 +140,15 @@ __device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, 
                                        int k0, int K) {
   constexpr int CPR = R / 8;             // 16-byte chunks per row
   constexpr int TOTAL = BK * CPR;        // chunks per tile
-  static_assert(TOTAL % (64 * NWAVES) == 0, "tile must split evenly over the waves");
-  constexpr int IPW = TOTAL / 64 / NWAVES;
+  static_assert(TOTAL % 64 == 0, "whole instructions");
+  constexpr int INSTR = TOTAL / 64;
+  constexpr bool EVEN = INSTR % NWAVES == 0;
+  constexpr int IPW = (INSTR + NWAVES - 1) / NWAVES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int ins = wave * IPW + i;
+    const int ins = EVEN ? wave * IPW + i : wave + i * NWAVES;
+    if (!EVEN && ins >= INSTR) break;
     const int g = ins * 64 + lane;
     const int k = g / CPR;
     const int c = kr_chunk<R>(k, g % CPR);
@@ -162,18 +169,22 @@ __device__ __forceinline__ void dma_kr(bf16* lds, const bf16* __restrict__ src, 
 // fill) for a ragged last K step.
 template <int ROWS, int BK, int NWAVES>
 struct RowsDma {
-  static constexpr int CPR = BK / 8, RPI = 64 / CPR, INSTR = ROWS / RPI, IPW = INSTR / NWAVES;
-  static_assert(INSTR % NWAVES == 0, "tile rows must split evenly over the waves");
+  static constexpr int CPR = BK / 8, RPI = 64 / CPR, INSTR = ROWS / RPI;
+  static constexpr bool EVEN = INSTR % NWAVES == 0;
+  static constexpr int IPW = (INSTR + NWAVES - 1) / NWAVES;
+  static_assert(ROWS % RPI == 0, "whole instructions");
   uint32_t off[IPW];
   int ins0;
+  // instruction i of this wave (EVEN: a contiguous run; else dealt in turn)
+  __device__ __forceinline__ int ins(int i) const { return EVEN ? ins0 + i : ins0 + i * NWAVES; }
   // tile rows row0 .. row0+ROWS of a [nrows][ld] matrix (row0 < nrows)
   __device__ __forceinline__ void init(int64_t ld, int row0, int nrows) {
     const int lane = threadIdx.x & 63;
-    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (EVEN ? IPW : 1);
     const int last = nrows - 1 - row0;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int r = (ins0 + i) * RPI + lane / CPR;
+      const int r = min(ins(i), INSTR - 1) * RPI + lane / CPR;
       const int c = swz_chunk<BK>(r, lane % CPR);
       off[i] = (uint32_t)(((int64_t)min(r, last) * ld + 8 * c) * 2);
     }
@@ -185,11 +196,11 @@ struct RowsDma {
   // with row0 = 0); rows past nvirt are clamped to the last one.
   __device__ __forceinline__ void init_swiglu(int64_t ld, int row0, int nvirt) {
     const int lane = threadIdx.x & 63;
-    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (EVEN ? IPW : 1);
     const int F = nvirt >> 1;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int r = (ins0 + i) * RPI + lane / CPR;
+      const int r = min(ins(i), INSTR - 1) * RPI + lane / CPR;
       const int c = swz_chunk<BK>(r, lane % CPR);
       const int v = min(row0 + r, nvirt - 1);
       const int w = v & 63, f = ((v >> 6) << 5) + (w & 31);
@@ -201,24 +212,27 @@ struct RowsDma {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)row0 * ld + k0);
 #pragma unroll
     for (int i = 0; i < IPW; ++i)
-      dma16_off(base, off[i], lds_addr(lds + (ins0 + i) * RPI * BK));
+      if (EVEN || ins(i) < INSTR) dma16_off(base, off[i], lds_addr(lds + ins(i) * RPI * BK));
   }
 };
 
 template <int R, int BK, int NWAVES>
 struct KrDma {
-  static constexpr int CPR = R / 8, TOTAL = BK * CPR, IPW = TOTAL / 64 / NWAVES;
-  static_assert(TOTAL % (64 * NWAVES) == 0, "tile must split evenly over the waves");
+  static constexpr int CPR = R / 8, TOTAL = BK * CPR, INSTR = TOTAL / 64;
+  static constexpr bool EVEN = INSTR % NWAVES == 0;
+  static constexpr int IPW = (INSTR + NWAVES - 1) / NWAVES;
+  static_assert(TOTAL % 64 == 0, "whole instructions");
   uint32_t off[IPW];
   int ins0;
+  __device__ __forceinline__ int ins(int i) const { return EVEN ? ins0 + i : ins0 + i * NWAVES; }
   // tile columns col0 .. col0+R of a [K][ld] matrix (col0 < ncols, ncols % 8 == 0)
   __device__ __forceinline__ void init(int64_t ld, int col0, int ncols) {
     const int lane = threadIdx.x & 63;
-    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (EVEN ? IPW : 1);
     const int last = ncols - 8 - col0;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int g = (ins0 + i) * 64 + lane;
+      const int g = min(ins(i), INSTR - 1) * 64 + lane;
       const int k = g / CPR;
       const int c = kr_chunk<R>(k, g % CPR);
       off[i] = (uint32_t)(((int64_t)k * ld + min(8 * c, last)) * 2);
@@ -228,7 +242,7 @@ struct KrDma {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * ld + col0);
 #pragma unroll
     for (int i = 0; i < IPW; ++i)
-      dma16_off(base, off[i], lds_addr(lds + (ins0 + i) * 512));
+      if (EVEN || ins(i) < INSTR) dma16_off(base, off[i], lds_addr(lds + ins(i) * 512));
   }
 };
 

@@ -208,6 +208,15 @@ static hipError_t dispatch_bf16(const Launch& L, GemmP p, int epi, bool ob) {
   p.k_per_split = (p.K + splits * 64 - 1) / (splits * 64) * 64;
   p.splits = (p.K + p.k_per_split - 1) / p.k_per_split;
   if (narrow) return dispatch_tile<192, 4, 3, A_K, B_K>(L, p, epi, ob);
+  // 256 x 256: 8 waves of 128 x 64, except the GELU_GRAD product with both
+  // operands K-major (the GPT-2 fc), 16 waves of 64 x 64 (41.2 -> 40.0 ms
+  // per step, same box).  Measured slower at 16 waves: the residual
+  // (rotary attn_proj 12.2 -> 14.4 ms per step), the paired rotary /
+  // SwiGLU epilogues (30.8 -> 32.5 ms), and with a K-slow operand the
+  // mlp_proj_dx product (39.1 -> 44.4 ms).
+  if constexpr (A_K && B_K) {
+    if (epi == GPT2_EPI_GELU_GRAD) return dispatch_tile<256, 4, 4, A_K, B_K>(L, p, epi, ob);
+  }
   return dispatch_tile<256, 2, 4, A_K, B_K>(L, p, epi, ob);
 }
 

@@ -970,8 +970,14 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit, bf16* lds0,
     // 4 consecutive columns of one row (16-byte reads of the residual or the
     // GELU input).
     bf16x8 a[2][TM], b[2][TN];
+    // 16-wave blocks with a K-major operand: the slice's chunk index is
+    // recomputed for every read from an opaque lane value, so that the
+    // compiler keeps no per-slice address registers
+    constexpr bool LEAN = NW >= 16 && (A_K || B_K);
     auto frag = [&](int kk, bf16x8* fa, bf16x8* fb) {
-      const int c = 2 * kk + lg;
+      int lgv = lg;
+      if constexpr (LEAN) asm volatile("" : "+v"(lgv));
+      const int c = 2 * kk + lgv;
       const int h = (lane >> 4) & 1;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -996,6 +1002,7 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit, bf16* lds0,
         }
       }
     };
+    if constexpr (!LEAN) {
     frag(0, a[0], b[0]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -1012,6 +1019,18 @@ __device__ __forceinline__ void gemm2_unit(const GemmP& p, int unit, bf16* lds0,
     // before that slice's MFMAs and waits for them there; this order keeps
     // the next slice's reads in flight behind the current slice's MFMAs.
     sched_kstep<TM * (A_K ? 1 : 2) + TN * (B_K ? 1 : 2), TM * TN, BK / 16>();
+    } else {
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      frag(kk, a[0], b[0]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[0][j], a[0][i], acc[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][i], b[0][j], acc[i][j], 0, 0, 0);
+    }
+    }
     if (do_rowsum && threadIdx.x < BM) {
       // row sums of this block's A tile (K values past kend read as zeros)
       const int t = threadIdx.x;

@@ -79,9 +79,9 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
 // [N, C], each destination row summing its source rows in increasing i, so
 // the result does not depend on scheduling (float addition is not
 // associative; atomics would make the gradient vary from run to run).
-//  1. a stable sort of (key, row) pairs by key: rows come out grouped by key
-//     and, within a key, in increasing row order (up to 16,384 rows: one
-//     block, in LDS; more: LSD radix passes of 8-bit digits over the grid);
+//  1. a stable sort of (key, row) pairs by key (LSD radix passes of 8-bit
+//     digits over the grid): rows come out grouped by key and, within a
+//     key, in increasing row order;
 //  2. the sorted list in tiles of 32 positions: each tile sums every run of
 //     one key that falls inside it, in order; a run that is the key's whole
 //     run is added to dst there, otherwise its sum goes to part[first

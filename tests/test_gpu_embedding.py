@@ -8,11 +8,10 @@ additions.  With general float values, a second call must give the same
 bits (every gradient row sums its rows in a fixed order).
 
 Cases: one row; ragged tiles with C % 4 != 0 (the one-column path); the
-benchmarked micro-step (16 x 1024 Zipf tokens, V = 50,304, C = 768; rows
-sorted by one block), with and without the document mask; 20 x 1024 rows
-(past one block's sort: the radix passes over the grid); a single token id
-(one run over every tile, joined from 256 partials); a small vocabulary
-(one radix digit)."""
+benchmarked micro-step (16 x 1024 Zipf tokens, V = 50,304, C = 768), with
+and without the document mask; 20 x 1024 rows (more blocks in every radix
+pass than the micro-step); a single token id (one run over every tile,
+joined from 256 partials); a small vocabulary (one radix digit)."""
 
 import numpy as np
 import pytest

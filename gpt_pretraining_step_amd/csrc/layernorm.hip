@@ -207,12 +207,13 @@ __device__ __forceinline__ float4 load4<bf16>(const bf16* p) {
   return make_float4(bf2f(v[0]), bf2f(v[1]), bf2f(v[2]), bf2f(v[3]));
 }
 
-// Backward over RPW consecutive rows per wave; the next row's dy, x and dR
-// are loaded before the current row is reduced, so each wave keeps two
-// rows of loads in flight.  dy is float32 or bf16.  RMS: the RMSNorm
-// backward, dx = rstd (g - xhat mean(g xhat)) (no centring term), no db.
-template <typename DYT, int NQ, int RPW, bool RMS>
-__global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__ dy, const float* __restrict__ x,
+// Backward over RPW consecutive rows per wave, WPB waves per block; the
+// next row's dy, x and dR are loaded before the current row is reduced, so
+// each wave keeps two rows of loads in flight.  dy is float32 or bf16.
+// RMS: the RMSNorm backward, dx = rstd (g - xhat mean(g xhat)) (no
+// centring term), no db.
+template <typename DYT, int NQ, int RPW, int WPB, bool RMS>
+__global__ __launch_bounds__(64 * WPB) void ln_bwd_vec_kernel(const DYT* __restrict__ dy, const float* __restrict__ x,
                                                          const float* __restrict__ mean,
                                                          const float* __restrict__ rstd,
                                                          const float* __restrict__ w, float* __restrict__ dR,
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__
     gw[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     gb[q] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const int row0 = (blockIdx.x * WPB + wave) * RPW;
   const int nrows = min(RPW, rows - row0);
   float4 d[NQ], xv[NQ], r[NQ];
   float mu = 0.f, rs = 0.f;
@@ -287,20 +288,31 @@ __global__ __launch_bounds__(256) void ln_bwd_vec_kernel(const DYT* __restrict__
     mu = nmu;
     rs = nrs;
   }
-  // the 4 waves' column partials through LDS, then one atomic per column
-  // (consecutive threads, consecutive columns)
-  __shared__ float red[2][4][256 * NQ];
+  // the waves' column partials through LDS, then one atomic per column and
+  // block (consecutive threads, consecutive columns; threads 0-255 sum dw,
+  // 256-511 db): the fewer blocks, the less the atomics contend
+  static_assert(WPB % 4 == 0 && WPB >= 8, "two groups of 256 threads");
+  __shared__ float red[2][WPB][256 * NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     *reinterpret_cast<float4*>(&red[0][wave][4 * lane + 256 * q]) = gw[q];
     *reinterpret_cast<float4*>(&red[1][wave][4 * lane + 256 * q]) = gb[q];
   }
   __syncthreads();
+  const int which = threadIdx.x >> 8;
+  if (which > 1 || (RMS && which == 1)) return;
+  const float (*rw)[256 * NQ] = red[which];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int c = threadIdx.x + 256 * q;
-    unsafeAtomicAdd(dw + c, (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]));
-    if constexpr (!RMS) unsafeAtomicAdd(db + c, (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]));
+    const int c = (threadIdx.x & 255) + 256 * q;
+    float t[WPB / 4];
+#pragma unroll
+    for (int k = 0; k < WPB / 4; ++k) t[k] = (rw[4 * k][c] + rw[4 * k + 1][c]) + (rw[4 * k + 2][c] + rw[4 * k + 3][c]);
+#pragma unroll
+    for (int h = 1; h < WPB / 4; h *= 2)
+#pragma unroll
+      for (int k = 0; k + h < WPB / 4; k += 2 * h) t[k] += t[k + h];
+    unsafeAtomicAdd((which ? db : dw) + c, t[0]);
   }
 }
 
@@ -329,16 +341,19 @@ template <typename DYT, bool RMS>
 static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const float* mean, const float* rstd,
                             const float* w, float* dx, bf16* dxb, float* dw, float* db, int rows, int C) {
   if (C % 256 == 0) {
-    // 8 rows per wave (two blocks per compute unit at 16,384 rows): few
-    // column atomics, and the next row's loads in flight keep HBM busy (16
-    // rows per wave measured 36.2 ms per GPT-2 step, 8 rows 34.2, 4 rows 39.2)
-    constexpr int RPW = 8;
-    const dim3 grid((rows + 4 * RPW - 1) / (4 * RPW));
+    // 8 rows per wave, 8 waves per block (one block per compute unit at
+    // 16,384 rows): the next row's loads in flight keep HBM busy, and the
+    // column atomics (one per column and block) are few.  Per GPT-2 step on
+    // one box: 4-wave blocks 34.5 ms (their atomics alone 5.1 ms), 8-wave
+    // 30.8 ms, 16-wave blocks of 4 rows per wave 52.9 ms; 16 rows per wave
+    // in 4-wave blocks was slower than 8
+    constexpr int RPW = 8, WPB = 8;
+    const dim3 grid((rows + WPB * RPW - 1) / (WPB * RPW));
     switch (C / 256) {
-      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      default: ln_bwd_vec_kernel<DYT, 4, RPW, RMS><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      default: ln_bwd_vec_kernel<DYT, 4, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
     }
   } else if constexpr (!RMS) {
     constexpr int RPW = 4;

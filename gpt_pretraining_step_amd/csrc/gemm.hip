@@ -295,33 +295,62 @@ hipError_t launch_gemm(const Launch& L, const gpt2_gemm_args& a, float* row_sum)
 // One block per 256x256 output tile, whole K, so the launch runs in rounds of
 // kUnits equal blocks.  A partial last round would leave CUs idle for a whole
 // tile's time: the products at the end of the list that cover the tiles past
-// the last full round are split in K into two halves (each adds its partial
-// sums atomically) when the halves fit in half a round, which then ends the
-// launch half a round earlier.  Units are placed in block order: the whole
-// tiles XCD-aware (each XCD a contiguous run of them, sharing panels in its
-// L2), then the halves, which the round-robin hands to every XCD alike.
+// the last full round are split in K into kTailSplit pieces (each adds its
+// partial sums atomically), or into two where K is too short for that, when
+// a list-scheduling estimate of the launch says the span gets shorter.  The
+// pieces then fill the CUs that the last whole tiles leave idle.  Units are
+// placed in block order: the whole tiles XCD-aware (each XCD a contiguous run
+// of them, sharing panels in its L2), then the pieces, which the round-robin
+// hands to every XCD alike.  GPT-2 124M at 16,384 tokens (1,296 tiles, a
+// 16-tile tail), same box: pieces of a half 79.6 ms per step, of a quarter
+// 76.4, an eighth 76.4, a sixteenth 76.2.
 
 namespace {
 constexpr int kGroupTile = 256;
+constexpr int kTailSplit = 4;
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 int group_tiles(const gpt2_gemm_args& a) {
   return ((a.M + kGroupTile - 1) / kGroupTile) * ((a.N + kGroupTile - 1) / kGroupTile);
 }
-// K splits of each product (1 or 2); returns the unit count or -1
+// In-order list scheduling over kUnits CUs: u0 units of cost c0, then u1 of
+// cost c1, each starting on the CU that frees up first; returns the span.
+double list_span(int64_t u0, double c0, int64_t u1, double c1) {
+  std::vector<double> load(kUnits, 0.0);  // a min-heap of CU finish times
+  std::make_heap(load.begin(), load.end(), std::greater<double>());
+  for (int64_t i = 0; i < u0 + u1; ++i) {
+    std::pop_heap(load.begin(), load.end(), std::greater<double>());
+    load.back() += i < u0 ? c0 : c1;
+    std::push_heap(load.begin(), load.end(), std::greater<double>());
+  }
+  return *std::max_element(load.begin(), load.end());
+}
+// K splits of each product (1, 2 or kTailSplit); returns the unit count
 int64_t group_plan(const gpt2_gemm_args* a, int n, std::vector<int>& splits) {
   splits.assign(n, 1);
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) tiles += group_tiles(a[i]);
   const int64_t tail = tiles % kUnits;
-  if (tiles > kUnits && tail > 0 && 2 * tail <= kUnits) {
-    int64_t covered = 0;
-    for (int i = n - 1; i >= 0 && covered < tail; --i) {
-      // halves must keep at least 16 K steps
-      if (a[i].K < 2 * 16 * 64) break;
-      splits[i] = 2;
-      covered += group_tiles(a[i]);
+  if (tiles > kUnits && tail > 0) {
+    for (int s = kTailSplit; s >= 2; s /= 2) {
+      std::vector<int> sp(n, 1);
+      int64_t covered = 0;
+      int kmin = a[n - 1].K;
+      for (int i = n - 1; i >= 0 && covered < tail; --i) {
+        if (a[i].K < s * 16 * 64) break;  // pieces keep at least 16 K steps
+        sp[i] = s;
+        covered += group_tiles(a[i]);
+        kmin = std::min(kmin, a[i].K);
+      }
+      // a table holds at most two units per tile
+      if (covered < tail || covered * (s - 1) > tiles) continue;
+      // costs in K steps; a tile's float32 read-modify-write epilogue as in
+      // the pair plan below (an atomic one 8 times as much)
+      const double k = (kmin + 63) / 64, whole = k + 4.0, piece = (k + s - 1) / s + 32.0;
+      if (list_span(tiles - covered, whole, covered * s, piece) < 0.99 * list_span(tiles, whole, 0, 0.0)) {
+        splits = sp;
+        break;
+      }
     }
-    if (covered < tail || 2 * covered > kUnits + tail) splits.assign(n, 1);  // no gain
   }
   int64_t units = 0;
   for (int i = 0; i < n; ++i) units += (int64_t)group_tiles(a[i]) * splits[i];
@@ -350,7 +379,7 @@ void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, 
   int* unit_map = reinterpret_cast<int*>(h + align256(n * sizeof(GemmP)));
   std::vector<int> splits;
   group_plan(a, n, splits);
-  std::vector<int> whole, halves;  // (product << 16) | unit, in product order
+  std::vector<int> whole, pieces;  // (product << 16) | unit, in product order
   for (int i = 0; i < n; ++i) {
     GemmP p = make_params(a[i]);
     p.row_sum = row_sums ? row_sums[i] : nullptr;
@@ -362,13 +391,13 @@ void gemm_grouped_table(const gpt2_gemm_args* a, float* const* row_sums, int n, 
     }
     ps[i] = p;
     const int nu = p.tiles_m * p.tiles_n * p.splits;
-    for (int k = 0; k < nu; ++k) (p.splits > 1 ? halves : whole).push_back((i << 16) | k);
+    for (int k = 0; k < nu; ++k) (p.splits > 1 ? pieces : whole).push_back((i << 16) | k);
   }
   // whole tiles: block b of the first 8 * floor(W / 8) takes the unit that
   // gives XCD b % 8 a contiguous run
   const int W = (int)whole.size(), W8 = W / 8 * 8;
   for (int b = 0; b < W; ++b) unit_map[b] = whole[b < W8 ? xcd_remap_host(b, W8) : b];
-  for (size_t k = 0; k < halves.size(); ++k) unit_map[W + k] = halves[k];
+  for (size_t k = 0; k < pieces.size(); ++k) unit_map[W + k] = pieces[k];
 }
 
 hipError_t launch_gemm_grouped(const Launch& L, const void* d_table, int n, int units, int K_all) {
@@ -404,18 +433,6 @@ struct PairPlan {
   int s0 = 1, s1 = 1;
   double span = 0.0;
 };
-double pair_span(int64_t u0, double c0, int64_t u1, double c1) {
-  // in-order list scheduling over kUnits CUs: each unit starts on the CU
-  // that frees up first
-  std::vector<double> load(kUnits, 0.0);  // a min-heap of CU finish times
-  std::make_heap(load.begin(), load.end(), std::greater<double>());
-  for (int64_t i = 0; i < u0 + u1; ++i) {
-    std::pop_heap(load.begin(), load.end(), std::greater<double>());
-    load.back() += i < u0 ? c0 : c1;
-    std::push_heap(load.begin(), load.end(), std::greater<double>());
-  }
-  return *std::max_element(load.begin(), load.end());
-}
 PairPlan plan_pair_uncached(int64_t t0, int k0, int64_t t1, int k1) {
   // epilogue of a 256x256 float32 read-modify-write, in K steps; an atomic
   // one is charged 8 times as much (measured: with 2 times, the plan split
@@ -428,7 +445,7 @@ PairPlan plan_pair_uncached(int64_t t0, int k0, int64_t t1, int k1) {
     for (int s1 = 1; s1 <= 4 && (s1 == 1 || k1 / s1 >= 8); ++s1) {
       const double c0 = (k0 + s0 - 1) / s0 + (s0 > 1 ? EPI_ATOMIC : EPI);
       const double c1 = (k1 + s1 - 1) / s1 + (s1 > 1 ? EPI_ATOMIC : EPI);
-      const double span = pair_span(t0 * s0, c0, t1 * s1, c1);
+      const double span = list_span(t0 * s0, c0, t1 * s1, c1);
       if (span < 0.99 * best.span) {
         best.s0 = s0;
         best.s1 = s1;

@@ -1137,8 +1137,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(GemmP p) {
 // units: blocks go to the XCDs round-robin in index order).  A product with
 // splits > 1 adds its partial sums atomically (ACCUMULATE).  K_all > 0
 // replaces every product's K (all products of one launch reduce over the
-// same tokens), so one table serves every token count: a product split in
-// two takes halves of ceil(K_all / 128) * 64.
+// same tokens), so one table serves every token count: a product split S
+// ways takes pieces of ceil(K_all / (64 S)) * 64.
 struct GemmGroups {
   const GemmP* __restrict__ p;
   const int* __restrict__ unit_map;

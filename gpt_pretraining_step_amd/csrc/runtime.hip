@@ -275,7 +275,7 @@ struct Layout {
   // attention branch; dUL[l], dQKVL[l] the gradients of the fc and qkv
   // outputs; dw_table the group table of that launch
   std::vector<size_t> dRbS, dUL, dQKVL;
-  // two copies of that table: [0] without K splits (fewer than 2048
+  // two copies of that table: [0] without K splits (fewer than 4096
   // tokens), [1] with the split tail (see run_dw)
   size_t dw_table[2] = {0, 0}, dw_table_bytes = 0;
 };
@@ -503,8 +503,8 @@ static void queue_dw(gpt2_ctx* c, DwQueue& q, const void* dy, int M, int N, cons
 // The grouped launch reads its products from a table in device memory.  All
 // products reduce over the micro-step's tokens, and the kernel takes that
 // count (K) as an argument, so the table depends on the token count only
-// through the split plan: without splits below 2048 tokens, with the split
-// tail from 2048 on.  Both tables are built from the first queue and copied
+// through the split plan: without splits below 4096 tokens, with the split
+// tail (pieces of at least 16 K steps) from 4096 on.  Both tables are built from the first queue and copied
 // once, asynchronously on the stream (their host images live as long as
 // the context); later calls only check that the queue is the same.
 static hipError_t run_dw(gpt2_ctx* c, DwQueue& q, int tokens) {
@@ -519,7 +519,7 @@ static hipError_t run_dw(gpt2_ctx* c, DwQueue& q, int tokens) {
       return hipErrorStreamCaptureUnsupported;
     for (int pl = 0; pl < 2; ++pl) {
       std::vector<gpt2_gemm_args> a = q.a;
-      for (auto& x : a) x.K = pl ? (1 << 20) : 1;  // no split below 2048 tokens; the split tail above
+      for (auto& x : a) x.K = pl ? (1 << 20) : 1;  // no split below 4096 tokens; the split tail above
       const int units = gemm_grouped_units(a.data(), n);
       const size_t bytes = gemm_grouped_table_bytes(n, units);
       if (units < 1 || bytes > c->lay.dw_table_bytes) return hipErrorInvalidValue;
@@ -541,7 +541,7 @@ static hipError_t run_dw(gpt2_ctx* c, DwQueue& q, int tokens) {
     for (size_t i = 0; i < sig.size(); ++i)
       if (!same(sig[i], c->dw_sig[i])) return hipErrorInvalidValue;
   }
-  const int pl = tokens >= 2048 ? 1 : 0;
+  const int pl = tokens >= 4096 ? 1 : 0;
   return launch_gemm_grouped(c->at("gemm.dw"), c->scr(c->lay.dw_table[pl]), n, c->dw_units[pl], tokens);
 }
 

@@ -194,6 +194,33 @@ def test_grouped_products_validate_on_the_host():
     assert L.gpt2_gemm_grouped_workspace_bytes(arr, 2) == nbytes
 
 
+def test_grouped_split_plan_for_the_gpt2_step():
+    """The weight-gradient products of one GPT-2 124M micro-step (per layer
+    mlp_proj, fc, attn_proj, qkv: 36 + 36 + 9 + 27 tiles of 256 x 256, 1,296
+    in all, 16 past five full rounds of 256 blocks): from 4,096 tokens the
+    last product (27 tiles) runs as quarters of K (27 x 3 more units in the
+    table), below that whole."""
+    L = _lib()
+    from gpt_pretraining_step_amd import _ffi
+    n = 48
+    arr = (_ffi.GemmArgs * n)()
+    shapes = [(768, 3072), (3072, 768), (768, 768), (2304, 768)] * 12
+    def table_bytes(K):
+        for i, (M, N) in enumerate(shapes):
+            a = arr[i]
+            a.M, a.N, a.K, a.dtype = M, N, K, _ffi.PRECISION_BF16
+            a.lda, a.ldb, a.ldc = M, N, N
+            a.A, a.B, a.C = 0x10000, 0x20000, 0x30000
+            a.alpha, a.epilogue = 1.0, _ffi.EPI_ACCUMULATE
+        return L.gpt2_gemm_grouped_workspace_bytes(arr, n)
+    a256 = lambda b: (b + 255) // 256 * 256
+    params = table_bytes(1024) - a256(1296 * 4)  # whole tiles only
+    assert params > 0 and params % 256 == 0
+    assert table_bytes(16384) == params + a256((1296 + 27 * 3) * 4)
+    assert table_bytes(4096) == params + a256((1296 + 27 * 3) * 4)
+    assert table_bytes(2048) == params + a256(1296 * 4)
+
+
 def _declarations():
     """name -> number of parameters, from the header's prototypes."""
     text = open(HEADER).read()

@@ -147,13 +147,14 @@ def test_gemm_grouped_exact(g):
             assert np.array_equal(host(R), refR.astype(np.float32)), i
 
 
-def test_gemm_grouped_split_tail_exact(g):
-    """276 output tiles: one full round of 256 blocks and a 20-tile tail, so
-    the last product runs split in K (two halves adding atomically): every
-    output and row sum stays exact on integer operands."""
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_gemm_grouped_split_tail_exact(g, K):
+    """276 output tiles: one full round of 256 blocks and a 20-tile tail.  At
+    K = 4096 the last product runs split in K (four quarters adding
+    atomically); at K = 2048 its pieces would be too short and it runs
+    whole.  Every output and row sum stays exact on integer operands."""
     import torch
     shapes = [(2048, 2048)] * 4 + [(1024, 1280)]
-    K = 2048
     announce(f"gemm grouped split tail {len(shapes)} products K={K}")
     rng = np.random.default_rng(6)
     items, refs = [], []

@@ -218,7 +218,8 @@ __global__ __launch_bounds__(64 * WPB) void ln_bwd_vec_kernel(const DYT* __restr
                                                          const float* __restrict__ rstd,
                                                          const float* __restrict__ w, float* __restrict__ dR,
                                                          bf16* __restrict__ dRb, float* __restrict__ dw,
-                                                         float* __restrict__ db, int rows, int C) {
+                                                         float* __restrict__ db, float* __restrict__ part, int rows,
+                                                         int C) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   float4 wr[NQ], gw[NQ], gb[NQ];
@@ -288,9 +289,11 @@ __global__ __launch_bounds__(64 * WPB) void ln_bwd_vec_kernel(const DYT* __restr
     mu = nmu;
     rs = nrs;
   }
-  // the waves' column partials through LDS, then one atomic per column and
-  // block (consecutive threads, consecutive columns; threads 0-255 sum dw,
-  // 256-511 db): the fewer blocks, the less the atomics contend
+  // the waves' column partials through LDS, then per column and block
+  // either one atomic (consecutive threads, consecutive columns; threads
+  // 0-255 sum dw, 256-511 db: the fewer blocks, the less the atomics
+  // contend) or, with `part`, a plain store of the block's row of partials
+  // (dw in columns [0, C), db in [C, 2C)) that ln_param_grad_kernel sums
   static_assert(WPB % 4 == 0 && WPB >= 8, "two groups of 256 threads");
   __shared__ float red[2][WPB][256 * NQ];
 #pragma unroll
@@ -312,7 +315,8 @@ __global__ __launch_bounds__(64 * WPB) void ln_bwd_vec_kernel(const DYT* __restr
     for (int h = 1; h < WPB / 4; h *= 2)
 #pragma unroll
       for (int k = 0; k + h < WPB / 4; k += 2 * h) t[k] += t[k + h];
-    unsafeAtomicAdd((which ? db : dw) + c, t[0]);
+    if (part) part[(int64_t)blockIdx.x * 2 * C + which * C + c] = t[0];
+    else unsafeAtomicAdd((which ? db : dw) + c, t[0]);
   }
 }
 
@@ -337,9 +341,17 @@ hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w,
   return hipGetLastError();
 }
 
+// Rows per block of the vector backward (8 waves of 8 rows): its blocks
+// each leave one row of column partials when the caller asks for them.
+constexpr int kLnBwdRows = 64;
+int ln_bwd_part_blocks(int rows, int C) {
+  return C % 256 == 0 && C <= 1024 ? (rows + kLnBwdRows - 1) / kLnBwdRows : 0;
+}
+
 template <typename DYT, bool RMS>
 static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const float* mean, const float* rstd,
-                            const float* w, float* dx, bf16* dxb, float* dw, float* db, int rows, int C) {
+                            const float* w, float* dx, bf16* dxb, float* dw, float* db, float* part, int rows,
+                            int C) {
   if (C % 256 == 0) {
     // 8 rows per wave, 8 waves per block (one block per compute unit at
     // 16,384 rows): the next row's loads in flight keep HBM busy, and the
@@ -348,12 +360,13 @@ static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const
     // 30.8 ms, 16-wave blocks of 4 rows per wave 52.9 ms; 16 rows per wave
     // in 4-wave blocks was slower than 8
     constexpr int RPW = 8, WPB = 8;
+    static_assert(RPW * WPB == kLnBwdRows, "rows per block");
     const dim3 grid((rows + WPB * RPW - 1) / (WPB * RPW));
     switch (C / 256) {
-      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
-      default: ln_bwd_vec_kernel<DYT, 4, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C); break;
+      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
+      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
+      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
+      default: ln_bwd_vec_kernel<DYT, 4, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
     }
   } else if constexpr (!RMS) {
     constexpr int RPW = 4;
@@ -364,13 +377,15 @@ static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const
 
 hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* mean,
                                   const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
-                                  int rows, int C) {
+                                  int rows, int C, float* part) {
+  if (part && ln_bwd_part_blocks(rows, C) == 0) return hipErrorInvalidValue;
   prof_begin(L);
   if (dy_bf16)
-    ln_bwd_dispatch<bf16, false>(L.stream, static_cast<const bf16*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+    ln_bwd_dispatch<bf16, false>(L.stream, static_cast<const bf16*>(dy), x, mean, rstd, w, dx, dxb, dw, db, part,
+                                 rows, C);
   else
-    ln_bwd_dispatch<float, false>(L.stream, static_cast<const float*>(dy), x, mean, rstd, w, dx, dxb, dw, db, rows,
-                                  C);
+    ln_bwd_dispatch<float, false>(L.stream, static_cast<const float*>(dy), x, mean, rstd, w, dx, dxb, dw, db, part,
+                                  rows, C);
   prof_end(L);
   return hipGetLastError();
 }
@@ -391,15 +406,66 @@ hipError_t launch_rmsnorm_fwd(const Launch& L, const float* x, const float* w, b
 }
 
 hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* rstd,
-                              const float* w, float* dx, bf16* dxb, float* dw, int rows, int C) {
+                              const float* w, float* dx, bf16* dxb, float* dw, int rows, int C, float* part) {
   if (C % 256 != 0 || C > 1024) return hipErrorInvalidValue;
   prof_begin(L);
   if (dy_bf16)
     ln_bwd_dispatch<bf16, true>(L.stream, static_cast<const bf16*>(dy), x, nullptr, rstd, w, dx, dxb, dw, nullptr,
-                                rows, C);
+                                part, rows, C);
   else
     ln_bwd_dispatch<float, true>(L.stream, static_cast<const float*>(dy), x, nullptr, rstd, w, dx, dxb, dw, nullptr,
-                                 rows, C);
+                                 part, rows, C);
+  prof_end(L);
+  return hipGetLastError();
+}
+
+// dw[s][c] += sum over blocks b of part[s][b][c] (and db from columns C + c
+// where db[s] is non-null), for every norm site s of one backward: the
+// blocks' partial rows are summed in block order, so the result does not
+// depend on scheduling.  A 1,024-thread block covers 64 columns of one site:
+// its 16 row groups each sum every 16th partial row, then the groups are
+// added in order.
+__global__ __launch_bounds__(1024) void ln_param_grad_kernel(const float* __restrict__ part, int nblk, int C,
+                                                             LnGradSites sites) {
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6, s = blockIdx.y;
+  const float* ps = part + (int64_t)s * nblk * 2 * C;
+  __shared__ float red[2][16][64];
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1 && !sites.db[s]) break;  // (no bias: its columns were never written)
+    float acc = 0.f;
+    if (col < C) {
+      // eight loads in flight, then added in row order
+      const float* pc = ps + h * C + col;
+      int b = grp;
+      for (; b + 7 * 16 < nblk; b += 8 * 16) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pc[(int64_t)(b + 16 * u) * 2 * C];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      for (; b < nblk; b += 16) acc += pc[(int64_t)b * 2 * C];
+    }
+    red[h][grp][threadIdx.x & 63] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < 128 && col < C) {
+    const int h = threadIdx.x >> 6, cc = threadIdx.x & 63;
+    float* dst = h ? sites.db[s] : sites.dw[s];
+    if (dst) {
+      float t = 0.f;
+      for (int k = 0; k < 16; ++k) t += red[h][k][cc];
+      dst[blockIdx.x * 64 + cc] += t;
+    }
+  }
+}
+
+hipError_t launch_ln_param_grad(const Launch& L, const float* part, int rows, int C, const LnGradSites& sites,
+                                int nsites) {
+  const int nblk = ln_bwd_part_blocks(rows, C);
+  if (nblk == 0 || nsites < 1 || nsites > kLnGradSites) return hipErrorInvalidValue;
+  prof_begin(L);
+  ln_param_grad_kernel<<<dim3((C + 63) / 64, nsites), 1024, 0, L.stream>>>(part, nblk, C, sites);
   prof_end(L);
   return hipGetLastError();
 }

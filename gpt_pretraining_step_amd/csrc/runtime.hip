@@ -268,6 +268,9 @@ struct Layout {
   // scratch
   size_t dR = 0, dA = 0, dQKV = 0, dY = 0, dU = 0, attnD = 0, logits = 0, dlogits = 0, rowloss = 0;
   size_t ce_stats = 0, rope = 0, seg = 0, embws = 0;
+  // the norm backward's column partials, one region per norm site (0: the
+  // sites add their weight gradients with atomics instead)
+  size_t lnpart = 0;
   size_t count = 0, flag = 0, parts = 0, loss = 0, norm = 0, step = 0, adam_sc = 0, scratch_bytes = 0;
   // bf16: the first operands of the weight-gradient products, kept per layer
   // until the products run together at the end of the backward: dRbS[2l+1]
@@ -341,6 +344,8 @@ Layout build_layout(const gpt2_config& c) {
   y.attnD = s.take(attention_bwd_scratch(1, (int)rows, H));
   y.seg = s.take(rows * 4);  // document starts of packed windows
   y.embws = s.take(embed_bwd_scratch((int)rows));  // sort of the embedding gradient
+  if (ln_bwd_part_blocks((int)rows, (int)C) > 0 && 2 * L + 1 <= kLnGradSites)
+    y.lnpart = s.take((size_t)(2 * L + 1) * ln_bwd_part_blocks((int)rows, (int)C) * 2 * C * 4);
   if (c.arch == GPT2_ARCH_ROTARY) y.rope = s.take((size_t)c.block_size * 32 * sizeof(float2));
   if (c.precision == GPT2_PRECISION_BF16) {
     for (int l = 0; l < 2 * L; ++l) y.dRbS.push_back(s.take(rows * C * 2));
@@ -696,10 +701,23 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     }
     return linear_dw(c, site, dy, M, N, x, K, wi, bi, dy_f32);
   };
+  // the norm sites' weight gradients: each backward leaves its blocks'
+  // column partials (site 2L: the final norm, 2l + 1 / 2l: layer l's second
+  // / first), summed in block order after the loop, so they do not depend on
+  // scheduling (no partial buffer: atomics)
+  const int lnb = y.lnpart ? ln_bwd_part_blocks(M, C) : 0;
+  LnGradSites lns{};
+  auto lnp = [&](int site, float* dw, float* db) -> float* {
+    if (!lnb) return nullptr;
+    lns.dw[site] = dw;
+    lns.db[site] = db;
+    return c->scr<float>(y.lnpart) + (size_t)site * lnb * 2 * C;
+  };
   HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
   HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dZ, 0, rlast, c->act<float>(y.meanf), c->act<float>(y.rstdf),
                                  c->P(c->tab.lnf_w), dR, dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w),
-                                 c->Gr(c->tab.lnf_b), M, C));
+                                 c->Gr(c->tab.lnf_b), M, C,
+                                 lnp(2 * g.n_layer, c->Gr(c->tab.lnf_w), c->Gr(c->tab.lnf_b))));
   void* dY = c->scr(y.dY);
   for (int l = g.n_layer - 1; l >= 0; --l) {
     const void* dRm = bf ? static_cast<const void*>(dRb_slot(2 * l + 1)) : static_cast<const void*>(dR);
@@ -714,7 +732,8 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     HIP_TRY(linear_dx(c, "gemm.fc_dx", dU, M, F, c->L(l, FC_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, bf, c->act<float>(y.Rmid[l]), c->act<float>(y.mean2[l]),
                                    c->act<float>(y.rstd2[l]), c->P(c->L(l, LN2_W)), dR, dRb_slot(2 * l),
-                                   c->Gr(c->L(l, LN2_W)), c->Gr(c->L(l, LN2_B)), M, C));
+                                   c->Gr(c->L(l, LN2_W)), c->Gr(c->L(l, LN2_B)), M, C,
+                                   lnp(2 * l + 1, c->Gr(c->L(l, LN2_W)), c->Gr(c->L(l, LN2_B)))));
     // attention branch: Rmid = R_l + Y Wo^T + b
     HIP_TRY(dw("gemm.attn_proj_dw", dRa, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), c->L(l, PROJ_B), dR));
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
@@ -725,8 +744,10 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, 3 * C, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dA, bf, c->act<float>(y.Rin[l]), c->act<float>(y.mean1[l]),
                                    c->act<float>(y.rstd1[l]), c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1),
-                                   c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)), M, C));
+                                   c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)), M, C,
+                                   lnp(2 * l, c->Gr(c->L(l, LN1_W)), c->Gr(c->L(l, LN1_B)))));
   }
+  if (lnb) HIP_TRY(launch_ln_param_grad(c->at("ln.bwd"), c->scr<float>(y.lnpart), M, C, lns, 2 * g.n_layer + 1));
   if (bf) HIP_TRY(run_dw(c, q, M));
   // (dA, free after the last block, holds the scatter's partial sums)
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), c->Gr(c->tab.wpe), B, T, C, V, seg,
@@ -813,9 +834,22 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
   auto dRb_slot = [&](int s) -> bf16* { return s >= 0 ? c->scr<bf16>(y.dRbS[s]) : nullptr; };
   void* dA = c->scr(y.dA);  // dZ (float32) first, then bf16 norm-output gradients
   void* dY = c->scr(y.dY);
+  // the norm sites' weight gradients: each backward leaves its blocks'
+  // column partials (site 2L: the final norm, 2l + 1 / 2l: layer l's second
+  // / first), summed in block order after the loop, so they do not depend on
+  // scheduling (no partial buffer: atomics)
+  const int lnb = y.lnpart ? ln_bwd_part_blocks(M, C) : 0;
+  LnGradSites lns{};
+  auto lnp = [&](int site, float* dw, float* db) -> float* {
+    if (!lnb) return nullptr;
+    lns.dw[site] = dw;
+    lns.db[site] = db;
+    return c->scr<float>(y.lnpart) + (size_t)site * lnb * 2 * C;
+  };
   HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
   HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dZ, 0, rlast, c->act<float>(y.rstdf), c->P(c->tab.lnf_w), dR,
-                             dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w), M, C));
+                             dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w), M, C,
+                             lnp(2 * g.n_layer, c->Gr(c->tab.lnf_w), nullptr)));
   for (int l = g.n_layer - 1; l >= 0; --l) {
     bf16* dRm = dRb_slot(2 * l + 1);
     bf16* dRa = dRb_slot(2 * l);
@@ -835,7 +869,8 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     queue_dw(c, q, dGU, M, 2 * F, c->act(y.A2[l]), C, c->L(l, FC_W), -1);
     HIP_TRY(linear_dx(c, "gemm.fc_dx", dGU, M, 2 * F, c->L(l, FC_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rmid[l]), c->act<float>(y.rstd2[l]),
-                               c->P(c->L(l, LN2_W)), dR, dRa, c->Gr(c->L(l, LN2_W)), M, C));
+                               c->P(c->L(l, LN2_W)), dR, dRa, c->Gr(c->L(l, LN2_W)), M, C,
+                               lnp(2 * l + 1, c->Gr(c->L(l, LN2_W)), nullptr)));
     // attention: Rmid = R_l + Y Wo^T
     queue_dw(c, q, dRa, M, C, c->act(y.Y[l]), C, c->L(l, PROJ_W), -1);
     HIP_TRY(linear_dx(c, "gemm.attn_proj_dx", dRa, M, C, c->L(l, PROJ_W), C, GPT2_EPI_STORE, true, dY, nullptr));
@@ -844,8 +879,10 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     queue_dw(c, q, dQKV, M, NQKV, c->act(y.A1[l]), C, c->L(l, QKV_W), -1);
     HIP_TRY(linear_dx(c, "gemm.qkv_dx", dQKV, M, NQKV, c->L(l, QKV_W), C, GPT2_EPI_STORE, true, dA, nullptr));
     HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dA, 1, c->act<float>(y.Rin[l]), c->act<float>(y.rstd1[l]),
-                               c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C));
+                               c->P(c->L(l, LN1_W)), dR, dRb_slot(2 * l - 1), c->Gr(c->L(l, LN1_W)), M, C,
+                               lnp(2 * l, c->Gr(c->L(l, LN1_W)), nullptr)));
   }
+  if (lnb) HIP_TRY(launch_ln_param_grad(c->at("norm.bwd"), c->scr<float>(y.lnpart), M, C, lns, 2 * g.n_layer + 1));
   HIP_TRY(run_dw(c, q, M));
   HIP_TRY(launch_embed_bwd(c->at("embed.bwd"), tok, dR, c->Gr(c->tab.wte), nullptr, B, T, C, V, seg,
                            static_cast<float*>(dA), c->scr(y.embws)));

@@ -424,9 +424,10 @@ int gpt2_op_gemm(void* stream, const gpt2_gemm_args* args);
  * pointers, or NULL; entries may be NULL) receive row_sum_i[m] +=
  * alpha_i * sum_k A_i(m, k) (the bias gradient).  One block per 256x256
  * output tile; when the tiles leave a partial last round of blocks, the
- * products at the end of the list are split in K into two halves that add
- * their partial sums atomically, every other tile is computed whole and
- * added once.  The n outputs must not overlap.  d_workspace: device memory of
+ * products at the end of the list may be split in K into four (or two)
+ * pieces that add their partial sums atomically, where a list-scheduling
+ * estimate says that shortens the launch (pieces keep at least 16 K steps
+ * of 64); every other tile is computed whole and added once.  The n outputs must not overlap.  d_workspace: device memory of
  * gpt2_gemm_grouped_workspace_bytes(args, n) bytes (16-byte aligned) that
  * receives the group table; the call copies it there synchronously (it
  * blocks until the copy is done), then launches on the stream.

@@ -249,7 +249,9 @@ def test_full_embedding_gradients_are_deterministic(g, full):
     is run again: the Zipf stream repeats ids hundreds of times among the
     16,384 rows, and each wte row sums its token's rows in row order (no
     atomics); with the document mask the restarted positions scatter into
-    wpe the same way."""
+    wpe the same way.  So are the 25 LayerNorms' weight and bias gradients
+    (every block of a norm backward leaves its column partials, summed in
+    block order)."""
     cfg, m, stream = full
     x, y = synthetic.micro_batch(stream, 0, 16, 1024)
     counts = np.bincount(x.reshape(-1))
@@ -262,9 +264,13 @@ def test_full_embedding_gradients_are_deterministic(g, full):
             m.zero_grad()
             run_gpu(g, m, x, y)
             gr = read_named(m, m.grads)
-            runs.append((gr["transformer.wte.weight"].copy(), gr["transformer.wpe.weight"].copy()))
+            norms = {k: v.copy() for k, v in gr.items() if ".ln_" in k}
+            runs.append((gr["transformer.wte.weight"].copy(), gr["transformer.wpe.weight"].copy(), norms))
         assert np.array_equal(runs[0][0], runs[1][0]), eot
         assert np.array_equal(runs[0][1], runs[1][1]), eot
+        assert len(runs[0][2]) == 50
+        for k in runs[0][2]:
+            assert np.array_equal(runs[0][2][k], runs[1][2][k]), (eot, k)
     m.set_doc_mask(None)
     m.zero_grad()
 

@@ -116,14 +116,15 @@ hipError_t launch_colsum(const Launch& L, const void* y, int y_bf16, int M, int 
 
 hipError_t launch_layernorm_fwd(const Launch& L, const float* x, const float* w, const float* b, void* y,
                                 int y_bf16, float* mean, float* rstd, int rows, int C);
-// dx is added into `dx`; when dxb is non-null it also receives bf16(dx_new).
+// dx is added into `dx` (accumulate = 0: written, `dx` not read); when dxb is
+// non-null it also receives bf16(dx_new).
 // dw / db are added into with atomics, or, when `part` is non-null, each of
 // ln_bwd_part_blocks(rows, C) blocks stores its row of 2C column partials
 // there (dw then db) for launch_ln_param_grad to sum; 0 blocks: no such mode.
 int ln_bwd_part_blocks(int rows, int C);
 hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* mean,
                                   const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
-                                  int rows, int C, float* part = nullptr);
+                                  int rows, int C, float* part = nullptr, int accumulate = 1);
 // The weight (and bias) gradients of up to kLnGradSites norm sites from their
 // partial rows: site s's rows start at part + s * blocks * 2C; db[s] may be
 // null (RMSNorm).
@@ -143,7 +144,7 @@ hipError_t launch_rope_bwd(const Launch& L, bf16* dqkv, int rows, int64_t ld, in
 hipError_t launch_rmsnorm_fwd(const Launch& L, const float* x, const float* w, bf16* y, float* rstd, int rows, int C);
 hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* rstd,
                               const float* w, float* dx, bf16* dxb, float* dw, int rows, int C,
-                              float* part = nullptr);
+                              float* part = nullptr, int accumulate = 1);
 
 // seg: [B, T] document starts of packed windows (nullptr: plain causal).
 // Hkv key/value heads (H % Hkv == 0); qkv rows [H q | Hkv k | Hkv v] heads.

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const DYT* __restrict__ dy,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
                                                      const float* __restrict__ w, float* __restrict__ dR,
                                                      bf16* __restrict__ dRb, float* __restrict__ dw,
-                                                     float* __restrict__ db, int rows, int C) {
+                                                     float* __restrict__ db, int rows, int C, int acc) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   constexpr int NV = LN_MAXV;  // values per lane
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const DYT* __restrict__ dy,
     for (int j = 0; j < NV; ++j) {
       const int c = lane + 64 * j;
       if (c < C) {
-        const float nv = dr[c] + rs * (g[j] - sg - xh[j] * sgx);
+        const float nv = (acc ? dr[c] : 0.f) + rs * (g[j] - sg - xh[j] * sgx);
         dr[c] = nv;
         if (dRb) dRb[(int64_t)row * C + c] = f2bf(nv);
       }
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(64 * WPB) void ln_bwd_vec_kernel(const DYT* __restr
                                                          const float* __restrict__ w, float* __restrict__ dR,
                                                          bf16* __restrict__ dRb, float* __restrict__ dw,
                                                          float* __restrict__ db, float* __restrict__ part, int rows,
-                                                         int C) {
+                                                         int C, int acc) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   float4 wr[NQ], gw[NQ], gb[NQ];
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64 * WPB) void ln_bwd_vec_kernel(const DYT* __restr
     for (int q = 0; q < NQ; ++q) {
       d_[q] = load4<DYT>(dy + o + 256 * q);
       x_[q] = *reinterpret_cast<const float4*>(x + o + 256 * q);
-      r_[q] = *reinterpret_cast<const float4*>(dR + o + 256 * q);
+      r_[q] = acc ? *reinterpret_cast<const float4*>(dR + o + 256 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     mu_ = RMS ? 0.f : mean[row];
     rs_ = rstd[row];
@@ -351,7 +351,7 @@ int ln_bwd_part_blocks(int rows, int C) {
 template <typename DYT, bool RMS>
 static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const float* mean, const float* rstd,
                             const float* w, float* dx, bf16* dxb, float* dw, float* db, float* part, int rows,
-                            int C) {
+                            int C, int acc) {
   if (C % 256 == 0) {
     // 8 rows per wave, 8 waves per block (one block per compute unit at
     // 16,384 rows): the next row's loads in flight keep HBM busy, and the
@@ -363,29 +363,29 @@ static void ln_bwd_dispatch(hipStream_t st, const DYT* dy, const float* x, const
     static_assert(RPW * WPB == kLnBwdRows, "rows per block");
     const dim3 grid((rows + WPB * RPW - 1) / (WPB * RPW));
     switch (C / 256) {
-      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
-      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
-      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
-      default: ln_bwd_vec_kernel<DYT, 4, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C); break;
+      case 1: ln_bwd_vec_kernel<DYT, 1, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C, acc); break;
+      case 2: ln_bwd_vec_kernel<DYT, 2, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C, acc); break;
+      case 3: ln_bwd_vec_kernel<DYT, 3, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C, acc); break;
+      default: ln_bwd_vec_kernel<DYT, 4, RPW, WPB, RMS><<<grid, 64 * WPB, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, part, rows, C, acc); break;
     }
   } else if constexpr (!RMS) {
     constexpr int RPW = 4;
     const dim3 grid((rows + 4 * RPW - 1) / (4 * RPW));
-    ln_bwd_kernel<DYT, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C);
+    ln_bwd_kernel<DYT, RPW><<<grid, 256, 0, st>>>(dy, x, mean, rstd, w, dx, dxb, dw, db, rows, C, acc);
   }
 }
 
 hipError_t launch_layernorm_bwd_b(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* mean,
                                   const float* rstd, const float* w, float* dx, bf16* dxb, float* dw, float* db,
-                                  int rows, int C, float* part) {
+                                  int rows, int C, float* part, int accumulate) {
   if (part && ln_bwd_part_blocks(rows, C) == 0) return hipErrorInvalidValue;
   prof_begin(L);
   if (dy_bf16)
     ln_bwd_dispatch<bf16, false>(L.stream, static_cast<const bf16*>(dy), x, mean, rstd, w, dx, dxb, dw, db, part,
-                                 rows, C);
+                                 rows, C, accumulate);
   else
     ln_bwd_dispatch<float, false>(L.stream, static_cast<const float*>(dy), x, mean, rstd, w, dx, dxb, dw, db, part,
-                                  rows, C);
+                                  rows, C, accumulate);
   prof_end(L);
   return hipGetLastError();
 }
@@ -406,15 +406,16 @@ hipError_t launch_rmsnorm_fwd(const Launch& L, const float* x, const float* w, b
 }
 
 hipError_t launch_rmsnorm_bwd(const Launch& L, const void* dy, int dy_bf16, const float* x, const float* rstd,
-                              const float* w, float* dx, bf16* dxb, float* dw, int rows, int C, float* part) {
+                              const float* w, float* dx, bf16* dxb, float* dw, int rows, int C, float* part,
+                              int accumulate) {
   if (C % 256 != 0 || C > 1024) return hipErrorInvalidValue;
   prof_begin(L);
   if (dy_bf16)
     ln_bwd_dispatch<bf16, true>(L.stream, static_cast<const bf16*>(dy), x, nullptr, rstd, w, dx, dxb, dw, nullptr,
-                                part, rows, C);
+                                part, rows, C, accumulate);
   else
     ln_bwd_dispatch<float, true>(L.stream, static_cast<const float*>(dy), x, nullptr, rstd, w, dx, dxb, dw, nullptr,
-                                 part, rows, C);
+                                 part, rows, C, accumulate);
   prof_end(L);
   return hipGetLastError();
 }

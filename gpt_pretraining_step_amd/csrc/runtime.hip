@@ -713,11 +713,11 @@ static int fwd_bwd_impl(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, int
     lns.db[site] = db;
     return c->scr<float>(y.lnpart) + (size_t)site * lnb * 2 * C;
   };
-  HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
+  // the final norm's backward writes dR (its first value) rather than adding to it
   HIP_TRY(launch_layernorm_bwd_b(c->at("ln.bwd"), dZ, 0, rlast, c->act<float>(y.meanf), c->act<float>(y.rstdf),
                                  c->P(c->tab.lnf_w), dR, dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w),
                                  c->Gr(c->tab.lnf_b), M, C,
-                                 lnp(2 * g.n_layer, c->Gr(c->tab.lnf_w), c->Gr(c->tab.lnf_b))));
+                                 lnp(2 * g.n_layer, c->Gr(c->tab.lnf_w), c->Gr(c->tab.lnf_b)), 0));
   void* dY = c->scr(y.dY);
   for (int l = g.n_layer - 1; l >= 0; --l) {
     const void* dRm = bf ? static_cast<const void*>(dRb_slot(2 * l + 1)) : static_cast<const void*>(dR);
@@ -846,10 +846,10 @@ static int fwd_bwd_rotary(gpt2_ctx* c, const int32_t* tok, const int32_t* tgt, i
     lns.db[site] = db;
     return c->scr<float>(y.lnpart) + (size_t)site * lnb * 2 * C;
   };
-  HIP_TRY(launch_fill_f32(c->at("fill"), dR, (size_t)M * C, 0.f));
+  // the final norm's backward writes dR (its first value) rather than adding to it
   HIP_TRY(launch_rmsnorm_bwd(c->at("norm.bwd"), dZ, 0, rlast, c->act<float>(y.rstdf), c->P(c->tab.lnf_w), dR,
                              dRb_slot(2 * g.n_layer - 1), c->Gr(c->tab.lnf_w), M, C,
-                             lnp(2 * g.n_layer, c->Gr(c->tab.lnf_w), nullptr)));
+                             lnp(2 * g.n_layer, c->Gr(c->tab.lnf_w), nullptr), 0));
   for (int l = g.n_layer - 1; l >= 0; --l) {
     bf16* dRm = dRb_slot(2 * l + 1);
     bf16* dRa = dRb_slot(2 * l);

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 }
 
 // dx = rstd (g - mean(g) - xhat mean(g xhat)), g = dy w; dx is added into
-// dR; optionally dRb = bf16(dR) for the bf16 products that consume it.  The
+// dR (acc = 1) or written there without reading it (acc = 0); optionally
+// dRb = bf16(dR) for the bf16 products that consume it.  The
 // weight and bias gradients are summed over the block's rows in registers,
 // then added with one atomic per column per block.  Any C <= 1024: one
 // column per lane (c = lane + 64 j); dy is float32 or bf16.
@@ -209,7 +210,8 @@ __device__ __forceinline__ float4 load4<bf16>(const bf16* p) {
 
 // Backward over RPW consecutive rows per wave, WPB waves per block; the
 // next row's dy, x and dR are loaded before the current row is reduced, so
-// each wave keeps two rows of loads in flight.  dy is float32 or bf16.
+// each wave keeps two rows of loads in flight (dR only with acc = 1: with
+// acc = 0 the branch is written to dR, not added).  dy is float32 or bf16.
 // RMS: the RMSNorm backward, dx = rstd (g - xhat mean(g xhat)) (no
 // centring term), no db.
 template <typename DYT, int NQ, int RPW, int WPB, bool RMS>

@@ -264,6 +264,31 @@ def test_rotary_small_step_parity(g):
             assert c >= 0.999, (k, c)
 
 
+def test_rotary_norm_gradients_are_reproducible(g):
+    """The RMSNorm weight gradients (5 norms, no bias) come from per-block
+    column partials summed in block order: a rerun of the same micro-step
+    gives the same bits."""
+    import torch
+    cfg = g.ModelConfig(**SMALL, max_batch=3, precision=g.PRECISION_BF16, arch=g.ARCH_ROTARY)
+    announce("rotary norm gradient reproducibility B=3 T=256")
+    m = g.GPT2(cfg)
+    load_params(m, synthetic.random_params(MM.param_specs(ocfg(cfg)), seed=5))
+    rng = np.random.default_rng(1)
+    x = rng.integers(0, cfg.vocab_size, size=(3, 256)).astype(np.int32)
+    y = rng.integers(0, cfg.vocab_size, size=(3, 256)).astype(np.int32)
+    runs = []
+    for _ in range(2):
+        m.zero_grad()
+        m.fwd_bwd(dev(x), dev(y), loss_scale=1.0)
+        torch.cuda.synchronize()
+        gr = read_named(m, m.grads)
+        runs.append({k: v.copy() for k, v in gr.items() if "norm" in k or ".ln_" in k})
+    assert len(runs[0]) == 2 * cfg.n_layer + 1, sorted(runs[0])
+    for k in runs[0]:
+        assert np.array_equal(runs[0][k], runs[1][k]), k
+    m.close()
+
+
 @pytest.mark.timeout(600)
 def test_rotary_124m_step_parity_b1(g):
     """The variant at its real width, one sequence of 1024 tokens: loss and
